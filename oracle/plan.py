@@ -1,0 +1,339 @@
+"""Token-prefix tree, staged submission rounds and KV page assignment.
+
+Test infrastructure only (see the package docstring).  An independent Python
+statement of the planner that the host library implements in C++; the two
+must agree bit for bit.
+
+Source: LLM2Jev shared-prefix page.  Its "why is the same material computed
+several times" section describes candidates that share a state, then a
+question's instructions, then differ in one criterion; its staged-submission
+section builds a shared prefix first and submits the candidates that reuse it
+in later rounds, with independent branches sharing a round and the number of
+rounds following the token tree; its Radix Cache section says reuse is keyed
+on the exact token prefix and that each candidate's last scored position is
+always computed.  Page size 16 tokens.
+
+Readings (the pages leave these open; listed in the design doc):
+
+* Trie: compressed, token-granular, over each candidate's tokens after its
+  resident match.  A node is a maximal token run shared by the same set of
+  candidates.
+* Dissolution: top-down, a node that has children, where no candidate ends,
+  and whose own run is shorter than one page, is removed; its tokens are
+  prepended to each child.  Short accidental common runs therefore never add a
+  round.
+* Rounds: level-synchronous by depth under the anchor (round k computes every
+  new node at depth k).
+* Canonical order: (depth, smallest candidate index through the node); node
+  ids are ranks in that order.
+* Pages: free ids in a min-heap; each new node takes ceil(len/16) lowest ids at
+  its round, in canonical order; every node starts on a fresh page.  Nodes
+  without children are released when their round ends, the plan's internal
+  nodes when the call ends.
+* Resident match: walk resident nodes from the root, taking the longest child
+  segment that matches in full and still leaves at least one token (the last
+  scored position must be computed).
+"""
+from __future__ import annotations
+
+import heapq
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence, Tuple
+
+PAGE = 16
+
+
+def n_pages_for(n_tokens: int) -> int:
+    return (n_tokens + PAGE - 1) // PAGE
+
+
+class PoolExhausted(Exception):
+    pass
+
+
+class PagePool:
+    def __init__(self, n_pages: int):
+        self.n_pages = n_pages
+        self.free = list(range(n_pages))
+        heapq.heapify(self.free)
+
+    def alloc(self, n: int) -> List[int]:
+        if n > len(self.free):
+            raise PoolExhausted(n)
+        return [heapq.heappop(self.free) for _ in range(n)]
+
+    def release(self, pages: Sequence[int]) -> None:
+        for p in pages:
+            heapq.heappush(self.free, p)
+
+    def n_free(self) -> int:
+        return len(self.free)
+
+
+@dataclass
+class ResNode:
+    handle: int
+    parent: int            # 0 = empty root
+    tokens: Tuple[int, ...]
+    pages: List[int]
+    start: int             # logical position of the first token
+    refs: int = 1
+    children: List[int] = field(default_factory=list)   # handles, creation order
+
+
+class ResidentTree:
+    """Resident prefixes, each owning its pages; handles are creation serials."""
+
+    def __init__(self, pool: PagePool):
+        self.pool = pool
+        self.nodes: Dict[int, ResNode] = {}
+        self.root_children: List[int] = []
+        self.next_handle = 1
+
+    def _children(self, parent: int) -> List[int]:
+        return self.root_children if parent == 0 else self.nodes[parent].children
+
+    def end_pos(self, h: int) -> int:
+        if h == 0:
+            return 0
+        n = self.nodes[h]
+        return n.start + len(n.tokens)
+
+    def path_pages(self, h: int) -> List[Tuple[int, int]]:
+        """(page id, valid tokens) of every page on the path root..h."""
+        chain = []
+        while h != 0:
+            chain.append(self.nodes[h])
+            h = self.nodes[h].parent
+        out = []
+        for n in reversed(chain):
+            L = len(n.tokens)
+            for i, p in enumerate(n.pages):
+                out.append((p, min(PAGE, L - PAGE * i)))
+        return out
+
+    def prefill(self, items: Sequence[Tuple[int, Sequence[int]]]) -> List[int]:
+        """Creates (or re-references) one node per (parent, tokens), in order.
+
+        All-or-nothing: raises PoolExhausted before any change if the new
+        nodes do not fit.  An existing child with the identical segment is
+        re-used (one more reference, no pages)."""
+        need, seen = 0, set()
+        for parent, toks in items:
+            if parent != 0 and parent not in self.nodes:
+                raise KeyError(parent)
+            key = (parent, tuple(int(t) for t in toks))
+            if self._find_child(parent, key[1]) is None and key not in seen:
+                seen.add(key)
+                need += n_pages_for(len(toks))
+        if need > self.pool.n_free():
+            raise PoolExhausted(need)
+        out = []
+        for parent, toks in items:
+            toks = tuple(int(t) for t in toks)
+            h = self._find_child(parent, toks)
+            if h is not None:
+                self.nodes[h].refs += 1
+                out.append(h)
+                continue
+            h = self.next_handle
+            self.next_handle += 1
+            self.nodes[h] = ResNode(h, parent, toks, self.pool.alloc(n_pages_for(len(toks))),
+                                    self.end_pos(parent))
+            self._children(parent).append(h)
+            out.append(h)
+        return out
+
+    def _find_child(self, parent: int, toks: Tuple[int, ...]) -> Optional[int]:
+        for c in self._children(parent):
+            if self.nodes[c].tokens == toks:
+                return c
+        return None
+
+    def release(self, h: int) -> None:
+        """Drops one caller reference; frees nodes left with no reference and no child."""
+        n = self.nodes[h]
+        n.refs -= 1
+        while n is not None and n.refs == 0 and not n.children:
+            self.pool.release(n.pages)
+            del self.nodes[n.handle]
+            sib = self._children(n.parent)
+            sib.remove(n.handle)
+            n = self.nodes.get(n.parent)
+
+    def match(self, seq: Sequence[int]) -> Tuple[int, int]:
+        """Deepest resident node whose whole path is a prefix of seq with at
+        least one token of seq left over; returns (handle, matched length)."""
+        h, pos = 0, 0
+        seq = [int(t) for t in seq]
+        while True:
+            best = None
+            for c in self._children(h):
+                t = self.nodes[c].tokens
+                if pos + len(t) < len(seq) and tuple(seq[pos:pos + len(t)]) == t:
+                    if best is None or len(t) > len(self.nodes[best].tokens):
+                        best = c
+            if best is None:
+                return h, pos
+            h, pos = best, pos + len(self.nodes[best].tokens)
+
+
+@dataclass
+class PlanNode:
+    cands: List[int]          # candidate indices through this node (sorted)
+    a: int                    # segment [a, b) relative to the anchor
+    b: int
+    anchor: int
+    readout: List[int] = field(default_factory=list)
+    children: List["PlanNode"] = field(default_factory=list)
+    parent: Optional["PlanNode"] = None
+    depth: int = 0
+    node_id: int = -1
+    pages: List[int] = field(default_factory=list)
+
+    @property
+    def cand_min(self) -> int:
+        return self.cands[0]
+
+
+def _build(cands: List[int], a: int, rel: Dict[int, List[int]], anchor: int) -> List[PlanNode]:
+    groups: Dict[int, List[int]] = {}
+    order: List[int] = []
+    for c in cands:
+        if len(rel[c]) == a:
+            continue
+        t = rel[c][a]
+        if t not in groups:
+            groups[t] = []
+            order.append(t)
+        groups[t].append(c)
+    out = []
+    for t in order:
+        part = groups[t]
+        b = a + 1
+        while all(len(rel[c]) > b for c in part) and len({rel[c][b] for c in part}) == 1:
+            b += 1
+        node = PlanNode(part, a, b, anchor, readout=[c for c in part if len(rel[c]) == b])
+        node.children = _build([c for c in part if len(rel[c]) > b], b, rel, anchor)
+        out.append(node)
+    return out
+
+
+def _dissolve(nodes: List[PlanNode]) -> List[PlanNode]:
+    out: List[PlanNode] = []
+    queue = list(nodes)
+    while queue:
+        n = queue.pop(0)
+        if n.children and not n.readout and (n.b - n.a) < PAGE:
+            for ch in n.children:
+                ch.a = n.a
+            queue = n.children + queue
+            continue
+        out.append(n)
+    out.sort(key=lambda x: x.cand_min)
+    for n in out:
+        n.children = _dissolve(n.children)
+    return out
+
+
+@dataclass
+class Plan:
+    rounds: List[List[PlanNode]]
+    anchors: List[int]            # per candidate: resident handle it continues
+    anchor_len: List[int]         # per candidate: tokens matched in the resident tree
+    readout_node: List[int]       # per candidate: node id it is read out at
+    released_after_round: List[List[int]]
+
+    def serialize(self) -> List[int]:
+        """Flat int32 image compared bit for bit with the host library."""
+        out = [len(self.rounds)]
+        for rnd in self.rounds:
+            out.append(len(rnd))
+            for n in rnd:
+                out += [n.node_id, n.parent.node_id if n.parent else -1, n.anchor, n.depth,
+                        n.cand_min, n.a, n.b - n.a, len(n.pages)] + n.pages
+                out += [len(n.readout)] + n.readout
+        out.append(len(self.readout_node))
+        for c in range(len(self.readout_node)):
+            out += [self.anchors[c], self.anchor_len[c], self.readout_node[c]]
+        return out
+
+
+def plan_candidates(tree: ResidentTree, seqs: Sequence[Sequence[int]]) -> Plan:
+    """Plans the staged rounds of a call and assigns pages (all-or-nothing).
+
+    Pages of nodes without children are returned to the pool at the end of
+    their round, the rest at the end of the plan (i.e. this function leaves
+    the pool as it found it once the plan has run; the caller replays that
+    with ``release_plan``)."""
+    n = len(seqs)
+    anchors, alen, rel = [], [], {}
+    for c, s in enumerate(seqs):
+        h, m = tree.match(s)
+        anchors.append(h)
+        alen.append(m)
+        rel[c] = [int(t) for t in s[m:]]
+    by_anchor: Dict[int, List[int]] = {}
+    for c in range(n):
+        by_anchor.setdefault(anchors[c], []).append(c)
+    tops: List[PlanNode] = []
+    for h, cs in by_anchor.items():
+        tops += _dissolve(_build(cs, 0, rel, h))
+    # depth levels
+    levels: List[List[PlanNode]] = []
+    frontier = sorted(tops, key=lambda x: x.cand_min)
+    d = 1
+    while frontier:
+        for x in frontier:
+            x.depth = d
+        levels.append(sorted(frontier, key=lambda x: x.cand_min))
+        nxt = []
+        for x in frontier:
+            for ch in x.children:
+                ch.parent = x
+                nxt.append(ch)
+        frontier = nxt
+        d += 1
+    nid = 0
+    for lvl in levels:
+        for x in lvl:
+            x.node_id = nid
+            nid += 1
+    # page assignment with a dry run first (all-or-nothing)
+    free_snapshot = list(tree.pool.free)
+    released: List[List[int]] = []
+    try:
+        for lvl in levels:
+            for x in lvl:
+                x.pages = tree.pool.alloc(n_pages_for(x.b - x.a))
+            rel_ids = [x.node_id for x in lvl if not x.children]
+            for x in lvl:
+                if not x.children:
+                    tree.pool.release(x.pages)
+            released.append(rel_ids)
+        for lvl in levels:
+            for x in lvl:
+                if x.children:
+                    tree.pool.release(x.pages)
+    except PoolExhausted:
+        tree.pool.free = free_snapshot
+        raise
+    readout_node = [-1] * n
+    for lvl in levels:
+        for x in lvl:
+            for c in x.readout:
+                readout_node[c] = x.node_id
+    return Plan(levels, anchors, alen, readout_node, released)
+
+
+def branch_pages(tree: ResidentTree, parents: Sequence[int],
+                 suffixes: Sequence[Sequence[int]]) -> List[List[int]]:
+    """Pages of one explicit scoring call: each branch is a new leaf under its
+    parent, allocated in input order and released when the call ends."""
+    need = sum(n_pages_for(len(s)) for s in suffixes)
+    if need > tree.pool.n_free():
+        raise PoolExhausted(need)
+    out = [tree.pool.alloc(n_pages_for(len(s))) for s in suffixes]
+    for p in out:
+        tree.pool.release(p)
+    return out
