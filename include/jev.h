@@ -1,0 +1,205 @@
+/*
+ * jev.h -- C ABI of the shared-prefix, prefill-only branch scorer (MI355X, gfx950).
+ *
+ * The method (jdon.com openjev-sglang article, "inference flow" and
+ * "prefill-only" sections; LLM2Jev shared-prefix page): a shared token prefix is
+ * prefilled once into a paged KV cache; every branch (question / candidate)
+ * continues from that prefix and computes only its own suffix tokens, attending
+ * to the cached prefix pages plus its own causal suffix; only the last
+ * position's logits at the requested candidate label ids are read and they are
+ * renormalised with a max-subtracted softmax over the labels.  No token is
+ * decoded.  Candidate sets given as full sequences are grouped by token prefix
+ * and submitted in staged rounds (LLM2Jev shared-prefix page, staged-submission
+ * section), each candidate scored exactly once and returned in input order.
+ *
+ * Conventions for every entry point:
+ *  - Return value: JEV_OK (0) or a JEV_E* status.  jev_last_error() returns a
+ *    thread-local message for the last failure of the calling thread.
+ *  - Everything is validated before any device work is queued; a call that
+ *    fails leaves the context unchanged (no pages taken, no handle created),
+ *    except JEV_EHIP, after which the context is unusable (every later call
+ *    returns JEV_EHIP).
+ *  - Host arrays (tokens, offsets, labels, parents, handles) are read during
+ *    the call only; the library keeps its own copies.
+ *  - Device work is queued on the given HIP stream (NULL = default stream) and
+ *    is asynchronous: device outputs are valid once that stream has reached
+ *    the end of the call.  Calls on one context must not overlap (the context
+ *    is not thread-safe); a call on a different stream than the previous one is
+ *    ordered after the previous call's device work by the library.
+ *  - Device buffers (weights, KV pool, workspace, outputs) are owned by the
+ *    caller and must outlive the context.  The library owns only host state.
+ */
+#ifndef JEV_H
+#define JEV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  JEV_OK = 0,
+  JEV_EINVAL = 1,  /* bad argument: shapes, ids, offsets, label count, empty suffix */
+  JEV_ENOMEM = 2,  /* not enough free KV pages or workspace for the whole call */
+  JEV_EHANDLE = 3, /* unknown or already released prefix handle */
+  JEV_EHIP = 4,    /* a HIP call failed; the context is dead */
+  JEV_ESTATE = 5   /* operation not available on this context (e.g. device work on a planning-only context) */
+};
+
+enum { JEV_DTYPE_F32 = 0, JEV_DTYPE_BF16 = 1 };
+
+/* Tokens per KV page. */
+#define JEV_PAGE_TOKENS 16
+/* Label count bounds per branch (jdon.com article, limits section: 2..64 options). */
+#define JEV_MIN_LABELS 2
+#define JEV_MAX_LABELS 64
+
+typedef int64_t jev_prefix; /* resident prefix handle; 0 = the empty prefix */
+typedef struct jev_ctx jev_ctx;
+
+/* Model shape.  Attention-only pre-norm stack:
+ *   x = E[token]; per layer: h = RMSNorm(x) * g_l; q,k,v = h Wq^T, h Wk^T, h Wv^T;
+ *   RoPE(q, k) at the logical position (rotate-half pairs (i, i+dh/2),
+ *   inverse frequency theta^(-2i/dh)); causal attention with KV head
+ *   floor(j / (Hq/Hkv)) for query head j, scale 1/sqrt(dh); x += o Wo^T;
+ *   final: RMSNorm(x) * g_f, logits = . U^T.
+ * bf16 models store activations in bf16 at: norm outputs, q/k after RoPE, v,
+ * attention output, residual stream, final-norm output; accumulation is fp32. */
+typedef struct {
+  int32_t n_layers;
+  int32_t d_model;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;       /* divides n_q_heads; n_q_heads/n_kv_heads divides 128 */
+  int32_t head_dim;         /* 64 or 128 */
+  int32_t vocab;
+  int32_t dtype;            /* JEV_DTYPE_F32 or JEV_DTYPE_BF16: weights, activations, KV pages */
+  float rope_theta;
+  float rms_eps;
+  int32_t max_positions;    /* longest sequence (prefix + suffix) the context will see */
+  int32_t max_round_tokens; /* most new tokens computed in one round (sizes the activations) */
+} jev_model_desc;
+
+/* Device pointers to the weights, row-major, all of the model's dtype.
+ * Matrices are [out][in]: embed/unembed [vocab][d], wq [Hq*dh][d],
+ * wk/wv [Hkv*dh][d], wo [d][Hq*dh]; norms [d].  The per-layer members are host
+ * arrays of n_layers device pointers (copied at create). */
+typedef struct {
+  const void* embed;
+  const void* unembed;
+  const void* final_norm;
+  const void* const* attn_norm;
+  const void* const* wq;
+  const void* const* wk;
+  const void* const* wv;
+  const void* const* wo;
+} jev_weights;
+
+/* Bytes of device workspace jev_create needs for this model (activations for
+ * max_round_tokens rows, LSE partial states, RoPE table, call descriptors). */
+size_t jev_workspace_bytes(const jev_model_desc* desc);
+
+/* Bytes of a KV pool of n_pages pages.  Layout, per element of the model dtype:
+ * [layer][page][kv_head][K|V][16 * head_dim]; the K block of a page is
+ * [slot][head_dim], the V block is [head_dim][slot] (transposed). */
+size_t jev_kv_pool_bytes(const jev_model_desc* desc, int32_t n_pages);
+
+/* Creates a context.  kv_pool: jev_kv_pool_bytes(desc, n_pages) bytes;
+ * workspace: at least jev_workspace_bytes(desc) bytes, 256-byte aligned.
+ * With weights == NULL, kv_pool == NULL and workspace == NULL the context is a
+ * planning-only context: prefix/plan/page-table calls run on the host and
+ * nothing touches a GPU (scoring calls return JEV_ESTATE).
+ * Errors: JEV_EINVAL (shape), JEV_ENOMEM (workspace too small), JEV_EHIP. */
+int jev_create(const jev_model_desc* desc, const jev_weights* weights, void* kv_pool,
+               int32_t n_pages, void* workspace, size_t workspace_bytes, jev_ctx** out);
+
+/* Waits for the context's queued work and frees its host state. */
+int jev_destroy(jev_ctx* ctx);
+
+/* Prefills n prefixes (the "warm-up" prefill of the N+1 flow: jdon.com article,
+ * N+1 section).  Prefix i continues resident prefix parents[i] (0 = none) with
+ * tokens[offsets[i] .. offsets[i+1]) (host int32, offsets has n+1 entries,
+ * offsets[0] = 0, every segment non-empty, ids in [0, vocab)).  All prefixes
+ * are computed in one round.  A prefix identical to an existing child of the
+ * same parent is not recomputed: its handle is returned with one more
+ * reference.  out_handles[i] receives one caller reference each.
+ * Errors: JEV_EINVAL, JEV_EHANDLE (unknown parent), JEV_ENOMEM (pages or
+ * workspace for the whole call), JEV_EHIP. */
+int jev_prefill_prefix(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const int32_t* tokens,
+                       const int64_t* offsets, jev_prefix* out_handles, void* hip_stream);
+
+/* Scores n branches (jdon.com article, prefill-only section).  Branch i
+ * continues resident prefix parents[i] with suffix tokens[tok_offsets[i] ..
+ * tok_offsets[i+1]) (non-empty: the last scored position is always computed)
+ * and reads the labels label_ids[label_offsets[i] .. label_offsets[i+1])
+ * (host int32, 2..64 distinct ids in [0, vocab)).  probs (device float32,
+ * label_offsets[n] entries) receives, per branch, the softmax over its labels
+ * of the last position's logits, in label order.  Branch KV pages are taken for
+ * the call and released when it ends.  Branches with the same parent share one
+ * pass over the parent's pages.
+ * Errors: JEV_EINVAL, JEV_EHANDLE, JEV_ENOMEM, JEV_EHIP, JEV_ESTATE. */
+int jev_score_branches(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const int32_t* tokens,
+                       const int64_t* tok_offsets, const int32_t* label_ids,
+                       const int64_t* label_offsets, float* probs, void* hip_stream);
+
+/* Scores n candidates given as full token sequences (LLM2Jev shared-prefix page,
+ * staged-submission section).  Each candidate is matched against the resident
+ * prefixes (longest full-node match leaving at least one token), the rest are
+ * grouped into a token-prefix tree and computed in staged rounds by tree depth;
+ * every candidate is read out exactly once; probs as for jev_score_branches, in
+ * input order.  Pages of the call's own tree nodes are released when it ends.
+ * Errors: as jev_score_branches. */
+int jev_score_candidates(jev_ctx* ctx, int32_t n, const int32_t* tokens, const int64_t* tok_offsets,
+                         const int32_t* label_ids, const int64_t* label_offsets, float* probs,
+                         void* hip_stream);
+
+/* Drops one caller reference of each handle.  A prefix with no reference and
+ * no resident child returns its pages to the pool (its parent may follow).
+ * Pages are re-used only by later calls, which the library orders after the
+ * device work that read them.  Errors: JEV_EHANDLE (nothing is released then). */
+int jev_free_pages(jev_ctx* ctx, int32_t n, const jev_prefix* handles);
+
+/* Host-only: the staged-round plan jev_score_candidates would execute now,
+ * serialised as int32 (format in the design doc; identical to the oracle's planner).
+ * out may be NULL to query *out_len.  Errors: JEV_EINVAL, JEV_ENOMEM (pool too
+ * small for the plan; the plan is not returned). */
+int jev_plan(jev_ctx* ctx, int32_t n, const int32_t* tokens, const int64_t* tok_offsets,
+             int32_t* out, int64_t cap, int64_t* out_len);
+
+/* Host-only: page ids and valid token counts of every page on the path from
+ * the root to handle h (root first).  cap = room in page_ids/valid; *n gets the
+ * count (also when cap is too small, with JEV_EINVAL). */
+int jev_page_table(jev_ctx* ctx, jev_prefix h, int32_t* page_ids, int32_t* valid, int32_t cap,
+                   int32_t* n);
+
+/* Host-only: deepest resident prefix whose whole path is a prefix of tokens[0..n)
+ * leaving at least one token; *matched = its length (0 and handle 0 if none). */
+int jev_match(jev_ctx* ctx, const int32_t* tokens, int64_t n, jev_prefix* handle, int64_t* matched);
+
+typedef struct {
+  int64_t logical_tokens;   /* tokens of every scored sequence incl. cached prefix (last call) */
+  int64_t computed_tokens;  /* tokens actually run through the model (last call) */
+  int64_t cached_tokens;    /* logical - computed (last call) */
+  int32_t rounds;           /* rounds of the last call */
+  int32_t pages_in_use;
+  int32_t pages_total;
+  int32_t resident_prefixes;
+  int64_t calls;
+} jev_stats_t;
+
+int jev_stats(jev_ctx* ctx, jev_stats_t* out);
+
+/* Debug tap for parity tests: when set, the next scoring/prefill call copies,
+ * for layer `layer`, the attention output (after the log-sum-exp merge, model
+ * dtype, [round token][Hq*dh] rows of the call's single round, in the call's
+ * token order) into dst (device, cap_rows rows).  NULL dst disables.  The tap
+ * covers single-round calls only. */
+int jev_debug_tap(jev_ctx* ctx, int32_t layer, void* dst, int64_t cap_rows);
+
+const char* jev_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* JEV_H */

@@ -1,0 +1,772 @@
+// C ABI (include/jev.h) and the host engine that turns a call into rounds of
+// kernel launches.
+//
+// A call is planned completely on the host first (validation, page
+// assignment, the descriptors of every round), the descriptors go to the
+// device in one copy, and then each round runs: embedding, per layer
+// [RMSNorm -> QKV GEMM + RoPE + page write -> attention tiles -> LSE merge ->
+// output projection + residual], then the label readout.
+//
+// Attention work of a round (the branch step the pages describe: each branch
+// computes only its own suffix while attending to the cached prefix; LLM2Jev
+// shared-prefix page, Radix Cache section; openjev-multimodal performance page,
+// "what changed" and "next steps" sections, which batch several questions
+// from one checkpoint):
+//  * own part: each node's tokens against its own pages, causal;
+//  * prefix part: all tokens of the sibling nodes that share a parent, packed
+//    together, against the parent's whole page path, unmasked, split into page
+//    chunks; the prefix pages are read once per sibling group and KV head
+//    instead of once per branch;
+//  * a node without a parent writes its output directly; otherwise every part
+//    leaves a normalised partial state and a log2-sum-exp, merged exactly.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <set>
+#include <string>
+#include <vector>
+
+#include "../../../include/jev.h"
+#include "../kernels/launch.hpp"
+#include "tree.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+constexpr int kMaxChunks = 8;   // prefix chunks per sibling group
+constexpr int kRowsPerTile = 128;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct WsLayout {
+  size_t rope, x, h, q, o, part_o, part_lse, desc, total;
+  int64_t part_rows;
+  int64_t desc_ints;
+};
+
+int elt_size(const jev_model_desc& d) { return d.dtype == JEV_DTYPE_BF16 ? 2 : 4; }
+
+WsLayout layout(const jev_model_desc& d) {
+  WsLayout L{};
+  const int64_t T = d.max_round_tokens;
+  const int G = d.n_q_heads / d.n_kv_heads;
+  const int64_t tt = kRowsPerTile / G;
+  const int64_t slots = ((T + tt - 1) / tt + 64) * (kMaxChunks + 1);
+  L.part_rows = slots * kRowsPerTile;
+  L.desc_ints = 32 * T + 4 * int64_t(d.max_positions) + (1 << 18);
+  const size_t e = elt_size(d);
+  size_t off = 0;
+  L.rope = off;
+  off = align256(off + size_t(d.max_positions) * (d.head_dim / 2) * 2 * sizeof(float));
+  L.x = off;
+  off = align256(off + size_t(T) * d.d_model * e);
+  L.h = off;
+  off = align256(off + size_t(T) * d.d_model * e);
+  L.q = off;
+  off = align256(off + size_t(T) * d.n_q_heads * d.head_dim * e);
+  L.o = off;
+  off = align256(off + size_t(T) * d.n_q_heads * d.head_dim * e);
+  L.part_o = off;
+  off = align256(off + size_t(L.part_rows) * d.head_dim * sizeof(float));
+  L.part_lse = off;
+  off = align256(off + size_t(L.part_rows) * sizeof(float));
+  L.desc = off;
+  off = align256(off + size_t(L.desc_ints) * sizeof(int32_t));
+  L.total = off;
+  return L;
+}
+
+bool desc_ok(const jev_model_desc* d, std::string* why) {
+  if (!d) return *why = "desc is NULL", false;
+  if (d->n_layers < 1 || d->d_model < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->vocab < 1)
+    return *why = "non-positive model dimension", false;
+  if (d->n_q_heads % d->n_kv_heads) return *why = "n_kv_heads must divide n_q_heads", false;
+  const int G = d->n_q_heads / d->n_kv_heads;
+  if (G > kRowsPerTile || kRowsPerTile % G) return *why = "query heads per KV head must divide 128", false;
+  if (!((d->dtype == JEV_DTYPE_BF16 && d->head_dim == 128) || (d->dtype == JEV_DTYPE_F32 && d->head_dim == 64)))
+    return *why = "supported: bf16 with head_dim 128, f32 with head_dim 64", false;
+  const int64_t nqkv = int64_t(d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim;
+  if (nqkv % 128 || d->d_model % 128) return *why = "projection widths must be multiples of 128", false;
+  const int chunk_elems = 16 / elt_size(*d);
+  if (d->d_model % (8 * chunk_elems) || (int64_t(d->n_q_heads) * d->head_dim) % (8 * chunk_elems))
+    return *why = "reduction widths must be multiples of 128 bytes", false;
+  if (d->d_model > 256 * 4 * chunk_elems) return *why = "d_model too large for the norm kernel", false;
+  if (d->max_positions < 1 || d->max_round_tokens < 1) return *why = "max_positions/max_round_tokens < 1", false;
+  if (!(d->rope_theta > 0.f) || !(d->rms_eps >= 0.f)) return *why = "bad rope_theta or rms_eps", false;
+  return true;
+}
+
+// ----------------------------------------------------------------- rounds
+
+struct ReadSpec {
+  int32_t cand;
+  const int32_t* labels;
+  int32_t k;
+  int64_t out_off;
+};
+
+// A node computed in a round.
+struct RNode {
+  int64_t group;                   // nodes with the same parent share a group
+  std::vector<jev::PageRef> anc;   // parent's page path (root first); empty: no parent
+  const int32_t* tok;
+  int64_t n;
+  int64_t start;                   // logical position of tok[0]
+  std::vector<int32_t> pages;
+  std::vector<ReadSpec> reads;
+};
+
+struct RoundDesc {
+  int32_t T = 0;
+  int64_t off_tok = 0, off_pos = 0, off_slot = 0, off_plist = 0, off_tiles = 0, off_merge = 0,
+          off_read = 0, off_labels = 0;
+  int32_t n_tiles = 0, n_merge = 0, n_read = 0;
+  int64_t part_slots = 0;
+};
+
+}  // namespace
+
+struct jev_ctx {
+  jev_model_desc desc{};
+  bool dry = true;
+  bool dead = false;
+  jev::ModelDims dims{};
+  std::vector<jev::LayerW> layers;
+  const void* embed = nullptr;
+  const void* unembed = nullptr;
+  const void* final_norm = nullptr;
+  char* pool = nullptr;
+  WsLayout L{};
+  char* ws = nullptr;
+  int32_t* desc_host = nullptr;  // pinned staging
+  hipEvent_t desc_copied = nullptr;
+  hipEvent_t last_done = nullptr;
+  bool have_last = false;
+  hipStream_t last_stream = nullptr;
+  jev::PagePool pages;
+  std::unique_ptr<jev::ResidentTree> tree;
+  jev_stats_t stats{};
+  int32_t tap_layer = -1;
+  void* tap_dst = nullptr;
+  int64_t tap_rows = 0;
+};
+
+namespace {
+
+#define HIPCHK(expr)                                                              \
+  do {                                                                            \
+    hipError_t e_ = (expr);                                                       \
+    if (e_ != hipSuccess) {                                                       \
+      ctx->dead = true;                                                           \
+      return fail(JEV_EHIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+    }                                                                             \
+  } while (0)
+
+int check_alive(jev_ctx* ctx) {
+  if (!ctx) return fail(JEV_EINVAL, "ctx is NULL");
+  if (ctx->dead) return fail(JEV_EHIP, "context is unusable after an earlier HIP failure");
+  return JEV_OK;
+}
+
+int check_segments(const jev_ctx* ctx, int32_t n, const int32_t* tokens, const int64_t* off, const char* what) {
+  if (n < 0) return fail(JEV_EINVAL, std::string(what) + ": n < 0");
+  if (n == 0) return JEV_OK;
+  if (!tokens || !off) return fail(JEV_EINVAL, std::string(what) + ": NULL tokens/offsets");
+  if (off[0] != 0) return fail(JEV_EINVAL, std::string(what) + ": offsets[0] != 0");
+  for (int32_t i = 0; i < n; ++i) {
+    if (off[i + 1] <= off[i])
+      return fail(JEV_EINVAL, std::string(what) + ": empty or decreasing segment " + std::to_string(i));
+  }
+  const int32_t V = ctx->desc.vocab;
+  for (int64_t i = 0; i < off[n]; ++i)
+    if (tokens[i] < 0 || tokens[i] >= V)
+      return fail(JEV_EINVAL, std::string(what) + ": token id out of range at " + std::to_string(i));
+  return JEV_OK;
+}
+
+int check_labels(const jev_ctx* ctx, int32_t n, const int32_t* labels, const int64_t* loff) {
+  if (!labels || !loff) return fail(JEV_EINVAL, "NULL labels/label_offsets");
+  if (loff[0] != 0) return fail(JEV_EINVAL, "label_offsets[0] != 0");
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t k = loff[i + 1] - loff[i];
+    if (k < JEV_MIN_LABELS || k > JEV_MAX_LABELS)
+      return fail(JEV_EINVAL, "branch " + std::to_string(i) + ": label count outside [2, 64]");
+    for (int64_t a = loff[i]; a < loff[i + 1]; ++a) {
+      if (labels[a] < 0 || labels[a] >= ctx->desc.vocab)
+        return fail(JEV_EINVAL, "branch " + std::to_string(i) + ": label id out of range");
+      for (int64_t b = loff[i]; b < a; ++b)
+        if (labels[b] == labels[a]) return fail(JEV_EINVAL, "branch " + std::to_string(i) + ": duplicate label");
+    }
+  }
+  return JEV_OK;
+}
+
+// Builds the descriptors of one round into hb (int32 words) and returns its layout.
+int build_round(jev_ctx* ctx, std::vector<RNode>& nodes, std::vector<int32_t>& hb, RoundDesc* rd) {
+  const int G = ctx->desc.n_q_heads / ctx->desc.n_kv_heads;
+  const int TT = kRowsPerTile / G;
+  // order nodes by group (groups in order of first appearance), stable
+  std::vector<int64_t> gorder;
+  for (auto& nd : nodes)
+    if (std::find(gorder.begin(), gorder.end(), nd.group) == gorder.end()) gorder.push_back(nd.group);
+  std::stable_sort(nodes.begin(), nodes.end(), [&](const RNode& a, const RNode& b) {
+    return std::find(gorder.begin(), gorder.end(), a.group) < std::find(gorder.begin(), gorder.end(), b.group);
+  });
+  int64_t T = 0;
+  for (auto& nd : nodes) T += nd.n;
+  if (T > ctx->desc.max_round_tokens)
+    return fail(JEV_ENOMEM, "round of " + std::to_string(T) + " tokens exceeds max_round_tokens");
+  rd->T = int32_t(T);
+  auto push = [&](int64_t words) {
+    int64_t o = int64_t(hb.size());
+    hb.resize(hb.size() + size_t(words), 0);
+    return o;
+  };
+  rd->off_tok = push(T);
+  rd->off_pos = push(T);
+  rd->off_slot = push(T);
+  std::vector<int64_t> node_t0(nodes.size());
+  {
+    int64_t t = 0;
+    for (size_t i = 0; i < nodes.size(); ++i) {
+      RNode& nd = nodes[i];
+      node_t0[i] = t;
+      for (int64_t j = 0; j < nd.n; ++j, ++t) {
+        hb[rd->off_tok + t] = nd.tok[j];
+        hb[rd->off_pos + t] = int32_t(nd.start + j);
+        hb[rd->off_slot + t] = nd.pages[j / jev::kPage] * jev::kPage + int32_t(j % jev::kPage);
+      }
+    }
+  }
+  // page lists: own pages per node, parent path per group
+  std::vector<int64_t> own_off(nodes.size());
+  std::vector<int64_t> plist;  // pairs
+  for (size_t i = 0; i < nodes.size(); ++i) {
+    own_off[i] = int64_t(plist.size() / 2);
+    const RNode& nd = nodes[i];
+    for (size_t p = 0; p < nd.pages.size(); ++p) {
+      int64_t v = nd.n - int64_t(jev::kPage) * int64_t(p);
+      plist.push_back(nd.pages[p]);
+      plist.push_back(int32_t(v < jev::kPage ? v : jev::kPage));
+    }
+  }
+  struct Group {
+    int64_t t0, t1, anc_off, anc_pages;
+  };
+  std::vector<Group> groups;
+  for (size_t i = 0; i < nodes.size(); ++i) {
+    if (i == 0 || nodes[i].group != nodes[i - 1].group) {
+      Group g{node_t0[i], node_t0[i], int64_t(plist.size() / 2), int64_t(nodes[i].anc.size())};
+      for (auto& pr : nodes[i].anc) {
+        plist.push_back(pr.page);
+        plist.push_back(pr.valid);
+      }
+      groups.push_back(g);
+    }
+    groups.back().t1 = node_t0[i] + nodes[i].n;
+  }
+  rd->off_plist = push(int64_t(plist.size()));
+  std::copy(plist.begin(), plist.end(), hb.begin() + rd->off_plist);
+
+  // chunking of the prefix part
+  int64_t anc_qtiles = 0, min_anc_pages = INT64_MAX;
+  for (auto& g : groups)
+    if (g.anc_pages > 0) {
+      anc_qtiles += (g.t1 - g.t0 + TT - 1) / TT;
+      min_anc_pages = std::min(min_anc_pages, g.anc_pages);
+    }
+  int64_t n_chunks = 1;
+  if (anc_qtiles > 0) {
+    const int64_t want = 512;
+    n_chunks = (want + anc_qtiles * ctx->desc.n_kv_heads - 1) / (anc_qtiles * ctx->desc.n_kv_heads);
+    n_chunks = std::max<int64_t>(1, std::min<int64_t>({n_chunks, kMaxChunks, min_anc_pages / 8}));
+  }
+
+  std::vector<jev::AttnTile> tiles;
+  std::vector<jev::MergeItem> merges;
+  int64_t slot = 0;
+  std::vector<int64_t> own_row(T, -1), anc_row(T, -1);
+  for (size_t i = 0; i < nodes.size(); ++i) {
+    const RNode& nd = nodes[i];
+    const bool has_anc = !nd.anc.empty();
+    for (int64_t i0 = 0; i0 < nd.n; i0 += TT) {
+      const int64_t nt = std::min<int64_t>(TT, nd.n - i0);
+      jev::AttnTile tl{};
+      tl.t0 = int32_t(node_t0[i] + i0);
+      tl.n_tok = int32_t(nt);
+      tl.page_off = int32_t(own_off[i]);
+      tl.n_pages = int32_t((i0 + nt - 1) / jev::kPage + 1);
+      tl.causal = 1;
+      tl.kv_pos0 = int32_t(nd.start);
+      tl.out_mode = has_anc ? 1 : 0;
+      tl.part_slot = has_anc ? int32_t(slot) : 0;
+      if (has_anc) {
+        for (int64_t j = 0; j < nt; ++j) own_row[node_t0[i] + i0 + j] = slot * kRowsPerTile + j * G;
+        ++slot;
+      }
+      tiles.push_back(tl);
+    }
+  }
+  for (auto& g : groups) {
+    if (g.anc_pages == 0) continue;
+    int64_t cp = (g.anc_pages + n_chunks - 1) / n_chunks;
+    cp += cp & 1;  // whole two-page steps per chunk
+    const int64_t nch = (g.anc_pages + cp - 1) / cp;
+    for (int64_t t0 = g.t0; t0 < g.t1; t0 += TT) {
+      const int64_t nt = std::min<int64_t>(TT, g.t1 - t0);
+      for (int64_t j = 0; j < nt; ++j) anc_row[t0 + j] = slot * kRowsPerTile + j * G;
+      for (int64_t c = 0; c < nch; ++c) {
+        jev::AttnTile tl{};
+        tl.t0 = int32_t(t0);
+        tl.n_tok = int32_t(nt);
+        tl.page_off = int32_t(g.anc_off + c * cp);
+        tl.n_pages = int32_t(std::min(cp, g.anc_pages - c * cp));
+        tl.causal = 0;
+        tl.out_mode = 1;
+        tl.part_slot = int32_t(slot++);
+        tiles.push_back(tl);
+      }
+      for (int64_t j = 0; j < nt; ++j)
+        merges.push_back(jev::MergeItem{int32_t(t0 + j), int32_t(own_row[t0 + j]), int32_t(anc_row[t0 + j]),
+                                        int32_t(nch)});
+    }
+  }
+  if (slot * kRowsPerTile > ctx->L.part_rows)
+    return fail(JEV_ENOMEM, "round needs more partial-state rows than the workspace holds");
+  rd->part_slots = slot;
+  // heavy tiles first
+  std::stable_sort(tiles.begin(), tiles.end(),
+                   [](const jev::AttnTile& a, const jev::AttnTile& b) { return a.n_pages > b.n_pages; });
+  rd->n_tiles = int32_t(tiles.size());
+  rd->off_tiles = push(int64_t(tiles.size()) * 8);
+  std::memcpy(hb.data() + rd->off_tiles, tiles.data(), tiles.size() * sizeof(jev::AttnTile));
+  rd->n_merge = int32_t(merges.size());
+  rd->off_merge = push(int64_t(merges.size()) * 4);
+  std::memcpy(hb.data() + rd->off_merge, merges.data(), merges.size() * sizeof(jev::MergeItem));
+  // readouts
+  std::vector<jev::ReadoutItem> reads;
+  std::vector<int32_t> labs;
+  for (size_t i = 0; i < nodes.size(); ++i)
+    for (auto& r : nodes[i].reads) {
+      reads.push_back(jev::ReadoutItem{int32_t(node_t0[i] + nodes[i].n - 1), int32_t(labs.size()), r.k,
+                                       int32_t(r.out_off)});
+      labs.insert(labs.end(), r.labels, r.labels + r.k);
+    }
+  rd->n_read = int32_t(reads.size());
+  rd->off_read = push(int64_t(reads.size()) * 4);
+  std::memcpy(hb.data() + rd->off_read, reads.data(), reads.size() * sizeof(jev::ReadoutItem));
+  rd->off_labels = push(int64_t(labs.size()));
+  std::copy(labs.begin(), labs.end(), hb.begin() + rd->off_labels);
+  return JEV_OK;
+}
+
+// Copies the descriptors of a call to the device and runs its rounds.
+int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vector<int32_t>& hb, float* probs,
+               hipStream_t s) {
+  if (int64_t(hb.size()) > ctx->L.desc_ints)
+    return fail(JEV_ENOMEM, "call descriptors exceed the workspace descriptor region");
+  if (ctx->have_last && s != ctx->last_stream) HIPCHK(hipStreamWaitEvent(s, ctx->last_done, 0));
+  if (ctx->have_last) HIPCHK(hipEventSynchronize(ctx->desc_copied));
+  std::memcpy(ctx->desc_host, hb.data(), hb.size() * sizeof(int32_t));
+  int32_t* dd = reinterpret_cast<int32_t*>(ctx->ws + ctx->L.desc);
+  HIPCHK(hipMemcpyAsync(dd, ctx->desc_host, hb.size() * sizeof(int32_t), hipMemcpyHostToDevice, s));
+  HIPCHK(hipEventRecord(ctx->desc_copied, s));
+  const jev::ModelDims& m = ctx->dims;
+  void* x = ctx->ws + ctx->L.x;
+  void* h = ctx->ws + ctx->L.h;
+  void* q = ctx->ws + ctx->L.q;
+  void* o = ctx->ws + ctx->L.o;
+  float* rope = reinterpret_cast<float*>(ctx->ws + ctx->L.rope);
+  float* part_o = reinterpret_cast<float*>(ctx->ws + ctx->L.part_o);
+  float* part_lse = reinterpret_cast<float*>(ctx->ws + ctx->L.part_lse);
+  for (const RoundDesc& rd : rds) {
+    const int32_t* tok = dd + rd.off_tok;
+    HIPCHK(jev::launch_embed(m, ctx->embed, tok, rd.T, x, s));
+    for (int l = 0; l < m.n_layers; ++l) {
+      const jev::LayerW& w = ctx->layers[l];
+      HIPCHK(jev::launch_rmsnorm(m, x, w.norm, rd.T, h, s));
+      HIPCHK(jev::launch_qkv(m, w, l, h, rd.T, dd + rd.off_pos, dd + rd.off_slot, rope, q, ctx->pool, s));
+      HIPCHK(jev::launch_attention(m, l, reinterpret_cast<const jev::AttnTile*>(dd + rd.off_tiles), rd.n_tiles,
+                                   dd + rd.off_plist, dd + rd.off_pos, q, ctx->pool, o, part_o, part_lse, s));
+      HIPCHK(jev::launch_merge(m, reinterpret_cast<const jev::MergeItem*>(dd + rd.off_merge), rd.n_merge, part_o,
+                               part_lse, o, s));
+      if (ctx->tap_dst && ctx->tap_layer == l && rds.size() == 1) {
+        const int64_t rows = std::min<int64_t>(rd.T, ctx->tap_rows);
+        HIPCHK(hipMemcpyAsync(ctx->tap_dst, o, size_t(rows) * m.hq * m.dh * elt_size(ctx->desc),
+                              hipMemcpyDeviceToDevice, s));
+      }
+      HIPCHK(jev::launch_oproj(m, w, o, rd.T, x, s));
+    }
+    HIPCHK(jev::launch_readout(m, ctx->unembed, ctx->final_norm, x,
+                               reinterpret_cast<const jev::ReadoutItem*>(dd + rd.off_read), rd.n_read,
+                               dd + rd.off_labels, probs, s));
+  }
+  HIPCHK(hipEventRecord(ctx->last_done, s));
+  ctx->have_last = true;
+  ctx->last_stream = s;
+  return JEV_OK;
+}
+
+}  // namespace
+
+// ===================================================================== C ABI
+extern "C" {
+
+const char* jev_last_error(void) { return g_err.c_str(); }
+
+size_t jev_workspace_bytes(const jev_model_desc* desc) {
+  std::string why;
+  if (!desc_ok(desc, &why)) return 0;
+  return layout(*desc).total;
+}
+
+size_t jev_kv_pool_bytes(const jev_model_desc* desc, int32_t n_pages) {
+  std::string why;
+  if (!desc_ok(desc, &why) || n_pages < 0) return 0;
+  return size_t(desc->n_layers) * size_t(n_pages) * desc->n_kv_heads * 2 * jev::kPage * desc->head_dim *
+         elt_size(*desc);
+}
+
+int jev_create(const jev_model_desc* desc, const jev_weights* weights, void* kv_pool, int32_t n_pages,
+               void* workspace, size_t workspace_bytes, jev_ctx** out) {
+  std::string why;
+  if (!out) return fail(JEV_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!desc_ok(desc, &why)) return fail(JEV_EINVAL, why);
+  if (n_pages < 1) return fail(JEV_EINVAL, "n_pages < 1");
+  std::unique_ptr<jev_ctx> c(new jev_ctx());
+  jev_ctx* ctx = c.get();
+  ctx->desc = *desc;
+  ctx->pages.reset(n_pages);
+  ctx->tree.reset(new jev::ResidentTree(&ctx->pages));
+  ctx->dims = jev::ModelDims{desc->n_layers, desc->d_model, desc->n_q_heads, desc->n_kv_heads,
+                             desc->head_dim, desc->vocab,  n_pages,          desc->rms_eps,
+                             desc->dtype == JEV_DTYPE_BF16 ? 1 : 0};
+  ctx->L = layout(*desc);
+  ctx->stats.pages_total = n_pages;
+  const bool dry = !weights && !kv_pool && !workspace;
+  ctx->dry = dry;
+  if (!dry) {
+    if (!weights || !kv_pool || !workspace) return fail(JEV_EINVAL, "weights, kv_pool and workspace are all required");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(JEV_EINVAL, "workspace must be 256-byte aligned");
+    if (workspace_bytes < ctx->L.total)
+      return fail(JEV_ENOMEM, "workspace too small: need " + std::to_string(ctx->L.total) + " bytes");
+    if (!weights->embed || !weights->unembed || !weights->final_norm || !weights->attn_norm || !weights->wq ||
+        !weights->wk || !weights->wv || !weights->wo)
+      return fail(JEV_EINVAL, "NULL weight pointer");
+    ctx->embed = weights->embed;
+    ctx->unembed = weights->unembed;
+    ctx->final_norm = weights->final_norm;
+    for (int l = 0; l < desc->n_layers; ++l) {
+      jev::LayerW w{weights->attn_norm[l], weights->wq[l], weights->wk[l], weights->wv[l], weights->wo[l]};
+      if (!w.norm || !w.wq || !w.wk || !w.wv || !w.wo) return fail(JEV_EINVAL, "NULL per-layer weight pointer");
+      ctx->layers.push_back(w);
+    }
+    ctx->pool = reinterpret_cast<char*>(kv_pool);
+    ctx->ws = reinterpret_cast<char*>(workspace);
+    HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&ctx->desc_host), size_t(ctx->L.desc_ints) * sizeof(int32_t),
+                         hipHostMallocDefault));
+    HIPCHK(hipEventCreateWithFlags(&ctx->desc_copied, hipEventDisableTiming));
+    HIPCHK(hipEventCreateWithFlags(&ctx->last_done, hipEventDisableTiming));
+    // RoPE table: angle = pos * theta^(-2i/dh) in double, stored as float (cos, sin)
+    const int half = desc->head_dim / 2;
+    std::vector<float> rope(size_t(desc->max_positions) * half * 2);
+    for (int64_t p = 0; p < desc->max_positions; ++p)
+      for (int i = 0; i < half; ++i) {
+        const double inv = std::pow(double(desc->rope_theta), -2.0 * i / desc->head_dim);
+        const double a = double(p) * inv;
+        rope[(size_t(p) * half + i) * 2] = float(std::cos(a));
+        rope[(size_t(p) * half + i) * 2 + 1] = float(std::sin(a));
+      }
+    HIPCHK(hipMemcpy(ctx->ws + ctx->L.rope, rope.data(), rope.size() * sizeof(float), hipMemcpyHostToDevice));
+    // pages never written hold zeros (a partly valid page is masked, never NaN)
+    HIPCHK(hipMemset(kv_pool, 0, jev_kv_pool_bytes(desc, n_pages)));
+    HIPCHK(hipDeviceSynchronize());
+  }
+  *out = c.release();
+  return JEV_OK;
+}
+
+int jev_destroy(jev_ctx* ctx) {
+  if (!ctx) return JEV_OK;
+  int rc = JEV_OK;
+  if (!ctx->dry) {
+    if (ctx->have_last && hipEventSynchronize(ctx->last_done) != hipSuccess) rc = fail(JEV_EHIP, "sync failed");
+    if (ctx->desc_host) (void)hipHostFree(ctx->desc_host);
+    if (ctx->desc_copied) (void)hipEventDestroy(ctx->desc_copied);
+    if (ctx->last_done) (void)hipEventDestroy(ctx->last_done);
+  }
+  delete ctx;
+  return rc;
+}
+
+int jev_prefill_prefix(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const int32_t* tokens,
+                       const int64_t* offsets, jev_prefix* out_handles, void* hip_stream) {
+  if (int rc = check_alive(ctx)) return rc;
+  if (int rc = check_segments(ctx, n, tokens, offsets, "prefill")) return rc;
+  if (n == 0) return JEV_OK;
+  if (!parents || !out_handles) return fail(JEV_EINVAL, "NULL parents/out_handles");
+  std::vector<jev::ResidentTree::PrefillItem> items;
+  for (int32_t i = 0; i < n; ++i) {
+    if (!ctx->tree->has(parents[i])) return fail(JEV_EHANDLE, "unknown parent handle " + std::to_string(parents[i]));
+    const int64_t len = offsets[i + 1] - offsets[i];
+    if (ctx->tree->end_pos(parents[i]) + len > ctx->desc.max_positions)
+      return fail(JEV_EINVAL, "prefix " + std::to_string(i) + " runs past max_positions");
+    items.push_back({parents[i], tokens + offsets[i], len});
+  }
+  if (ctx->tree->prefill_need(items) > ctx->pages.n_free()) return fail(JEV_ENOMEM, "not enough free KV pages");
+  // Simulate the allocation tree->prefill() will make (new nodes take the
+  // lowest free ids in input order; an identical resident child or an earlier
+  // identical item of this call creates nothing), so that descriptors are built
+  // and checked before any state changes.
+  std::vector<RNode> rn;
+  {
+    std::set<int32_t> snap = ctx->pages.snapshot();
+    std::vector<size_t> made;  // indices of items that create a node
+    for (int32_t i = 0; i < n; ++i) {
+      const auto& it = items[i];
+      bool exists = ctx->tree->prefill_need({it}) == 0;
+      for (size_t j : made)
+        if (!exists && items[j].parent == it.parent && items[j].n == it.n &&
+            std::equal(it.tok, it.tok + it.n, items[j].tok))
+          exists = true;
+      if (exists) continue;
+      made.push_back(size_t(i));
+      RNode nd;
+      nd.group = it.parent;
+      if (it.parent != 0) nd.anc = ctx->tree->path_pages(it.parent);
+      nd.tok = it.tok;
+      nd.n = it.n;
+      nd.start = ctx->tree->end_pos(it.parent);
+      nd.pages = ctx->pages.alloc(jev::pages_for(it.n));
+      rn.push_back(std::move(nd));
+    }
+    ctx->pages.restore(std::move(snap));
+  }
+  std::vector<int32_t> hb;
+  std::vector<RoundDesc> rds(1);
+  int64_t computed = 0;
+  for (auto& nd : rn) computed += nd.n;
+  if (!rn.empty() && !ctx->dry) {
+    if (int rc = build_round(ctx, rn, hb, &rds[0])) return rc;
+    if (int64_t(hb.size()) > ctx->L.desc_ints)
+      return fail(JEV_ENOMEM, "call descriptors exceed the workspace descriptor region");
+  }
+  // commit the tree change, then run (the tree allocates the same lowest ids)
+  std::vector<int64_t> handles;
+  std::vector<char> created;
+  ctx->tree->prefill(items, &handles, &created);
+  for (int32_t i = 0; i < n; ++i) out_handles[i] = handles[i];
+  ctx->stats.logical_tokens = computed;
+  ctx->stats.computed_tokens = computed;
+  ctx->stats.cached_tokens = 0;
+  ctx->stats.rounds = rn.empty() ? 0 : 1;
+  ctx->stats.calls += 1;
+  if (!rn.empty() && !ctx->dry) {
+    if (int rc = run_rounds(ctx, rds, hb, nullptr, reinterpret_cast<hipStream_t>(hip_stream))) return rc;
+  }
+  return JEV_OK;
+}
+
+int jev_score_branches(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const int32_t* tokens,
+                       const int64_t* tok_offsets, const int32_t* label_ids, const int64_t* label_offsets,
+                       float* probs, void* hip_stream) {
+  if (int rc = check_alive(ctx)) return rc;
+  if (int rc = check_segments(ctx, n, tokens, tok_offsets, "branches")) return rc;
+  if (n == 0) return JEV_OK;
+  if (!parents) return fail(JEV_EINVAL, "NULL parents");
+  if (int rc = check_labels(ctx, n, label_ids, label_offsets)) return rc;
+  if (ctx->dry) return fail(JEV_ESTATE, "scoring needs a device context");
+  if (!probs) return fail(JEV_EINVAL, "NULL probs");
+  int64_t need = 0, logical = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (!ctx->tree->has(parents[i])) return fail(JEV_EHANDLE, "unknown parent handle " + std::to_string(parents[i]));
+    const int64_t len = tok_offsets[i + 1] - tok_offsets[i];
+    if (ctx->tree->end_pos(parents[i]) + len > ctx->desc.max_positions)
+      return fail(JEV_EINVAL, "branch " + std::to_string(i) + " runs past max_positions");
+    need += jev::pages_for(len);
+    logical += ctx->tree->end_pos(parents[i]) + len;
+  }
+  if (need > ctx->pages.n_free()) return fail(JEV_ENOMEM, "not enough free KV pages");
+  std::set<int32_t> snap = ctx->pages.snapshot();
+  std::vector<RNode> rn;
+  std::map<int64_t, std::vector<jev::PageRef>> anc_cache;
+  int64_t computed = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    RNode nd;
+    nd.group = parents[i];
+    if (parents[i] != 0) {
+      auto it = anc_cache.find(parents[i]);
+      if (it == anc_cache.end()) it = anc_cache.emplace(parents[i], ctx->tree->path_pages(parents[i])).first;
+      nd.anc = it->second;
+    }
+    nd.tok = tokens + tok_offsets[i];
+    nd.n = tok_offsets[i + 1] - tok_offsets[i];
+    nd.start = ctx->tree->end_pos(parents[i]);
+    nd.pages = ctx->pages.alloc(jev::pages_for(nd.n));
+    nd.reads.push_back(ReadSpec{i, label_ids + label_offsets[i], int32_t(label_offsets[i + 1] - label_offsets[i]),
+                                label_offsets[i]});
+    computed += nd.n;
+    rn.push_back(std::move(nd));
+  }
+  ctx->pages.restore(std::move(snap));  // branch pages live for this call only
+  std::vector<int32_t> hb;
+  std::vector<RoundDesc> rds(1);
+  if (int rc = build_round(ctx, rn, hb, &rds[0])) return rc;
+  ctx->stats.logical_tokens = logical;
+  ctx->stats.computed_tokens = computed;
+  ctx->stats.cached_tokens = logical - computed;
+  ctx->stats.rounds = 1;
+  ctx->stats.calls += 1;
+  return run_rounds(ctx, rds, hb, probs, reinterpret_cast<hipStream_t>(hip_stream));
+}
+
+int jev_score_candidates(jev_ctx* ctx, int32_t n, const int32_t* tokens, const int64_t* tok_offsets,
+                         const int32_t* label_ids, const int64_t* label_offsets, float* probs, void* hip_stream) {
+  if (int rc = check_alive(ctx)) return rc;
+  if (int rc = check_segments(ctx, n, tokens, tok_offsets, "candidates")) return rc;
+  if (n == 0) return JEV_OK;
+  if (int rc = check_labels(ctx, n, label_ids, label_offsets)) return rc;
+  if (ctx->dry) return fail(JEV_ESTATE, "scoring needs a device context");
+  if (!probs) return fail(JEV_EINVAL, "NULL probs");
+  for (int32_t i = 0; i < n; ++i)
+    if (tok_offsets[i + 1] - tok_offsets[i] > ctx->desc.max_positions)
+      return fail(JEV_EINVAL, "candidate " + std::to_string(i) + " runs past max_positions");
+  jev::Plan plan;
+  if (!jev::plan_candidates(*ctx->tree, &ctx->pages, n, tokens, tok_offsets, &plan))
+    return fail(JEV_ENOMEM, "not enough free KV pages for the plan");
+  // rounds
+  std::vector<std::vector<RNode>> rounds(plan.rounds.size());
+  std::map<int64_t, std::vector<jev::PageRef>> anchor_pages;
+  int64_t computed = 0, logical = 0;
+  for (int32_t c = 0; c < n; ++c) logical += tok_offsets[c + 1] - tok_offsets[c];
+  for (size_t r = 0; r < plan.rounds.size(); ++r) {
+    for (int32_t idx : plan.rounds[r]) {
+      const jev::PlanNode& x = plan.nodes[idx];
+      RNode nd;
+      const int32_t c0 = x.cand_min();
+      const int64_t alen = plan.anchor_len[c0];
+      // group: parent node id within the plan, or the anchor handle (negated, offset)
+      nd.group = x.parent >= 0 ? int64_t(plan.nodes[x.parent].id) : -1 - x.anchor;
+      if (x.anchor != 0) {
+        auto it = anchor_pages.find(x.anchor);
+        if (it == anchor_pages.end()) it = anchor_pages.emplace(x.anchor, ctx->tree->path_pages(x.anchor)).first;
+        nd.anc = it->second;
+      }
+      // plan ancestors, root first
+      std::vector<int32_t> chain;
+      for (int32_t p = x.parent; p >= 0; p = plan.nodes[p].parent) chain.push_back(p);
+      for (auto it = chain.rbegin(); it != chain.rend(); ++it) {
+        const jev::PlanNode& a = plan.nodes[*it];
+        const int64_t L = a.b - a.a;
+        for (size_t pi = 0; pi < a.pages.size(); ++pi) {
+          const int64_t v = L - int64_t(jev::kPage) * int64_t(pi);
+          nd.anc.push_back(jev::PageRef{a.pages[pi], int32_t(v < jev::kPage ? v : jev::kPage)});
+        }
+      }
+      nd.tok = tokens + tok_offsets[c0] + alen + x.a;
+      nd.n = x.b - x.a;
+      nd.start = alen + x.a;
+      nd.pages = x.pages;
+      for (int32_t c : x.readout)
+        nd.reads.push_back(ReadSpec{c, label_ids + label_offsets[c],
+                                    int32_t(label_offsets[c + 1] - label_offsets[c]), label_offsets[c]});
+      computed += nd.n;
+      rounds[r].push_back(std::move(nd));
+    }
+  }
+  std::vector<int32_t> hb;
+  std::vector<RoundDesc> rds(rounds.size());
+  for (size_t r = 0; r < rounds.size(); ++r)
+    if (int rc = build_round(ctx, rounds[r], hb, &rds[r])) return rc;
+  ctx->stats.logical_tokens = logical;
+  ctx->stats.computed_tokens = computed;
+  ctx->stats.cached_tokens = logical - computed;
+  ctx->stats.rounds = int32_t(rounds.size());
+  ctx->stats.calls += 1;
+  return run_rounds(ctx, rds, hb, probs, reinterpret_cast<hipStream_t>(hip_stream));
+}
+
+int jev_free_pages(jev_ctx* ctx, int32_t n, const jev_prefix* handles) {
+  if (!ctx) return fail(JEV_EINVAL, "ctx is NULL");
+  if (n < 0 || (n > 0 && !handles)) return fail(JEV_EINVAL, "bad handle array");
+  // validate first: every handle must hold enough caller references
+  std::map<int64_t, int64_t> count;
+  for (int32_t i = 0; i < n; ++i) {
+    if (handles[i] == 0 || !ctx->tree->has(handles[i]))
+      return fail(JEV_EHANDLE, "unknown handle " + std::to_string(handles[i]));
+    count[handles[i]] += 1;
+  }
+  for (auto& kv : count)
+    if (ctx->tree->node(kv.first).refs < kv.second) return fail(JEV_EHANDLE, "handle released more times than held");
+  for (int32_t i = 0; i < n; ++i) ctx->tree->release(handles[i]);
+  return JEV_OK;
+}
+
+int jev_plan(jev_ctx* ctx, int32_t n, const int32_t* tokens, const int64_t* tok_offsets, int32_t* out,
+             int64_t cap, int64_t* out_len) {
+  if (!ctx || !out_len) return fail(JEV_EINVAL, "NULL ctx/out_len");
+  if (int rc = check_segments(ctx, n, tokens, tok_offsets, "candidates")) return rc;
+  jev::Plan plan;
+  if (n > 0 && !jev::plan_candidates(*ctx->tree, &ctx->pages, n, tokens, tok_offsets, &plan))
+    return fail(JEV_ENOMEM, "not enough free KV pages for the plan");
+  std::vector<int32_t> s = n > 0 ? plan.serialize() : std::vector<int32_t>{0, 0};
+  *out_len = int64_t(s.size());
+  if (!out) return JEV_OK;
+  if (cap < int64_t(s.size())) return fail(JEV_EINVAL, "output buffer too small");
+  std::copy(s.begin(), s.end(), out);
+  return JEV_OK;
+}
+
+int jev_page_table(jev_ctx* ctx, jev_prefix h, int32_t* page_ids, int32_t* valid, int32_t cap, int32_t* n) {
+  if (!ctx || !n) return fail(JEV_EINVAL, "NULL ctx/n");
+  if (h == 0 || !ctx->tree->has(h)) return fail(JEV_EHANDLE, "unknown handle");
+  std::vector<jev::PageRef> p = ctx->tree->path_pages(h);
+  *n = int32_t(p.size());
+  if (cap < int32_t(p.size())) return fail(JEV_EINVAL, "output buffer too small");
+  for (size_t i = 0; i < p.size(); ++i) {
+    if (page_ids) page_ids[i] = p[i].page;
+    if (valid) valid[i] = p[i].valid;
+  }
+  return JEV_OK;
+}
+
+int jev_match(jev_ctx* ctx, const int32_t* tokens, int64_t n, jev_prefix* handle, int64_t* matched) {
+  if (!ctx || !handle || !matched || (n > 0 && !tokens) || n < 0) return fail(JEV_EINVAL, "bad arguments");
+  int64_t h, m;
+  ctx->tree->match(tokens, n, &h, &m);
+  *handle = h;
+  *matched = m;
+  return JEV_OK;
+}
+
+int jev_stats(jev_ctx* ctx, jev_stats_t* out) {
+  if (!ctx || !out) return fail(JEV_EINVAL, "NULL ctx/out");
+  ctx->stats.pages_total = ctx->pages.n_total();
+  ctx->stats.pages_in_use = ctx->pages.n_total() - ctx->pages.n_free();
+  ctx->stats.resident_prefixes = ctx->tree->size();
+  *out = ctx->stats;
+  return JEV_OK;
+}
+
+int jev_debug_tap(jev_ctx* ctx, int32_t layer, void* dst, int64_t cap_rows) {
+  if (!ctx) return fail(JEV_EINVAL, "NULL ctx");
+  if (dst && (layer < 0 || layer >= ctx->desc.n_layers || cap_rows < 1)) return fail(JEV_EINVAL, "bad tap");
+  ctx->tap_layer = layer;
+  ctx->tap_dst = dst;
+  ctx->tap_rows = cap_rows;
+  return JEV_OK;
+}
+
+}  // extern "C"

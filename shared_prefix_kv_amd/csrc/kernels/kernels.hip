@@ -1,0 +1,740 @@
+// gfx950 kernels of the shared-prefix scoring path.
+//
+//  embed      x[t] = E[token t]
+//  rmsnorm    h = x / sqrt(mean x^2 + eps) * g  (fp32 math, stored)
+//  qkv        h [T,d] x [Wq;Wk;Wv]^T on MFMA, fp32 accumulate; epilogue applies
+//             RoPE to q and k at the token's logical position, writes q to the
+//             round buffer and k, v straight into the token's KV page
+//  attention  paged attention of packed query rows (token x query head of one
+//             KV head) against a page list; causal over a node's own pages,
+//             unmasked over a shared prefix's pages (read once for all rows of
+//             the sibling group); online softmax in fp32; writes the output or
+//             a normalised partial state plus its log2-sum-exp
+//  merge      log-sum-exp merge of the partial states of a token
+//  oproj      x += o Wo^T on MFMA
+//  readout    final norm of a candidate's last row, logits at its label ids
+//             only, max-subtracted softmax over the labels
+//
+// The scoring rule (last position only, label ids only, stable softmax over
+// the labels) is the jdon.com openjev-sglang article's "prefill-only" section;
+// reading only the labels' logits is exact because the full-vocabulary
+// log-normaliser cancels in the label softmax.
+#include <float.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace jev {
+namespace dev {
+
+constexpr float kNegInf = -INFINITY;
+
+// ------------------------------------------------------------------ embed
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ E, const int32_t* __restrict__ tok,
+                                                    int d, T* __restrict__ x) {
+  const int t = blockIdx.x;
+  const uint4* src = reinterpret_cast<const uint4*>(E + (size_t)tok[t] * d);
+  uint4* dst = reinterpret_cast<uint4*>(x + (size_t)t * d);
+  const int n = d * int(sizeof(T)) / 16;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = src[i];
+}
+
+// block-wide sum over 256 threads
+__device__ __forceinline__ float block_sum256(float v, float* scratch) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) scratch[wave] = v;
+  __syncthreads();
+  float r = scratch[0] + scratch[1] + scratch[2] + scratch[3];
+  __syncthreads();
+  return r;
+}
+
+template <typename T>
+__device__ __forceinline__ void load16(const T* p, float* out);
+template <>
+__device__ __forceinline__ void load16<bf16s>(const bf16s* p, float* out) {
+  uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void load16<float>(const float* p, float* out) {
+  float4 u = *reinterpret_cast<const float4*>(p);
+  out[0] = u.x;
+  out[1] = u.y;
+  out[2] = u.z;
+  out[3] = u.w;
+}
+
+// ------------------------------------------------------------------ rmsnorm
+// One block per row; d <= 256 * 8 * (16 / sizeof(T)) / 8 handled by the loop.
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x, const T* __restrict__ g, int d,
+                                                      float eps, T* __restrict__ h) {
+  constexpr int CH = 16 / sizeof(T);
+  __shared__ float scratch[4];
+  const T* xr = x + (size_t)blockIdx.x * d;
+  T* hr = h + (size_t)blockIdx.x * d;
+  constexpr int MAXV = 4;  // chunks per thread held in registers (d <= 256*CH*4)
+  float v[MAXV][CH];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) {
+    const int i = (threadIdx.x + 256 * j) * CH;
+    if (i < d) {
+      load16<T>(xr + i, v[j]);
+#pragma unroll
+      for (int e = 0; e < CH; ++e) ss += v[j][e] * v[j][e];
+    }
+  }
+  ss = block_sum256(ss, scratch);
+  const float r = 1.0f / sqrtf(ss / float(d) + eps);
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) {
+    const int i = (threadIdx.x + 256 * j) * CH;
+    if (i < d) {
+      float gg[CH];
+      load16<T>(g + i, gg);
+#pragma unroll
+      for (int e = 0; e < CH; ++e) hr[i + e] = from_f32<T>(v[j][e] * r * gg[e]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ GEMM (NT)
+// C[M,N] = A[M,K] . B[N,K]^T with 128x128 tiles, 4 waves of 64x64, MFMA 32x32,
+// 128 bytes of K per stage, double-buffered LDS with a 16-byte-chunk XOR swizzle.
+constexpr int GBM = 128, GBN = 128;
+
+template <typename T>
+struct GemmB {
+  const T* b0;
+  const T* b1;
+  const T* b2;
+  int n0end, n1end;
+  int perm_dh;  // rows of segments 0 and 1 are permuted so RoPE pairs meet in one lane
+};
+
+// GEMM column n -> weight row.  Within a head of dh columns, a wave's 64
+// columns [64w, 64w+64) carry features 32w + c (first 32) and 32w + c + dh/2
+// (last 32) for dh = 128, and c / c + 32 for dh = 64, so that the rotate-half
+// pair of a feature sits in the same lane of the two 32-column MFMA tiles.
+template <typename T>
+__device__ __forceinline__ const T* gemm_brow(const GemmB<T>& g, int n, int K) {
+  const T* base;
+  int local, seg;
+  if (n < g.n0end) {
+    base = g.b0;
+    local = n;
+    seg = 0;
+  } else if (n < g.n1end) {
+    base = g.b1;
+    local = n - g.n0end;
+    seg = 1;
+  } else {
+    base = g.b2;
+    local = n - g.n1end;
+    seg = 2;
+  }
+  if (g.perm_dh && seg < 2) {
+    const int dh = g.perm_dh;
+    const int head = local / dh, jj = local % dh;
+    const int w = jj >> 6, r = jj & 63, half = r >> 5, c = r & 31;
+    const int f = (dh == 128 ? 32 * w : 0) + c + half * (dh >> 1);
+    local = head * dh + f;
+  }
+  return base + (size_t)local * K;
+}
+
+struct QkvEpi {
+  int hq, hkv, dh, nq_end, nk_end;
+  const int32_t* pos;
+  const int32_t* kvslot;
+  const float2* rope;
+  void* qbuf;
+  void* pool;
+  size_t layer_base;  // element offset of this layer in the pool
+};
+
+struct ResEpi {
+  void* x;
+  int ld;
+};
+
+enum { EPI_QKV = 0, EPI_RES = 1 };
+
+template <typename T, int EPI>
+__global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int M, int K, GemmB<T> gb, int N,
+                                                   QkvEpi qe, ResEpi re) {
+  using MF = Mfma<T>;
+  constexpr int CH = 16 / sizeof(T);
+  constexpr int BK = 8 * CH;
+  __shared__ uint4 sA[2][GBM * 8];
+  __shared__ uint4 sB[2][GBN * 8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * GBM, n0 = blockIdx.x * GBN;
+  const int lrow = tid >> 3, lch = tid & 7;
+
+  const uint4* ap[4];
+  const uint4* bp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = lrow + 32 * i;
+    const int am = min(m0 + r, M - 1);
+    ap[i] = reinterpret_cast<const uint4*>(A + (size_t)am * K) + lch;
+    const int bn = min(n0 + r, N - 1);
+    bp[i] = reinterpret_cast<const uint4*>(gemm_brow(gb, bn, K)) + lch;
+  }
+  uint4 ra[4], rb[4];
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int KT = K / BK;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ra[i] = ap[i][0];
+    rb[i] = bp[i][0];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = lrow + 32 * i;
+    sA[0][r * 8 + (lch ^ (r & 7))] = ra[i];
+    sB[0][r * 8 + (lch ^ (r & 7))] = rb[i];
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    // prefetch the next stage (the last iteration re-reads the final stage and
+    // stores it into the idle buffer, which nothing reads afterwards)
+    const int kn = min(kt + 1, KT - 1) * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra[i] = ap[i][kn];
+      rb[i] = bp[i][kn];
+    }
+#pragma unroll
+    for (int ks = 0; ks < BK / MF::KSTEP; ++ks) {
+      const int k = ks * MF::KSTEP + MF::KL * (lane >> 5);
+      const int ch = k / CH, within = k % CH;
+      typename MF::frag a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + 32 * i + (lane & 31);
+        a[i] = MF::load(reinterpret_cast<const T*>(&sA[buf][r * 8 + (ch ^ (r & 7))]) + within);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = wn * 64 + 32 * j + (lane & 31);
+        b[j] = MF::load(reinterpret_cast<const T*>(&sB[buf][r * 8 + (ch ^ (r & 7))]) + within);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = MF::mma(a[i], b[j], acc[i][j]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = lrow + 32 * i;
+      sA[buf ^ 1][r * 8 + (lch ^ (r & 7))] = ra[i];
+      sB[buf ^ 1][r * 8 + (lch ^ (r & 7))] = rb[i];
+    }
+    __syncthreads();
+  }
+
+  const int c = lane & 31, hh = lane >> 5;
+  const int nw = n0 + wn * 64;
+  if constexpr (EPI == EPI_RES) {
+    T* x = reinterpret_cast<T*>(re.x);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          T* p = x + (size_t)m * re.ld + nw + 32 * j + c;
+          *p = from_f32<T>(to_f32(*p) + acc[i][j][r]);
+        }
+      }
+  } else {
+    T* pool = reinterpret_cast<T*>(qe.pool) + qe.layer_base;
+    const int dh = qe.dh;
+    const size_t page_elems = (size_t)16 * dh;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (m >= M) continue;
+        if (nw < qe.nk_end) {
+          const bool isq = nw < qe.nq_end;
+          const int local = isq ? nw : nw - qe.nq_end;
+          const int head = local / dh;
+          const int f0 = (dh == 128 ? ((local % dh) >> 6) * 32 : 0) + c;
+          const int f1 = f0 + (dh >> 1);
+          const float a0 = acc[i][0][r], a1 = acc[i][1][r];
+          const float2 cs = qe.rope[(size_t)qe.pos[m] * (dh >> 1) + f0];
+          const float o0 = a0 * cs.x - a1 * cs.y;
+          const float o1 = a1 * cs.x + a0 * cs.y;
+          if (isq) {
+            T* qp = reinterpret_cast<T*>(qe.qbuf) + ((size_t)m * qe.hq + head) * dh;
+            qp[f0] = from_f32<T>(o0);
+            qp[f1] = from_f32<T>(o1);
+          } else {
+            const int sl = qe.kvslot[m];
+            T* kb = pool + ((size_t)(sl >> 4) * qe.hkv + head) * 2 * page_elems + (size_t)(sl & 15) * dh;
+            kb[f0] = from_f32<T>(o0);
+            kb[f1] = from_f32<T>(o1);
+          }
+        } else {
+          const int sl = qe.kvslot[m];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int local = nw + 32 * j + c - qe.nk_end;
+            const int head = local / dh, f = local % dh;
+            T* vb = pool + ((size_t)(sl >> 4) * qe.hkv + head) * 2 * page_elems + page_elems;
+            vb[(size_t)f * 16 + (sl & 15)] = from_f32<T>(acc[i][j][r]);
+          }
+        }
+      }
+  }
+}
+
+// ------------------------------------------------------------------ attention
+// Block = 4 waves = 128 query rows (tokens_per_tile x G heads of one KV head);
+// wave w owns rows [32w, 32w+32).  Per step two pages (32 keys) of K and V go
+// through LDS.  S^T = K Q^T (keys as MFMA rows, query rows as columns) keeps a
+// query row's softmax statistics in one lane column, so that O^T = V^T P^T
+// rescales per lane with no cross-lane traffic besides the two half-waves.
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::frag frag_zero();
+template <>
+__device__ __forceinline__ bf16x8 frag_zero<bf16s>() {
+  bf16x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = (__bf16)0.0f;
+  return z;
+}
+template <>
+__device__ __forceinline__ float frag_zero<float>() { return 0.f; }
+
+// LDS V tile [DH][32 keys], 4-key units swizzled by the row.
+__device__ __forceinline__ int v_off(int d, int key) {
+  const int u = (key >> 2) ^ (d & 7);
+  return d * 32 + u * 4 + (key & 3);
+}
+
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void attn_kernel(const AttnTile* __restrict__ tiles,
+                                                   const int32_t* __restrict__ plist,
+                                                   const int32_t* __restrict__ tok_pos, const T* __restrict__ q,
+                                                   const T* __restrict__ pool, T* __restrict__ o,
+                                                   float* __restrict__ part_o, float* __restrict__ part_lse,
+                                                   int hq, int hkv, size_t layer_base, float scale_log2) {
+  using MF = Mfma<T>;
+  constexpr int KL = MF::KL, KSTEP = MF::KSTEP;
+  constexpr int NKS = DH / KSTEP;
+  constexpr int CH = 16 / sizeof(T);
+  constexpr int KCH = DH / CH;            // 16-byte chunks per K row
+  constexpr int PAGE_ELEMS = 16 * DH;
+  constexpr int PAGE_CHUNKS = PAGE_ELEMS / CH;
+  constexpr int VCPR = 16 / CH;           // 16-byte chunks per V^T row of a page
+  constexpr int NDB = DH / 32;
+  static_assert(PAGE_CHUNKS == 256, "two pages per step = 512 chunks = 2 per thread");
+  __shared__ __attribute__((aligned(16))) T sK[2][32 * DH];
+  __shared__ __attribute__((aligned(16))) T sV[2][DH * 32];
+
+  const AttnTile tile = tiles[blockIdx.x];
+  const int kvh = blockIdx.y;
+  const int G = hq / hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 31, hh = lane >> 5;
+  const int row = wave * 32 + c;
+  const int ti = row / G, hg = row % G;
+  const bool row_ok = ti < tile.n_tok;
+  const int t = tile.t0 + (row_ok ? ti : 0);
+  const int qhead = kvh * G + hg;
+  const int qpos = tok_pos[t];
+
+  typename MF::frag qf[NKS];
+  {
+    const T* qrow = q + ((size_t)t * hq + qhead) * DH;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = row_ok ? MF::load(qrow + ks * KSTEP + KL * hh) : frag_zero<T>();
+  }
+
+  const T* kvbase = pool + layer_base + (size_t)kvh * 2 * PAGE_ELEMS;
+  const size_t page_stride = (size_t)hkv * 2 * PAGE_ELEMS;
+  const int nst = (tile.n_pages + 1) >> 1;
+
+  uint4 rk[2], rv[2];
+  auto gload = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int lp = 2 * st + i;  // chunk tid + 256 i belongs to page i of the step
+      if (lp < tile.n_pages) {
+        const T* kb = kvbase + (size_t)plist[2 * (tile.page_off + lp)] * page_stride;
+        rk[i] = reinterpret_cast<const uint4*>(kb)[tid];
+        rv[i] = reinterpret_cast<const uint4*>(kb + PAGE_ELEMS)[tid];
+      } else {
+        rk[i] = make_uint4(0, 0, 0, 0);
+        rv[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int krow = 16 * i + tid / KCH, kch = tid % KCH;
+      *reinterpret_cast<uint4*>(&sK[buf][krow * DH + ((kch ^ (krow & (KCH - 1))) * CH)]) = rk[i];
+      const int d = tid / VCPR, key0 = 16 * i + (tid % VCPR) * CH;
+      if constexpr (CH == 8) {
+        *reinterpret_cast<uint2*>(&sV[buf][v_off(d, key0)]) = make_uint2(rv[i].x, rv[i].y);
+        *reinterpret_cast<uint2*>(&sV[buf][v_off(d, key0 + 4)]) = make_uint2(rv[i].z, rv[i].w);
+      } else {
+        *reinterpret_cast<uint4*>(&sV[buf][v_off(d, key0)]) = rv[i];
+      }
+    }
+  };
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int b = 0; b < NDB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
+  float mrun = kNegInf, lrun = 0.f;
+
+  if (nst > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nst) gload(st + 1);
+
+    // S^T = K Q^T
+    f32x16 S;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int e = ks * KSTEP + KL * hh;
+      const int ch = e / CH, within = e % CH;
+      const typename MF::frag a = MF::load(&sK[buf][c * DH + ((ch ^ (c & (KCH - 1))) * CH) + within]);
+      S = MF::mma(a, qf[ks], S);
+    }
+    // mask, scale, online softmax (statistics per lane column)
+    const int lp0 = 2 * st;
+    const int v0 = plist[2 * (tile.page_off + lp0) + 1];
+    const int v1 = (lp0 + 1 < tile.n_pages) ? plist[2 * (tile.page_off + lp0 + 1) + 1] : 0;
+    float p[16];
+    float mloc = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * hh + (r & 3);
+      const int pi = key >> 4, slot = key & 15;
+      bool ok = slot < (pi ? v1 : v0);
+      if (tile.causal) ok = ok && (tile.kv_pos0 + 16 * (lp0 + pi) + slot <= qpos);
+      p[r] = ok ? S[r] * scale_log2 : kNegInf;
+      mloc = fmaxf(mloc, p[r]);
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float mnew = fmaxf(mrun, mloc);
+    const float muse = (mnew == kNegInf) ? 0.f : mnew;
+    const float alpha = exp2f(mrun - muse);
+    float lsum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[r] = exp2f(p[r] - muse);
+      lsum += p[r];
+    }
+    lsum += __shfl_xor(lsum, 32, 64);
+    lrun = lrun * alpha + lsum;
+    mrun = mnew;
+#pragma unroll
+    for (int b = 0; b < NDB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+
+    // O^T += V^T P^T; MFMA t covers keys {8j + 4*hh + i : 4j + i in [t*KL, t*KL+KL)}
+#pragma unroll
+    for (int tt = 0; tt < 16 / KL; ++tt) {
+      typename MF::frag pb;
+      if constexpr (KL == 8) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) pb[s] = (__bf16)p[8 * tt + s];
+      } else {
+        pb = p[tt];
+      }
+#pragma unroll
+      for (int b = 0; b < NDB; ++b) {
+        const int d = 32 * b + c;
+        typename MF::frag va;
+        if constexpr (KL == 8) {
+          const uint2 lo = *reinterpret_cast<const uint2*>(&sV[buf][v_off(d, 16 * tt + 4 * hh)]);
+          const uint2 hi = *reinterpret_cast<const uint2*>(&sV[buf][v_off(d, 16 * tt + 8 + 4 * hh)]);
+          va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        } else {
+          const int key = 8 * (tt >> 2) + 4 * hh + (tt & 3);
+          va = MF::load(&sV[buf][v_off(d, key)]);
+        }
+        oacc[b] = MF::mma(va, pb, oacc[b]);
+      }
+    }
+    if (st + 1 < nst) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!row_ok) return;
+  const float inv = lrun > 0.f ? 1.0f / lrun : 0.f;
+  if (tile.out_mode == 0) {
+    T* orow = o + ((size_t)t * hq + qhead) * DH;
+#pragma unroll
+    for (int b = 0; b < NDB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) orow[32 * b + 8 * (r >> 2) + 4 * hh + (r & 3)] = from_f32<T>(oacc[b][r] * inv);
+  } else {
+    const size_t prow = (size_t)tile.part_slot * 128 + row;
+    float* orow = part_o + prow * DH;
+#pragma unroll
+    for (int b = 0; b < NDB; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float4 v = make_float4(oacc[b][4 * j] * inv, oacc[b][4 * j + 1] * inv, oacc[b][4 * j + 2] * inv,
+                               oacc[b][4 * j + 3] * inv);
+        *reinterpret_cast<float4*>(orow + 32 * b + 8 * j + 4 * hh) = v;
+      }
+    if (hh == 0) part_lse[prow] = lrun > 0.f ? mrun + log2f(lrun) : kNegInf;
+  }
+}
+
+// ------------------------------------------------------------------ merge
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void merge_kernel(const MergeItem* __restrict__ items,
+                                                    const float* __restrict__ part_o,
+                                                    const float* __restrict__ part_lse, T* __restrict__ o, int hq,
+                                                    int G) {
+  const MergeItem it = items[blockIdx.x];
+  for (int e = threadIdx.x; e < hq * DH / 4; e += blockDim.x) {
+    const int head = e / (DH / 4), d4 = (e % (DH / 4)) * 4, hg = head % G;
+    const int r0 = it.own_row + hg;
+    float M = part_lse[r0];
+    for (int c = 0; c < it.n_chunks; ++c) M = fmaxf(M, part_lse[it.anc_row0 + 128 * c + hg]);
+    float w = exp2f(part_lse[r0] - M);
+    float4 v = *reinterpret_cast<const float4*>(part_o + (size_t)r0 * DH + d4);
+    float4 acc = make_float4(w * v.x, w * v.y, w * v.z, w * v.w);
+    float ws = w;
+    for (int c = 0; c < it.n_chunks; ++c) {
+      const int rc = it.anc_row0 + 128 * c + hg;
+      w = exp2f(part_lse[rc] - M);
+      v = *reinterpret_cast<const float4*>(part_o + (size_t)rc * DH + d4);
+      acc.x += w * v.x;
+      acc.y += w * v.y;
+      acc.z += w * v.z;
+      acc.w += w * v.w;
+      ws += w;
+    }
+    const float inv = 1.0f / ws;
+    T* orow = o + ((size_t)it.t * hq + head) * DH + d4;
+    orow[0] = from_f32<T>(acc.x * inv);
+    orow[1] = from_f32<T>(acc.y * inv);
+    orow[2] = from_f32<T>(acc.z * inv);
+    orow[3] = from_f32<T>(acc.w * inv);
+  }
+}
+
+// ------------------------------------------------------------------ readout
+template <typename T>
+__global__ __launch_bounds__(256) void readout_kernel(const T* __restrict__ U, const T* __restrict__ g,
+                                                      const T* __restrict__ x, const ReadoutItem* __restrict__ items,
+                                                      const int32_t* __restrict__ labels, float* __restrict__ probs,
+                                                      int d, float eps) {
+  constexpr int CH = 16 / sizeof(T);
+  extern __shared__ float sh[];  // d floats of normed hidden, then 64 logits
+  __shared__ float scratch[4];
+  float* hn = sh;
+  float* logit = sh + d;
+  const ReadoutItem it = items[blockIdx.x];
+  const T* xr = x + (size_t)it.row * d;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float ss = 0.f;
+  for (int i = tid * CH; i < d; i += 256 * CH) {
+    float v[CH];
+    load16<T>(xr + i, v);
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      ss += v[e] * v[e];
+      hn[i + e] = v[e];
+    }
+  }
+  ss = block_sum256(ss, scratch);
+  const float r = 1.0f / sqrtf(ss / float(d) + eps);
+  for (int i = tid * CH; i < d; i += 256 * CH) {
+    float gg[CH];
+    load16<T>(g + i, gg);
+#pragma unroll
+    for (int e = 0; e < CH; ++e) hn[i + e] = to_f32(from_f32<T>(hn[i + e] * r * gg[e]));
+  }
+  __syncthreads();
+  for (int k = wave; k < it.k; k += 4) {
+    const T* ur = U + (size_t)labels[it.label_off + k] * d;
+    float z = 0.f;
+    for (int i = lane * CH; i < d; i += 64 * CH) {
+      float u[CH];
+      load16<T>(ur + i, u);
+#pragma unroll
+      for (int e = 0; e < CH; ++e) z += hn[i + e] * u[e];
+    }
+    z = wave_sum(z);
+    if (lane == 0) logit[k] = z;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const float z = lane < it.k ? logit[lane] : kNegInf;
+    const float mx = wave_max(z);
+    const float e = lane < it.k ? expf(z - mx) : 0.f;
+    const float s = wave_sum(e);
+    if (lane < it.k) probs[it.out_off + lane] = e / s;
+  }
+}
+
+}  // namespace dev
+
+// ------------------------------------------------------------------ launchers
+using dev::bf16s;
+
+#define JEV_DISPATCH_T(m, ...)      \
+  if ((m).dtype == 1) {             \
+    using T = bf16s;                \
+    __VA_ARGS__                     \
+  } else {                          \
+    using T = float;                \
+    __VA_ARGS__                     \
+  }
+
+hipError_t launch_embed(const ModelDims& m, const void* embed, const int32_t* tok, int32_t T_, void* x,
+                        hipStream_t s) {
+  if (T_ <= 0) return hipSuccess;
+  JEV_DISPATCH_T(m, {
+    hipLaunchKernelGGL(dev::embed_kernel<T>, dim3(T_), dim3(256), 0, s, reinterpret_cast<const T*>(embed), tok,
+                       m.d, reinterpret_cast<T*>(x));
+  })
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const ModelDims& m, const void* x, const void* g, int32_t T_, void* h, hipStream_t s) {
+  if (T_ <= 0) return hipSuccess;
+  JEV_DISPATCH_T(m, {
+    hipLaunchKernelGGL(dev::rmsnorm_kernel<T>, dim3(T_), dim3(256), 0, s, reinterpret_cast<const T*>(x),
+                       reinterpret_cast<const T*>(g), m.d, m.eps, reinterpret_cast<T*>(h));
+  })
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv(const ModelDims& m, const LayerW& w, int32_t layer, const void* h, int32_t T_,
+                      const int32_t* pos, const int32_t* kvslot, const float* rope, void* qbuf, void* pool,
+                      hipStream_t s) {
+  if (T_ <= 0) return hipSuccess;
+  const int N = (m.hq + 2 * m.hkv) * m.dh;
+  dev::QkvEpi qe;
+  qe.hq = m.hq;
+  qe.hkv = m.hkv;
+  qe.dh = m.dh;
+  qe.nq_end = m.hq * m.dh;
+  qe.nk_end = (m.hq + m.hkv) * m.dh;
+  qe.pos = pos;
+  qe.kvslot = kvslot;
+  qe.rope = reinterpret_cast<const float2*>(rope);
+  qe.qbuf = qbuf;
+  qe.pool = pool;
+  qe.layer_base = (size_t)layer * m.n_pages * m.hkv * 2 * 16 * m.dh;
+  dev::ResEpi re{nullptr, 0};
+  dim3 grid(N / dev::GBN, (T_ + dev::GBM - 1) / dev::GBM);
+  JEV_DISPATCH_T(m, {
+    dev::GemmB<T> gb{reinterpret_cast<const T*>(w.wq), reinterpret_cast<const T*>(w.wk),
+                     reinterpret_cast<const T*>(w.wv), qe.nq_end, qe.nk_end, m.dh};
+    hipLaunchKernelGGL((dev::gemm_kernel<T, dev::EPI_QKV>), grid, dim3(256), 0, s, reinterpret_cast<const T*>(h),
+                       T_, m.d, gb, N, qe, re);
+  })
+  return hipGetLastError();
+}
+
+hipError_t launch_oproj(const ModelDims& m, const LayerW& w, const void* o, int32_t T_, void* x, hipStream_t s) {
+  if (T_ <= 0) return hipSuccess;
+  const int N = m.d, K = m.hq * m.dh;
+  dev::QkvEpi qe{};
+  dev::ResEpi re{x, m.d};
+  dim3 grid(N / dev::GBN, (T_ + dev::GBM - 1) / dev::GBM);
+  JEV_DISPATCH_T(m, {
+    dev::GemmB<T> gb{reinterpret_cast<const T*>(w.wo), nullptr, nullptr, N, N, 0};
+    hipLaunchKernelGGL((dev::gemm_kernel<T, dev::EPI_RES>), grid, dim3(256), 0, s, reinterpret_cast<const T*>(o),
+                       T_, K, gb, N, qe, re);
+  })
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const ModelDims& m, int32_t layer, const AttnTile* tiles, int32_t n_tiles,
+                            const int32_t* page_list, const int32_t* tok_pos, const void* qbuf, const void* pool,
+                            void* o, float* part_o, float* part_lse, hipStream_t s) {
+  if (n_tiles <= 0) return hipSuccess;
+  const size_t layer_base = (size_t)layer * m.n_pages * m.hkv * 2 * 16 * m.dh;
+  const float scale_log2 = float(1.4426950408889634 / std::sqrt((double)m.dh));
+  dim3 grid(n_tiles, m.hkv);
+  if (m.dtype == 1 && m.dh == 128) {
+    hipLaunchKernelGGL((dev::attn_kernel<bf16s, 128>), grid, dim3(256), 0, s, tiles, page_list, tok_pos,
+                       reinterpret_cast<const bf16s*>(qbuf), reinterpret_cast<const bf16s*>(pool),
+                       reinterpret_cast<bf16s*>(o), part_o, part_lse, m.hq, m.hkv, layer_base, scale_log2);
+  } else if (m.dtype == 0 && m.dh == 64) {
+    hipLaunchKernelGGL((dev::attn_kernel<float, 64>), grid, dim3(256), 0, s, tiles, page_list, tok_pos,
+                       reinterpret_cast<const float*>(qbuf), reinterpret_cast<const float*>(pool),
+                       reinterpret_cast<float*>(o), part_o, part_lse, m.hq, m.hkv, layer_base, scale_log2);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const ModelDims& m, const MergeItem* items, int32_t n_items, const float* part_o,
+                        const float* part_lse, void* o, hipStream_t s) {
+  if (n_items <= 0) return hipSuccess;
+  const int G = m.hq / m.hkv;
+  if (m.dtype == 1 && m.dh == 128) {
+    hipLaunchKernelGGL((dev::merge_kernel<bf16s, 128>), dim3(n_items), dim3(256), 0, s, items, part_o, part_lse,
+                       reinterpret_cast<bf16s*>(o), m.hq, G);
+  } else if (m.dtype == 0 && m.dh == 64) {
+    hipLaunchKernelGGL((dev::merge_kernel<float, 64>), dim3(n_items), dim3(256), 0, s, items, part_o, part_lse,
+                       reinterpret_cast<float*>(o), m.hq, G);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_readout(const ModelDims& m, const void* unembed, const void* final_norm, const void* x,
+                          const ReadoutItem* items, int32_t n_items, const int32_t* labels, float* probs,
+                          hipStream_t s) {
+  if (n_items <= 0) return hipSuccess;
+  const size_t shmem = (size_t)(m.d + 64) * sizeof(float);
+  JEV_DISPATCH_T(m, {
+    hipLaunchKernelGGL(dev::readout_kernel<T>, dim3(n_items), dim3(256), shmem, s,
+                       reinterpret_cast<const T*>(unembed), reinterpret_cast<const T*>(final_norm),
+                       reinterpret_cast<const T*>(x), items, labels, probs, m.d, m.eps);
+  })
+  return hipGetLastError();
+}
+
+}  // namespace jev

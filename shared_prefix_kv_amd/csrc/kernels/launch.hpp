@@ -1,0 +1,73 @@
+// Host-callable launchers of the gfx950 kernels and the descriptor formats the
+// host engine fills in.  All pointers are device pointers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jev {
+
+// One attention work item: query rows of `n_tok` consecutive round tokens
+// starting at `t0` (each token contributes Hq/Hkv rows, one per query head of
+// the KV head) against a key list of `n_pages` pages at `page_off` in the
+// page-list array (pairs page id, valid slots).  causal: key slot s of list
+// page i sits at position kv_pos0 + 16*i + s and is visible to a query at
+// position p iff that is <= p; otherwise every valid key is visible.
+// out_mode 0: normalised output written straight to the attention output;
+// 1: normalised output and log2-sum-exp written to partial slot `part_slot`
+// (rows part_slot*128 + token_in_tile*G + head_in_group).
+struct AttnTile {
+  int32_t t0, n_tok, page_off, n_pages, causal, kv_pos0, out_mode, part_slot;
+};
+
+// Merge of the partial states of one round token: its own causal part (row
+// base own_row) and n_chunks prefix chunks (row bases anc_row0 + 128*c).
+struct MergeItem {
+  int32_t t, own_row, anc_row0, n_chunks;
+};
+
+// Readout of one candidate: final norm of round row `row`, logits at
+// labels[label_off .. label_off+k), softmax written to probs[out_off ..].
+struct ReadoutItem {
+  int32_t row, label_off, k, out_off;
+};
+
+struct ModelDims {
+  int32_t n_layers, d, hq, hkv, dh, vocab, n_pages;
+  float eps;
+  int32_t dtype;  // 0 f32, 1 bf16
+};
+
+struct LayerW {
+  const void* norm;
+  const void* wq;
+  const void* wk;
+  const void* wv;
+  const void* wo;
+};
+
+// x[t] = E[tok[t]]
+hipError_t launch_embed(const ModelDims& m, const void* embed, const int32_t* tok, int32_t T, void* x,
+                        hipStream_t s);
+// h = RMSNorm(x) * g, stored
+hipError_t launch_rmsnorm(const ModelDims& m, const void* x, const void* g, int32_t T, void* h,
+                          hipStream_t s);
+// q/k/v projections of h with RoPE at pos[t]; q -> qbuf [T][Hq][dh]; k, v -> the
+// layer's pages at kvslot[t] = page*16 + slot.  rope: float2 [pos][dh/2].
+hipError_t launch_qkv(const ModelDims& m, const LayerW& w, int32_t layer, const void* h, int32_t T,
+                      const int32_t* pos, const int32_t* kvslot, const float* rope, void* qbuf,
+                      void* pool, hipStream_t s);
+// attention tiles (grid n_tiles x Hkv)
+hipError_t launch_attention(const ModelDims& m, int32_t layer, const AttnTile* tiles, int32_t n_tiles,
+                            const int32_t* page_list, const int32_t* tok_pos, const void* qbuf,
+                            const void* pool, void* o, float* part_o, float* part_lse, hipStream_t s);
+hipError_t launch_merge(const ModelDims& m, const MergeItem* items, int32_t n_items, const float* part_o,
+                        const float* part_lse, void* o, hipStream_t s);
+// x += o Wo^T (stored)
+hipError_t launch_oproj(const ModelDims& m, const LayerW& w, const void* o, int32_t T, void* x,
+                        hipStream_t s);
+hipError_t launch_readout(const ModelDims& m, const void* unembed, const void* final_norm, const void* x,
+                          const ReadoutItem* items, int32_t n_items, const int32_t* labels, float* probs,
+                          hipStream_t s);
+
+}  // namespace jev

@@ -1,0 +1,170 @@
+"""Host library on the CPU: exported symbols, bit-exact plans and page tables
+against the oracle's planner, and error paths (planning-only contexts)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import plan as op
+from synth import make_instance, workload
+
+jev = pytest.importorskip("shared_prefix_kv_amd.jev")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "jev.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(jev_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert "jev_prefill_prefix" in names and "jev_score_branches" in names and "jev_free_pages" in names
+    L = jev.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(jev.EXPORTED) == names
+
+
+def desc_for(wl, max_pos=40000, max_tok=4096):
+    m = wl.model
+    return jev.make_desc(m.n_layers, m.d, m.hq, m.hkv, m.dh, m.vocab, m.dtype, m.rope_theta, m.eps, max_pos,
+                         max_tok)
+
+
+def dry(wl, n_pages):
+    return jev.Context(desc_for(wl), n_pages)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_plan_of_each_config_matches_oracle(idx):
+    wl = workload(idx)
+    inst = make_instance(wl)
+    seqs = [s for s, _ in inst.full_sequences(0)]
+    ctx = dry(wl, 4096)
+    tree = op.ResidentTree(op.PagePool(4096))
+    assert ctx.plan(seqs) == op.plan_candidates(tree, seqs).serialize()
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_plan_random_tries_bit_exact(seed):
+    rng = np.random.default_rng(500 + seed)
+    n = int(rng.integers(1, 10))
+    base = list(rng.integers(0, 3, 90))
+    seqs = []
+    for _ in range(n):
+        cut = int(rng.integers(0, 90))
+        seqs.append(base[:cut] + list(rng.integers(0, 3, int(rng.integers(1, 45)))))
+    if rng.integers(0, 3) == 0:
+        seqs.append(list(seqs[0]))          # duplicate candidate
+    wl = workload(1)
+    n_pages = int(rng.integers(20, 200))
+    ctx = dry(wl, n_pages)
+    tree = op.ResidentTree(op.PagePool(n_pages))
+    # optional resident prefixes shared by some candidates
+    if rng.integers(0, 2):
+        k = int(rng.integers(1, 40))
+        (h,) = ctx.prefill_prefix([0], [base[:k]])
+        assert tree.prefill([(0, base[:k])]) == [h]
+    try:
+        want = op.plan_candidates(tree, seqs).serialize()
+    except op.PoolExhausted:
+        with pytest.raises(jev.JevError) as e:
+            ctx.plan(seqs)
+        assert e.value.code == jev.JEV_ENOMEM
+        return
+    assert ctx.plan(seqs) == want
+
+
+def test_config_page_tables_and_refcounts():
+    wl = workload(4)
+    inst = make_instance(wl)
+    ctx = dry(wl, 2000)
+    hs = ctx.prefill_prefix([0] * 16, inst.prefixes)
+    for r, h in enumerate(hs):
+        pages, valid = ctx.page_table(h)
+        assert pages == list(range(75 * r, 75 * r + 75)) and valid == [16] * 75
+    st = ctx.stats()
+    assert st["pages_in_use"] == 1200 and st["resident_prefixes"] == 16
+    # identical prefix again: same handle, no pages
+    assert ctx.prefill_prefix([0], [inst.prefixes[3]]) == [hs[3]]
+    assert ctx.stats()["pages_in_use"] == 1200
+    ctx.free_pages([hs[3]])
+    assert ctx.stats()["pages_in_use"] == 1200
+    ctx.free_pages([hs[3]])
+    assert ctx.stats()["pages_in_use"] == 1125
+    with pytest.raises(jev.JevError) as e:
+        ctx.free_pages([hs[3]])
+    assert e.value.code == jev.JEV_EHANDLE
+
+
+def test_tree_of_prefixes_path_pages_and_match():
+    wl = workload(1)
+    ctx = dry(wl, 64)
+    (a,) = ctx.prefill_prefix([0], [list(range(20))])
+    (b,) = ctx.prefill_prefix([a], [list(range(20, 25))])
+    assert ctx.page_table(b) == ([0, 1, 2], [16, 4, 5])
+    assert ctx.match(list(range(30))) == (b, 25)
+    assert ctx.match(list(range(25))) == (a, 20)
+    assert ctx.match([7]) == (0, 0)
+    # the candidate plan anchors below the resident prefix
+    seqs = [list(range(25)) + [1, 2], list(range(25)) + [3]]
+    tree = op.ResidentTree(op.PagePool(64))
+    (oa,) = tree.prefill([(0, list(range(20)))])
+    (ob,) = tree.prefill([(oa, list(range(20, 25)))])
+    assert ctx.plan(seqs) == op.plan_candidates(tree, seqs).serialize()
+    # releasing the parent first keeps it alive for its child
+    ctx.free_pages([a])
+    assert ctx.stats()["resident_prefixes"] == 2
+    ctx.free_pages([b])
+    assert ctx.stats()["resident_prefixes"] == 0 and ctx.stats()["pages_in_use"] == 0
+
+
+def test_errors_leave_state_unchanged():
+    wl = workload(1)
+    ctx = dry(wl, 10)
+    with pytest.raises(jev.JevError) as e:
+        ctx.prefill_prefix([0, 0], [list(range(100)), list(range(100, 200))])
+    assert e.value.code == jev.JEV_ENOMEM
+    assert ctx.stats()["pages_in_use"] == 0 and ctx.stats()["resident_prefixes"] == 0
+    with pytest.raises(jev.JevError) as e:
+        ctx.prefill_prefix([0], [[]])
+    assert e.value.code == jev.JEV_EINVAL
+    with pytest.raises(jev.JevError) as e:
+        ctx.prefill_prefix([0], [[1024]])          # vocab is 1024
+    assert e.value.code == jev.JEV_EINVAL
+    with pytest.raises(jev.JevError) as e:
+        ctx.prefill_prefix([99], [[1]])
+    assert e.value.code == jev.JEV_EHANDLE
+    (h,) = ctx.prefill_prefix([0], [list(range(100))])
+    # scoring on a planning-only context: validation first, then ESTATE
+    with pytest.raises(jev.JevError) as e:
+        ctx.score_branches([h], [[1]], [[5]])      # one label only
+    assert e.value.code == jev.JEV_EINVAL
+    with pytest.raises(jev.JevError) as e:
+        ctx.score_branches([h], [[1]], [[5, 5]])   # duplicate labels
+    assert e.value.code == jev.JEV_EINVAL
+    with pytest.raises(jev.JevError) as e:
+        ctx.score_branches([h], [[1]], [list(range(65))])
+    assert e.value.code == jev.JEV_EINVAL
+    with pytest.raises(jev.JevError) as e:
+        ctx.score_branches([h], [[]], [[1, 2]])    # the last position must be computed
+    assert e.value.code == jev.JEV_EINVAL
+    with pytest.raises(jev.JevError) as e:
+        ctx.score_branches([h], [[1]], [[1, 2]])
+    assert e.value.code == jev.JEV_ESTATE
+    assert ctx.stats()["pages_in_use"] == 7
+
+
+def test_unsupported_shapes_rejected():
+    L = jev.lib()
+    bad = jev.make_desc(1, 256, 4, 3, 64, 1024, "f32", 1e4, 1e-6, 100, 100)   # Hkv does not divide Hq
+    assert L.jev_workspace_bytes(ctypes.byref(bad)) == 0
+    bad = jev.make_desc(1, 256, 4, 4, 96, 1024, "bf16", 1e4, 1e-6, 100, 100)
+    assert L.jev_workspace_bytes(ctypes.byref(bad)) == 0
+    with pytest.raises(jev.JevError):
+        jev.Context(bad, 10)
