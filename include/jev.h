@@ -190,12 +190,15 @@ typedef struct {
 
 int jev_stats(jev_ctx* ctx, jev_stats_t* out);
 
-/* Debug tap for parity tests: when set, the next scoring/prefill call copies,
- * for layer `layer`, the attention output (after the log-sum-exp merge, model
- * dtype, [round token][Hq*dh] rows of the call's single round, in the call's
- * token order) into dst (device, cap_rows rows).  NULL dst disables.  The tap
- * covers single-round calls only. */
-int jev_debug_tap(jev_ctx* ctx, int32_t layer, void* dst, int64_t cap_rows);
+/* Debug taps for parity tests.  Each call registers one tap (up to 16); a
+ * NULL dst removes every tap.  what = JEV_TAP_ATTN: the attention output of
+ * `layer` (after the log-sum-exp merge); what = JEV_TAP_RESID: the residual
+ * stream entering `layer` (layer == n_layers: the stream entering the final
+ * norm).  Rows are model-dtype [token][width] in the round's token order (nodes
+ * grouped by parent, input order within a group); at most cap_rows rows are
+ * copied to dst (device).  Taps apply to single-round calls only. */
+enum { JEV_TAP_ATTN = 0, JEV_TAP_RESID = 1 };
+int jev_debug_tap(jev_ctx* ctx, int32_t what, int32_t layer, void* dst, int64_t cap_rows);
 
 const char* jev_last_error(void);
 

@@ -62,8 +62,9 @@ WsLayout layout(const jev_model_desc& d) {
   const int64_t T = d.max_round_tokens;
   const int G = d.n_q_heads / d.n_kv_heads;
   const int64_t tt = kRowsPerTile / G;
-  const int64_t slots = ((T + tt - 1) / tt + 64) * (kMaxChunks + 1);
-  L.part_rows = slots * kRowsPerTile;
+  // partial rows: own tiles plus prefix-chunk tiles of a round, per KV head
+  // (the chunk count is chosen so that tiles x chunks x Hkv stays near 512)
+  L.part_rows = int64_t(kRowsPerTile) * (int64_t(d.n_kv_heads) * (2 * ((T + tt - 1) / tt) + 64) + 1024);
   L.desc_ints = 32 * T + 4 * int64_t(d.max_positions) + (1 << 18);
   const size_t e = elt_size(d);
   size_t off = 0;
@@ -157,9 +158,12 @@ struct jev_ctx {
   jev::PagePool pages;
   std::unique_ptr<jev::ResidentTree> tree;
   jev_stats_t stats{};
-  int32_t tap_layer = -1;
-  void* tap_dst = nullptr;
-  int64_t tap_rows = 0;
+  struct Tap {
+    int32_t what, layer;
+    void* dst;
+    int64_t rows;
+  };
+  std::vector<Tap> taps;
 };
 
 namespace {
@@ -296,7 +300,7 @@ int build_round(jev_ctx* ctx, std::vector<RNode>& nodes, std::vector<int32_t>& h
   std::vector<jev::AttnTile> tiles;
   std::vector<jev::MergeItem> merges;
   int64_t slot = 0;
-  std::vector<int64_t> own_row(T, -1), anc_row(T, -1);
+  std::vector<int32_t> own_slot(T, -1), own_ti(T, -1);
   for (size_t i = 0; i < nodes.size(); ++i) {
     const RNode& nd = nodes[i];
     const bool has_anc = !nd.anc.empty();
@@ -312,7 +316,10 @@ int build_round(jev_ctx* ctx, std::vector<RNode>& nodes, std::vector<int32_t>& h
       tl.out_mode = has_anc ? 1 : 0;
       tl.part_slot = has_anc ? int32_t(slot) : 0;
       if (has_anc) {
-        for (int64_t j = 0; j < nt; ++j) own_row[node_t0[i] + i0 + j] = slot * kRowsPerTile + j * G;
+        for (int64_t j = 0; j < nt; ++j) {
+          own_slot[node_t0[i] + i0 + j] = int32_t(slot);
+          own_ti[node_t0[i] + i0 + j] = int32_t(j);
+        }
         ++slot;
       }
       tiles.push_back(tl);
@@ -325,7 +332,7 @@ int build_round(jev_ctx* ctx, std::vector<RNode>& nodes, std::vector<int32_t>& h
     const int64_t nch = (g.anc_pages + cp - 1) / cp;
     for (int64_t t0 = g.t0; t0 < g.t1; t0 += TT) {
       const int64_t nt = std::min<int64_t>(TT, g.t1 - t0);
-      for (int64_t j = 0; j < nt; ++j) anc_row[t0 + j] = slot * kRowsPerTile + j * G;
+      const int64_t slot0 = slot;
       for (int64_t c = 0; c < nch; ++c) {
         jev::AttnTile tl{};
         tl.t0 = int32_t(t0);
@@ -338,11 +345,11 @@ int build_round(jev_ctx* ctx, std::vector<RNode>& nodes, std::vector<int32_t>& h
         tiles.push_back(tl);
       }
       for (int64_t j = 0; j < nt; ++j)
-        merges.push_back(jev::MergeItem{int32_t(t0 + j), int32_t(own_row[t0 + j]), int32_t(anc_row[t0 + j]),
-                                        int32_t(nch)});
+        merges.push_back(jev::MergeItem{int32_t(t0 + j), own_slot[t0 + j], own_ti[t0 + j], int32_t(slot0),
+                                        int32_t(j), int32_t(nch)});
     }
   }
-  if (slot * kRowsPerTile > ctx->L.part_rows)
+  if (slot * ctx->desc.n_kv_heads * kRowsPerTile > ctx->L.part_rows)
     return fail(JEV_ENOMEM, "round needs more partial-state rows than the workspace holds");
   rd->part_slots = slot;
   // heavy tiles first
@@ -352,7 +359,7 @@ int build_round(jev_ctx* ctx, std::vector<RNode>& nodes, std::vector<int32_t>& h
   rd->off_tiles = push(int64_t(tiles.size()) * 8);
   std::memcpy(hb.data() + rd->off_tiles, tiles.data(), tiles.size() * sizeof(jev::AttnTile));
   rd->n_merge = int32_t(merges.size());
-  rd->off_merge = push(int64_t(merges.size()) * 4);
+  rd->off_merge = push(int64_t(merges.size()) * 6);
   std::memcpy(hb.data() + rd->off_merge, merges.data(), merges.size() * sizeof(jev::MergeItem));
   // readouts
   std::vector<jev::ReadoutItem> reads;
@@ -390,24 +397,32 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
   float* rope = reinterpret_cast<float*>(ctx->ws + ctx->L.rope);
   float* part_o = reinterpret_cast<float*>(ctx->ws + ctx->L.part_o);
   float* part_lse = reinterpret_cast<float*>(ctx->ws + ctx->L.part_lse);
+  const size_t elt = size_t(elt_size(ctx->desc));
+  auto tap = [&](int what, int layer, const void* src, int64_t T, size_t width) -> int {
+    if (rds.size() != 1) return JEV_OK;
+    for (const auto& tp : ctx->taps)
+      if (tp.what == what && tp.layer == layer) {
+        const int64_t rows = std::min<int64_t>(T, tp.rows);
+        HIPCHK(hipMemcpyAsync(tp.dst, src, size_t(rows) * width * elt, hipMemcpyDeviceToDevice, s));
+      }
+    return JEV_OK;
+  };
   for (const RoundDesc& rd : rds) {
     const int32_t* tok = dd + rd.off_tok;
     HIPCHK(jev::launch_embed(m, ctx->embed, tok, rd.T, x, s));
     for (int l = 0; l < m.n_layers; ++l) {
       const jev::LayerW& w = ctx->layers[l];
+      if (int rc = tap(JEV_TAP_RESID, l, x, rd.T, size_t(m.d))) return rc;
       HIPCHK(jev::launch_rmsnorm(m, x, w.norm, rd.T, h, s));
       HIPCHK(jev::launch_qkv(m, w, l, h, rd.T, dd + rd.off_pos, dd + rd.off_slot, rope, q, ctx->pool, s));
       HIPCHK(jev::launch_attention(m, l, reinterpret_cast<const jev::AttnTile*>(dd + rd.off_tiles), rd.n_tiles,
                                    dd + rd.off_plist, dd + rd.off_pos, q, ctx->pool, o, part_o, part_lse, s));
       HIPCHK(jev::launch_merge(m, reinterpret_cast<const jev::MergeItem*>(dd + rd.off_merge), rd.n_merge, part_o,
                                part_lse, o, s));
-      if (ctx->tap_dst && ctx->tap_layer == l && rds.size() == 1) {
-        const int64_t rows = std::min<int64_t>(rd.T, ctx->tap_rows);
-        HIPCHK(hipMemcpyAsync(ctx->tap_dst, o, size_t(rows) * m.hq * m.dh * elt_size(ctx->desc),
-                              hipMemcpyDeviceToDevice, s));
-      }
+      if (int rc = tap(JEV_TAP_ATTN, l, o, rd.T, size_t(m.hq) * m.dh)) return rc;
       HIPCHK(jev::launch_oproj(m, w, o, rd.T, x, s));
     }
+    if (int rc = tap(JEV_TAP_RESID, m.n_layers, x, rd.T, size_t(m.d))) return rc;
     HIPCHK(jev::launch_readout(m, ctx->unembed, ctx->final_norm, x,
                                reinterpret_cast<const jev::ReadoutItem*>(dd + rd.off_read), rd.n_read,
                                dd + rd.off_labels, probs, s));
@@ -760,12 +775,17 @@ int jev_stats(jev_ctx* ctx, jev_stats_t* out) {
   return JEV_OK;
 }
 
-int jev_debug_tap(jev_ctx* ctx, int32_t layer, void* dst, int64_t cap_rows) {
+int jev_debug_tap(jev_ctx* ctx, int32_t what, int32_t layer, void* dst, int64_t cap_rows) {
   if (!ctx) return fail(JEV_EINVAL, "NULL ctx");
-  if (dst && (layer < 0 || layer >= ctx->desc.n_layers || cap_rows < 1)) return fail(JEV_EINVAL, "bad tap");
-  ctx->tap_layer = layer;
-  ctx->tap_dst = dst;
-  ctx->tap_rows = cap_rows;
+  if (!dst) {
+    ctx->taps.clear();
+    return JEV_OK;
+  }
+  const int32_t max_layer = what == JEV_TAP_RESID ? ctx->desc.n_layers : ctx->desc.n_layers - 1;
+  if ((what != JEV_TAP_ATTN && what != JEV_TAP_RESID) || layer < 0 || layer > max_layer || cap_rows < 1)
+    return fail(JEV_EINVAL, "bad tap");
+  if (ctx->taps.size() >= 16) return fail(JEV_ENOMEM, "too many taps");
+  ctx->taps.push_back({what, layer, dst, cap_rows});
   return JEV_OK;
 }
 

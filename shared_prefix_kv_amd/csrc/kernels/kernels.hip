@@ -508,7 +508,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnTile* __restrict__ 
 #pragma unroll
       for (int r = 0; r < 16; ++r) orow[32 * b + 8 * (r >> 2) + 4 * hh + (r & 3)] = from_f32<T>(oacc[b][r] * inv);
   } else {
-    const size_t prow = (size_t)tile.part_slot * 128 + row;
+    const size_t prow = ((size_t)tile.part_slot * hkv + kvh) * 128 + row;
     float* orow = part_o + prow * DH;
 #pragma unroll
     for (int b = 0; b < NDB; ++b)
@@ -527,21 +527,24 @@ template <typename T, int DH>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeItem* __restrict__ items,
                                                     const float* __restrict__ part_o,
                                                     const float* __restrict__ part_lse, T* __restrict__ o, int hq,
-                                                    int G) {
+                                                    int hkv) {
   const MergeItem it = items[blockIdx.x];
+  const int G = hq / hkv;
   for (int e = threadIdx.x; e < hq * DH / 4; e += blockDim.x) {
-    const int head = e / (DH / 4), d4 = (e % (DH / 4)) * 4, hg = head % G;
-    const int r0 = it.own_row + hg;
+    const int head = e / (DH / 4), d4 = (e % (DH / 4)) * 4;
+    const int kvh = head / G, hg = head % G;
+    const size_t r0 = ((size_t)it.own_slot * hkv + kvh) * 128 + it.own_ti * G + hg;
+    auto chunk_row = [&](int c) { return ((size_t)(it.anc_slot0 + c) * hkv + kvh) * 128 + it.anc_ti * G + hg; };
     float M = part_lse[r0];
-    for (int c = 0; c < it.n_chunks; ++c) M = fmaxf(M, part_lse[it.anc_row0 + 128 * c + hg]);
+    for (int c = 0; c < it.n_chunks; ++c) M = fmaxf(M, part_lse[chunk_row(c)]);
     float w = exp2f(part_lse[r0] - M);
-    float4 v = *reinterpret_cast<const float4*>(part_o + (size_t)r0 * DH + d4);
+    float4 v = *reinterpret_cast<const float4*>(part_o + r0 * DH + d4);
     float4 acc = make_float4(w * v.x, w * v.y, w * v.z, w * v.w);
     float ws = w;
     for (int c = 0; c < it.n_chunks; ++c) {
-      const int rc = it.anc_row0 + 128 * c + hg;
+      const size_t rc = chunk_row(c);
       w = exp2f(part_lse[rc] - M);
-      v = *reinterpret_cast<const float4*>(part_o + (size_t)rc * DH + d4);
+      v = *reinterpret_cast<const float4*>(part_o + rc * DH + d4);
       acc.x += w * v.x;
       acc.y += w * v.y;
       acc.z += w * v.z;
@@ -711,13 +714,12 @@ hipError_t launch_attention(const ModelDims& m, int32_t layer, const AttnTile* t
 hipError_t launch_merge(const ModelDims& m, const MergeItem* items, int32_t n_items, const float* part_o,
                         const float* part_lse, void* o, hipStream_t s) {
   if (n_items <= 0) return hipSuccess;
-  const int G = m.hq / m.hkv;
   if (m.dtype == 1 && m.dh == 128) {
     hipLaunchKernelGGL((dev::merge_kernel<bf16s, 128>), dim3(n_items), dim3(256), 0, s, items, part_o, part_lse,
-                       reinterpret_cast<bf16s*>(o), m.hq, G);
+                       reinterpret_cast<bf16s*>(o), m.hq, m.hkv);
   } else if (m.dtype == 0 && m.dh == 64) {
     hipLaunchKernelGGL((dev::merge_kernel<float, 64>), dim3(n_items), dim3(256), 0, s, items, part_o, part_lse,
-                       reinterpret_cast<float*>(o), m.hq, G);
+                       reinterpret_cast<float*>(o), m.hq, m.hkv);
   } else {
     return hipErrorInvalidValue;
   }

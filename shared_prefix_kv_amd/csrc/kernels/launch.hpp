@@ -14,16 +14,17 @@ namespace jev {
 // page i sits at position kv_pos0 + 16*i + s and is visible to a query at
 // position p iff that is <= p; otherwise every valid key is visible.
 // out_mode 0: normalised output written straight to the attention output;
-// 1: normalised output and log2-sum-exp written to partial slot `part_slot`
-// (rows part_slot*128 + token_in_tile*G + head_in_group).
+// 1: normalised output and log2-sum-exp written to partial slot `part_slot`,
+// rows (part_slot*Hkv + kv_head)*128 + token_in_tile*G + head_in_group.
 struct AttnTile {
   int32_t t0, n_tok, page_off, n_pages, causal, kv_pos0, out_mode, part_slot;
 };
 
-// Merge of the partial states of one round token: its own causal part (row
-// base own_row) and n_chunks prefix chunks (row bases anc_row0 + 128*c).
+// Merge of the partial states of one round token: its own causal part (slot
+// own_slot, token own_ti of that tile) and n_chunks prefix chunks (slots
+// anc_slot0 + c, token anc_ti of those tiles).
 struct MergeItem {
-  int32_t t, own_row, anc_row0, n_chunks;
+  int32_t t, own_slot, own_ti, anc_slot0, anc_ti, n_chunks;
 };
 
 // Readout of one candidate: final norm of round row `row`, logits at

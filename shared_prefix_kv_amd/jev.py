@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libjev.so")
 
 JEV_OK, JEV_EINVAL, JEV_ENOMEM, JEV_EHANDLE, JEV_EHIP, JEV_ESTATE = range(6)
 JEV_DTYPE_F32, JEV_DTYPE_BF16 = 0, 1
+JEV_TAP_ATTN, JEV_TAP_RESID = 0, 1
 _NAMES = {0: "JEV_OK", 1: "JEV_EINVAL", 2: "JEV_ENOMEM", 3: "JEV_EHANDLE", 4: "JEV_EHIP", 5: "JEV_ESTATE"}
 
 EXPORTED = ["jev_workspace_bytes", "jev_kv_pool_bytes", "jev_create", "jev_destroy", "jev_prefill_prefix",
@@ -79,7 +80,7 @@ def lib() -> ctypes.CDLL:
         L.jev_page_table.argtypes = [vp, i64, P(i32), P(i32), i32, P(i32)]
         L.jev_match.argtypes = [vp, P(i32), i64, P(i64), P(i64)]
         L.jev_stats.argtypes = [vp, P(Stats)]
-        L.jev_debug_tap.argtypes = [vp, i32, vp, i64]
+        L.jev_debug_tap.argtypes = [vp, i32, i32, vp, i64]
         L.jev_last_error.restype = ctypes.c_char_p
         _lib = L
     return _lib
@@ -247,11 +248,12 @@ class Context:
         _check(lib().jev_stats(self.ctx, ctypes.byref(s)))
         return s.as_dict()
 
-    def debug_tap(self, layer: int, dst=None) -> None:
+    def debug_tap(self, what: int = 0, layer: int = 0, dst=None) -> None:
+        """what: JEV_TAP_ATTN or JEV_TAP_RESID; dst=None removes every tap."""
         if dst is None:
-            _check(lib().jev_debug_tap(self.ctx, -1, None, 0))
+            _check(lib().jev_debug_tap(self.ctx, 0, 0, None, 0))
         else:
-            _check(lib().jev_debug_tap(self.ctx, layer, ctypes.c_void_p(dst.data_ptr()), dst.shape[0]))
+            _check(lib().jev_debug_tap(self.ctx, what, layer, ctypes.c_void_p(dst.data_ptr()), dst.shape[0]))
 
     # ------------------------------------------------------------------ helpers
     def _stream(self):

@@ -1,0 +1,261 @@
+"""GPU path vs the oracle through the C ABI (needs an MI355X and libjev.so).
+
+Bars:
+* float32 workload: label probabilities within 1e-5 absolute, attention
+  outputs within 1e-4 relative per (token, head) row;
+* bf16 workloads, checks that are well conditioned: attention outputs and the
+  residual stream of every layer within 2e-2 relative per row when the oracle
+  layer is fed the GPU's own layer input (teacher forcing), and label
+  probabilities within 1e-3 absolute when the oracle reads out the GPU's own
+  final hidden state;
+* bf16 workloads end to end (oracle from scratch vs GPU): 1e-2 absolute.  The
+  1e-3 bar is below the reproducibility floor of these random-weight bf16
+  models: the oracle itself moves by up to 3.2e-3 when only its GEMM
+  accumulation changes from float32 to float64, because bf16 rounding flips
+  cascade through the layers.  The derivation of 1e-2 is in the design doc.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import model as om
+from synth import make_instance, workload
+from tests.gpu_common import (device_context, golden, host_weights, max_abs, row_rel_err,
+                              split_probs)
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_BF16 = 1e-3          # well-conditioned bf16 checks
+TOL_BF16_E2E = 1e-2      # end to end, bf16 storage (derived; see module docstring)
+TAP_ATTN, TAP_RESID = 0, 1
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+def oracle_attention_layer0(m, prefix, suffixes):
+    """Oracle layer-0 attention output of the suffix tokens of each branch."""
+    pos_p = np.arange(len(prefix))
+    x = om.store(m, m.embed[np.asarray(prefix)])
+    _, kp, vp = om.layer_qkv(m, 0, x, pos_p)
+    outs = []
+    for s in suffixes:
+        pos = len(prefix) + np.arange(len(s))
+        xs = om.store(m, m.embed[np.asarray(s)])
+        q, k, v = om.layer_qkv(m, 0, xs, pos)
+        a = om.attention(m, q, np.concatenate([kp, k]), np.concatenate([vp, v]), pos,
+                         np.arange(len(prefix) + len(s)))
+        outs.append(om.store(m, a))
+    return np.concatenate(outs)
+
+
+# ------------------------------------------------------------------ workload 1 (float32)
+@pytest.fixture(scope="module")
+def w1():
+    wl = workload(1)
+    inst = make_instance(wl)
+    m = om.from_weights(host_weights(1))
+    seqs = inst.full_sequences(0)
+    ref = om.score_from_scratch(m, [s for s, _ in seqs], [l for _, l in seqs])
+    ctx, wd = device_context(1, n_pages=256, max_pos=1024, max_tok=1024)
+    return wl, inst, m, ref, ctx, wd
+
+
+def test_w1_shared_prefix_matches_oracle(w1):
+    wl, inst, m, ref, ctx, _ = w1
+    (h,) = ctx.prefill_prefix([0], [inst.prefixes[0]])
+    br = inst.passes[0]
+    probs, loff = ctx.score_branches([h] * len(br), [b.tokens for b in br], [b.labels for b in br])
+    _sync()
+    got = split_probs(probs, loff)
+    assert max_abs(got, ref) <= TOL_F32
+    st = ctx.stats()
+    assert st["computed_tokens"] == 64 and st["logical_tokens"] == 4 * 144
+    ctx.free_pages([h])
+    assert ctx.stats()["pages_in_use"] == 0
+
+
+def test_w1_unshared_and_candidate_paths_match_oracle(w1):
+    wl, inst, m, ref, ctx, _ = w1
+    seqs = inst.full_sequences(0)
+    probs, loff = ctx.score_branches([0] * len(seqs), [s for s, _ in seqs], [l for _, l in seqs])
+    _sync()
+    assert max_abs(split_probs(probs, loff), ref) <= TOL_F32
+    probs, loff = ctx.score_candidates([s for s, _ in seqs], [l for _, l in seqs])
+    _sync()
+    assert max_abs(split_probs(probs, loff), ref) <= TOL_F32
+    assert ctx.stats()["rounds"] == 2 and ctx.stats()["pages_in_use"] == 0
+
+
+def test_w1_attention_output_matches_oracle(w1):
+    wl, inst, m, ref, ctx, _ = w1
+    (h,) = ctx.prefill_prefix([0], [inst.prefixes[0]])
+    br = inst.passes[0]
+    T = sum(len(b.tokens) for b in br)
+    tap = torch.zeros((T, m.hq * m.dh), dtype=torch.float32, device="cuda:0")
+    ctx.debug_tap(TAP_ATTN, 0, tap)
+    ctx.score_branches([h] * len(br), [b.tokens for b in br], [b.labels for b in br])
+    _sync()
+    ctx.debug_tap()
+    got = tap.cpu().numpy().reshape(T, m.hq, m.dh)
+    want = oracle_attention_layer0(m, inst.prefixes[0], [b.tokens for b in br])
+    assert row_rel_err(got, want) <= 1e-4
+    ctx.free_pages([h])
+
+
+def test_w1_ragged_and_edge_cases(w1):
+    """Single-token suffixes, suffix lengths that straddle pages and tiles,
+    partial parent pages, many labels, and a one-token prefix."""
+    wl, inst, m, _, ctx, _ = w1
+    rng = np.random.default_rng(77)
+    pre = list(rng.integers(0, 1024, 37))                 # last page holds 5 tokens
+    sufs = [list(rng.integers(0, 1024, n)) for n in (1, 15, 16, 17, 130)]
+    labs = [list(rng.choice(1024, k, replace=False)) for k in (2, 3, 64, 7, 2)]
+    (h,) = ctx.prefill_prefix([0], [pre])
+    probs, loff = ctx.score_branches([h] * 5, sufs, labs)
+    _sync()
+    ref = om.score_from_scratch(m, [pre + s for s in sufs], labs)
+    assert max_abs(split_probs(probs, loff), ref) <= TOL_F32
+    (h1,) = ctx.prefill_prefix([0], [[5]])
+    probs, loff = ctx.score_branches([h1], [[9]], [[1, 2, 3]])
+    _sync()
+    ref = om.score_from_scratch(m, [[5, 9]], [[1, 2, 3]])
+    assert max_abs(split_probs(probs, loff), ref) <= TOL_F32
+    ctx.free_pages([h, h1])
+
+
+# ------------------------------------------------------------------ workload 2 (bf16, headline)
+@pytest.fixture(scope="module")
+def w2():
+    wl = workload(2)
+    inst = make_instance(wl)
+    g = golden(2)
+    ctx, wd = device_context(2, n_pages=1024, max_pos=4096, max_tok=10240)
+    return wl, inst, g, ctx, wd
+
+
+def test_w2_shared_prefix_matches_oracle(w2):
+    wl, inst, g, ctx, _ = w2
+    (h,) = ctx.prefill_prefix([0], [inst.prefixes[0]])
+    br = inst.passes[0]
+    probs, loff = ctx.score_branches([h] * 5, [b.tokens for b in br], [b.labels for b in br])
+    _sync()
+    got = split_probs(probs, loff)
+    ref = g["passes"][0]["probs"]
+    err = max_abs(got, ref)
+    print("w2 shared max abs err", err)
+    pages = ctx.page_table(h)[0]
+    ctx.free_pages([h])
+    assert err <= TOL_BF16_E2E
+    assert pages == list(range(125))
+
+
+def test_w2_unshared_matches_oracle(w2):
+    wl, inst, g, ctx, _ = w2
+    seqs = inst.full_sequences(0)
+    probs, loff = ctx.score_branches([0] * 5, [s for s, _ in seqs], [l for _, l in seqs])
+    _sync()
+    err = max_abs(split_probs(probs, loff), g["passes"][0]["probs"])
+    print("w2 unshared max abs err", err)
+    assert err <= TOL_BF16_E2E
+
+
+def teacher_forced_check(ctx, m, prefix, branches, layers):
+    """Runs prefill + scoring with taps on every layer, then re-runs each oracle
+    layer on the GPU's own input of that layer and compares."""
+    P = len(prefix)
+    T = sum(len(b.tokens) for b in branches)
+    dev = "cuda:0"
+    dt = torch.bfloat16
+    pre_x = [torch.zeros((P, m.d), dtype=dt, device=dev) for _ in range(layers)]
+    for l in range(layers):
+        ctx.debug_tap(TAP_RESID, l, pre_x[l])
+    (h,) = ctx.prefill_prefix([0], [prefix])
+    _sync()
+    ctx.debug_tap()
+    suf_x = [torch.zeros((T, m.d), dtype=dt, device=dev) for _ in range(layers + 1)]
+    att = [torch.zeros((T, m.hq * m.dh), dtype=dt, device=dev) for _ in range(layers)]
+    for l in range(layers + 1):
+        ctx.debug_tap(TAP_RESID, l, suf_x[l])
+    for l in range(layers):
+        ctx.debug_tap(TAP_ATTN, l, att[l])
+    probs, loff = ctx.score_branches([h] * len(branches), [b.tokens for b in branches],
+                                     [b.labels for b in branches])
+    _sync()
+    ctx.debug_tap()
+    npf = lambda t: t.float().cpu().numpy()
+    worst_att = worst_res = 0.0
+    for l in range(layers):
+        xp = npf(pre_x[l])
+        _, kp, vp = om.layer_qkv(m, l, xp, np.arange(P))
+        xs = npf(suf_x[l])
+        o_ref = []
+        t0 = 0
+        for b in branches:
+            n = len(b.tokens)
+            pos = P + np.arange(n)
+            q, k, v = om.layer_qkv(m, l, xs[t0:t0 + n], pos)
+            a = om.attention(m, q, np.concatenate([kp, k]), np.concatenate([vp, v]), pos,
+                             np.arange(P + n))
+            o_ref.append(om.store(m, a))
+            t0 += n
+        o_ref = np.concatenate(o_ref)
+        worst_att = max(worst_att, row_rel_err(npf(att[l]).reshape(T, m.hq, m.dh), o_ref))
+        x_next = om.layer_out(m, l, xs, npf(att[l]).reshape(T, m.hq, m.dh))
+        worst_res = max(worst_res, row_rel_err(npf(suf_x[l + 1]), x_next))
+    # readout of the GPU's own final residual stream
+    xl = npf(suf_x[layers])
+    last = np.cumsum([len(b.tokens) for b in branches]) - 1
+    hid = om.store(m, om.rmsnorm(xl[last], m.final_norm, m.eps))
+    lp = om.full_logprobs(m, hid)
+    ref = [om.label_softmax(lp[i, np.asarray(b.labels)]) for i, b in enumerate(branches)]
+    err_read = max_abs(split_probs(probs, loff), ref)
+    ctx.free_pages([h])
+    return worst_att, worst_res, err_read
+
+
+def test_w2_teacher_forced_layers_and_readout(w2):
+    wl, inst, g, ctx, _ = w2
+    m = om.from_weights(host_weights(2))
+    att, res, rd = teacher_forced_check(ctx, m, inst.prefixes[0], inst.passes[0], wl.model.n_layers)
+    print(f"w2 teacher-forced: attention {att:.2e}, residual {res:.2e}, readout {rd:.2e}")
+    assert att <= 2e-2 and res <= 2e-2
+    assert rd <= TOL_BF16
+
+
+def test_w2_attention_output_matches_oracle(w2):
+    wl, inst, g, ctx, _ = w2
+    m = om.from_weights(host_weights(2))
+    (h,) = ctx.prefill_prefix([0], [inst.prefixes[0]])
+    br = inst.passes[0]
+    T = sum(len(b.tokens) for b in br)
+    tap = torch.zeros((T, 32 * 128), dtype=torch.bfloat16, device="cuda:0")
+    ctx.debug_tap(TAP_ATTN, 0, tap)
+    ctx.score_branches([h] * 5, [b.tokens for b in br], [b.labels for b in br])
+    _sync()
+    ctx.debug_tap()
+    got = tap.float().cpu().numpy().reshape(T, 32, 128)
+    want = oracle_attention_layer0(m, inst.prefixes[0], [b.tokens for b in br])
+    err = row_rel_err(got, want)
+    print("w2 layer-0 attention max row rel err", err)
+    assert err <= 2e-2
+    ctx.free_pages([h])
+
+
+def test_w3_staged_rounds_match_oracle(w2):
+    """Workload 3 uses the same model shapes as workload 2 (weights of its own
+    seed), submitted as full candidate sequences in staged rounds."""
+    g = golden(3)
+    wl = workload(3)
+    inst = make_instance(wl)
+    ctx, _ = device_context(3, n_pages=1024, max_pos=4096, max_tok=4096)
+    probs, loff = ctx.score_candidates(inst.candidates, inst.cand_labels)
+    _sync()
+    err = max_abs(split_probs(probs, loff), g["passes"][0]["probs"])
+    print("w3 staged max abs err", err)
+    assert err <= TOL_BF16_E2E
+    st = ctx.stats()
+    assert st["rounds"] == 3 and st["computed_tokens"] == 800 + 120 + 240
+    assert st["pages_in_use"] == 0
