@@ -200,6 +200,35 @@ int jev_stats(jev_ctx* ctx, jev_stats_t* out);
 enum { JEV_TAP_ATTN = 0, JEV_TAP_RESID = 1 };
 int jev_debug_tap(jev_ctx* ctx, int32_t what, int32_t layer, void* dst, int64_t cap_rows);
 
+/* Kernel timing for measurement.  While a kind is enabled (bit 1<<kind of the
+ * mask), every launch of that kernel is bracketed by HIP events on the call's
+ * stream and recorded with its algorithmic work: FLOPs for the contractions
+ * (QKV and output projections: 2*M*N*K; attention: 4*head_dim per visible
+ * query-key pair) and bytes for the memory-bound kernels (each input and
+ * output element once).  jev_profile(ctx, 0) disables and clears the records.
+ * jev_profile_read waits for the recorded events and copies up to cap records;
+ * *n receives the number recorded. */
+enum {
+  JEV_K_EMBED = 0,
+  JEV_K_RMSNORM = 1,
+  JEV_K_QKV = 2,
+  JEV_K_ATTN = 3,
+  JEV_K_MERGE = 4,
+  JEV_K_OPROJ = 5,
+  JEV_K_READOUT = 6,
+  JEV_K_COUNT = 7
+};
+typedef struct {
+  int32_t kind;
+  int32_t layer;  /* -1 for per-round kernels */
+  int64_t rows;   /* token rows (or readout items) of the launch */
+  double flops;   /* algorithmic FLOPs (0 for memory-bound kernels) */
+  double bytes;   /* algorithmic HBM bytes */
+  float ms;       /* event-measured duration */
+} jev_launch_record;
+int jev_profile(jev_ctx* ctx, uint32_t kind_mask);
+int jev_profile_read(jev_ctx* ctx, jev_launch_record* out, int64_t cap, int64_t* n);
+
 const char* jev_last_error(void);
 
 #ifdef __cplusplus

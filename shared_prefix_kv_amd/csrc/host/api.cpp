@@ -134,6 +134,8 @@ struct RoundDesc {
           off_read = 0, off_labels = 0;
   int32_t n_tiles = 0, n_merge = 0, n_read = 0;
   int64_t part_slots = 0;
+  double attn_pairs = 0;  // visible (query row, key) pairs of one layer
+  int64_t n_part_rows = 0;
 };
 
 }  // namespace
@@ -164,6 +166,13 @@ struct jev_ctx {
     int64_t rows;
   };
   std::vector<Tap> taps;
+  struct Prof {
+    jev_launch_record rec;
+    hipEvent_t e0, e1;
+  };
+  uint32_t prof_mask = 0;
+  std::vector<Prof> prof;
+  std::vector<hipEvent_t> prof_free;  // events kept for re-use
 };
 
 namespace {
@@ -315,6 +324,8 @@ int build_round(jev_ctx* ctx, std::vector<RNode>& nodes, std::vector<int32_t>& h
       tl.kv_pos0 = int32_t(nd.start);
       tl.out_mode = has_anc ? 1 : 0;
       tl.part_slot = has_anc ? int32_t(slot) : 0;
+      // causal pairs of the tile: token i0+j sees i0+j+1 own keys
+      rd->attn_pairs += double(G) * double(ctx->desc.n_kv_heads) * double(nt * i0 + nt * (nt + 1) / 2);
       if (has_anc) {
         for (int64_t j = 0; j < nt; ++j) {
           own_slot[node_t0[i] + i0 + j] = int32_t(slot);
@@ -330,6 +341,9 @@ int build_round(jev_ctx* ctx, std::vector<RNode>& nodes, std::vector<int32_t>& h
     int64_t cp = (g.anc_pages + n_chunks - 1) / n_chunks;
     cp += cp & 1;  // whole two-page steps per chunk
     const int64_t nch = (g.anc_pages + cp - 1) / cp;
+    int64_t anc_keys = 0;
+    for (int64_t pi = 0; pi < g.anc_pages; ++pi) anc_keys += plist[2 * (g.anc_off + pi) + 1];
+    rd->attn_pairs += double(g.t1 - g.t0) * G * double(ctx->desc.n_kv_heads) * double(anc_keys);
     for (int64_t t0 = g.t0; t0 < g.t1; t0 += TT) {
       const int64_t nt = std::min<int64_t>(TT, g.t1 - t0);
       const int64_t slot0 = slot;
@@ -352,6 +366,7 @@ int build_round(jev_ctx* ctx, std::vector<RNode>& nodes, std::vector<int32_t>& h
   if (slot * ctx->desc.n_kv_heads * kRowsPerTile > ctx->L.part_rows)
     return fail(JEV_ENOMEM, "round needs more partial-state rows than the workspace holds");
   rd->part_slots = slot;
+  rd->n_part_rows = int64_t(merges.size());
   // heavy tiles first
   std::stable_sort(tiles.begin(), tiles.end(),
                    [](const jev::AttnTile& a, const jev::AttnTile& b) { return a.n_pages > b.n_pages; });
@@ -398,6 +413,26 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
   float* part_o = reinterpret_cast<float*>(ctx->ws + ctx->L.part_o);
   float* part_lse = reinterpret_cast<float*>(ctx->ws + ctx->L.part_lse);
   const size_t elt = size_t(elt_size(ctx->desc));
+  // times one launch with events when its kind is being profiled
+  auto timed = [&](int kind, int layer, int64_t rows, double flops, double bytes, auto&& launch) -> hipError_t {
+    if (!(ctx->prof_mask & (1u << kind))) return launch();
+    jev_ctx::Prof p;
+    p.rec = jev_launch_record{kind, layer, rows, flops, bytes, 0.f};
+    for (hipEvent_t* e : {&p.e0, &p.e1}) {
+      if (!ctx->prof_free.empty()) {
+        *e = ctx->prof_free.back();
+        ctx->prof_free.pop_back();
+      } else {
+        hipError_t err = hipEventCreate(e);
+        if (err != hipSuccess) return err;
+      }
+    }
+    hipError_t err = hipEventRecord(p.e0, s);
+    if (err == hipSuccess) err = launch();
+    if (err == hipSuccess) err = hipEventRecord(p.e1, s);
+    ctx->prof.push_back(p);
+    return err;
+  };
   auto tap = [&](int what, int layer, const void* src, int64_t T, size_t width) -> int {
     if (rds.size() != 1) return JEV_OK;
     for (const auto& tp : ctx->taps)
@@ -407,25 +442,40 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
       }
     return JEV_OK;
   };
+  const double D = m.d, HD = double(m.hq) * m.dh, NQKV = double(m.hq + 2 * m.hkv) * m.dh, E = double(elt);
   for (const RoundDesc& rd : rds) {
     const int32_t* tok = dd + rd.off_tok;
-    HIPCHK(jev::launch_embed(m, ctx->embed, tok, rd.T, x, s));
+    const double T = rd.T;
+    HIPCHK(timed(JEV_K_EMBED, -1, rd.T, 0, 2 * T * D * E + 4 * T,
+                 [&] { return jev::launch_embed(m, ctx->embed, tok, rd.T, x, s); }));
     for (int l = 0; l < m.n_layers; ++l) {
       const jev::LayerW& w = ctx->layers[l];
       if (int rc = tap(JEV_TAP_RESID, l, x, rd.T, size_t(m.d))) return rc;
-      HIPCHK(jev::launch_rmsnorm(m, x, w.norm, rd.T, h, s));
-      HIPCHK(jev::launch_qkv(m, w, l, h, rd.T, dd + rd.off_pos, dd + rd.off_slot, rope, q, ctx->pool, s));
-      HIPCHK(jev::launch_attention(m, l, reinterpret_cast<const jev::AttnTile*>(dd + rd.off_tiles), rd.n_tiles,
-                                   dd + rd.off_plist, dd + rd.off_pos, q, ctx->pool, o, part_o, part_lse, s));
-      HIPCHK(jev::launch_merge(m, reinterpret_cast<const jev::MergeItem*>(dd + rd.off_merge), rd.n_merge, part_o,
-                               part_lse, o, s));
+      HIPCHK(timed(JEV_K_RMSNORM, l, rd.T, 0, (2 * T + 1) * D * E,
+                   [&] { return jev::launch_rmsnorm(m, x, w.norm, rd.T, h, s); }));
+      HIPCHK(timed(JEV_K_QKV, l, rd.T, 2 * T * NQKV * D, (T * D + NQKV * D + T * NQKV) * E, [&] {
+        return jev::launch_qkv(m, w, l, h, rd.T, dd + rd.off_pos, dd + rd.off_slot, rope, q, ctx->pool, s);
+      }));
+      HIPCHK(timed(JEV_K_ATTN, l, rd.T, 4.0 * m.dh * rd.attn_pairs, 0, [&] {
+        return jev::launch_attention(m, l, reinterpret_cast<const jev::AttnTile*>(dd + rd.off_tiles), rd.n_tiles,
+                                     dd + rd.off_plist, dd + rd.off_pos, q, ctx->pool, o, part_o, part_lse, s);
+      }));
+      if (rd.n_merge > 0)
+        HIPCHK(timed(JEV_K_MERGE, l, rd.n_merge, 0, 0, [&] {
+          return jev::launch_merge(m, reinterpret_cast<const jev::MergeItem*>(dd + rd.off_merge), rd.n_merge,
+                                   part_o, part_lse, o, s);
+        }));
       if (int rc = tap(JEV_TAP_ATTN, l, o, rd.T, size_t(m.hq) * m.dh)) return rc;
-      HIPCHK(jev::launch_oproj(m, w, o, rd.T, x, s));
+      HIPCHK(timed(JEV_K_OPROJ, l, rd.T, 2 * T * D * HD, (T * HD + D * HD + 2 * T * D) * E,
+                   [&] { return jev::launch_oproj(m, w, o, rd.T, x, s); }));
     }
     if (int rc = tap(JEV_TAP_RESID, m.n_layers, x, rd.T, size_t(m.d))) return rc;
-    HIPCHK(jev::launch_readout(m, ctx->unembed, ctx->final_norm, x,
-                               reinterpret_cast<const jev::ReadoutItem*>(dd + rd.off_read), rd.n_read,
-                               dd + rd.off_labels, probs, s));
+    if (rd.n_read > 0)
+      HIPCHK(timed(JEV_K_READOUT, -1, rd.n_read, 0, 0, [&] {
+        return jev::launch_readout(m, ctx->unembed, ctx->final_norm, x,
+                                   reinterpret_cast<const jev::ReadoutItem*>(dd + rd.off_read), rd.n_read,
+                                   dd + rd.off_labels, probs, s);
+      }));
   }
   HIPCHK(hipEventRecord(ctx->last_done, s));
   ctx->have_last = true;
@@ -521,6 +571,11 @@ int jev_destroy(jev_ctx* ctx) {
     if (ctx->desc_host) (void)hipHostFree(ctx->desc_host);
     if (ctx->desc_copied) (void)hipEventDestroy(ctx->desc_copied);
     if (ctx->last_done) (void)hipEventDestroy(ctx->last_done);
+    for (auto& p : ctx->prof) {
+      (void)hipEventDestroy(p.e0);
+      (void)hipEventDestroy(p.e1);
+    }
+    for (hipEvent_t e : ctx->prof_free) (void)hipEventDestroy(e);
   }
   delete ctx;
   return rc;
@@ -786,6 +841,35 @@ int jev_debug_tap(jev_ctx* ctx, int32_t what, int32_t layer, void* dst, int64_t 
     return fail(JEV_EINVAL, "bad tap");
   if (ctx->taps.size() >= 16) return fail(JEV_ENOMEM, "too many taps");
   ctx->taps.push_back({what, layer, dst, cap_rows});
+  return JEV_OK;
+}
+
+int jev_profile(jev_ctx* ctx, uint32_t kind_mask) {
+  if (!ctx) return fail(JEV_EINVAL, "NULL ctx");
+  if (ctx->dry) return fail(JEV_ESTATE, "profiling needs a device context");
+  if (kind_mask >> JEV_K_COUNT) return fail(JEV_EINVAL, "unknown kernel kind");
+  if (kind_mask == 0) {
+    if (ctx->have_last) HIPCHK(hipEventSynchronize(ctx->last_done));
+    for (auto& p : ctx->prof) {
+      ctx->prof_free.push_back(p.e0);
+      ctx->prof_free.push_back(p.e1);
+    }
+    ctx->prof.clear();
+  }
+  ctx->prof_mask = kind_mask;
+  return JEV_OK;
+}
+
+int jev_profile_read(jev_ctx* ctx, jev_launch_record* out, int64_t cap, int64_t* n) {
+  if (!ctx || !n || cap < 0) return fail(JEV_EINVAL, "bad arguments");
+  *n = int64_t(ctx->prof.size());
+  const int64_t k = std::min<int64_t>(cap, *n);
+  for (int64_t i = 0; i < k; ++i) {
+    auto& p = ctx->prof[size_t(i)];
+    HIPCHK(hipEventSynchronize(p.e1));
+    HIPCHK(hipEventElapsedTime(&p.rec.ms, p.e0, p.e1));
+    if (out) out[i] = p.rec;
+  }
   return JEV_OK;
 }
 

@@ -23,7 +23,8 @@ _NAMES = {0: "JEV_OK", 1: "JEV_EINVAL", 2: "JEV_ENOMEM", 3: "JEV_EHANDLE", 4: "J
 
 EXPORTED = ["jev_workspace_bytes", "jev_kv_pool_bytes", "jev_create", "jev_destroy", "jev_prefill_prefix",
             "jev_score_branches", "jev_score_candidates", "jev_free_pages", "jev_plan", "jev_page_table",
-            "jev_match", "jev_stats", "jev_debug_tap", "jev_last_error"]
+            "jev_match", "jev_stats", "jev_debug_tap", "jev_profile", "jev_profile_read", "jev_last_error"]
+KERNELS = ["embed", "rmsnorm", "qkv", "attn", "merge", "oproj", "readout"]
 
 
 class JevError(RuntimeError):
@@ -44,6 +45,11 @@ class WeightsC(ctypes.Structure):
                 ("attn_norm", ctypes.POINTER(ctypes.c_void_p)), ("wq", ctypes.POINTER(ctypes.c_void_p)),
                 ("wk", ctypes.POINTER(ctypes.c_void_p)), ("wv", ctypes.POINTER(ctypes.c_void_p)),
                 ("wo", ctypes.POINTER(ctypes.c_void_p))]
+
+
+class LaunchRecord(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("layer", ctypes.c_int32), ("rows", ctypes.c_int64),
+                ("flops", ctypes.c_double), ("bytes", ctypes.c_double), ("ms", ctypes.c_float)]
 
 
 class Stats(ctypes.Structure):
@@ -81,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.jev_match.argtypes = [vp, P(i32), i64, P(i64), P(i64)]
         L.jev_stats.argtypes = [vp, P(Stats)]
         L.jev_debug_tap.argtypes = [vp, i32, i32, vp, i64]
+        L.jev_profile.argtypes = [vp, ctypes.c_uint32]
+        L.jev_profile_read.argtypes = [vp, P(LaunchRecord), i64, P(i64)]
         L.jev_last_error.restype = ctypes.c_char_p
         _lib = L
     return _lib
@@ -254,6 +262,21 @@ class Context:
             _check(lib().jev_debug_tap(self.ctx, 0, 0, None, 0))
         else:
             _check(lib().jev_debug_tap(self.ctx, what, layer, ctypes.c_void_p(dst.data_ptr()), dst.shape[0]))
+
+    def profile(self, kinds: Sequence[str] = ()) -> None:
+        """Enables event timing of the named kernels; () disables and clears."""
+        mask = 0
+        for k in kinds:
+            mask |= 1 << KERNELS.index(k)
+        _check(lib().jev_profile(self.ctx, mask))
+
+    def profile_read(self) -> List[dict]:
+        n = ctypes.c_int64()
+        _check(lib().jev_profile_read(self.ctx, None, 0, ctypes.byref(n)))
+        recs = (LaunchRecord * max(1, n.value))()
+        _check(lib().jev_profile_read(self.ctx, recs, n.value, ctypes.byref(n)))
+        return [{"kernel": KERNELS[r.kind], "layer": r.layer, "rows": r.rows, "flops": r.flops,
+                 "bytes": r.bytes, "ms": r.ms} for r in recs[:n.value]]
 
     # ------------------------------------------------------------------ helpers
     def _stream(self):
