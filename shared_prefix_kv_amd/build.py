@@ -23,6 +23,7 @@ OBJ_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = [
     os.path.join(CSRC, "kernels", "kernels.hip"),
+    os.path.join(CSRC, "kernels", "gemm.hip"),
     os.path.join(CSRC, "host", "tree.cpp"),
     os.path.join(CSRC, "host", "api.cpp"),
 ]

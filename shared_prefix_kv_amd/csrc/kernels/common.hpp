@@ -12,6 +12,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// 16-byte register / LDS staging unit (a native vector, so copies stay in registers)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // bf16 is stored as its 16-bit pattern.
 struct bf16s {
@@ -50,7 +53,7 @@ struct Mfma<bf16s> {
   }
   // 16 bytes at p (8 consecutive k elements)
   __device__ static __forceinline__ frag load(const void* p) {
-    return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(p));
+    return __builtin_bit_cast(frag, *reinterpret_cast<const u32x4*>(p));
   }
 };
 

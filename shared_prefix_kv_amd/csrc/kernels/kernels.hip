@@ -1,17 +1,14 @@
-// gfx950 kernels of the shared-prefix scoring path.
+// gfx950 kernels of the shared-prefix scoring path (the projection GEMMs are
+// in gemm.hip).
 //
 //  embed      x[t] = E[token t]
 //  rmsnorm    h = x / sqrt(mean x^2 + eps) * g  (fp32 math, stored)
-//  qkv        h [T,d] x [Wq;Wk;Wv]^T on MFMA, fp32 accumulate; epilogue applies
-//             RoPE to q and k at the token's logical position, writes q to the
-//             round buffer and k, v straight into the token's KV page
 //  attention  paged attention of packed query rows (token x query head of one
 //             KV head) against a page list; causal over a node's own pages,
 //             unmasked over a shared prefix's pages (read once for all rows of
 //             the sibling group); online softmax in fp32; writes the output or
 //             a normalised partial state plus its log2-sum-exp
 //  merge      log-sum-exp merge of the partial states of a token
-//  oproj      x += o Wo^T on MFMA
 //  readout    final norm of a candidate's last row, logits at its label ids
 //             only, max-subtracted softmax over the labels
 //
@@ -20,6 +17,8 @@
 // reading only the labels' logits is exact because the full-vocabulary
 // log-normaliser cancels in the label softmax.
 #include <float.h>
+
+#include <cmath>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -34,8 +33,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ E, const int32_t* __restrict__ tok,
                                                     int d, T* __restrict__ x) {
   const int t = blockIdx.x;
-  const uint4* src = reinterpret_cast<const uint4*>(E + (size_t)tok[t] * d);
-  uint4* dst = reinterpret_cast<uint4*>(x + (size_t)t * d);
+  const u32x4* src = reinterpret_cast<const u32x4*>(E + (size_t)tok[t] * d);
+  u32x4* dst = reinterpret_cast<u32x4*>(x + (size_t)t * d);
   const int n = d * int(sizeof(T)) / 16;
   for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = src[i];
 }
@@ -55,7 +54,7 @@ template <typename T>
 __device__ __forceinline__ void load16(const T* p, float* out);
 template <>
 __device__ __forceinline__ void load16<bf16s>(const bf16s* p, float* out) {
-  uint4 u = *reinterpret_cast<const uint4*>(p);
+  u32x4 u = *reinterpret_cast<const u32x4*>(p);
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -104,213 +103,6 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x, c
 #pragma unroll
       for (int e = 0; e < CH; ++e) hr[i + e] = from_f32<T>(v[j][e] * r * gg[e]);
     }
-  }
-}
-
-// ------------------------------------------------------------------ GEMM (NT)
-// C[M,N] = A[M,K] . B[N,K]^T with 128x128 tiles, 4 waves of 64x64, MFMA 32x32,
-// 128 bytes of K per stage, double-buffered LDS with a 16-byte-chunk XOR swizzle.
-constexpr int GBM = 128, GBN = 128;
-
-template <typename T>
-struct GemmB {
-  const T* b0;
-  const T* b1;
-  const T* b2;
-  int n0end, n1end;
-  int perm_dh;  // rows of segments 0 and 1 are permuted so RoPE pairs meet in one lane
-};
-
-// GEMM column n -> weight row.  Within a head of dh columns, a wave's 64
-// columns [64w, 64w+64) carry features 32w + c (first 32) and 32w + c + dh/2
-// (last 32) for dh = 128, and c / c + 32 for dh = 64, so that the rotate-half
-// pair of a feature sits in the same lane of the two 32-column MFMA tiles.
-template <typename T>
-__device__ __forceinline__ const T* gemm_brow(const GemmB<T>& g, int n, int K) {
-  const T* base;
-  int local, seg;
-  if (n < g.n0end) {
-    base = g.b0;
-    local = n;
-    seg = 0;
-  } else if (n < g.n1end) {
-    base = g.b1;
-    local = n - g.n0end;
-    seg = 1;
-  } else {
-    base = g.b2;
-    local = n - g.n1end;
-    seg = 2;
-  }
-  if (g.perm_dh && seg < 2) {
-    const int dh = g.perm_dh;
-    const int head = local / dh, jj = local % dh;
-    const int w = jj >> 6, r = jj & 63, half = r >> 5, c = r & 31;
-    const int f = (dh == 128 ? 32 * w : 0) + c + half * (dh >> 1);
-    local = head * dh + f;
-  }
-  return base + (size_t)local * K;
-}
-
-struct QkvEpi {
-  int hq, hkv, dh, nq_end, nk_end;
-  const int32_t* pos;
-  const int32_t* kvslot;
-  const float2* rope;
-  void* qbuf;
-  void* pool;
-  size_t layer_base;  // element offset of this layer in the pool
-};
-
-struct ResEpi {
-  void* x;
-  int ld;
-};
-
-enum { EPI_QKV = 0, EPI_RES = 1 };
-
-template <typename T, int EPI>
-__global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int M, int K, GemmB<T> gb, int N,
-                                                   QkvEpi qe, ResEpi re) {
-  using MF = Mfma<T>;
-  constexpr int CH = 16 / sizeof(T);
-  constexpr int BK = 8 * CH;
-  __shared__ uint4 sA[2][GBM * 8];
-  __shared__ uint4 sB[2][GBN * 8];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * GBM, n0 = blockIdx.x * GBN;
-  const int lrow = tid >> 3, lch = tid & 7;
-
-  const uint4* ap[4];
-  const uint4* bp[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = lrow + 32 * i;
-    const int am = min(m0 + r, M - 1);
-    ap[i] = reinterpret_cast<const uint4*>(A + (size_t)am * K) + lch;
-    const int bn = min(n0 + r, N - 1);
-    bp[i] = reinterpret_cast<const uint4*>(gemm_brow(gb, bn, K)) + lch;
-  }
-  uint4 ra[4], rb[4];
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const int KT = K / BK;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ra[i] = ap[i][0];
-    rb[i] = bp[i][0];
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = lrow + 32 * i;
-    sA[0][r * 8 + (lch ^ (r & 7))] = ra[i];
-    sB[0][r * 8 + (lch ^ (r & 7))] = rb[i];
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    // prefetch the next stage (the last iteration re-reads the final stage and
-    // stores it into the idle buffer, which nothing reads afterwards)
-    const int kn = min(kt + 1, KT - 1) * 8;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = ap[i][kn];
-      rb[i] = bp[i][kn];
-    }
-#pragma unroll
-    for (int ks = 0; ks < BK / MF::KSTEP; ++ks) {
-      const int k = ks * MF::KSTEP + MF::KL * (lane >> 5);
-      const int ch = k / CH, within = k % CH;
-      typename MF::frag a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = wm * 64 + 32 * i + (lane & 31);
-        a[i] = MF::load(reinterpret_cast<const T*>(&sA[buf][r * 8 + (ch ^ (r & 7))]) + within);
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = wn * 64 + 32 * j + (lane & 31);
-        b[j] = MF::load(reinterpret_cast<const T*>(&sB[buf][r * 8 + (ch ^ (r & 7))]) + within);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = MF::mma(a[i], b[j], acc[i][j]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = lrow + 32 * i;
-      sA[buf ^ 1][r * 8 + (lch ^ (r & 7))] = ra[i];
-      sB[buf ^ 1][r * 8 + (lch ^ (r & 7))] = rb[i];
-    }
-    __syncthreads();
-  }
-
-  const int c = lane & 31, hh = lane >> 5;
-  const int nw = n0 + wn * 64;
-  if constexpr (EPI == EPI_RES) {
-    T* x = reinterpret_cast<T*>(re.x);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (m >= M) continue;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          T* p = x + (size_t)m * re.ld + nw + 32 * j + c;
-          *p = from_f32<T>(to_f32(*p) + acc[i][j][r]);
-        }
-      }
-  } else {
-    T* pool = reinterpret_cast<T*>(qe.pool) + qe.layer_base;
-    const int dh = qe.dh;
-    const size_t page_elems = (size_t)16 * dh;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (m >= M) continue;
-        if (nw < qe.nk_end) {
-          const bool isq = nw < qe.nq_end;
-          const int local = isq ? nw : nw - qe.nq_end;
-          const int head = local / dh;
-          const int f0 = (dh == 128 ? ((local % dh) >> 6) * 32 : 0) + c;
-          const int f1 = f0 + (dh >> 1);
-          const float a0 = acc[i][0][r], a1 = acc[i][1][r];
-          const float2 cs = qe.rope[(size_t)qe.pos[m] * (dh >> 1) + f0];
-          const float o0 = a0 * cs.x - a1 * cs.y;
-          const float o1 = a1 * cs.x + a0 * cs.y;
-          if (isq) {
-            T* qp = reinterpret_cast<T*>(qe.qbuf) + ((size_t)m * qe.hq + head) * dh;
-            qp[f0] = from_f32<T>(o0);
-            qp[f1] = from_f32<T>(o1);
-          } else {
-            const int sl = qe.kvslot[m];
-            T* kb = pool + ((size_t)(sl >> 4) * qe.hkv + head) * 2 * page_elems + (size_t)(sl & 15) * dh;
-            kb[f0] = from_f32<T>(o0);
-            kb[f1] = from_f32<T>(o1);
-          }
-        } else {
-          const int sl = qe.kvslot[m];
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int local = nw + 32 * j + c - qe.nk_end;
-            const int head = local / dh, f = local % dh;
-            T* vb = pool + ((size_t)(sl >> 4) * qe.hkv + head) * 2 * page_elems + page_elems;
-            vb[(size_t)f * 16 + (sl & 15)] = from_f32<T>(acc[i][j][r]);
-          }
-        }
-      }
   }
 }
 
@@ -380,18 +172,18 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnTile* __restrict__ 
   const size_t page_stride = (size_t)hkv * 2 * PAGE_ELEMS;
   const int nst = (tile.n_pages + 1) >> 1;
 
-  uint4 rk[2], rv[2];
+  u32x4 rk[2], rv[2];
   auto gload = [&](int st) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int lp = 2 * st + i;  // chunk tid + 256 i belongs to page i of the step
       if (lp < tile.n_pages) {
         const T* kb = kvbase + (size_t)plist[2 * (tile.page_off + lp)] * page_stride;
-        rk[i] = reinterpret_cast<const uint4*>(kb)[tid];
-        rv[i] = reinterpret_cast<const uint4*>(kb + PAGE_ELEMS)[tid];
+        rk[i] = reinterpret_cast<const u32x4*>(kb)[tid];
+        rv[i] = reinterpret_cast<const u32x4*>(kb + PAGE_ELEMS)[tid];
       } else {
-        rk[i] = make_uint4(0, 0, 0, 0);
-        rv[i] = make_uint4(0, 0, 0, 0);
+        rk[i] = u32x4{0, 0, 0, 0};
+        rv[i] = u32x4{0, 0, 0, 0};
       }
     }
   };
@@ -399,13 +191,13 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnTile* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int krow = 16 * i + tid / KCH, kch = tid % KCH;
-      *reinterpret_cast<uint4*>(&sK[buf][krow * DH + ((kch ^ (krow & (KCH - 1))) * CH)]) = rk[i];
+      *reinterpret_cast<u32x4*>(&sK[buf][krow * DH + ((kch ^ (krow & (KCH - 1))) * CH)]) = rk[i];
       const int d = tid / VCPR, key0 = 16 * i + (tid % VCPR) * CH;
       if constexpr (CH == 8) {
-        *reinterpret_cast<uint2*>(&sV[buf][v_off(d, key0)]) = make_uint2(rv[i].x, rv[i].y);
-        *reinterpret_cast<uint2*>(&sV[buf][v_off(d, key0 + 4)]) = make_uint2(rv[i].z, rv[i].w);
+        *reinterpret_cast<u32x2*>(&sV[buf][v_off(d, key0)]) = u32x2{rv[i].x, rv[i].y};
+        *reinterpret_cast<u32x2*>(&sV[buf][v_off(d, key0 + 4)]) = u32x2{rv[i].z, rv[i].w};
       } else {
-        *reinterpret_cast<uint4*>(&sV[buf][v_off(d, key0)]) = rv[i];
+        *reinterpret_cast<u32x4*>(&sV[buf][v_off(d, key0)]) = rv[i];
       }
     }
   };
@@ -485,9 +277,9 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnTile* __restrict__ 
         const int d = 32 * b + c;
         typename MF::frag va;
         if constexpr (KL == 8) {
-          const uint2 lo = *reinterpret_cast<const uint2*>(&sV[buf][v_off(d, 16 * tt + 4 * hh)]);
-          const uint2 hi = *reinterpret_cast<const uint2*>(&sV[buf][v_off(d, 16 * tt + 8 + 4 * hh)]);
-          va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(&sV[buf][v_off(d, 16 * tt + 4 * hh)]);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(&sV[buf][v_off(d, 16 * tt + 8 + 4 * hh)]);
+          va = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
         } else {
           const int key = 8 * (tt >> 2) + 4 * hh + (tt & 3);
           va = MF::load(&sV[buf][v_off(d, key)]);
@@ -644,48 +436,6 @@ hipError_t launch_rmsnorm(const ModelDims& m, const void* x, const void* g, int3
   JEV_DISPATCH_T(m, {
     hipLaunchKernelGGL(dev::rmsnorm_kernel<T>, dim3(T_), dim3(256), 0, s, reinterpret_cast<const T*>(x),
                        reinterpret_cast<const T*>(g), m.d, m.eps, reinterpret_cast<T*>(h));
-  })
-  return hipGetLastError();
-}
-
-hipError_t launch_qkv(const ModelDims& m, const LayerW& w, int32_t layer, const void* h, int32_t T_,
-                      const int32_t* pos, const int32_t* kvslot, const float* rope, void* qbuf, void* pool,
-                      hipStream_t s) {
-  if (T_ <= 0) return hipSuccess;
-  const int N = (m.hq + 2 * m.hkv) * m.dh;
-  dev::QkvEpi qe;
-  qe.hq = m.hq;
-  qe.hkv = m.hkv;
-  qe.dh = m.dh;
-  qe.nq_end = m.hq * m.dh;
-  qe.nk_end = (m.hq + m.hkv) * m.dh;
-  qe.pos = pos;
-  qe.kvslot = kvslot;
-  qe.rope = reinterpret_cast<const float2*>(rope);
-  qe.qbuf = qbuf;
-  qe.pool = pool;
-  qe.layer_base = (size_t)layer * m.n_pages * m.hkv * 2 * 16 * m.dh;
-  dev::ResEpi re{nullptr, 0};
-  dim3 grid(N / dev::GBN, (T_ + dev::GBM - 1) / dev::GBM);
-  JEV_DISPATCH_T(m, {
-    dev::GemmB<T> gb{reinterpret_cast<const T*>(w.wq), reinterpret_cast<const T*>(w.wk),
-                     reinterpret_cast<const T*>(w.wv), qe.nq_end, qe.nk_end, m.dh};
-    hipLaunchKernelGGL((dev::gemm_kernel<T, dev::EPI_QKV>), grid, dim3(256), 0, s, reinterpret_cast<const T*>(h),
-                       T_, m.d, gb, N, qe, re);
-  })
-  return hipGetLastError();
-}
-
-hipError_t launch_oproj(const ModelDims& m, const LayerW& w, const void* o, int32_t T_, void* x, hipStream_t s) {
-  if (T_ <= 0) return hipSuccess;
-  const int N = m.d, K = m.hq * m.dh;
-  dev::QkvEpi qe{};
-  dev::ResEpi re{x, m.d};
-  dim3 grid(N / dev::GBN, (T_ + dev::GBM - 1) / dev::GBM);
-  JEV_DISPATCH_T(m, {
-    dev::GemmB<T> gb{reinterpret_cast<const T*>(w.wo), nullptr, nullptr, N, N, 0};
-    hipLaunchKernelGGL((dev::gemm_kernel<T, dev::EPI_RES>), grid, dim3(256), 0, s, reinterpret_cast<const T*>(o),
-                       T_, K, gb, N, qe, re);
   })
   return hipGetLastError();
 }

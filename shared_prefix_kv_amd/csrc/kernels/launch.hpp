@@ -47,6 +47,21 @@ struct LayerW {
   const void* wo;
 };
 
+// Scratch of the projection GEMMs: split-K partial tiles and per-column-tile
+// arrival counters (zero at creation; each launch leaves them zero).
+struct GemmWs {
+  float* partial;
+  size_t partial_elems;
+  int32_t* counters;
+  int32_t n_counters;
+};
+
+struct GemmTuning {
+  int splits;  // split-K count of the skinny GEMM (0 = automatic)
+  int bn;      // column tile of the large GEMM (0 = automatic)
+};
+extern GemmTuning g_gemm_tuning;
+
 // x[t] = E[tok[t]]
 hipError_t launch_embed(const ModelDims& m, const void* embed, const int32_t* tok, int32_t T, void* x,
                         hipStream_t s);
@@ -57,7 +72,7 @@ hipError_t launch_rmsnorm(const ModelDims& m, const void* x, const void* g, int3
 // layer's pages at kvslot[t] = page*16 + slot.  rope: float2 [pos][dh/2].
 hipError_t launch_qkv(const ModelDims& m, const LayerW& w, int32_t layer, const void* h, int32_t T,
                       const int32_t* pos, const int32_t* kvslot, const float* rope, void* qbuf,
-                      void* pool, hipStream_t s);
+                      void* pool, const GemmWs& ws, hipStream_t s);
 // attention tiles (grid n_tiles x Hkv)
 hipError_t launch_attention(const ModelDims& m, int32_t layer, const AttnTile* tiles, int32_t n_tiles,
                             const int32_t* page_list, const int32_t* tok_pos, const void* qbuf,
@@ -66,7 +81,7 @@ hipError_t launch_merge(const ModelDims& m, const MergeItem* items, int32_t n_it
                         const float* part_lse, void* o, hipStream_t s);
 // x += o Wo^T (stored)
 hipError_t launch_oproj(const ModelDims& m, const LayerW& w, const void* o, int32_t T, void* x,
-                        hipStream_t s);
+                        const GemmWs& ws, hipStream_t s);
 hipError_t launch_readout(const ModelDims& m, const void* unembed, const void* final_norm, const void* x,
                           const ReadoutItem* items, int32_t n_items, const int32_t* labels, float* probs,
                           hipStream_t s);
