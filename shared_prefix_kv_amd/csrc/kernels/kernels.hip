@@ -124,11 +124,24 @@ __device__ __forceinline__ bf16x8 frag_zero<bf16s>() {
 template <>
 __device__ __forceinline__ float frag_zero<float>() { return 0.f; }
 
-// LDS V tile [DH][32 keys], 4-key units swizzled by the row.
+// LDS V^T tile [DH][32 keys] for bf16: within each 16-key half the key quads
+// are stored in the order (0-3, 8-11, 4-7, 12-15), so that the 8 keys one lane
+// feeds to an MFMA (quads hh and hh+2 of the half) are 16 contiguous bytes; the
+// four 16-byte units of a 64-byte row are XOR-swizzled by (d >> 2) & 3, which
+// puts the 16 rows of a 16-lane read in 16 different bank groups.
+__device__ __forceinline__ int vq_unit(int d, int unit) { return d * 4 + (unit ^ ((d >> 2) & 3)); }
+// f32 (8 quads of 4 keys per 32-key row): plain 16-byte units swizzled by d.
 __device__ __forceinline__ int v_off(int d, int key) {
   const int u = (key >> 2) ^ (d & 7);
   return d * 32 + u * 4 + (key & 3);
 }
+
+// Lazy rescaling: a row's running maximum m is only moved when a new score
+// exceeds it by more than 2^RESCALE_SLACK (log2 units); until then
+// probabilities exp2(s - m) may exceed 1 (by at most 2^8) and the output and
+// normaliser keep accumulating on the same scale.  The result is the same
+// softmax; only the rounding order changes.
+constexpr float RESCALE_SLACK = 8.0f;
 
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void attn_kernel(const AttnTile* __restrict__ tiles,
@@ -138,6 +151,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnTile* __restrict__ 
                                                    float* __restrict__ part_o, float* __restrict__ part_lse,
                                                    int hq, int hkv, size_t layer_base, float scale_log2) {
   using MF = Mfma<T>;
+  using frag = typename MF::frag;
   constexpr int KL = MF::KL, KSTEP = MF::KSTEP;
   constexpr int NKS = DH / KSTEP;
   constexpr int CH = 16 / sizeof(T);
@@ -160,8 +174,12 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnTile* __restrict__ 
   const int t = tile.t0 + (row_ok ? ti : 0);
   const int qhead = kvh * G + hg;
   const int qpos = tok_pos[t];
+  // smallest query position of the wave: keys up to it are visible to every row
+  int qmin = qpos;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) qmin = min(qmin, __shfl_xor(qmin, off, 64));
 
-  typename MF::frag qf[NKS];
+  frag qf[NKS];
   {
     const T* qrow = q + ((size_t)t * hq + qhead) * DH;
 #pragma unroll
@@ -172,11 +190,22 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnTile* __restrict__ 
   const size_t page_stride = (size_t)hkv * 2 * PAGE_ELEMS;
   const int nst = (tile.n_pages + 1) >> 1;
 
+  // loop-invariant LDS offsets
+  int koff[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int e = ks * KSTEP + KL * hh;
+    koff[ks] = c * DH + (((e / CH) ^ (c & (KCH - 1))) * CH) + e % CH;
+  }
+  const int st_krow = tid / KCH, st_kch = tid % KCH;
+  const int st_koff = st_krow * DH + ((st_kch ^ (st_krow & (KCH - 1))) * CH);  // + 16*DH*i for page i
+  const int st_d = tid / VCPR, st_half = tid % VCPR;
+
   u32x4 rk[2], rv[2];
   auto gload = [&](int st) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int lp = 2 * st + i;  // chunk tid + 256 i belongs to page i of the step
+      const int lp = 2 * st + i;
       if (lp < tile.n_pages) {
         const T* kb = kvbase + (size_t)plist[2 * (tile.page_off + lp)] * page_stride;
         rk[i] = reinterpret_cast<const u32x4*>(kb)[tid];
@@ -190,14 +219,18 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnTile* __restrict__ 
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int krow = 16 * i + tid / KCH, kch = tid % KCH;
-      *reinterpret_cast<u32x4*>(&sK[buf][krow * DH + ((kch ^ (krow & (KCH - 1))) * CH)]) = rk[i];
-      const int d = tid / VCPR, key0 = 16 * i + (tid % VCPR) * CH;
+      *reinterpret_cast<u32x4*>(&sK[buf][st_koff + 16 * DH * i]) = rk[i];
       if constexpr (CH == 8) {
-        *reinterpret_cast<u32x2*>(&sV[buf][v_off(d, key0)]) = u32x2{rv[i].x, rv[i].y};
-        *reinterpret_cast<u32x2*>(&sV[buf][v_off(d, key0 + 4)]) = u32x2{rv[i].z, rv[i].w};
+        // page i holds keys 16i..16i+15 = half i of the row; this chunk is
+        // quads 2*st_half and 2*st_half+1 of that half (stored order 0, 2, 1, 3)
+        u32x2* vrow = reinterpret_cast<u32x2*>(&sV[buf][0]);
+        const int q0 = 2 * st_half, q1 = q0 + 1;
+        const int pos0 = (q0 & 1) * 2 + (q0 >> 1), pos1 = (q1 & 1) * 2 + (q1 >> 1);  // quad slot 0..3 in the half
+        const int u0 = 2 * i + (pos0 >> 1), u1 = 2 * i + (pos1 >> 1);
+        vrow[vq_unit(st_d, u0) * 2 + (pos0 & 1)] = u32x2{rv[i].x, rv[i].y};
+        vrow[vq_unit(st_d, u1) * 2 + (pos1 & 1)] = u32x2{rv[i].z, rv[i].w};
       } else {
-        *reinterpret_cast<u32x4*>(&sV[buf][v_off(d, key0)]) = rv[i];
+        *reinterpret_cast<u32x4*>(&sV[buf][v_off(st_d, 16 * i + st_half * CH)]) = rv[i];
       }
     }
   };
@@ -223,63 +256,66 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnTile* __restrict__ 
 #pragma unroll
     for (int r = 0; r < 16; ++r) S[r] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int e = ks * KSTEP + KL * hh;
-      const int ch = e / CH, within = e % CH;
-      const typename MF::frag a = MF::load(&sK[buf][c * DH + ((ch ^ (c & (KCH - 1))) * CH) + within]);
-      S = MF::mma(a, qf[ks], S);
-    }
-    // mask, scale, online softmax (statistics per lane column)
+    for (int ks = 0; ks < NKS; ++ks) S = MF::mma(MF::load(&sK[buf][koff[ks]]), qf[ks], S);
+
+    // mask only where needed: partial pages, or keys past the wave's first query
     const int lp0 = 2 * st;
     const int v0 = plist[2 * (tile.page_off + lp0) + 1];
     const int v1 = (lp0 + 1 < tile.n_pages) ? plist[2 * (tile.page_off + lp0 + 1) + 1] : 0;
-    float p[16];
-    float mloc = kNegInf;
+    const bool mask = (v0 < 16) || (v1 < 16) || (tile.causal && tile.kv_pos0 + 16 * lp0 + 31 > qmin);
+    if (mask) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 8 * (r >> 2) + 4 * hh + (r & 3);
-      const int pi = key >> 4, slot = key & 15;
-      bool ok = slot < (pi ? v1 : v0);
-      if (tile.causal) ok = ok && (tile.kv_pos0 + 16 * (lp0 + pi) + slot <= qpos);
-      p[r] = ok ? S[r] * scale_log2 : kNegInf;
-      mloc = fmaxf(mloc, p[r]);
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * hh + (r & 3);
+        const int pi = key >> 4, slot = key & 15;
+        bool ok = slot < (pi ? v1 : v0);
+        if (tile.causal) ok = ok && (tile.kv_pos0 + 16 * (lp0 + pi) + slot <= qpos);
+        if (!ok) S[r] = kNegInf;
+      }
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float mnew = fmaxf(mrun, mloc);
-    const float muse = (mnew == kNegInf) ? 0.f : mnew;
-    const float alpha = exp2f(mrun - muse);
+    float mloc = S[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, S[r]);
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * scale_log2;
+    if (__any(mloc > mrun + RESCALE_SLACK)) {
+      const float mnew = fmaxf(mrun, mloc);
+      const float alpha = (mnew == kNegInf) ? 1.f : exp2f(mrun - mnew);
+      lrun *= alpha;
+#pragma unroll
+      for (int b = 0; b < NDB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+      mrun = mnew;
+    }
+    const float nm = (mrun == kNegInf) ? 0.f : -mrun;
+    float p[16];
     float lsum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      p[r] = exp2f(p[r] - muse);
+      p[r] = __builtin_amdgcn_exp2f(fmaf(S[r], scale_log2, nm));
       lsum += p[r];
     }
     lsum += __shfl_xor(lsum, 32, 64);
-    lrun = lrun * alpha + lsum;
-    mrun = mnew;
-#pragma unroll
-    for (int b = 0; b < NDB; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+    lrun += lsum;
 
-    // O^T += V^T P^T; MFMA t covers keys {8j + 4*hh + i : 4j + i in [t*KL, t*KL+KL)}
+    // O^T += V^T P^T; MFMA tt covers keys {8j + 4*hh + i : 4j + i in [tt*KL, tt*KL+KL)}
 #pragma unroll
     for (int tt = 0; tt < 16 / KL; ++tt) {
-      typename MF::frag pb;
+      frag pb;
       if constexpr (KL == 8) {
 #pragma unroll
-        for (int s = 0; s < 8; ++s) pb[s] = (__bf16)p[8 * tt + s];
+        for (int sidx = 0; sidx < 8; ++sidx) pb[sidx] = (__bf16)p[8 * tt + sidx];
       } else {
         pb = p[tt];
       }
 #pragma unroll
       for (int b = 0; b < NDB; ++b) {
         const int d = 32 * b + c;
-        typename MF::frag va;
+        frag va;
         if constexpr (KL == 8) {
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(&sV[buf][v_off(d, 16 * tt + 4 * hh)]);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(&sV[buf][v_off(d, 16 * tt + 8 + 4 * hh)]);
-          va = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+          // keys 16tt + {4hh..4hh+3, 8+4hh..8+4hh+3}: quads hh, hh+2 of half tt,
+          // stored at quad slots 2hh, 2hh+1 = unit 2tt + hh
+          va = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(&sV[buf][0])[vq_unit(d, 2 * tt + hh)]);
         } else {
           const int key = 8 * (tt >> 2) + 4 * hh + (tt & 3);
           va = MF::load(&sV[buf][v_off(d, key)]);
@@ -315,6 +351,10 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnTile* __restrict__ 
 }
 
 // ------------------------------------------------------------------ merge
+// At most 1 own part + MAX_CHUNKS prefix chunks per token (the host never
+// plans more).
+constexpr int MAX_PARTS = 9;
+
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeItem* __restrict__ items,
                                                     const float* __restrict__ part_o,
@@ -322,25 +362,34 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeItem* __restrict_
                                                     int hkv) {
   const MergeItem it = items[blockIdx.x];
   const int G = hq / hkv;
+  const int np = 1 + it.n_chunks;
   for (int e = threadIdx.x; e < hq * DH / 4; e += blockDim.x) {
     const int head = e / (DH / 4), d4 = (e % (DH / 4)) * 4;
     const int kvh = head / G, hg = head % G;
-    const size_t r0 = ((size_t)it.own_slot * hkv + kvh) * 128 + it.own_ti * G + hg;
-    auto chunk_row = [&](int c) { return ((size_t)(it.anc_slot0 + c) * hkv + kvh) * 128 + it.anc_ti * G + hg; };
-    float M = part_lse[r0];
-    for (int c = 0; c < it.n_chunks; ++c) M = fmaxf(M, part_lse[chunk_row(c)]);
-    float w = exp2f(part_lse[r0] - M);
-    float4 v = *reinterpret_cast<const float4*>(part_o + r0 * DH + d4);
-    float4 acc = make_float4(w * v.x, w * v.y, w * v.z, w * v.w);
-    float ws = w;
-    for (int c = 0; c < it.n_chunks; ++c) {
-      const size_t rc = chunk_row(c);
-      w = exp2f(part_lse[rc] - M);
-      v = *reinterpret_cast<const float4*>(part_o + rc * DH + d4);
-      acc.x += w * v.x;
-      acc.y += w * v.y;
-      acc.z += w * v.z;
-      acc.w += w * v.w;
+    size_t rows[MAX_PARTS];
+    float L[MAX_PARTS];
+#pragma unroll
+    for (int p = 0; p < MAX_PARTS; ++p) {
+      rows[p] = p == 0 ? ((size_t)it.own_slot * hkv + kvh) * 128 + it.own_ti * G + hg
+                       : ((size_t)(it.anc_slot0 + p - 1) * hkv + kvh) * 128 + it.anc_ti * G + hg;
+      L[p] = p < np ? part_lse[rows[p]] : kNegInf;
+    }
+    float4 v[MAX_PARTS];
+#pragma unroll
+    for (int p = 0; p < MAX_PARTS; ++p)
+      v[p] = p < np ? *reinterpret_cast<const float4*>(part_o + rows[p] * DH + d4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float M = L[0];
+#pragma unroll
+    for (int p = 1; p < MAX_PARTS; ++p) M = fmaxf(M, L[p]);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float ws = 0.f;
+#pragma unroll
+    for (int p = 0; p < MAX_PARTS; ++p) {
+      const float w = p < np ? exp2f(L[p] - M) : 0.f;
+      acc.x += w * v[p].x;
+      acc.y += w * v[p].y;
+      acc.z += w * v[p].z;
+      acc.w += w * v[p].w;
       ws += w;
     }
     const float inv = 1.0f / ws;
