@@ -28,6 +28,7 @@ import time
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
 def algorithmic(wl, inst):
@@ -70,6 +71,92 @@ def cpu_baseline(wl, inst, weights, n_branches: int):
                       f"'{wl.name}' recomputed from scratch by the numpy oracle ({dt:.1f} s)"}
 
 
+def launch_key(rec) -> str:
+    """Launches of one kind over the same number of rows run the same kernel instance."""
+    return f"{rec['kernel']}[{rec['rows']} rows]"
+
+
+def kernel_sources_sha() -> str:
+    import hashlib
+    kdir = os.path.join(ROOT, "shared_prefix_kv_amd", "csrc", "kernels")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(kdir)):
+        with open(os.path.join(kdir, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(key: str):
+    """HBM bytes per launch of `key` from the committed counter runs, or None.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each divided by what the
+    same counter read per byte for a plain device copy of known size.  The
+    figure is dropped (None) once any kernel source differs from the sources
+    the counters were taken on.
+    """
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    k = t.get("kernels", {}).get(key)
+    if not k or k.get("kernel_sources_sha256") != kernel_sources_sha():
+        return None
+    c = t["copy"]
+    rd = k["fetch_kib"] * c["bytes_read"] / c["fetch_kib"]
+    wr = k["write_kib"] * c["bytes_written"] / c["write_kib"]
+    return round(rd + wr)
+
+
+def copy_calibration(mib: int) -> None:
+    """A plain device-to-device copy of known size, for the HBM byte counters."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copy calibration: 3 copies of {n} bytes", file=sys.stderr)
+
+
+def summarize(d: str) -> int:
+    """Markdown summary of rocprofv3 --stats / --pmc CSV files found under d."""
+    import csv
+    import glob
+
+    def short(name: str) -> str:
+        name = name.split("(")[0]
+        return name.replace("void ", "").replace("jev::dev::", "")
+
+    for path in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+        print(f"### kernel time ({os.path.relpath(path, d)})\n")
+        print("| kernel | calls | total ms | avg us | min us | max us | % |")
+        print("|---|---:|---:|---:|---:|---:|---:|")
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                print(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+                      f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                      f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+        print()
+    for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        agg = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                k = (short(r["Kernel_Name"]), r.get("Grid_Size", "?"), r["Counter_Name"])
+                a = agg.setdefault(k, [0, 0.0])
+                a[0] += 1
+                a[1] += float(r["Counter_Value"])
+        print(f"### counters per dispatch ({os.path.relpath(path, d)})\n")
+        print("| kernel | grid | counter | dispatches | mean value |")
+        print("|---|---:|---|---:|---:|")
+        for (kn, grid, cn), (n, v) in sorted(agg.items()):
+            print(f"| `{kn}` | {grid} | {cn} | {n} | {v / n:.1f} |")
+        print()
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -78,8 +165,14 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--cpu-branches", type=int, default=2, help="oracle sample size (0 = skip)")
     ap.add_argument("--roofline-kernel", default="auto",
-                    help="kernel whose roofline is reported (auto = largest total time)")
+                    help="kernel whose roofline is reported, as 'kind[rows]' (auto = largest total time)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the run, copy a MIB-MiB buffer 3 times (counter calibration for traffic)")
+    ap.add_argument("--summarize", metavar="DIR", default=None,
+                    help="print a summary of the rocprofv3 CSV output under DIR and exit")
     args = ap.parse_args(argv)
+    if args.summarize:
+        return summarize(args.summarize)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU sharding of this path is "
               f"a design note, not built", file=sys.stderr)
@@ -132,9 +225,13 @@ def main(argv=None) -> int:
     recs = ctx.profile_read()
     ctx.profile(())
     per_kind = {}
+    per_launch = {}
     for r in recs:
         per_kind[r["kernel"]] = per_kind.get(r["kernel"], 0.0) + r["ms"]
-    kern = max(per_kind, key=per_kind.get) if args.roofline_kernel == "auto" else args.roofline_kernel
+        key = launch_key(r)
+        per_launch[key] = per_launch.get(key, 0.0) + r["ms"]
+    key = max(per_launch, key=per_launch.get) if args.roofline_kernel == "auto" else args.roofline_kernel
+    kern = key.split("[")[0]
 
     # timed region: exactly K steps, the dominant kernel event-timed live
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -145,7 +242,7 @@ def main(argv=None) -> int:
         step(evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    recs = ctx.profile_read()
+    recs = [r for r in ctx.profile_read() if launch_key(r) == key]
     ctx.profile(())
     elapsed = t1 - t0
     st = ctx.stats()
@@ -168,9 +265,10 @@ def main(argv=None) -> int:
         ach = nbytes / (tot_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
-    roof.update({"kernel": kern, "launches": len(recs), "avg_launch_us": round(1e3 * tot_ms / max(1, len(recs)), 2),
+    roof["traffic"] = measured_traffic(key)
+    roof.update({"kernel": key, "launches": len(recs), "avg_launch_us": round(1e3 * tot_ms / max(1, len(recs)), 2),
                  "work_per_launch": (flops or nbytes) / max(1, len(recs)),
-                 "share_of_step": round(per_kind.get(kern, 0) / max(1e-9, sum(per_kind.values())), 3)})
+                 "share_of_step": round(per_launch.get(key, 0) / max(1e-9, sum(per_launch.values())), 3)})
 
     out = {
         "metric": "scored branches/sec + effective prefill tok/s, 2k prefix x 5 branches",
@@ -207,6 +305,8 @@ def main(argv=None) -> int:
     else:
         out["cpu_baseline"] = None
     ctx.close()
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration)
     print(json.dumps(out))
     return 0
 

@@ -50,9 +50,8 @@ constexpr int kRowsPerTile = 128;
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-  size_t rope, x, h, q, o, part_o, part_lse, gemm_part, gemm_cnt, desc, total;
+  size_t rope, x, h, q, o, part_o, part_lse, gemm_part, desc, total;
   size_t gemm_part_elems;
-  int32_t gemm_counters;
   int64_t part_rows;
   int64_t desc_ints;
 };
@@ -84,15 +83,12 @@ WsLayout layout(const jev_model_desc& d) {
   off = align256(off + size_t(L.part_rows) * d.head_dim * sizeof(float));
   L.part_lse = off;
   off = align256(off + size_t(L.part_rows) * sizeof(float));
-  // split-K scratch of the branch-phase GEMMs: an fp32 [256][N] sum tile (kept
-  // zero between launches) and one arrival counter per 128-column tile
+  // split-K scratch of the branch-phase GEMMs: one fp32 [256][N] partial tile
+  // per K split
   const int64_t nmax = std::max<int64_t>(int64_t(d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim, d.d_model);
-  L.gemm_counters = int32_t(nmax / 128 + 1);
-  L.gemm_part_elems = size_t(256) * size_t(nmax);
+  L.gemm_part_elems = size_t(jev::kMaxSplits) * 256 * size_t(nmax);
   L.gemm_part = off;
   off = align256(off + L.gemm_part_elems * sizeof(float));
-  L.gemm_cnt = off;
-  off = align256(off + size_t(L.gemm_counters) * sizeof(int32_t));
   L.desc = off;
   off = align256(off + size_t(L.desc_ints) * sizeof(int32_t));
   L.total = off;
@@ -423,8 +419,7 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
   float* rope = reinterpret_cast<float*>(ctx->ws + ctx->L.rope);
   float* part_o = reinterpret_cast<float*>(ctx->ws + ctx->L.part_o);
   float* part_lse = reinterpret_cast<float*>(ctx->ws + ctx->L.part_lse);
-  const jev::GemmWs gws{reinterpret_cast<float*>(ctx->ws + ctx->L.gemm_part), ctx->L.gemm_part_elems,
-                        reinterpret_cast<int32_t*>(ctx->ws + ctx->L.gemm_cnt), ctx->L.gemm_counters};
+  const jev::GemmWs gws{reinterpret_cast<float*>(ctx->ws + ctx->L.gemm_part), ctx->L.gemm_part_elems};
   const size_t elt = size_t(elt_size(ctx->desc));
   // times one launch with events when its kind is being profiled
   auto timed = [&](int kind, int layer, int64_t rows, double flops, double bytes, auto&& launch) -> hipError_t {
@@ -570,8 +565,6 @@ int jev_create(const jev_model_desc* desc, const jev_weights* weights, void* kv_
     HIPCHK(hipMemcpy(ctx->ws + ctx->L.rope, rope.data(), rope.size() * sizeof(float), hipMemcpyHostToDevice));
     // pages never written hold zeros (a partly valid page is masked, never NaN)
     HIPCHK(hipMemset(kv_pool, 0, jev_kv_pool_bytes(desc, n_pages)));
-    HIPCHK(hipMemset(ctx->ws + ctx->L.gemm_cnt, 0, size_t(ctx->L.gemm_counters) * sizeof(int32_t)));
-    HIPCHK(hipMemset(ctx->ws + ctx->L.gemm_part, 0, ctx->L.gemm_part_elems * sizeof(float)));
     HIPCHK(hipDeviceSynchronize());
   }
   *out = c.release();

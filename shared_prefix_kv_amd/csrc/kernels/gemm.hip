@@ -6,10 +6,11 @@
 // bound.  Branch scoring: M = suffix tokens of all branches (a few hundred),
 // bound by streaming the weights once.
 //
-// One kernel, gemm_v3 (below): 256-row x BN-column tiles, 4 waves of 64 rows;
-// BN = 160 where it makes the tile count fit the 256 CUs (QKV at 2,000 rows:
-// 8 x 32 tiles), else 128.  Up to 256 rows (branch scoring) it splits K over
-// ~4 workgroups per column tile so that the weights stream from every CU.
+// One kernel, gemm_kernel (below): 256-row x BN-column tiles, 4 waves of 64
+// rows; BN = 160 where it makes the tile count fit the 256 CUs (QKV at 2,000
+// rows: 8 x 32 tiles), else 128.  Up to 256 rows (branch scoring) it splits K
+// over several workgroups per column tile so that the weights stream from
+// every CU.
 //
 // Epilogues run on an fp32 tile staged in LDS (full K) or in the fp32 scratch
 // (split K), so their element mapping is independent of the MFMA layout:
@@ -94,136 +95,137 @@ struct ResOut {
 
 enum { EPI_QKV = 0, EPI_RES = 1 };
 
-// Writes one rotate-half pair (or one V element) of row m.
+// Eight consecutive stored elements <-> fp32 (16 bytes of bf16, 32 of fp32).
+// The address is aligned to the eight elements.
 template <typename T>
-__device__ __forceinline__ void qkv_store_pair(const QkvOut& qo, const ColMap& cm, int m, int pair, float a0,
-                                               float a1) {
-  const int h2 = qo.dh >> 1;
-  const int head = pair / h2, i = pair % h2;
-  const float2 cs = qo.rope[(size_t)qo.pos[m] * h2 + i];
-  const float o0 = a0 * cs.x - a1 * cs.y;
-  const float o1 = a1 * cs.x + a0 * cs.y;
-  if (head < cm.hq) {
-    T* q = reinterpret_cast<T*>(qo.qbuf) + ((size_t)m * qo.hq + head) * qo.dh;
-    q[i] = from_f32<T>(o0);
-    q[i + h2] = from_f32<T>(o1);
-  } else {
-    const int sl = qo.kvslot[m];
-    const size_t pe = (size_t)16 * qo.dh;
-    T* kb = reinterpret_cast<T*>(qo.pool) + ((size_t)(sl >> 4) * qo.hkv + (head - cm.hq)) * 2 * pe +
-            (size_t)(sl & 15) * qo.dh;
-    kb[i] = from_f32<T>(o0);
-    kb[i + h2] = from_f32<T>(o1);
+__device__ __forceinline__ void load8(const T* src, float v[8]);
+template <>
+__device__ __forceinline__ void load8<bf16s>(const bf16s* src, float v[8]) {
+  const u32x4 u = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(u[i] << 16);
+    v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
   }
 }
-
-template <typename T>
-__device__ __forceinline__ void qkv_store_v(const QkvOut& qo, int m, int vcol, float a) {
-  const int sl = qo.kvslot[m];
-  const size_t pe = (size_t)16 * qo.dh;
-  const int head = vcol / qo.dh, f = vcol % qo.dh;
-  T* vb = reinterpret_cast<T*>(qo.pool) + ((size_t)(sl >> 4) * qo.hkv + head) * 2 * pe + pe;
-  vb[(size_t)f * 16 + (sl & 15)] = from_f32<T>(a);
-}
-
-// Two adjacent stored elements (address aligned to their pair).
-template <typename T>
-__device__ __forceinline__ void store_pair(T* dst, float x, float y);
 template <>
-__device__ __forceinline__ void store_pair<bf16s>(bf16s* dst, float x, float y) {
-  *reinterpret_cast<uint32_t*>(dst) = uint32_t(from_f32<bf16s>(x).bits) | (uint32_t(from_f32<bf16s>(y).bits) << 16);
+__device__ __forceinline__ void load8<float>(const float* src, float v[8]) {
+  const float4 a = reinterpret_cast<const float4*>(src)[0], b = reinterpret_cast<const float4*>(src)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <typename T>
+__device__ __forceinline__ void store8(T* dst, const float v[8]);
+template <>
+__device__ __forceinline__ void store8<bf16s>(bf16s* dst, const float v[8]) {
+  u32x4 u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) u[i] = uint32_t(from_f32<bf16s>(v[2 * i]).bits) | (uint32_t(from_f32<bf16s>(v[2 * i + 1]).bits) << 16);
+  *reinterpret_cast<u32x4*>(dst) = u;
 }
 template <>
-__device__ __forceinline__ void store_pair<float>(float* dst, float x, float y) {
-  *reinterpret_cast<float2*>(dst) = make_float2(x, y);
+__device__ __forceinline__ void store8<float>(float* dst, const float v[8]) {
+  reinterpret_cast<float4*>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-// Epilogue over an fp32 tile: rows [0, rows) of tile_row0.., columns [0, BN) of
-// column tile nt; element (r, j) at tile[r * ld + j].
+// Epilogue over an fp32 tile: rows [0, rows) are output rows m0.., columns
+// [0, BN) are column tile nt; element (r, j) at tile[r * ld + j] (LDS or
+// global).  Work is cut into vector units so that every thread issues 16-byte
+// loads and stores:
+//  * RES: 8 columns of one row, x += tile;
+//  * QKV, rotate-half pairs: 4 consecutive pairs (i, i + dh/2) of one row and
+//    head, rotated at the row's position and written as 8 adjacent elements
+//    (pair i at 2i, 2i+1) of q or of the row's K page slot;
+//  * QKV, V columns: one column over 8 rows; when the rows' KV slots are 8
+//    consecutive, 8-aligned slots of one page (the usual case) they are one
+//    16-byte run of the transposed V block, else single stores.
 template <typename T, int EPI>
 __device__ __forceinline__ void tile_epilogue(const float* tile, int ld, int rows, int m0, int M, int nt, int BN,
                                               const ColMap& cm, const QkvOut& qo, const ResOut& ro, int tid,
                                               int nthreads) {
+  rows = min(rows, M - m0);
   if constexpr (EPI == EPI_RES) {
-    constexpr int CH = 16 / sizeof(T);
-    const int cpr = BN / CH;  // 16-byte chunks per row
-    for (int e = tid; e < rows * cpr; e += nthreads) {
-      const int r = e / cpr, c = (e % cpr) * CH;
-      const int m = m0 + r;
-      if (m >= M) continue;
-      T* xp = reinterpret_cast<T*>(ro.x) + (size_t)m * ro.ld + (size_t)nt * BN + c;
-      float xv[CH];
-#pragma unroll
-      for (int i = 0; i < CH; ++i) xv[i] = to_f32(xp[i]) + tile[r * ld + c + i];
-#pragma unroll
-      for (int i = 0; i < CH; ++i) xp[i] = from_f32<T>(xv[i]);
+    const int cpr = BN / 8;
+    const int rstep = nthreads / cpr;
+    const int c8 = tid % cpr;
+    for (int r = tid / cpr; r < rows && tid < rstep * cpr; r += rstep) {
+      T* xp = reinterpret_cast<T*>(ro.x) + (size_t)(m0 + r) * ro.ld + (size_t)nt * BN + 8 * c8;
+      const float* tp = tile + (size_t)r * ld + 8 * c8;
+      float v[8];
+      load8<T>(xp, v);
+      const float4 t0 = reinterpret_cast<const float4*>(tp)[0], t1 = reinterpret_cast<const float4*>(tp)[1];
+      v[0] += t0.x; v[1] += t0.y; v[2] += t0.z; v[3] += t0.w;
+      v[4] += t1.x; v[5] += t1.y; v[6] += t1.z; v[7] += t1.w;
+      store8<T>(xp, v);
     }
   } else {
-    // QKV: per-row (position, KV slot) and per-column (kind, pair or V
-    // column) data are staged in LDS once per tile; the element loop is
-    // unrolled so that the RoPE table loads of 8 elements are in flight
-    // together.
-    __shared__ int s_pos[256], s_slot[256], s_col[256];
-    const int32_t* __restrict__ pos = qo.pos;
-    const int32_t* __restrict__ kvslot = qo.kvslot;
-    const float2* __restrict__ rope = qo.rope;
+    const int h2 = cm.dh >> 1;
+    const int half = BN >> 1;
+    const int np_t = max(0, min(half, cm.n_pairs - half * nt));
+    const int pairs_before = min(cm.n_pairs, half * nt);
+    const size_t pe = (size_t)16 * qo.dh;
     T* __restrict__ qbuf = reinterpret_cast<T*>(qo.qbuf);
     T* __restrict__ pool = reinterpret_cast<T*>(qo.pool);
-    const int h2 = cm.dh >> 1;
-    const int np_t = max(0, min(BN >> 1, cm.n_pairs - (BN >> 1) * nt));
-    for (int r = tid; r < rows; r += nthreads) {
-      const int m = min(m0 + r, M - 1);
-      s_pos[r] = pos[m];
-      s_slot[r] = kvslot[m];
-    }
-    for (int j = tid; j < BN; j += nthreads) {
-      const ColInfo ci = qkv_col(cm, BN, nt, j);
-      // bits 0-1 kind, 2-13 head, 14-27 index within the head (pair index i
-      // for q/k, feature f for v)
-      int head, idx;
-      if (ci.kind == COL_V) {
-        head = ci.vcol / qo.dh;
-        idx = ci.vcol % qo.dh;
-      } else {
-        head = ci.pair / h2;
-        idx = ci.pair % h2;
-      }
-      s_col[j] = ci.kind | (head << 2) | (idx << 14);
-    }
-    __syncthreads();
-    const size_t pe = (size_t)16 * qo.dh;
-    const int valid_rows = min(rows, M - m0);
-    // active columns: the np_t pair heads, then the V columns (partners are
-    // handled with their pair)
-    const int n_act = BN - np_t;
-    const int total = valid_rows * n_act;
-#pragma unroll 8
-    for (int e = tid; e < total; e += nthreads) {
-      const int r = e / n_act, a = e - (e / n_act) * n_act;
-      const int j = a < np_t ? a : a + np_t;
-      const int cc = s_col[j];
-      const int kind = cc & 3, head = (cc >> 2) & 4095, idx = cc >> 14;
-      const int m = m0 + r;
-      if (kind == COL_FIRST) {
-        const float2 cs = rope[(size_t)s_pos[r] * h2 + idx];
-        const float a0 = tile[r * ld + j], a1 = tile[r * ld + j + np_t];
+    if (np_t > 0) {
+      const int g4 = np_t >> 2;  // units of 4 pairs per row
+      const int rstep = nthreads / g4;
+      const int g = tid % g4;
+      const int p0 = pairs_before + 4 * g;  // global pair index of the unit
+      const int head = p0 / h2, i0 = p0 % h2;
+      for (int r = tid / g4; r < rows && tid < rstep * g4; r += rstep) {
+        const int m = m0 + r;
+        const float* tp = tile + (size_t)r * ld + 4 * g;
+        const float4 a0 = *reinterpret_cast<const float4*>(tp);
+        const float4 a1 = *reinterpret_cast<const float4*>(tp + np_t);
+        const float4* rp = reinterpret_cast<const float4*>(qo.rope + (size_t)qo.pos[m] * h2 + i0);
+        const float4 cs01 = rp[0], cs23 = rp[1];  // (cos, sin) of pairs i0 .. i0+3
+        float v[8];
+        v[0] = a0.x * cs01.x - a1.x * cs01.y; v[1] = a1.x * cs01.x + a0.x * cs01.y;
+        v[2] = a0.y * cs01.z - a1.y * cs01.w; v[3] = a1.y * cs01.z + a0.y * cs01.w;
+        v[4] = a0.z * cs23.x - a1.z * cs23.y; v[5] = a1.z * cs23.x + a0.z * cs23.y;
+        v[6] = a0.w * cs23.z - a1.w * cs23.w; v[7] = a1.w * cs23.z + a0.w * cs23.w;
         // q and k store each rotate-half pair (i, i + dh/2) adjacently, at
         // 2i and 2i+1: both sides of every q.k product use the same order
         T* dst;
         if (head < cm.hq) {
-          dst = qbuf + ((size_t)m * qo.hq + head) * qo.dh + 2 * idx;
+          dst = qbuf + ((size_t)m * qo.hq + head) * qo.dh + 2 * i0;
         } else {
-          const int sl = s_slot[r];
-          dst = pool + ((size_t)(sl >> 4) * qo.hkv + (head - cm.hq)) * 2 * pe + (size_t)(sl & 15) * qo.dh + 2 * idx;
+          const int sl = qo.kvslot[m];
+          dst = pool + ((size_t)(sl >> 4) * qo.hkv + (head - cm.hq)) * 2 * pe + (size_t)(sl & 15) * qo.dh + 2 * i0;
         }
-        store_pair<T>(dst, a0 * cs.x - a1 * cs.y, a1 * cs.x + a0 * cs.y);
-      } else if (kind == COL_V) {
-        const int sl = s_slot[r];
-        pool[((size_t)(sl >> 4) * qo.hkv + head) * 2 * pe + pe + (size_t)idx * 16 + (sl & 15)] =
-            from_f32<T>(tile[r * ld + j]);
+        store8<T>(dst, v);
       }
     }
-    __syncthreads();
+    const int nv = BN - 2 * np_t;  // V columns of this tile
+    if (nv > 0) {
+      const int vcol0 = BN * nt - 2 * pairs_before;
+      const int rstep = (nthreads / nv) * 8;
+      const int j = tid % nv;
+      const int vcol = vcol0 + j, head = vcol / qo.dh, f = vcol % qo.dh;
+      T* vb_head = pool + (size_t)head * 2 * pe + pe + (size_t)f * 16;
+      for (int r = (tid / nv) * 8; r < rows && tid < (nthreads / nv) * nv; r += rstep) {
+        const float* tp = tile + (size_t)r * ld + 2 * np_t + j;
+        const int n = min(8, rows - r);
+        int sl[8];
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          sl[q] = qo.kvslot[m0 + r + min(q, n - 1)];
+          v[q] = tp[(size_t)min(q, n - 1) * ld];
+        }
+        bool run = n == 8 && (sl[0] & 7) == 0;
+#pragma unroll
+        for (int q = 1; q < 8; ++q) run = run && sl[q] == sl[0] + q;
+        if (run) {
+          store8<T>(vb_head + (size_t)(sl[0] >> 4) * qo.hkv * 2 * pe + (sl[0] & 15), v);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (q < n) vb_head[(size_t)(sl[q] >> 4) * qo.hkv * 2 * pe + (sl[q] & 15)] = from_f32<T>(v[q]);
+        }
+      }
+    }
   }
 }
 
@@ -246,18 +248,20 @@ __device__ __forceinline__ void xcd_tile(int b, int n_blocks, int m_tiles, int* 
 }
 
 // --------------------------------------------------------------- main kernel
-// Block = 4 waves; wave w owns rows [64w, 64w+64) of a 256-row tile and all BN
-// columns.  A rows are private to a wave, so A fragments go straight from
-// global memory into MFMA-layout registers (one stage ahead); B rows are shared
-// by the 4 waves and go through LDS (rows padded to 144 bytes so the 16 rows of
-// one 16-lane fragment read fall in 16 different bank groups), register-staged
-// two stages ahead.  With SPLIT, blockIdx.y selects a slice of K and partial sums
-// are added (agent-scope fp32 atomics) into an fp32 [M][N] scratch tile;
-// split_epilogue (next launch) runs the epilogue on the sums over all CUs and
-// clears the scratch for the next use.
+// Block = 4 waves over a 256-row x BN-column tile; wave w owns rows
+// [64w, 64w+64) and all BN columns (2 x BN/32 MFMA 32x32 blocks).  Both
+// operands are staged through LDS: global loads are fully coalesced (8 lanes
+// per 128-byte row segment), held in registers two K stages ahead and written
+// to a double-buffered LDS stage whose rows are padded to 144 bytes, so that
+// the 16 rows touched by one 16-lane fragment read (or one 16-lane write) fall
+// in different bank groups; the stores of the next stage are spread between
+// the MFMAs of the current one.  One barrier per 128-byte K stage.  With SPLIT,
+// blockIdx.y selects a slice of K and partial sums are added (agent-scope fp32
+// atomics) into an fp32 [M][N] scratch; split_epilogue (next launch) runs the
+// epilogue on the sums over all CUs and clears the scratch for the next use.
 template <typename T, int BN, int EPI, bool SPLIT>
-__global__ __launch_bounds__(256) void gemm_v3(const T* __restrict__ A, int M, int K, int N, ColMap cm, QkvOut qo,
-                                               ResOut ro, float* __restrict__ scratch) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(const T* __restrict__ A, int M, int K, int N, ColMap cm,
+                                                   QkvOut qo, ResOut ro, float* __restrict__ scratch) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
   constexpr int BM = 256;
@@ -265,16 +269,19 @@ __global__ __launch_bounds__(256) void gemm_v3(const T* __restrict__ A, int M, i
   constexpr int BK = 8 * CH;           // 128 bytes of K per stage
   constexpr int KS = BK / MF::KSTEP;   // MFMA k-steps per stage
   constexpr int TN = BN / 32;
+  constexpr int LA = BM * 8 / 256;     // A chunks per thread per stage
   constexpr int LB = BN * 8 / 256;     // B chunks per thread per stage
-  constexpr int LDS_B = 2 * BN * 9;                 // in 16-byte units
+  constexpr int NST = LA + LB;         // LDS stores per thread per stage
+  constexpr int RS = 9;                // LDS row stride, 16-byte units
+  constexpr int STAGE = (BM + BN) * RS;
+  constexpr int LDS_MAIN = 2 * STAGE;
   constexpr int LDS_EPI = SPLIT ? 0 : 128 * (BN + 4) / 4;
-  constexpr int LDS_UNITS = LDS_B > LDS_EPI ? LDS_B : LDS_EPI;
+  constexpr int LDS_UNITS = LDS_MAIN > LDS_EPI ? LDS_MAIN : LDS_EPI;
   static_assert((BN * 8) % 256 == 0, "tile");
   __shared__ __attribute__((aligned(16))) u32x4 smem[LDS_UNITS];
-  u32x4* sB[2] = {smem, smem + BN * 9};
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n_tiles_n = N / BN;
+  const int c = lane & 31, hh = lane >> 5;
   int mt, nt;
   if (SPLIT) {
     mt = 0;
@@ -288,15 +295,14 @@ __global__ __launch_bounds__(256) void gemm_v3(const T* __restrict__ A, int M, i
   const int kt0 = SPLIT ? (KTall * (int)blockIdx.y) / (int)gridDim.y : 0;
   const int KT = SPLIT ? (KTall * ((int)blockIdx.y + 1)) / (int)gridDim.y - kt0 : KTall;
 
-  const T* ap[2];
+  const u32x4* ap[LA];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-    ap[i] = A + (size_t)min(m0 + wave * 64 + 32 * i + (lane & 31), M - 1) * K + MF::KL * (lane >> 5) + (size_t)kt0 * BK;
+  for (int i = 0; i < LA; ++i)
+    ap[i] = reinterpret_cast<const u32x4*>(A + (size_t)min(m0 + lrow + 32 * i, M - 1) * K + (size_t)kt0 * BK) + lch;
   const u32x4* bp[LB];
 #pragma unroll
   for (int i = 0; i < LB; ++i)
     bp[i] = reinterpret_cast<const u32x4*>(weight_row<T>(cm, BN, n0 + lrow + 32 * i, K) + (size_t)kt0 * BK) + lch;
-  (void)n_tiles_n;
 
   f32x16 acc[2][TN];
 #pragma unroll
@@ -306,67 +312,108 @@ __global__ __launch_bounds__(256) void gemm_v3(const T* __restrict__ A, int M, i
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  frag a0[2][KS], a1[2][KS];
-  u32x4 rb0[LB], rb1[LB];
-#define V3_ALOAD(AA, KT_)                                                              \
-  do {                                                                                 \
-    const int kk_ = min((KT_), KT - 1) * BK;                                           \
-    _Pragma("unroll") for (int i = 0; i < 2; ++i) _Pragma("unroll") for (int s = 0; s < KS; ++s) \
-        AA[i][s] = MF::load(ap[i] + kk_ + s * MF::KSTEP);                              \
+  u32x4 ra0[LA], rb0[LB], ra1[LA], rb1[LB];
+#define G_LOAD(RA, RB, KT_)                                                                 \
+  do {                                                                                      \
+    const int kk_ = min((KT_), KT - 1) * 8;                                                 \
+    _Pragma("unroll") for (int i = 0; i < LA; ++i) RA[i] = ap[i][kk_];                      \
+    _Pragma("unroll") for (int i = 0; i < LB; ++i) RB[i] = bp[i][kk_];                      \
   } while (0)
-#define V3_BLOAD(RB, KT_)                                                              \
-  do {                                                                                 \
-    const int kk_ = min((KT_), KT - 1) * 8;                                            \
-    _Pragma("unroll") for (int i = 0; i < LB; ++i) RB[i] = bp[i][kk_];                 \
+#define G_STORE(RA, RB, BUF)                                                                \
+  do {                                                                                      \
+    u32x4* sA_ = smem + (BUF) * STAGE;                                                      \
+    u32x4* sB_ = sA_ + BM * RS;                                                             \
+    _Pragma("unroll") for (int i = 0; i < LA; ++i) sA_[(lrow + 32 * i) * RS + lch] = RA[i]; \
+    _Pragma("unroll") for (int i = 0; i < LB; ++i) sB_[(lrow + 32 * i) * RS + lch] = RB[i]; \
   } while (0)
-#define V3_BSTORE(RB, BUF)                                                             \
-  do {                                                                                 \
-    _Pragma("unroll") for (int i = 0; i < LB; ++i) sB[BUF][(lrow + 32 * i) * 9 + lch] = RB[i]; \
+  // One stage of compute on LDS buffer BUF, with the next stage's staged
+  // registers (RA, RB) written into the other buffer during it (W_ = 1).
+  // Fragments of k-step s+1 are read into the other fragment set before the
+  // MFMAs of k-step s; inside each k-step's region the scheduling groups put
+  // one LDS read or write between consecutive MFMAs, so LDS traffic overlaps
+  // MFMA execution instead of following it.
+#define G_FRAGS(FA, FB, S_)                                                                      \
+  do {                                                                                           \
+    const int k_ = (S_) * MF::KSTEP + MF::KL * hh;                                               \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i) FA[i] =                                        \
+        MF::load(reinterpret_cast<const T*>(&sA_[(64 * wave + 32 * i + c) * RS + k_ / CH]) + k_ % CH); \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j) FB[j] =                                       \
+        MF::load(reinterpret_cast<const T*>(&sB_[(32 * j + c) * RS + k_ / CH]) + k_ % CH);       \
   } while (0)
-#define V3_COMPUTE(AA, BUF)                                                                          \
-  do {                                                                                               \
-    _Pragma("unroll") for (int s = 0; s < KS; ++s) {                                                 \
-      const int k_ = s * MF::KSTEP + MF::KL * (lane >> 5);                                           \
-      frag b_[TN];                                                                                   \
-      _Pragma("unroll") for (int j = 0; j < TN; ++j) b_[j] =                                         \
-          MF::load(reinterpret_cast<const T*>(&sB[BUF][(32 * j + (lane & 31)) * 9 + k_ / CH]) + k_ % CH); \
-      _Pragma("unroll") for (int i = 0; i < 2; ++i) _Pragma("unroll") for (int j = 0; j < TN; ++j) acc[i][j] = \
-          MF::mma(AA[i][s], b_[j], acc[i][j]);                                                       \
-    }                                                                                                \
+#define G_MMA(FA, FB)                                                                            \
+  do {                                                                                           \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i) _Pragma("unroll") for (int j = 0; j < TN; ++j) \
+        acc[i][j] = MF::mma(FA[i], FB[j], acc[i][j]);                                            \
+  } while (0)
+#define G_WRITES(RA, RB, S_)                                                                     \
+  do {                                                                                           \
+    _Pragma("unroll") for (int q = (S_) * NST / KS; q < ((S_) + 1) * NST / KS; ++q) {            \
+      if (q < LA) wA_[(lrow + 32 * q) * RS + lch] = RA[q < LA ? q : 0];                          \
+      else wB_[(lrow + 32 * (q - LA)) * RS + lch] = RB[q < LA ? 0 : q - LA];                     \
+    }                                                                                            \
+  } while (0)
+#define G_GROUPS(NR_, NW_)                                                                       \
+  do {                                                                                           \
+    _Pragma("unroll") for (int m_ = 0; m_ < 2 * TN; ++m_) {                                      \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                         \
+      if (m_ < (NR_)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                         \
+      if (m_ < (NW_)) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                         \
+    }                                                                                            \
+  } while (0)
+#define G_PHASE(BUF, RA, RB, W_)                                                                 \
+  do {                                                                                           \
+    const u32x4* sA_ = smem + (BUF) * STAGE;                                                     \
+    const u32x4* sB_ = sA_ + BM * RS;                                                            \
+    u32x4* wA_ = smem + ((BUF) ^ 1) * STAGE;                                                     \
+    u32x4* wB_ = wA_ + BM * RS;                                                                  \
+    (void)wA_;                                                                                   \
+    (void)wB_;                                                                                   \
+    frag fa0[2], fb0[TN], fa1[2], fb1[TN];                                                       \
+    G_FRAGS(fa0, fb0, 0);                                                                        \
+    __builtin_amdgcn_sched_barrier(0);                                                           \
+    _Pragma("unroll") for (int s = 0; s < KS; s += 2) {                                          \
+      if (s + 1 < KS) G_FRAGS(fa1, fb1, s + 1);                                                  \
+      G_MMA(fa0, fb0);                                                                           \
+      if (W_) G_WRITES(RA, RB, s);                                                               \
+      G_GROUPS(s + 1 < KS ? 2 + TN : 0, (W_) ? ((s + 1) * NST / KS - s * NST / KS) : 0);        \
+      __builtin_amdgcn_sched_barrier(0);                                                         \
+      if (s + 1 < KS) {                                                                          \
+        if (s + 2 < KS) G_FRAGS(fa0, fb0, s + 2);                                                \
+        G_MMA(fa1, fb1);                                                                         \
+        if (W_) G_WRITES(RA, RB, s + 1);                                                         \
+        G_GROUPS(s + 2 < KS ? 2 + TN : 0, (W_) ? ((s + 2) * NST / KS - (s + 1) * NST / KS) : 0); \
+        __builtin_amdgcn_sched_barrier(0);                                                       \
+      }                                                                                          \
+    }                                                                                            \
   } while (0)
 
-  V3_ALOAD(a0, 0);
-  V3_BLOAD(rb0, 0);
-  V3_BLOAD(rb1, 1);
-  V3_BSTORE(rb0, 0);
+  G_LOAD(ra0, rb0, 0);
+  G_LOAD(ra1, rb1, 1);
+  G_STORE(ra0, rb0, 0);
   __syncthreads();
   int kt = 0;
-  // two stages per trip keep the register sets static; scheduling barriers keep
-  // the prefetch loads ahead of the MFMA block
+  // two stages per trip keep the register sets static
   for (; kt + 1 < KT; kt += 2) {
-    V3_ALOAD(a1, kt + 1);
-    V3_BLOAD(rb0, kt + 2);
+    G_LOAD(ra0, rb0, kt + 2);
     __builtin_amdgcn_sched_barrier(0);
-    V3_COMPUTE(a0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    V3_BSTORE(rb1, 1);
+    G_PHASE(0, ra1, rb1, 1);
     __syncthreads();
-    V3_ALOAD(a0, kt + 2);
-    V3_BLOAD(rb1, kt + 3);
+    G_LOAD(ra1, rb1, kt + 3);
     __builtin_amdgcn_sched_barrier(0);
-    V3_COMPUTE(a1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    V3_BSTORE(rb0, 0);
+    G_PHASE(1, ra0, rb0, 1);
     __syncthreads();
   }
-  if (kt < KT) V3_COMPUTE(a0, 0);
-#undef V3_ALOAD
-#undef V3_BLOAD
-#undef V3_BSTORE
-#undef V3_COMPUTE
+  if (kt < KT) G_PHASE(0, ra1, rb1, 0);
+#undef G_LOAD
+#undef G_STORE
+#undef G_PHASE
+#undef G_FRAGS
+#undef G_MMA
+#undef G_WRITES
+#undef G_GROUPS
 
-  const int c = lane & 31, hh = lane >> 5;
   if constexpr (SPLIT) {
+    float* part = scratch + (size_t)blockIdx.y * BM * N;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -374,9 +421,7 @@ __global__ __launch_bounds__(256) void gemm_v3(const T* __restrict__ A, int M, i
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = wave * 64 + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (m < M)
-            __hip_atomic_fetch_add(scratch + (size_t)m * N + n0 + 32 * j + c, acc[i][j][r], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+          if (m < M) part[(size_t)m * N + n0 + 32 * j + c] = acc[i][j][r];
         }
   } else {
     float* stile = reinterpret_cast<float*>(smem);
@@ -396,26 +441,35 @@ __global__ __launch_bounds__(256) void gemm_v3(const T* __restrict__ A, int M, i
             }
       }
       __syncthreads();
-      tile_epilogue<T, EPI>(stile, LD, 128, m0 + 128 * half, M, nt, BN, cm, qo, ro, tid, 256);
+      if (m0 + 128 * half < M)
+        tile_epilogue<T, EPI>(stile, LD, 128, m0 + 128 * half, M, nt, BN, cm, qo, ro, tid, 256);
       __syncthreads();
     }
   }
 }
 
-// Epilogue of a split-K GEMM: block (column tile of 128, 16 rows).
+// Epilogue of a split-K GEMM: block (column tile of 128, 16 rows) sums the
+// `splits` partial slices into slice 0, then runs the epilogue on it.
 template <typename T, int EPI>
-__global__ __launch_bounds__(256) void split_epilogue(float* __restrict__ scratch, int M, int N, ColMap cm, QkvOut qo,
-                                                      ResOut ro) {
+__global__ __launch_bounds__(256) void split_epilogue(float* __restrict__ scratch, int splits, int M, int N, ColMap cm,
+                                                      QkvOut qo, ResOut ro) {
   constexpr int BN = 128, RB = 16;
   const int nt = blockIdx.x, r0 = blockIdx.y * RB;
   const int rows = min(RB, M - r0);
   float* tile = scratch + (size_t)r0 * N + nt * BN;
-  tile_epilogue<T, EPI>(tile, N, rows, r0, M, nt, BN, cm, qo, ro, threadIdx.x, 256);
-  __syncthreads();
+  const size_t slice = (size_t)256 * N;
   for (int e = threadIdx.x; e < rows * (BN / 4); e += 256) {
     const int r = e / (BN / 4), q4 = e % (BN / 4);
-    *reinterpret_cast<float4*>(tile + (size_t)r * N + 4 * q4) = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4* p = reinterpret_cast<float4*>(tile + (size_t)r * N + 4 * q4);
+    float4 v = *p;
+    for (int y = 1; y < splits; ++y) {
+      const float4 w = *reinterpret_cast<const float4*>(tile + y * slice + (size_t)r * N + 4 * q4);
+      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+    }
+    *p = v;
   }
+  __syncthreads();
+  tile_epilogue<T, EPI>(tile, N, rows, r0, M, nt, BN, cm, qo, ro, threadIdx.x, 256);
 }
 
 }  // namespace dev
@@ -433,20 +487,20 @@ hipError_t gemm_dispatch(const ModelDims& m, const GemmWs& ws, const void* A, in
                          const dev::ColMap& cm, const dev::QkvOut& qo, const dev::ResOut& ro, hipStream_t s) {
   const T* a = reinterpret_cast<const T*>(A);
   if (M <= 256) {
-    // split-K over ~4 workgroups per 128-column tile
+    // split K so that the column tiles times the splits fill the CUs once
     constexpr int BN = 128;
     if (N % BN) return hipErrorInvalidValue;
     const int tiles = N / BN;
     const int KT = K / (8 * (16 / int(sizeof(T))));
-    int S = g_gemm_tuning.splits > 0 ? g_gemm_tuning.splits : std::max(1, 512 / tiles);
-    S = std::max(1, std::min({S, 8, KT / 2 > 0 ? KT / 2 : 1}));
-    if ((size_t)256 * N > ws.partial_elems) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((dev::gemm_v3<T, BN, EPI, true>), dim3(tiles, S), dim3(256), 0, s, a, M, K, N, cm, qo, ro,
+    int S = g_gemm_tuning.splits > 0 ? g_gemm_tuning.splits : std::max(1, 256 / tiles);
+    S = std::max(1, std::min({S, kMaxSplits, KT / 2 > 0 ? KT / 2 : 1}));
+    if ((size_t)S * 256 * N > ws.partial_elems) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((dev::gemm_kernel<T, BN, EPI, true>), dim3(tiles, S), dim3(256), 0, s, a, M, K, N, cm, qo, ro,
                        ws.partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dev::split_epilogue<T, EPI>), dim3(tiles, (M + 15) / 16), dim3(256), 0, s, ws.partial, M, N,
-                       cm, qo, ro);
+    hipLaunchKernelGGL((dev::split_epilogue<T, EPI>), dim3(tiles, (M + 15) / 16), dim3(256), 0, s, ws.partial, S, M,
+                       N, cm, qo, ro);
     return hipGetLastError();
   }
   const int mt = (M + 255) / 256;
@@ -461,9 +515,9 @@ hipError_t gemm_dispatch(const ModelDims& m, const GemmWs& ws, const void* A, in
   if (N % bn) return hipErrorInvalidValue;
   dim3 grid((N / bn) * mt);
   if (bn == 160)
-    hipLaunchKernelGGL((dev::gemm_v3<T, 160, EPI, false>), grid, dim3(256), 0, s, a, M, K, N, cm, qo, ro, nullptr);
+    hipLaunchKernelGGL((dev::gemm_kernel<T, 160, EPI, false>), grid, dim3(256), 0, s, a, M, K, N, cm, qo, ro, nullptr);
   else
-    hipLaunchKernelGGL((dev::gemm_v3<T, 128, EPI, false>), grid, dim3(256), 0, s, a, M, K, N, cm, qo, ro, nullptr);
+    hipLaunchKernelGGL((dev::gemm_kernel<T, 128, EPI, false>), grid, dim3(256), 0, s, a, M, K, N, cm, qo, ro, nullptr);
   return hipGetLastError();
 }
 

@@ -47,13 +47,12 @@ struct LayerW {
   const void* wo;
 };
 
-// Scratch of the projection GEMMs: split-K partial tiles and per-column-tile
-// arrival counters (zero at creation; each launch leaves them zero).
+// Scratch of the projection GEMMs with at most 256 rows: one fp32 [256][N]
+// partial tile per K split (up to kMaxSplits), overwritten by every launch.
+constexpr int kMaxSplits = 8;
 struct GemmWs {
   float* partial;
   size_t partial_elems;
-  int32_t* counters;
-  int32_t n_counters;
 };
 
 struct GemmTuning {
