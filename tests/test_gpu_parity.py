@@ -259,3 +259,32 @@ def test_w3_staged_rounds_match_oracle(w2):
     st = ctx.stats()
     assert st["rounds"] == 3 and st["computed_tokens"] == 800 + 120 + 240
     assert st["pages_in_use"] == 0
+
+
+# ------------------------------------------------------------------ workload 4 (batch of requests)
+def test_w4_batch_of_requests_matches_oracle():
+    """Sixteen 1,200-token prefixes prefilled in one call, eight 64-token
+    branches per prefix scored in one call with 64 labels each: every branch
+    attends to its own request's pages only."""
+    g = golden(4)
+    wl = workload(4)
+    inst = make_instance(wl)
+    ctx, _ = device_context(4, n_pages=2048, max_pos=1536, max_tok=20480)
+    hs = ctx.prefill_prefix([0] * len(inst.prefixes), inst.prefixes)
+    tables = [ctx.page_table(h)[0] for h in hs]
+    br = inst.passes[0]
+    probs, loff = ctx.score_branches([hs[b.request] for b in br], [b.tokens for b in br],
+                                     [b.labels for b in br])
+    _sync()
+    got = split_probs(probs, loff)
+    err = max_abs(got, g["passes"][0]["probs"])
+    print("w4 max abs err", err)
+    st = ctx.stats()
+    ctx.free_pages(hs)
+    assert err <= TOL_BF16_E2E
+    assert all(len(t) == 75 for t in tables)
+    assert len({p for t in tables for p in t}) == 16 * 75
+    assert st["computed_tokens"] == 128 * 64 and st["logical_tokens"] == 128 * (1200 + 64)
+    assert ctx.stats()["pages_in_use"] == 0
+    for p in got:
+        assert abs(float(np.sum(p)) - 1.0) < 1e-4 and len(p) == 64
