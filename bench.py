@@ -140,6 +140,20 @@ def summarize(d: str) -> int:
                       f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                       f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
         print()
+    for path in sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)):
+        inst = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                k = (short(r["Kernel_Name"]), int(r["Grid_Size_X"]))
+                a = inst.setdefault(k, [])
+                a.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        print(f"### kernel instances by grid ({os.path.relpath(path, d)})\n")
+        print("| kernel | grid x | calls | avg us | median us |")
+        print("|---|---:|---:|---:|---:|")
+        for (kn, gx), v in sorted(inst.items(), key=lambda x: -sum(x[1])):
+            v = sorted(v)
+            print(f"| `{kn}` | {gx} | {len(v)} | {sum(v) / len(v):.2f} | {v[len(v) // 2]:.2f} |")
+        print()
     for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
         agg = {}
         with open(path) as f:
