@@ -44,7 +44,10 @@ int fail(int code, const std::string& msg) {
   return code;
 }
 
-constexpr int kMaxChunks = 8;   // prefix chunks per sibling group
+constexpr int kMaxChunks = jev::kMaxAncParts;  // prefix chunks per sibling group
+// own causal tiles are split in two when a round has fewer (tile, KV head)
+// pairs than the GPU has CUs (otherwise every CU already holds work)
+constexpr int64_t kSplitTilesBelow = 256;
 constexpr int kRowsPerTile = 128;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -316,33 +319,64 @@ int build_round(jev_ctx* ctx, std::vector<RNode>& nodes, std::vector<int32_t>& h
   std::vector<jev::AttnTile> tiles;
   std::vector<jev::MergeItem> merges;
   int64_t slot = 0;
-  std::vector<int32_t> own_slot(T, -1), own_ti(T, -1);
+  // When a round has too few attention tiles to occupy every CU, its time is
+  // set by the longest causal tile; tiles longer than cpo pages are then split
+  // in two: the pages before the tile's first query page (every key visible,
+  // unmasked) and the rest (causal), merged like prefix chunks.
+  int64_t n_own_tiles = 0, max_own_pages = 0;
+  for (auto& nd : nodes) {
+    n_own_tiles += (nd.n + TT - 1) / TT;
+    max_own_pages = std::max<int64_t>(max_own_pages, (nd.n + jev::kPage - 1) / jev::kPage);
+  }
+  int64_t cpo = INT64_MAX;
+  if (n_own_tiles * ctx->desc.n_kv_heads < kSplitTilesBelow && max_own_pages >= 32) {
+    cpo = (max_own_pages + 1) / 2;
+    cpo += cpo & 1;
+  }
+  std::vector<int32_t> own_slot(T, -1), own_ti(T, -1), own_n(T, 0);
   for (size_t i = 0; i < nodes.size(); ++i) {
     const RNode& nd = nodes[i];
     const bool has_anc = !nd.anc.empty();
     for (int64_t i0 = 0; i0 < nd.n; i0 += TT) {
       const int64_t nt = std::min<int64_t>(TT, nd.n - i0);
-      jev::AttnTile tl{};
-      tl.t0 = int32_t(node_t0[i] + i0);
-      tl.n_tok = int32_t(nt);
-      tl.page_off = int32_t(own_off[i]);
-      tl.n_pages = int32_t((i0 + nt - 1) / jev::kPage + 1);
-      tl.causal = 1;
-      tl.kv_pos0 = int32_t(nd.start);
-      tl.out_mode = has_anc ? 1 : 0;
-      tl.part_slot = has_anc ? int32_t(slot) : 0;
+      const int64_t np = (i0 + nt - 1) / jev::kPage + 1;
+      // split point: an even page count, at or before the first query's page
+      int64_t sp = 0;
+      if (np > cpo) sp = std::min<int64_t>(np / 2, i0 / jev::kPage) & ~int64_t(1);
+      const bool partial = has_anc || sp > 0;
       // causal pairs of the tile: token i0+j sees i0+j+1 own keys
       rd->attn_pairs += double(G) * double(ctx->desc.n_kv_heads) * double(nt * i0 + nt * (nt + 1) / 2);
-      if (has_anc) {
+      if (partial)
         for (int64_t j = 0; j < nt; ++j) {
           own_slot[node_t0[i] + i0 + j] = int32_t(slot);
           own_ti[node_t0[i] + i0 + j] = int32_t(j);
+          own_n[node_t0[i] + i0 + j] = sp > 0 ? 2 : 1;
         }
-        ++slot;
+      if (sp > 0) {
+        jev::AttnTile tl{};
+        tl.t0 = int32_t(node_t0[i] + i0);
+        tl.n_tok = int32_t(nt);
+        tl.page_off = int32_t(own_off[i]);
+        tl.n_pages = int32_t(sp);
+        tl.causal = 0;
+        tl.kv_pos0 = int32_t(nd.start);
+        tl.out_mode = 1;
+        tl.part_slot = int32_t(slot++);
+        tiles.push_back(tl);
       }
+      jev::AttnTile tl{};
+      tl.t0 = int32_t(node_t0[i] + i0);
+      tl.n_tok = int32_t(nt);
+      tl.page_off = int32_t(own_off[i] + sp);
+      tl.n_pages = int32_t(np - sp);
+      tl.causal = 1;
+      tl.kv_pos0 = int32_t(nd.start + jev::kPage * sp);
+      tl.out_mode = partial ? 1 : 0;
+      tl.part_slot = partial ? int32_t(slot++) : 0;
       tiles.push_back(tl);
     }
   }
+  std::vector<char> merged(T, 0);
   for (auto& g : groups) {
     if (g.anc_pages == 0) continue;
     int64_t cp = (g.anc_pages + n_chunks - 1) / n_chunks;
@@ -365,11 +399,18 @@ int build_round(jev_ctx* ctx, std::vector<RNode>& nodes, std::vector<int32_t>& h
         tl.part_slot = int32_t(slot++);
         tiles.push_back(tl);
       }
-      for (int64_t j = 0; j < nt; ++j)
-        merges.push_back(jev::MergeItem{int32_t(t0 + j), own_slot[t0 + j], own_ti[t0 + j], int32_t(slot0),
-                                        int32_t(j), int32_t(nch)});
+      for (int64_t j = 0; j < nt; ++j) {
+        const int64_t t = t0 + j;
+        merges.push_back(jev::MergeItem{int32_t(t), own_slot[t], own_ti[t], own_n[t], int32_t(slot0), int32_t(j),
+                                        int32_t(nch), 0});
+        merged[t] = 1;
+      }
     }
   }
+  // tokens of split tiles without a prefix part
+  for (int64_t t = 0; t < T; ++t)
+    if (!merged[t] && own_n[t] > 1)
+      merges.push_back(jev::MergeItem{int32_t(t), own_slot[t], own_ti[t], own_n[t], 0, 0, 0, 0});
   if (slot * ctx->desc.n_kv_heads * kRowsPerTile > ctx->L.part_rows)
     return fail(JEV_ENOMEM, "round needs more partial-state rows than the workspace holds");
   rd->part_slots = slot;
@@ -381,7 +422,7 @@ int build_round(jev_ctx* ctx, std::vector<RNode>& nodes, std::vector<int32_t>& h
   rd->off_tiles = push(int64_t(tiles.size()) * 8);
   std::memcpy(hb.data() + rd->off_tiles, tiles.data(), tiles.size() * sizeof(jev::AttnTile));
   rd->n_merge = int32_t(merges.size());
-  rd->off_merge = push(int64_t(merges.size()) * 6);
+  rd->off_merge = push(int64_t(merges.size()) * int64_t(sizeof(jev::MergeItem) / sizeof(int32_t)));
   std::memcpy(hb.data() + rd->off_merge, merges.data(), merges.size() * sizeof(jev::MergeItem));
   // readouts
   std::vector<jev::ReadoutItem> reads;

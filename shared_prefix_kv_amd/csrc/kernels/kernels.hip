@@ -351,9 +351,9 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnTile* __restrict__ 
 }
 
 // ------------------------------------------------------------------ merge
-// At most 1 own part + MAX_CHUNKS prefix chunks per token (the host never
-// plans more).
-constexpr int MAX_PARTS = 9;
+// At most kMaxOwnParts own parts + kMaxAncParts prefix chunks per token (the
+// host never plans more).
+constexpr int MAX_PARTS = kMaxOwnParts + kMaxAncParts;
 
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeItem* __restrict__ items,
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeItem* __restrict_
                                                     int hkv) {
   const MergeItem it = items[blockIdx.x];
   const int G = hq / hkv;
-  const int np = 1 + it.n_chunks;
+  const int np = it.n_own + it.n_anc;
   for (int e = threadIdx.x; e < hq * DH / 4; e += blockDim.x) {
     const int head = e / (DH / 4), d4 = (e % (DH / 4)) * 4;
     const int kvh = head / G, hg = head % G;
@@ -370,8 +370,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeItem* __restrict_
     float L[MAX_PARTS];
 #pragma unroll
     for (int p = 0; p < MAX_PARTS; ++p) {
-      rows[p] = p == 0 ? ((size_t)it.own_slot * hkv + kvh) * 128 + it.own_ti * G + hg
-                       : ((size_t)(it.anc_slot0 + p - 1) * hkv + kvh) * 128 + it.anc_ti * G + hg;
+      rows[p] = p < it.n_own ? ((size_t)(it.own_slot0 + p) * hkv + kvh) * 128 + it.own_ti * G + hg
+                             : ((size_t)(it.anc_slot0 + p - it.n_own) * hkv + kvh) * 128 + it.anc_ti * G + hg;
       L[p] = p < np ? part_lse[rows[p]] : kNegInf;
     }
     float4 v[MAX_PARTS];

@@ -20,11 +20,14 @@ struct AttnTile {
   int32_t t0, n_tok, page_off, n_pages, causal, kv_pos0, out_mode, part_slot;
 };
 
-// Merge of the partial states of one round token: its own causal part (slot
-// own_slot, token own_ti of that tile) and n_chunks prefix chunks (slots
-// anc_slot0 + c, token anc_ti of those tiles).
+// Merge of the partial states of one round token: n_own parts over its own
+// node's pages (slots own_slot0 + c, token own_ti of those tiles; more than one
+// when a long causal tile is split into page chunks) and n_anc prefix chunks
+// (slots anc_slot0 + c, token anc_ti of those tiles).
+constexpr int kMaxOwnParts = 2;
+constexpr int kMaxAncParts = 8;
 struct MergeItem {
-  int32_t t, own_slot, own_ti, anc_slot0, anc_ti, n_chunks;
+  int32_t t, own_slot0, own_ti, n_own, anc_slot0, anc_ti, n_anc, pad;
 };
 
 // Readout of one candidate: final norm of round row `row`, logits at

@@ -126,6 +126,25 @@ def test_w1_ragged_and_edge_cases(w1):
     ctx.free_pages([h, h1])
 
 
+def test_w1_long_prefix_split_causal_tiles(w1):
+    """A 600-token prefix (38 pages) makes the prefill round split its long
+    causal tiles into an unmasked and a causal page chunk merged by LSE; the
+    branches then merge prefix chunks with their own parts."""
+    wl, inst, m, _, ctx, _ = w1
+    rng = np.random.default_rng(78)
+    pre = list(rng.integers(0, 1024, 600))
+    sufs = [list(rng.integers(0, 1024, n)) for n in (1, 33, 200)]
+    labs = [list(rng.choice(1024, 5, replace=False)) for _ in sufs]
+    (h,) = ctx.prefill_prefix([0], [pre])
+    probs, loff = ctx.score_branches([h] * 3, sufs, labs)
+    _sync()
+    ref = om.score_from_scratch(m, [pre + s for s in sufs], labs)
+    err = max_abs(split_probs(probs, loff), ref)
+    ctx.free_pages([h])
+    print("w1 long prefix max abs err", err)
+    assert err <= TOL_F32
+
+
 # ------------------------------------------------------------------ workload 2 (bf16, headline)
 @pytest.fixture(scope="module")
 def w2():
