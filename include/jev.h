@@ -77,7 +77,7 @@ typedef struct {
   int32_t dtype;            /* JEV_DTYPE_F32 or JEV_DTYPE_BF16: weights, activations, KV pages */
   float rope_theta;
   float rms_eps;
-  int32_t max_positions;    /* longest sequence (prefix + suffix) the context will see */
+  int32_t max_positions;    /* longest sequence (prefix + suffix) the context will see, <= 65536 */
   int32_t max_round_tokens; /* most new tokens computed in one round (sizes the activations) */
 } jev_model_desc;
 
@@ -109,8 +109,10 @@ size_t jev_kv_pool_bytes(const jev_model_desc* desc, int32_t n_pages);
  * workspace: at least jev_workspace_bytes(desc) bytes, 256-byte aligned.
  * With weights == NULL, kv_pool == NULL and workspace == NULL the context is a
  * planning-only context: prefix/plan/page-table calls run on the host and
- * nothing touches a GPU (scoring calls return JEV_ESTATE).
- * Errors: JEV_EINVAL (shape), JEV_ENOMEM (workspace too small), JEV_EHIP. */
+ * nothing touches a GPU (scoring calls return JEV_ESTATE).  n_pages in
+ * [1, 2^26].
+ * Errors: JEV_EINVAL (shape, n_pages), JEV_ENOMEM (workspace too small),
+ * JEV_EHIP. */
 int jev_create(const jev_model_desc* desc, const jev_weights* weights, void* kv_pool,
                int32_t n_pages, void* workspace, size_t workspace_bytes, jev_ctx** out);
 

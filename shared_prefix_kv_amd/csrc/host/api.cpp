@@ -114,6 +114,7 @@ bool desc_ok(const jev_model_desc* d, std::string* why) {
     return *why = "reduction widths must be multiples of 128 bytes", false;
   if (d->d_model > 256 * 4 * chunk_elems) return *why = "d_model too large for the norm kernel", false;
   if (d->max_positions < 1 || d->max_round_tokens < 1) return *why = "max_positions/max_round_tokens < 1", false;
+  if (d->max_positions > 65536) return *why = "max_positions above 65536", false;
   if (!(d->rope_theta > 0.f) || !(d->rms_eps >= 0.f)) return *why = "bad rope_theta or rms_eps", false;
   return true;
 }
@@ -558,7 +559,7 @@ int jev_create(const jev_model_desc* desc, const jev_weights* weights, void* kv_
   if (!out) return fail(JEV_EINVAL, "out is NULL");
   *out = nullptr;
   if (!desc_ok(desc, &why)) return fail(JEV_EINVAL, why);
-  if (n_pages < 1) return fail(JEV_EINVAL, "n_pages < 1");
+  if (n_pages < 1 || n_pages > (1 << 26)) return fail(JEV_EINVAL, "n_pages must be in [1, 2^26]");
   std::unique_ptr<jev_ctx> c(new jev_ctx());
   jev_ctx* ctx = c.get();
   ctx->desc = *desc;

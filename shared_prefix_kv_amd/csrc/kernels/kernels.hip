@@ -143,8 +143,11 @@ __device__ __forceinline__ int v_off(int d, int key) {
 // softmax; only the rounding order changes.
 constexpr float RESCALE_SLACK = 8.0f;
 
+// Longest page list of one attention tile (the host checks max_positions).
+constexpr int kMaxTilePages = 4096;
+
 template <typename T, int DH>
-__global__ __launch_bounds__(256) void attn_kernel(const AttnTile* __restrict__ tiles,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(const AttnTile* __restrict__ tiles,
                                                    const int32_t* __restrict__ plist,
                                                    const int32_t* __restrict__ tok_pos, const T* __restrict__ q,
                                                    const T* __restrict__ pool, T* __restrict__ o,
@@ -163,8 +166,12 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnTile* __restrict__ 
   static_assert(PAGE_CHUNKS == 256, "two pages per step = 512 chunks = 2 per thread");
   __shared__ __attribute__((aligned(16))) T sK[2][32 * DH];
   __shared__ __attribute__((aligned(16))) T sV[2][DH * 32];
+  // the tile's page list, page id * 32 + valid keys (read once per workgroup)
+  __shared__ int32_t sP[kMaxTilePages];
 
   const AttnTile tile = tiles[blockIdx.x];
+  for (int i = threadIdx.x; i < tile.n_pages; i += blockDim.x)
+    sP[i] = plist[2 * (tile.page_off + i)] * 32 + plist[2 * (tile.page_off + i) + 1];
   const int kvh = blockIdx.y;
   const int G = hq / hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 31, hh = lane >> 5;
@@ -201,25 +208,34 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnTile* __restrict__ 
   const int st_koff = st_krow * DH + ((st_kch ^ (st_krow & (KCH - 1))) * CH);  // + 16*DH*i for page i
   const int st_d = tid / VCPR, st_half = tid % VCPR;
 
+  // K and V of a step (two pages) are staged separately: at step st the loop
+  // computes S for step st+1 from LDS K buffer (st+1)&1 while it applies the
+  // softmax of step st and PV with V buffer st&1; meanwhile K of step st+2 goes
+  // into K buffer st&1 (last read for S of step st, one barrier ago) and V of
+  // step st+1 into V buffer (st+1)&1 (last read at step st-1).
   u32x4 rk[2], rv[2];
-  auto gload = [&](int st) {
+  auto page_ptr = [&](int lp) -> const T* { return kvbase + (size_t)(sP[lp] >> 5) * page_stride; };
+  auto gload_k = [&](int st) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int lp = 2 * st + i;
-      if (lp < tile.n_pages) {
-        const T* kb = kvbase + (size_t)plist[2 * (tile.page_off + lp)] * page_stride;
-        rk[i] = reinterpret_cast<const u32x4*>(kb)[tid];
-        rv[i] = reinterpret_cast<const u32x4*>(kb + PAGE_ELEMS)[tid];
-      } else {
-        rk[i] = u32x4{0, 0, 0, 0};
-        rv[i] = u32x4{0, 0, 0, 0};
-      }
+      rk[i] = lp < tile.n_pages ? reinterpret_cast<const u32x4*>(page_ptr(lp))[tid] : u32x4{0, 0, 0, 0};
     }
   };
-  auto sstore = [&](int buf) {
+  auto gload_v = [&](int st) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      *reinterpret_cast<u32x4*>(&sK[buf][st_koff + 16 * DH * i]) = rk[i];
+      const int lp = 2 * st + i;
+      rv[i] = lp < tile.n_pages ? reinterpret_cast<const u32x4*>(page_ptr(lp) + PAGE_ELEMS)[tid] : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto sstore_k = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(&sK[buf][st_koff + 16 * DH * i]) = rk[i];
+  };
+  auto sstore_v = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
       if constexpr (CH == 8) {
         // page i holds keys 16i..16i+15 = half i of the row; this chunk is
         // quads 2*st_half and 2*st_half+1 of that half (stored order 0, 2, 1, 3)
@@ -234,6 +250,14 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnTile* __restrict__ 
       }
     }
   };
+  auto qk = [&](int buf) {
+    f32x16 S;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) S = MF::mma(MF::load(&sK[buf][koff[ks]]), qf[ks], S);
+    return S;
+  };
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -242,35 +266,42 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnTile* __restrict__ 
     for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
   float mrun = kNegInf, lrun = 0.f;
 
+  f32x16 S_cur;
+  __syncthreads();  // page list
   if (nst > 0) {
-    gload(0);
-    sstore(0);
+    gload_k(0);
+    gload_v(0);
+    sstore_k(0);
+    sstore_v(0);
+    if (nst > 1) {
+      gload_k(1);
+      sstore_k(1);
+    }
   }
   __syncthreads();
+  if (nst > 0) S_cur = qk(0);
   for (int st = 0; st < nst; ++st) {
     const int buf = st & 1;
-    if (st + 1 < nst) gload(st + 1);
+    if (st + 2 < nst) gload_k(st + 2);
+    if (st + 1 < nst) gload_v(st + 1);
 
-    // S^T = K Q^T
-    f32x16 S;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) S[r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) S = MF::mma(MF::load(&sK[buf][koff[ks]]), qf[ks], S);
+    // S of the next step (independent of this step's softmax below)
+    f32x16 S_next;
+    if (st + 1 < nst) S_next = qk(buf ^ 1);
 
+    f32x16 S = S_cur;
     // mask only where needed: partial pages, or keys past the wave's first query
     const int lp0 = 2 * st;
-    const int v0 = plist[2 * (tile.page_off + lp0) + 1];
-    const int v1 = (lp0 + 1 < tile.n_pages) ? plist[2 * (tile.page_off + lp0 + 1) + 1] : 0;
+    const int v0 = sP[lp0] & 31;
+    const int v1 = (lp0 + 1 < tile.n_pages) ? (sP[lp0 + 1] & 31) : 0;
     const bool mask = (v0 < 16) || (v1 < 16) || (tile.causal && tile.kv_pos0 + 16 * lp0 + 31 > qmin);
     if (mask) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 8 * (r >> 2) + 4 * hh + (r & 3);
         const int pi = key >> 4, slot = key & 15;
-        bool ok = slot < (pi ? v1 : v0);
-        if (tile.causal) ok = ok && (tile.kv_pos0 + 16 * (lp0 + pi) + slot <= qpos);
-        if (!ok) S[r] = kNegInf;
+        const bool ok = slot < (pi ? v1 : v0) && (!tile.causal || tile.kv_pos0 + 16 * (lp0 + pi) + slot <= qpos);
+        S[r] = ok ? S[r] : kNegInf;
       }
     }
     float mloc = S[0];
@@ -323,8 +354,10 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnTile* __restrict__ 
         oacc[b] = MF::mma(va, pb, oacc[b]);
       }
     }
-    if (st + 1 < nst) sstore(buf ^ 1);
+    if (st + 2 < nst) sstore_k(buf);
+    if (st + 1 < nst) sstore_v(buf ^ 1);
     __syncthreads();
+    S_cur = S_next;
   }
 
   if (!row_ok) return;
