@@ -169,10 +169,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // the tile's page list, page id * 32 + valid keys (read once per workgroup)
   __shared__ int32_t sP[kMaxTilePages];
 
-  const AttnTile tile = tiles[blockIdx.x];
+  // one workgroup per (tile, KV head); the KV head is the fast index, so that
+  // neighbouring workgroups read the same pages (whose KV heads are adjacent)
+  const int kvh = blockIdx.x % hkv;
+  const AttnTile tile = tiles[blockIdx.x / hkv];
   for (int i = threadIdx.x; i < tile.n_pages; i += blockDim.x)
     sP[i] = plist[2 * (tile.page_off + i)] * 32 + plist[2 * (tile.page_off + i) + 1];
-  const int kvh = blockIdx.y;
   const int G = hq / hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 31, hh = lane >> 5;
   const int row = wave * 32 + c;
@@ -528,7 +530,7 @@ hipError_t launch_attention(const ModelDims& m, int32_t layer, const AttnTile* t
   if (n_tiles <= 0) return hipSuccess;
   const size_t layer_base = (size_t)layer * m.n_pages * m.hkv * 2 * 16 * m.dh;
   const float scale_log2 = float(1.4426950408889634 / std::sqrt((double)m.dh));
-  dim3 grid(n_tiles, m.hkv);
+  dim3 grid(n_tiles * m.hkv);
   if (m.dtype == 1 && m.dh == 128) {
     hipLaunchKernelGGL((dev::attn_kernel<bf16s, 128>), grid, dim3(256), 0, s, tiles, page_list, tok_pos,
                        reinterpret_cast<const bf16s*>(qbuf), reinterpret_cast<const bf16s*>(pool),
