@@ -473,7 +473,9 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
         *e = ctx->prof_free.back();
         ctx->prof_free.pop_back();
       } else {
-        hipError_t err = hipEventCreate(e);
+        // timing only, read after the caller has synchronised the stream: no
+        // system-scope fence (it costs a cache writeback between kernels)
+        hipError_t err = hipEventCreateWithFlags(e, hipEventDisableSystemFence);
         if (err != hipSuccess) return err;
       }
     }
