@@ -145,6 +145,91 @@ def test_w1_long_prefix_split_causal_tiles(w1):
     assert err <= TOL_F32
 
 
+def test_w1_nested_prefixes_candidates_and_errors(w1):
+    """A prefix continued by a child prefix; branches under either in one call;
+    staged candidates with a duplicate, a fully resident one (backed off by one
+    token) and a fresh one; an empty call; errors that change nothing."""
+    from shared_prefix_kv_amd import jev
+    wl, inst, m, _, ctx, _ = w1
+    rng = np.random.default_rng(79)
+    A = list(rng.integers(0, 1024, 100))
+    B = list(rng.integers(0, 1024, 50))
+    (ha,) = ctx.prefill_prefix([0], [A])
+    (hb,) = ctx.prefill_prefix([ha], [B])
+    sufs = [list(rng.integers(0, 1024, n)) for n in (1, 20, 40, 7)]
+    labs = [list(rng.choice(1024, 4, replace=False)) for _ in sufs]
+    parents = [hb, ha, hb, ha]
+    probs, loff = ctx.score_branches(parents, sufs, labs)
+    _sync()
+    full = [(A + B if p == hb else A) + s for p, s in zip(parents, sufs)]
+    ref = om.score_from_scratch(m, full, labs)
+    assert max_abs(split_probs(probs, loff), ref) <= TOL_F32
+    st = ctx.stats()
+    assert st["computed_tokens"] == sum(len(s) for s in sufs)
+    assert st["cached_tokens"] == sum(len(f) - len(s) for f, s in zip(full, sufs))
+
+    x = list(rng.integers(0, 1024, 30))
+    y = list(rng.integers(0, 1024, 25))
+    z = list(rng.integers(0, 1024, 60))
+    cands = [A + B + x, A + B + x, A + B, A + y, z, A + B + x[:3]]
+    clabs = [list(rng.choice(1024, 3, replace=False)) for _ in cands]
+    clabs[1] = clabs[0]
+    probs, loff = ctx.score_candidates(cands, clabs)
+    _sync()
+    got = split_probs(probs, loff)
+    ref = om.score_from_scratch(m, cands, clabs)
+    assert max_abs(got, ref) <= TOL_F32
+    assert np.array_equal(got[0], got[1])
+
+    in_use = ctx.stats()["pages_in_use"]
+    probs, loff = ctx.score_branches([], [], [])
+    assert len(loff) == 1 and in_use == ctx.stats()["pages_in_use"]
+    with pytest.raises(jev.JevError) as e:
+        ctx.score_branches([hb, hb], [[1, 2], [3]], [[1, 2], [5, 5]])      # duplicate label ids
+    assert e.value.code == jev.JEV_EINVAL
+    with pytest.raises(jev.JevError) as e:
+        ctx.score_branches([hb], [[1, 2]], [[1, 1024]])                  # label id out of range
+    assert e.value.code == jev.JEV_EINVAL
+    with pytest.raises(jev.JevError) as e:
+        ctx.score_branches([hb + 1000], [[1, 2]], [[1, 2]])              # unknown handle
+    assert e.value.code == jev.JEV_EHANDLE
+    with pytest.raises(jev.JevError) as e:
+        ctx.prefill_prefix([0], [list(range(2000))])                     # past max_positions
+    assert e.value.code == jev.JEV_EINVAL
+    assert ctx.stats()["pages_in_use"] == in_use
+    probs, loff = ctx.score_branches([hb], [sufs[1]], [labs[1]])        # still works
+    _sync()
+    ref = om.score_from_scratch(m, [A + B + sufs[1]], [labs[1]])
+    assert max_abs(split_probs(probs, loff), ref) <= TOL_F32
+    ctx.free_pages([hb, ha])
+    assert ctx.stats()["pages_in_use"] == 0
+
+
+def test_w1_out_of_pages_leaves_state_unchanged():
+    """A pool of 10 pages: a call needing more pages than are free fails with
+    JEV_ENOMEM before any work and leaves the resident prefix usable."""
+    from shared_prefix_kv_amd import jev
+    wl = workload(1)
+    m = om.from_weights(host_weights(1))
+    ctx, _ = device_context(1, n_pages=10, max_pos=1024, max_tok=1024)
+    rng = np.random.default_rng(80)
+    A = list(rng.integers(0, 1024, 128))                                  # 8 pages
+    (ha,) = ctx.prefill_prefix([0], [A])
+    sufs = [list(rng.integers(0, 1024, 20)) for _ in range(2)]           # 2 pages each
+    labs = [[1, 2], [3, 4]]
+    with pytest.raises(jev.JevError) as e:
+        ctx.score_branches([ha, ha], sufs, labs)
+    assert e.value.code == jev.JEV_ENOMEM
+    assert ctx.stats()["pages_in_use"] == 8
+    probs, loff = ctx.score_branches([ha], sufs[:1], labs[:1])
+    _sync()
+    ref = om.score_from_scratch(m, [A + sufs[0]], labs[:1])
+    assert max_abs(split_probs(probs, loff), ref) <= TOL_F32
+    ctx.free_pages([ha])
+    assert ctx.stats()["pages_in_use"] == 0
+    ctx.close()
+
+
 # ------------------------------------------------------------------ workload 2 (bf16, headline)
 @pytest.fixture(scope="module")
 def w2():
