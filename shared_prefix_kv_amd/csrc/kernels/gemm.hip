@@ -259,8 +259,8 @@ __device__ __forceinline__ void xcd_tile(int b, int n_blocks, int m_tiles, int* 
 // blockIdx.y selects a slice of K and partial sums are added (agent-scope fp32
 // atomics) into an fp32 [M][N] scratch; split_epilogue (next launch) runs the
 // epilogue on the sums over all CUs and clears the scratch for the next use.
-template <typename T, int BN, int EPI, bool SPLIT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(const T* __restrict__ A, int M, int K, int N, ColMap cm,
+template <typename T, int BN, int EPI, bool SPLIT, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_kernel(const T* __restrict__ A, int M, int K, int N, ColMap cm,
                                                    QkvOut qo, ResOut ro, float* __restrict__ scratch) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
@@ -268,20 +268,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int CH = 16 / sizeof(T);   // elements per 16-byte chunk
   constexpr int BK = 8 * CH;           // 128 bytes of K per stage
   constexpr int KS = BK / MF::KSTEP;   // MFMA k-steps per stage
-  constexpr int TN = BN / 32;
-  constexpr int LA = BM * 8 / 256;     // A chunks per thread per stage
-  constexpr int LB = BN * 8 / 256;     // B chunks per thread per stage
+  constexpr int NTH = WM * WN * 64;
+  constexpr int NRB = BM / WM / 32;    // row blocks per wave
+  constexpr int TN = BN / WN / 32;     // column blocks per wave
+  constexpr int RPL = NTH / 8;         // rows per staging load (8 lanes per 128-byte row)
+  constexpr int LA = BM / RPL;         // A chunks per thread per stage
+  constexpr int LB = (BN + RPL - 1) / RPL;  // B chunks per thread per stage (the last may idle)
   constexpr int NST = LA + LB;         // LDS stores per thread per stage
   constexpr int RS = 9;                // LDS row stride, 16-byte units
   constexpr int STAGE = (BM + BN) * RS;
   constexpr int LDS_MAIN = 2 * STAGE;
   constexpr int LDS_EPI = SPLIT ? 0 : 128 * (BN + 4) / 4;
   constexpr int LDS_UNITS = LDS_MAIN > LDS_EPI ? LDS_MAIN : LDS_EPI;
-  static_assert((BN * 8) % 256 == 0, "tile");
+  static_assert(BM % (WM * 32) == 0 && BN % (WN * 32) == 0 && BM % RPL == 0, "tile");
   __shared__ __attribute__((aligned(16))) u32x4 smem[LDS_UNITS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 31, hh = lane >> 5;
+  const int rowA0 = (BM / WM) * (wave / WN), colB0 = (BN / WN) * (wave % WN);
   int mt, nt;
   if (SPLIT) {
     mt = 0;
@@ -298,15 +302,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const u32x4* ap[LA];
 #pragma unroll
   for (int i = 0; i < LA; ++i)
-    ap[i] = reinterpret_cast<const u32x4*>(A + (size_t)min(m0 + lrow + 32 * i, M - 1) * K + (size_t)kt0 * BK) + lch;
+    ap[i] = reinterpret_cast<const u32x4*>(A + (size_t)min(m0 + lrow + RPL * i, M - 1) * K + (size_t)kt0 * BK) + lch;
   const u32x4* bp[LB];
 #pragma unroll
   for (int i = 0; i < LB; ++i)
-    bp[i] = reinterpret_cast<const u32x4*>(weight_row<T>(cm, BN, n0 + lrow + 32 * i, K) + (size_t)kt0 * BK) + lch;
+    bp[i] = reinterpret_cast<const u32x4*>(weight_row<T>(cm, BN, n0 + min(lrow + RPL * i, BN - 1), K) +
+                                           (size_t)kt0 * BK) + lch;
 
-  f32x16 acc[2][TN];
+  f32x16 acc[NRB][TN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NRB; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -323,8 +328,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   do {                                                                                      \
     u32x4* sA_ = smem + (BUF) * STAGE;                                                      \
     u32x4* sB_ = sA_ + BM * RS;                                                             \
-    _Pragma("unroll") for (int i = 0; i < LA; ++i) sA_[(lrow + 32 * i) * RS + lch] = RA[i]; \
-    _Pragma("unroll") for (int i = 0; i < LB; ++i) sB_[(lrow + 32 * i) * RS + lch] = RB[i]; \
+    _Pragma("unroll") for (int i = 0; i < LA; ++i) sA_[(lrow + RPL * i) * RS + lch] = RA[i]; \
+    _Pragma("unroll") for (int i = 0; i < LB; ++i) if (lrow + RPL * i < BN) sB_[(lrow + RPL * i) * RS + lch] = RB[i]; \
   } while (0)
   // One stage of compute on LDS buffer BUF, with the next stage's staged
   // registers (RA, RB) written into the other buffer during it (W_ = 1).
@@ -335,26 +340,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #define G_FRAGS(FA, FB, S_)                                                                      \
   do {                                                                                           \
     const int k_ = (S_) * MF::KSTEP + MF::KL * hh;                                               \
-    _Pragma("unroll") for (int i = 0; i < 2; ++i) FA[i] =                                        \
-        MF::load(reinterpret_cast<const T*>(&sA_[(64 * wave + 32 * i + c) * RS + k_ / CH]) + k_ % CH); \
+    _Pragma("unroll") for (int i = 0; i < NRB; ++i) FA[i] =                                      \
+        MF::load(reinterpret_cast<const T*>(&sA_[(rowA0 + 32 * i + c) * RS + k_ / CH]) + k_ % CH); \
     _Pragma("unroll") for (int j = 0; j < TN; ++j) FB[j] =                                       \
-        MF::load(reinterpret_cast<const T*>(&sB_[(32 * j + c) * RS + k_ / CH]) + k_ % CH);       \
+        MF::load(reinterpret_cast<const T*>(&sB_[(colB0 + 32 * j + c) * RS + k_ / CH]) + k_ % CH); \
   } while (0)
 #define G_MMA(FA, FB)                                                                            \
   do {                                                                                           \
-    _Pragma("unroll") for (int i = 0; i < 2; ++i) _Pragma("unroll") for (int j = 0; j < TN; ++j) \
+    _Pragma("unroll") for (int i = 0; i < NRB; ++i) _Pragma("unroll") for (int j = 0; j < TN; ++j) \
         acc[i][j] = MF::mma(FA[i], FB[j], acc[i][j]);                                            \
   } while (0)
 #define G_WRITES(RA, RB, S_)                                                                     \
   do {                                                                                           \
     _Pragma("unroll") for (int q = (S_) * NST / KS; q < ((S_) + 1) * NST / KS; ++q) {            \
-      if (q < LA) wA_[(lrow + 32 * q) * RS + lch] = RA[q < LA ? q : 0];                          \
-      else wB_[(lrow + 32 * (q - LA)) * RS + lch] = RB[q < LA ? 0 : q - LA];                     \
+      if (q < LA) wA_[(lrow + RPL * q) * RS + lch] = RA[q < LA ? q : 0];                         \
+      else if (lrow + RPL * (q - LA) < BN) wB_[(lrow + RPL * (q - LA)) * RS + lch] = RB[q < LA ? 0 : q - LA]; \
     }                                                                                            \
   } while (0)
 #define G_GROUPS(NR_, NW_)                                                                       \
   do {                                                                                           \
-    _Pragma("unroll") for (int m_ = 0; m_ < 2 * TN; ++m_) {                                      \
+    _Pragma("unroll") for (int m_ = 0; m_ < NRB * TN; ++m_) {                                    \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                         \
       if (m_ < (NR_)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                         \
       if (m_ < (NW_)) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);                         \
@@ -368,20 +373,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     u32x4* wB_ = wA_ + BM * RS;                                                                  \
     (void)wA_;                                                                                   \
     (void)wB_;                                                                                   \
-    frag fa0[2], fb0[TN], fa1[2], fb1[TN];                                                       \
+    frag fa0[NRB], fb0[TN], fa1[NRB], fb1[TN];                                                   \
     G_FRAGS(fa0, fb0, 0);                                                                        \
     __builtin_amdgcn_sched_barrier(0);                                                           \
     _Pragma("unroll") for (int s = 0; s < KS; s += 2) {                                          \
       if (s + 1 < KS) G_FRAGS(fa1, fb1, s + 1);                                                  \
       G_MMA(fa0, fb0);                                                                           \
       if (W_) G_WRITES(RA, RB, s);                                                               \
-      G_GROUPS(s + 1 < KS ? 2 + TN : 0, (W_) ? ((s + 1) * NST / KS - s * NST / KS) : 0);        \
+      G_GROUPS(s + 1 < KS ? NRB + TN : 0, (W_) ? ((s + 1) * NST / KS - s * NST / KS) : 0);      \
       __builtin_amdgcn_sched_barrier(0);                                                         \
       if (s + 1 < KS) {                                                                          \
         if (s + 2 < KS) G_FRAGS(fa0, fb0, s + 2);                                                \
         G_MMA(fa1, fb1);                                                                         \
         if (W_) G_WRITES(RA, RB, s + 1);                                                         \
-        G_GROUPS(s + 2 < KS ? 2 + TN : 0, (W_) ? ((s + 2) * NST / KS - (s + 1) * NST / KS) : 0); \
+        G_GROUPS(s + 2 < KS ? NRB + TN : 0, (W_) ? ((s + 2) * NST / KS - (s + 1) * NST / KS) : 0); \
         __builtin_amdgcn_sched_barrier(0);                                                       \
       }                                                                                          \
     }                                                                                            \
@@ -415,13 +420,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if constexpr (SPLIT) {
     float* part = scratch + (size_t)blockIdx.y * BM * N;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NRB; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int m = wave * 64 + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (m < M) part[(size_t)m * N + n0 + 32 * j + c] = acc[i][j][r];
+          const int m = rowA0 + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (m < M) part[(size_t)m * N + n0 + colB0 + 32 * j + c] = acc[i][j][r];
         }
   } else {
     float* stile = reinterpret_cast<float*>(smem);
@@ -429,20 +434,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __syncthreads();
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      if ((wave >> 1) == half) {
+      if (rowA0 / 128 == half) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < NRB; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int row = (wave & 1) * 64 + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
-              stile[row * LD + 32 * j + c] = acc[i][j][r];
+              const int row = rowA0 % 128 + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+              stile[row * LD + colB0 + 32 * j + c] = acc[i][j][r];
             }
       }
       __syncthreads();
       if (m0 + 128 * half < M)
-        tile_epilogue<T, EPI>(stile, LD, 128, m0 + 128 * half, M, nt, BN, cm, qo, ro, tid, 256);
+        tile_epilogue<T, EPI>(stile, LD, 128, m0 + 128 * half, M, nt, BN, cm, qo, ro, tid, NTH);
       __syncthreads();
     }
   }
@@ -495,8 +500,8 @@ hipError_t gemm_dispatch(const ModelDims& m, const GemmWs& ws, const void* A, in
     int S = g_gemm_tuning.splits > 0 ? g_gemm_tuning.splits : std::max(1, 256 / tiles);
     S = std::max(1, std::min({S, kMaxSplits, KT / 2 > 0 ? KT / 2 : 1}));
     if ((size_t)S * 256 * N > ws.partial_elems) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((dev::gemm_kernel<T, BN, EPI, true>), dim3(tiles, S), dim3(256), 0, s, a, M, K, N, cm, qo, ro,
-                       ws.partial);
+    hipLaunchKernelGGL((dev::gemm_kernel<T, BN, EPI, true, 4, 1>), dim3(tiles, S), dim3(256), 0, s, a, M, K, N, cm,
+                       qo, ro, ws.partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((dev::split_epilogue<T, EPI>), dim3(tiles, (M + 15) / 16), dim3(256), 0, s, ws.partial, S, M,
@@ -514,10 +519,13 @@ hipError_t gemm_dispatch(const ModelDims& m, const GemmWs& ws, const void* A, in
   if (g_gemm_tuning.bn == 128 || g_gemm_tuning.bn == 160) bn = g_gemm_tuning.bn;
   if (N % bn) return hipErrorInvalidValue;
   dim3 grid((N / bn) * mt);
+  // eight waves (two per SIMD): 8 x 1 over a 160-wide tile, 4 x 2 over 128
   if (bn == 160)
-    hipLaunchKernelGGL((dev::gemm_kernel<T, 160, EPI, false>), grid, dim3(256), 0, s, a, M, K, N, cm, qo, ro, nullptr);
+    hipLaunchKernelGGL((dev::gemm_kernel<T, 160, EPI, false, 8, 1>), grid, dim3(512), 0, s, a, M, K, N, cm, qo, ro,
+                       nullptr);
   else
-    hipLaunchKernelGGL((dev::gemm_kernel<T, 128, EPI, false>), grid, dim3(256), 0, s, a, M, K, N, cm, qo, ro, nullptr);
+    hipLaunchKernelGGL((dev::gemm_kernel<T, 128, EPI, false, 4, 2>), grid, dim3(512), 0, s, a, M, K, N, cm, qo, ro,
+                       nullptr);
   return hipGetLastError();
 }
 
