@@ -500,7 +500,7 @@ hipError_t gemm_dispatch(const ModelDims& m, const GemmWs& ws, const void* A, in
     int S = g_gemm_tuning.splits > 0 ? g_gemm_tuning.splits : std::max(1, 256 / tiles);
     S = std::max(1, std::min({S, kMaxSplits, KT / 2 > 0 ? KT / 2 : 1}));
     if ((size_t)S * 256 * N > ws.partial_elems) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((dev::gemm_kernel<T, BN, EPI, true, 4, 1>), dim3(tiles, S), dim3(256), 0, s, a, M, K, N, cm,
+    hipLaunchKernelGGL((dev::gemm_kernel<T, BN, EPI, true, 4, 2>), dim3(tiles, S), dim3(512), 0, s, a, M, K, N, cm,
                        qo, ro, ws.partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
