@@ -215,21 +215,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // softmax of step st and PV with V buffer st&1; meanwhile K of step st+2 goes
   // into K buffer st&1 (last read for S of step st, one barrier ago) and V of
   // step st+1 into V buffer (st+1)&1 (last read at step st-1).
-  u32x4 rk[2], rv[2];
-  auto page_ptr = [&](int lp) -> const T* { return kvbase + (size_t)(sP[lp] >> 5) * page_stride; };
-  auto gload_k = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int lp = 2 * st + i;
-      rk[i] = lp < tile.n_pages ? reinterpret_cast<const u32x4*>(page_ptr(lp))[tid] : u32x4{0, 0, 0, 0};
-    }
+  // Global loads are unconditional (page index clamped to the tile's last
+  // page; keys of pages past the end are masked by their zero valid count),
+  // so the number of loads in flight is static and each LDS store waits only
+  // for the loads of its own step, issued one step earlier.
+  u32x4 rk[2], rv[2];    // staged K / V of the step stored at the end of this step
+  u32x4 rk2[2], rv2[2];  // and of the step after
+  auto page_ptr = [&](int lp) -> const T* {
+    return kvbase + (size_t)(sP[min(lp, tile.n_pages - 1)] >> 5) * page_stride;
   };
-  auto gload_v = [&](int st) {
+  auto gload_k = [&](int st, u32x4* dst) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int lp = 2 * st + i;
-      rv[i] = lp < tile.n_pages ? reinterpret_cast<const u32x4*>(page_ptr(lp) + PAGE_ELEMS)[tid] : u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < 2; ++i) dst[i] = reinterpret_cast<const u32x4*>(page_ptr(2 * st + i))[tid];
+  };
+  auto gload_v = [&](int st, u32x4* dst) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dst[i] = reinterpret_cast<const u32x4*>(page_ptr(2 * st + i) + PAGE_ELEMS)[tid];
   };
   auto sstore_k = [&](int buf) {
 #pragma unroll
@@ -271,21 +272,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   f32x16 S_cur;
   __syncthreads();  // page list
   if (nst > 0) {
-    gload_k(0);
-    gload_v(0);
+    gload_k(0, rk);
+    gload_v(0, rv);
     sstore_k(0);
     sstore_v(0);
-    if (nst > 1) {
-      gload_k(1);
-      sstore_k(1);
-    }
+    gload_k(1, rk);
+    sstore_k(1);
+    // staged for the first step's stores: K of step 2, V of step 1
+    gload_k(2, rk);
+    gload_v(1, rv);
   }
   __syncthreads();
   if (nst > 0) S_cur = qk(0);
   for (int st = 0; st < nst; ++st) {
     const int buf = st & 1;
-    if (st + 2 < nst) gload_k(st + 2);
-    if (st + 1 < nst) gload_v(st + 1);
+    // loads for the next step's stores
+    gload_k(st + 3, rk2);
+    gload_v(st + 2, rv2);
 
     // S of the next step (independent of this step's softmax below)
     f32x16 S_next;
@@ -360,6 +363,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (st + 1 < nst) sstore_v(buf ^ 1);
     __syncthreads();
     S_cur = S_next;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      rk[i] = rk2[i];
+      rv[i] = rv2[i];
+    }
   }
 
   if (!row_ok) return;
