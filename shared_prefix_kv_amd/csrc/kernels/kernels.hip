@@ -312,7 +312,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     float mloc = S[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, S[r]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * scale_log2;
+    mloc = xor32_max(mloc) * scale_log2;
     if (__any(mloc > mrun + RESCALE_SLACK)) {
       const float mnew = fmaxf(mrun, mloc);
       const float alpha = (mnew == kNegInf) ? 1.f : exp2f(mrun - mnew);
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       p[r] = __builtin_amdgcn_exp2f(fmaf(S[r], scale_log2, nm));
       lsum += p[r];
     }
-    lsum += __shfl_xor(lsum, 32, 64);
+    lsum = xor32_sum(lsum);
     lrun += lsum;
 
     // O^T += V^T P^T; MFMA tt covers keys {8j + 4*hh + i : 4j + i in [tt*KL, tt*KL+KL)}
