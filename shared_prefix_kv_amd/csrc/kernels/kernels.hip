@@ -221,9 +221,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // for the loads of its own step, issued one step earlier.
   u32x4 rk[2], rv[2];    // staged K / V of the step stored at the end of this step
   u32x4 rk2[2], rv2[2];  // and of the step after
-  auto page_ptr = [&](int lp) -> const T* {
-    return kvbase + (size_t)(sP[min(lp, tile.n_pages - 1)] >> 5) * page_stride;
+  // A window of 64 page-list entries, one per lane (entries pw_base + lane),
+  // read by readlane: a step needs entries 2st .. 2st+7, so the window is
+  // moved every 16 steps and page ids cost no memory access in between.
+  int pw = 0, pw_base = 0;
+  auto page_entry = [&](int lp) -> int {
+    return __builtin_amdgcn_readlane(pw, min(lp, tile.n_pages - 1) - pw_base);
   };
+  auto page_ptr = [&](int lp) -> const T* { return kvbase + (size_t)(page_entry(lp) >> 5) * page_stride; };
   auto gload_k = [&](int st, u32x4* dst) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) dst[i] = reinterpret_cast<const u32x4*>(page_ptr(2 * st + i))[tid];
@@ -271,6 +276,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   f32x16 S_cur;
   __syncthreads();  // page list
+  pw = sP[min(lane, tile.n_pages - 1)];
   if (nst > 0) {
     gload_k(0, rk);
     gload_v(0, rv);
@@ -286,6 +292,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (nst > 0) S_cur = qk(0);
   for (int st = 0; st < nst; ++st) {
     const int buf = st & 1;
+    if (st > 0 && (st & 15) == 0) {
+      pw_base = 2 * st;
+      pw = sP[min(pw_base + lane, tile.n_pages - 1)];
+    }
     // loads for the next step's stores
     gload_k(st + 3, rk2);
     gload_v(st + 2, rv2);
@@ -297,8 +307,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     f32x16 S = S_cur;
     // mask only where needed: partial pages, or keys past the wave's first query
     const int lp0 = 2 * st;
-    const int v0 = sP[lp0] & 31;
-    const int v1 = (lp0 + 1 < tile.n_pages) ? (sP[lp0 + 1] & 31) : 0;
+    const int v0 = page_entry(lp0) & 31;
+    const int v1 = (lp0 + 1 < tile.n_pages) ? (page_entry(lp0 + 1) & 31) : 0;
     const bool mask = (v0 < 16) || (v1 < 16) || (tile.causal && tile.kv_pos0 + 16 * lp0 + 31 > qmin);
     if (mask) {
 #pragma unroll
