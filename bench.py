@@ -177,7 +177,7 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--cpu-branches", type=int, default=2, help="oracle sample size (0 = skip)")
+    ap.add_argument("--cpu-branches", type=int, default=4, help="oracle sample size (0 = skip)")
     ap.add_argument("--roofline-kernel", default="auto",
                     help="kernel whose roofline is reported, as 'kind[rows]' (auto = largest total time)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
