@@ -413,12 +413,14 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeItem* __restrict_
                                                     const float* __restrict__ part_o,
                                                     const float* __restrict__ part_lse, T* __restrict__ o, int hq,
                                                     int hkv) {
-  const MergeItem it = items[blockIdx.x];
+  // one workgroup per (token, KV head): the G query heads of the group
+  const MergeItem it = items[blockIdx.x / hkv];
+  const int kvh = blockIdx.x % hkv;
   const int G = hq / hkv;
   const int np = it.n_own + it.n_anc;
-  for (int e = threadIdx.x; e < hq * DH / 4; e += blockDim.x) {
-    const int head = e / (DH / 4), d4 = (e % (DH / 4)) * 4;
-    const int kvh = head / G, hg = head % G;
+  for (int e = threadIdx.x; e < G * DH / 4; e += blockDim.x) {
+    const int hg = e / (DH / 4), d4 = (e % (DH / 4)) * 4;
+    const int head = kvh * G + hg;
     size_t rows[MAX_PARTS];
     float L[MAX_PARTS];
 #pragma unroll
@@ -567,10 +569,10 @@ hipError_t launch_merge(const ModelDims& m, const MergeItem* items, int32_t n_it
                         const float* part_lse, void* o, hipStream_t s) {
   if (n_items <= 0) return hipSuccess;
   if (m.dtype == 1 && m.dh == 128) {
-    hipLaunchKernelGGL((dev::merge_kernel<bf16s, 128>), dim3(n_items), dim3(256), 0, s, items, part_o, part_lse,
+    hipLaunchKernelGGL((dev::merge_kernel<bf16s, 128>), dim3(n_items * m.hkv), dim3(256), 0, s, items, part_o, part_lse,
                        reinterpret_cast<bf16s*>(o), m.hq, m.hkv);
   } else if (m.dtype == 0 && m.dh == 64) {
-    hipLaunchKernelGGL((dev::merge_kernel<float, 64>), dim3(n_items), dim3(256), 0, s, items, part_o, part_lse,
+    hipLaunchKernelGGL((dev::merge_kernel<float, 64>), dim3(n_items * m.hkv), dim3(256), 0, s, items, part_o, part_lse,
                        reinterpret_cast<float*>(o), m.hq, m.hkv);
   } else {
     return hipErrorInvalidValue;
