@@ -479,9 +479,17 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
         if (err != hipSuccess) return err;
       }
     }
-    hipError_t err = hipEventRecord(p.e0, s);
-    if (err == hipSuccess) err = launch();
-    if (err == hipSuccess) err = hipEventRecord(p.e1, s);
+    // the launcher's own dispatches carry the events (no separate event
+    // packets between kernels); a launcher that launched nothing gets a pair
+    // of plain records
+    jev::g_launch_timing = jev::LaunchTiming{p.e0, p.e1};
+    hipError_t err = launch();
+    const bool launched = jev::g_launch_timing.start == nullptr;
+    jev::g_launch_timing = jev::LaunchTiming{nullptr, nullptr};
+    if (err == hipSuccess && !launched) {
+      err = hipEventRecord(p.e0, s);
+      if (err == hipSuccess) err = hipEventRecord(p.e1, s);
+    }
     ctx->prof.push_back(p);
     return err;
   };

@@ -500,11 +500,11 @@ hipError_t gemm_dispatch(const ModelDims& m, const GemmWs& ws, const void* A, in
     int S = g_gemm_tuning.splits > 0 ? g_gemm_tuning.splits : std::max(1, 256 / tiles);
     S = std::max(1, std::min({S, kMaxSplits, KT / 2 > 0 ? KT / 2 : 1}));
     if ((size_t)S * 256 * N > ws.partial_elems) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((dev::gemm_kernel<T, BN, EPI, true, 4, 2>), dim3(tiles, S), dim3(512), 0, s, a, M, K, N, cm,
+    JEV_LAUNCH((dev::gemm_kernel<T, BN, EPI, true, 4, 2>), dim3(tiles, S), dim3(512), 0, s, a, M, K, N, cm,
                        qo, ro, ws.partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dev::split_epilogue<T, EPI>), dim3(tiles, (M + 15) / 16), dim3(256), 0, s, ws.partial, S, M,
+    JEV_LAUNCH((dev::split_epilogue<T, EPI>), dim3(tiles, (M + 15) / 16), dim3(256), 0, s, ws.partial, S, M,
                        N, cm, qo, ro);
     return hipGetLastError();
   }
@@ -521,10 +521,10 @@ hipError_t gemm_dispatch(const ModelDims& m, const GemmWs& ws, const void* A, in
   dim3 grid((N / bn) * mt);
   // eight waves (two per SIMD): 8 x 1 over a 160-wide tile, 4 x 2 over 128
   if (bn == 160)
-    hipLaunchKernelGGL((dev::gemm_kernel<T, 160, EPI, false, 8, 1>), grid, dim3(512), 0, s, a, M, K, N, cm, qo, ro,
+    JEV_LAUNCH((dev::gemm_kernel<T, 160, EPI, false, 8, 1>), grid, dim3(512), 0, s, a, M, K, N, cm, qo, ro,
                        nullptr);
   else
-    hipLaunchKernelGGL((dev::gemm_kernel<T, 128, EPI, false, 4, 2>), grid, dim3(512), 0, s, a, M, K, N, cm, qo, ro,
+    JEV_LAUNCH((dev::gemm_kernel<T, 128, EPI, false, 4, 2>), grid, dim3(512), 0, s, a, M, K, N, cm, qo, ro,
                        nullptr);
   return hipGetLastError();
 }

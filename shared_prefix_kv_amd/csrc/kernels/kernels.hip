@@ -513,6 +513,8 @@ __global__ __launch_bounds__(256) void readout_kernel(const T* __restrict__ U, c
 
 }  // namespace dev
 
+thread_local LaunchTiming g_launch_timing{nullptr, nullptr};
+
 // ------------------------------------------------------------------ launchers
 using dev::bf16s;
 
@@ -529,7 +531,7 @@ hipError_t launch_embed(const ModelDims& m, const void* embed, const int32_t* to
                         hipStream_t s) {
   if (T_ <= 0) return hipSuccess;
   JEV_DISPATCH_T(m, {
-    hipLaunchKernelGGL(dev::embed_kernel<T>, dim3(T_), dim3(256), 0, s, reinterpret_cast<const T*>(embed), tok,
+    JEV_LAUNCH(dev::embed_kernel<T>, dim3(T_), dim3(256), 0, s, reinterpret_cast<const T*>(embed), tok,
                        m.d, reinterpret_cast<T*>(x));
   })
   return hipGetLastError();
@@ -538,7 +540,7 @@ hipError_t launch_embed(const ModelDims& m, const void* embed, const int32_t* to
 hipError_t launch_rmsnorm(const ModelDims& m, const void* x, const void* g, int32_t T_, void* h, hipStream_t s) {
   if (T_ <= 0) return hipSuccess;
   JEV_DISPATCH_T(m, {
-    hipLaunchKernelGGL(dev::rmsnorm_kernel<T>, dim3(T_), dim3(256), 0, s, reinterpret_cast<const T*>(x),
+    JEV_LAUNCH(dev::rmsnorm_kernel<T>, dim3(T_), dim3(256), 0, s, reinterpret_cast<const T*>(x),
                        reinterpret_cast<const T*>(g), m.d, m.eps, reinterpret_cast<T*>(h));
   })
   return hipGetLastError();
@@ -552,11 +554,11 @@ hipError_t launch_attention(const ModelDims& m, int32_t layer, const AttnTile* t
   const float scale_log2 = float(1.4426950408889634 / std::sqrt((double)m.dh));
   dim3 grid(n_tiles * m.hkv);
   if (m.dtype == 1 && m.dh == 128) {
-    hipLaunchKernelGGL((dev::attn_kernel<bf16s, 128>), grid, dim3(256), 0, s, tiles, page_list, tok_pos,
+    JEV_LAUNCH((dev::attn_kernel<bf16s, 128>), grid, dim3(256), 0, s, tiles, page_list, tok_pos,
                        reinterpret_cast<const bf16s*>(qbuf), reinterpret_cast<const bf16s*>(pool),
                        reinterpret_cast<bf16s*>(o), part_o, part_lse, m.hq, m.hkv, layer_base, scale_log2);
   } else if (m.dtype == 0 && m.dh == 64) {
-    hipLaunchKernelGGL((dev::attn_kernel<float, 64>), grid, dim3(256), 0, s, tiles, page_list, tok_pos,
+    JEV_LAUNCH((dev::attn_kernel<float, 64>), grid, dim3(256), 0, s, tiles, page_list, tok_pos,
                        reinterpret_cast<const float*>(qbuf), reinterpret_cast<const float*>(pool),
                        reinterpret_cast<float*>(o), part_o, part_lse, m.hq, m.hkv, layer_base, scale_log2);
   } else {
@@ -569,10 +571,10 @@ hipError_t launch_merge(const ModelDims& m, const MergeItem* items, int32_t n_it
                         const float* part_lse, void* o, hipStream_t s) {
   if (n_items <= 0) return hipSuccess;
   if (m.dtype == 1 && m.dh == 128) {
-    hipLaunchKernelGGL((dev::merge_kernel<bf16s, 128>), dim3(n_items * m.hkv), dim3(256), 0, s, items, part_o, part_lse,
+    JEV_LAUNCH((dev::merge_kernel<bf16s, 128>), dim3(n_items * m.hkv), dim3(256), 0, s, items, part_o, part_lse,
                        reinterpret_cast<bf16s*>(o), m.hq, m.hkv);
   } else if (m.dtype == 0 && m.dh == 64) {
-    hipLaunchKernelGGL((dev::merge_kernel<float, 64>), dim3(n_items * m.hkv), dim3(256), 0, s, items, part_o, part_lse,
+    JEV_LAUNCH((dev::merge_kernel<float, 64>), dim3(n_items * m.hkv), dim3(256), 0, s, items, part_o, part_lse,
                        reinterpret_cast<float*>(o), m.hq, m.hkv);
   } else {
     return hipErrorInvalidValue;
@@ -586,7 +588,7 @@ hipError_t launch_readout(const ModelDims& m, const void* unembed, const void* f
   if (n_items <= 0) return hipSuccess;
   const size_t shmem = (size_t)(m.d + 64) * sizeof(float);
   JEV_DISPATCH_T(m, {
-    hipLaunchKernelGGL(dev::readout_kernel<T>, dim3(n_items), dim3(256), shmem, s,
+    JEV_LAUNCH(dev::readout_kernel<T>, dim3(n_items), dim3(256), shmem, s,
                        reinterpret_cast<const T*>(unembed), reinterpret_cast<const T*>(final_norm),
                        reinterpret_cast<const T*>(x), items, labels, probs, m.d, m.eps);
   })

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 namespace jev {
@@ -57,6 +58,23 @@ struct GemmWs {
   float* partial;
   size_t partial_elems;
 };
+
+// Timing of the next launcher call (profiling): its first kernel records
+// `start` when it begins and its kernels record `stop` when they end (the last
+// one leaves the final value), carried by the dispatches themselves
+// (hipExtLaunchKernel), without separate event packets between kernels.
+struct LaunchTiming {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+extern thread_local LaunchTiming g_launch_timing;
+
+#define JEV_LAUNCH(KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                                                  \
+  do {                                                                                                       \
+    hipEvent_t e0_ = ::jev::g_launch_timing.start;                                                           \
+    ::jev::g_launch_timing.start = nullptr;                                                                  \
+    hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, e0_, ::jev::g_launch_timing.stop, 0u, __VA_ARGS__); \
+  } while (0)
 
 struct GemmTuning {
   int splits;  // split-K count of the skinny GEMM (0 = automatic)
