@@ -218,9 +218,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Global loads are unconditional (page index clamped to the tile's last
   // page; keys of pages past the end are masked by their zero valid count),
   // so the number of loads in flight is static and each LDS store waits only
-  // for the loads of its own step, issued one step earlier.
-  u32x4 rk[2], rv[2];    // staged K / V of the step stored at the end of this step
-  u32x4 rk2[2], rv2[2];  // and of the step after
+  // for the loads of its own step, issued one step earlier. The staging
+  // registers alternate between two sets from step to step (the loop is
+  // unrolled by two), so no register copy waits for loads still in flight.
+  u32x4 rkA[2], rvA[2], rkB[2], rvB[2];
   // A window of 64 page-list entries, one per lane (entries pw_base + lane),
   // read by readlane: a step needs entries 2st .. 2st+7, so the window is
   // moved every 16 steps and page ids cost no memory access in between.
@@ -237,11 +238,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int i = 0; i < 2; ++i) dst[i] = reinterpret_cast<const u32x4*>(page_ptr(2 * st + i) + PAGE_ELEMS)[tid];
   };
-  auto sstore_k = [&](int buf) {
+  auto sstore_k = [&](int buf, const u32x4* rk) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(&sK[buf][st_koff + 16 * DH * i]) = rk[i];
   };
-  auto sstore_v = [&](int buf) {
+  auto sstore_v = [&](int buf, const u32x4* rv) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       if constexpr (CH == 8) {
@@ -274,110 +275,111 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
   float mrun = kNegInf, lrun = 0.f;
 
-  f32x16 S_cur;
   __syncthreads();  // page list
   pw = sP[min(lane, tile.n_pages - 1)];
   if (nst > 0) {
-    gload_k(0, rk);
-    gload_v(0, rv);
-    sstore_k(0);
-    sstore_v(0);
-    gload_k(1, rk);
-    sstore_k(1);
+    gload_k(0, rkA);
+    gload_v(0, rvA);
+    sstore_k(0, rkA);
+    sstore_v(0, rvA);
+    gload_k(1, rkA);
+    sstore_k(1, rkA);
     // staged for the first step's stores: K of step 2, V of step 1
-    gload_k(2, rk);
-    gload_v(1, rv);
+    gload_k(2, rkA);
+    gload_v(1, rvA);
   }
   __syncthreads();
-  if (nst > 0) S_cur = qk(0);
-  for (int st = 0; st < nst; ++st) {
+  f32x16 SA, SB;
+  if (nst > 0) SA = qk(0);
+  // One step: stores K of step st+2 and V of step st+1 from (kst, vst), loads
+  // K of step st+3 and V of step st+2 into (kld, vld), turns S_in (scores of
+  // step st) into probabilities and leaves the scores of step st+1 in S_out.
+  auto step = [&](const int st, const u32x4* kst, const u32x4* vst, u32x4* kld, u32x4* vld, const f32x16& S_in,
+                  f32x16& S_out) __attribute__((always_inline)) {
     const int buf = st & 1;
     if (st > 0 && (st & 15) == 0) {
       pw_base = 2 * st;
       pw = sP[min(pw_base + lane, tile.n_pages - 1)];
     }
     // loads for the next step's stores
-    gload_k(st + 3, rk2);
-    gload_v(st + 2, rv2);
+    gload_k(st + 3, kld);
+    gload_v(st + 2, vld);
 
     // S of the next step (independent of this step's softmax below)
-    f32x16 S_next;
-    if (st + 1 < nst) S_next = qk(buf ^ 1);
+    if (st + 1 < nst) S_out = qk(buf ^ 1);
 
-    f32x16 S = S_cur;
-    // mask only where needed: partial pages, or keys past the wave's first query
-    const int lp0 = 2 * st;
-    const int v0 = page_entry(lp0) & 31;
-    const int v1 = (lp0 + 1 < tile.n_pages) ? (page_entry(lp0 + 1) & 31) : 0;
-    const bool mask = (v0 < 16) || (v1 < 16) || (tile.causal && tile.kv_pos0 + 16 * lp0 + 31 > qmin);
-    if (mask) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 8 * (r >> 2) + 4 * hh + (r & 3);
-        const int pi = key >> 4, slot = key & 15;
-        const bool ok = slot < (pi ? v1 : v0) && (!tile.causal || tile.kv_pos0 + 16 * (lp0 + pi) + slot <= qpos);
-        S[r] = ok ? S[r] : kNegInf;
-      }
-    }
-    float mloc = S[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, S[r]);
-    mloc = xor32_max(mloc) * scale_log2;
-    if (__any(mloc > mrun + RESCALE_SLACK)) {
-      const float mnew = fmaxf(mrun, mloc);
-      const float alpha = (mnew == kNegInf) ? 1.f : exp2f(mrun - mnew);
-      lrun *= alpha;
-#pragma unroll
-      for (int b = 0; b < NDB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
-      mrun = mnew;
-    }
-    const float nm = (mrun == kNegInf) ? 0.f : -mrun;
-    float p[16];
-    float lsum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      p[r] = __builtin_amdgcn_exp2f(fmaf(S[r], scale_log2, nm));
-      lsum += p[r];
-    }
-    lsum = xor32_sum(lsum);
-    lrun += lsum;
-
-    // O^T += V^T P^T; MFMA tt covers keys {8j + 4*hh + i : 4j + i in [tt*KL, tt*KL+KL)}
-#pragma unroll
-    for (int tt = 0; tt < 16 / KL; ++tt) {
-      frag pb;
-      if constexpr (KL == 8) {
-#pragma unroll
-        for (int sidx = 0; sidx < 8; ++sidx) pb[sidx] = (__bf16)p[8 * tt + sidx];
-      } else {
-        pb = p[tt];
-      }
-#pragma unroll
-      for (int b = 0; b < NDB; ++b) {
-        const int d = 32 * b + c;
-        frag va;
-        if constexpr (KL == 8) {
-          // keys 16tt + {4hh..4hh+3, 8+4hh..8+4hh+3}: quads hh, hh+2 of half tt,
-          // stored at quad slots 2hh, 2hh+1 = unit 2tt + hh
-          va = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(&sV[buf][0])[vq_unit(d, 2 * tt + hh)]);
-        } else {
-          const int key = 8 * (tt >> 2) + 4 * hh + (tt & 3);
-          va = MF::load(&sV[buf][v_off(d, key)]);
+      f32x16 S = S_in;
+      // mask only where needed: partial pages, or keys past the wave's first query
+      const int lp0 = 2 * st;
+      const int v0 = page_entry(lp0) & 31;
+      const int v1 = (lp0 + 1 < tile.n_pages) ? (page_entry(lp0 + 1) & 31) : 0;
+      const bool mask = (v0 < 16) || (v1 < 16) || (tile.causal && tile.kv_pos0 + 16 * lp0 + 31 > qmin);
+      if (mask) {
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 8 * (r >> 2) + 4 * hh + (r & 3);
+          const int pi = key >> 4, slot = key & 15;
+          const bool ok = slot < (pi ? v1 : v0) && (!tile.causal || tile.kv_pos0 + 16 * (lp0 + pi) + slot <= qpos);
+          S[r] = ok ? S[r] : kNegInf;
         }
-        oacc[b] = MF::mma(va, pb, oacc[b]);
       }
-    }
-    if (st + 2 < nst) sstore_k(buf);
-    if (st + 1 < nst) sstore_v(buf ^ 1);
+      float mloc = S[0];
+  #pragma unroll
+      for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, S[r]);
+      mloc = xor32_max(mloc) * scale_log2;
+      if (__any(mloc > mrun + RESCALE_SLACK)) {
+        const float mnew = fmaxf(mrun, mloc);
+        const float alpha = (mnew == kNegInf) ? 1.f : exp2f(mrun - mnew);
+        lrun *= alpha;
+  #pragma unroll
+        for (int b = 0; b < NDB; ++b)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+        mrun = mnew;
+      }
+      const float nm = (mrun == kNegInf) ? 0.f : -mrun;
+      float p[16];
+      float lsum = 0.f;
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = __builtin_amdgcn_exp2f(fmaf(S[r], scale_log2, nm));
+        lsum += p[r];
+      }
+      lsum = xor32_sum(lsum);
+      lrun += lsum;
+
+      // O^T += V^T P^T; MFMA tt covers keys {8j + 4*hh + i : 4j + i in [tt*KL, tt*KL+KL)}
+  #pragma unroll
+      for (int tt = 0; tt < 16 / KL; ++tt) {
+        frag pb;
+        if constexpr (KL == 8) {
+  #pragma unroll
+          for (int sidx = 0; sidx < 8; ++sidx) pb[sidx] = (__bf16)p[8 * tt + sidx];
+        } else {
+          pb = p[tt];
+        }
+  #pragma unroll
+        for (int b = 0; b < NDB; ++b) {
+          const int d = 32 * b + c;
+          frag va;
+          if constexpr (KL == 8) {
+            // keys 16tt + {4hh..4hh+3, 8+4hh..8+4hh+3}: quads hh, hh+2 of half tt,
+            // stored at quad slots 2hh, 2hh+1 = unit 2tt + hh
+            va = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(&sV[buf][0])[vq_unit(d, 2 * tt + hh)]);
+          } else {
+            const int key = 8 * (tt >> 2) + 4 * hh + (tt & 3);
+            va = MF::load(&sV[buf][v_off(d, key)]);
+          }
+          oacc[b] = MF::mma(va, pb, oacc[b]);
+        }
+      }
+    if (st + 2 < nst) sstore_k(buf, kst);
+    if (st + 1 < nst) sstore_v(buf ^ 1, vst);
     __syncthreads();
-    S_cur = S_next;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      rk[i] = rk2[i];
-      rv[i] = rv2[i];
-    }
+  };
+  for (int st = 0; st < nst; st += 2) {
+    step(st, rkA, rvA, rkB, rvB, SA, SB);
+    if (st + 1 < nst) step(st + 1, rkB, rvB, rkA, rvA, SB, SA);
   }
 
   if (!row_ok) return;
