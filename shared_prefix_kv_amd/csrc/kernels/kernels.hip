@@ -196,7 +196,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   const T* kvbase = pool + layer_base + (size_t)kvh * 2 * PAGE_ELEMS;
-  const size_t page_stride = (size_t)hkv * 2 * PAGE_ELEMS;
   const int nst = (tile.n_pages + 1) >> 1;
 
   // loop-invariant LDS offsets
@@ -229,7 +228,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto page_entry = [&](int lp) -> int {
     return __builtin_amdgcn_readlane(pw, min(lp, tile.n_pages - 1) - pw_base);
   };
-  auto page_ptr = [&](int lp) -> const T* { return kvbase + (size_t)(page_entry(lp) >> 5) * page_stride; };
+  // page byte offsets as one unsigned 32 x 32 -> 64-bit product (a page id is
+  // below 2^26 and a page's K+V for all KV heads is hkv * 2 * PAGE_ELEMS
+  // elements, far below 4 GiB)
+  const char* kvbytes = reinterpret_cast<const char*>(kvbase);
+  const uint32_t page_bytes = (uint32_t)hkv * (uint32_t)(2 * PAGE_ELEMS * sizeof(T));
+  auto page_ptr = [&](int lp) -> const T* {
+    const uint32_t pg = (uint32_t)page_entry(lp) >> 5;
+    return reinterpret_cast<const T*>(kvbytes + (uint64_t)pg * page_bytes);
+  };
   auto gload_k = [&](int st, u32x4* dst) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) dst[i] = reinterpret_cast<const u32x4*>(page_ptr(2 * st + i))[tid];
@@ -294,7 +301,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // One step: stores K of step st+2 and V of step st+1 from (kst, vst), loads
   // K of step st+3 and V of step st+2 into (kld, vld), turns S_in (scores of
   // step st) into probabilities and leaves the scores of step st+1 in S_out.
-  auto step = [&](const int st, const u32x4* kst, const u32x4* vst, u32x4* kld, u32x4* vld, const f32x16& S_in,
+  auto step = [&](const int st, const u32x4* kst, const u32x4* vst, u32x4* kld, u32x4* vld, f32x16& S_in,
                   f32x16& S_out) __attribute__((always_inline)) {
     const int buf = st & 1;
     if (st > 0 && (st & 15) == 0) {
@@ -305,74 +312,98 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     gload_k(st + 3, kld);
     gload_v(st + 2, vld);
 
-    // S of the next step (independent of this step's softmax below)
-    if (st + 1 < nst) S_out = qk(buf ^ 1);
-
-      f32x16 S = S_in;
-      // mask only where needed: partial pages, or keys past the wave's first query
-      const int lp0 = 2 * st;
-      const int v0 = page_entry(lp0) & 31;
-      const int v1 = (lp0 + 1 < tile.n_pages) ? (page_entry(lp0 + 1) & 31) : 0;
-      const bool mask = (v0 < 16) || (v1 < 16) || (tile.causal && tile.kv_pos0 + 16 * lp0 + 31 > qmin);
-      if (mask) {
-  #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 8 * (r >> 2) + 4 * hh + (r & 3);
-          const int pi = key >> 4, slot = key & 15;
-          const bool ok = slot < (pi ? v1 : v0) && (!tile.causal || tile.kv_pos0 + 16 * (lp0 + pi) + slot <= qpos);
-          S[r] = ok ? S[r] : kNegInf;
-        }
-      }
-      float mloc = S[0];
-  #pragma unroll
-      for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, S[r]);
-      mloc = xor32_max(mloc) * scale_log2;
-      if (__any(mloc > mrun + RESCALE_SLACK)) {
-        const float mnew = fmaxf(mrun, mloc);
-        const float alpha = (mnew == kNegInf) ? 1.f : exp2f(mrun - mnew);
-        lrun *= alpha;
-  #pragma unroll
-        for (int b = 0; b < NDB; ++b)
-  #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
-        mrun = mnew;
-      }
-      const float nm = (mrun == kNegInf) ? 0.f : -mrun;
-      float p[16];
-      float lsum = 0.f;
-  #pragma unroll
+    f32x16& S = S_in;  // consumed here: masked in place
+    // mask only where needed: partial pages, or keys past the wave's first query
+    const int lp0 = 2 * st;
+    const int v0 = page_entry(lp0) & 31;
+    const int v1 = (lp0 + 1 < tile.n_pages) ? (page_entry(lp0 + 1) & 31) : 0;
+    const bool mask = (v0 < 16) || (v1 < 16) || (tile.causal && tile.kv_pos0 + 16 * lp0 + 31 > qmin);
+    if (mask) {
+#pragma unroll
       for (int r = 0; r < 16; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(fmaf(S[r], scale_log2, nm));
-        lsum += p[r];
+        const int key = 8 * (r >> 2) + 4 * hh + (r & 3);
+        const int pi = key >> 4, slot = key & 15;
+        const bool ok = slot < (pi ? v1 : v0) && (!tile.causal || tile.kv_pos0 + 16 * (lp0 + pi) + slot <= qpos);
+        S[r] = ok ? S[r] : kNegInf;
       }
-      lsum = xor32_sum(lsum);
-      lrun += lsum;
+    }
+    float mloc = S[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, S[r]);
+    mloc = xor32_max(mloc) * scale_log2;
+    if (__any(mloc > mrun + RESCALE_SLACK)) {
+      const float mnew = fmaxf(mrun, mloc);
+      const float alpha = (mnew == kNegInf) ? 1.f : exp2f(mrun - mnew);
+      lrun *= alpha;
+#pragma unroll
+      for (int b = 0; b < NDB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+      mrun = mnew;
+    }
+    const float nm = (mrun == kNegInf) ? 0.f : -mrun;
 
-      // O^T += V^T P^T; MFMA tt covers keys {8j + 4*hh + i : 4j + i in [tt*KL, tt*KL+KL)}
-  #pragma unroll
-      for (int tt = 0; tt < 16 / KL; ++tt) {
-        frag pb;
-        if constexpr (KL == 8) {
-  #pragma unroll
-          for (int sidx = 0; sidx < 8; ++sidx) pb[sidx] = (__bf16)p[8 * tt + sidx];
-        } else {
-          pb = p[tt];
-        }
-  #pragma unroll
-        for (int b = 0; b < NDB; ++b) {
-          const int d = 32 * b + c;
-          frag va;
-          if constexpr (KL == 8) {
-            // keys 16tt + {4hh..4hh+3, 8+4hh..8+4hh+3}: quads hh, hh+2 of half tt,
-            // stored at quad slots 2hh, 2hh+1 = unit 2tt + hh
-            va = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(&sV[buf][0])[vq_unit(d, 2 * tt + hh)]);
-          } else {
-            const int key = 8 * (tt >> 2) + 4 * hh + (tt & 3);
-            va = MF::load(&sV[buf][v_off(d, key)]);
-          }
-          oacc[b] = MF::mma(va, pb, oacc[b]);
-        }
+    // Branch-free from here: the S MFMAs of the next step (a dependent chain)
+    // are interleaved with this step's exponentials, so that one wave per
+    // SIMD keeps the MFMA and VALU pipes busy together. On the last step the
+    // product reads stale LDS and is never used.
+    S_out = qk(buf ^ 1);
+    float p[16];
+    float lsum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[r] = __builtin_amdgcn_exp2f(fmaf(S[r], scale_log2, nm));
+      lsum += p[r];
+    }
+    lsum = xor32_sum(lsum);
+    lrun += lsum;
+    frag pb[16 / KL];
+#pragma unroll
+    for (int tt = 0; tt < 16 / KL; ++tt) {
+      if constexpr (KL == 8) {
+#pragma unroll
+        for (int sidx = 0; sidx < 8; ++sidx) pb[tt][sidx] = (__bf16)p[8 * tt + sidx];
+      } else {
+        pb[tt] = p[tt];
       }
+    }
+    // O^T += V^T P^T; MFMA tt covers keys {8j + 4*hh + i : 4j + i in [tt*KL, tt*KL+KL)}
+#pragma unroll
+    for (int tt = 0; tt < 16 / KL; ++tt) {
+#pragma unroll
+      for (int b = 0; b < NDB; ++b) {
+        const int d = 32 * b + c;
+        frag va;
+        if constexpr (KL == 8) {
+          // keys 16tt + {4hh..4hh+3, 8+4hh..8+4hh+3}: quads hh, hh+2 of half tt,
+          // stored at quad slots 2hh, 2hh+1 = unit 2tt + hh
+          va = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(&sV[buf][0])[vq_unit(d, 2 * tt + hh)]);
+        } else {
+          const int key = 8 * (tt >> 2) + 4 * hh + (tt & 3);
+          va = MF::load(&sV[buf][v_off(d, key)]);
+        }
+        oacc[b] = MF::mma(va, pb[tt], oacc[b]);
+      }
+    }
+    if constexpr (KL == 8) {
+      // Order of the branch-free block: 2 K-fragment reads ahead; per S MFMA
+      // ~7 VALU and the next K read, plus, over the last four, the V reads of
+      // the first PV half; then per PV MFMA one V read four ahead.
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < NKS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+        if (i + 2 < NKS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (i >= NKS - NDB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * NDB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + NDB < 2 * NDB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+
     if (st + 2 < nst) sstore_k(buf, kst);
     if (st + 1 < nst) sstore_v(buf ^ 1, vst);
     __syncthreads();
