@@ -231,6 +231,28 @@ typedef struct {
 int jev_profile(jev_ctx* ctx, uint32_t kind_mask);
 int jev_profile_read(jev_ctx* ctx, jev_launch_record* out, int64_t cap, int64_t* n);
 
+/* Answer layer (jdon.com openjev-sglang article, "three question types" and
+ * "confidence" sections), on the host.  Branch i's label distribution is
+ * probs[label_offsets[i] .. label_offsets[i+1]) (host float32, K = 2..64
+ * entries in label order, each finite and >= 0; offsets has n+1 entries,
+ * offsets[0] = 0).  Per branch, with options numbered from 0:
+ *   kinds[i] = JEV_ANSWER_NOUL:   value[i] = P(yes), the first label's probability;
+ *   kinds[i] = JEV_ANSWER_CHOICE: value[i] = index of the largest probability
+ *                                 (ties go to the lowest index);
+ *   kinds[i] = JEV_ANSWER_SCORE:  value[i] = sum_j j * P_j.
+ * choice[i] receives that argmax for every kind and confidence[i] receives
+ * 1 - H(P) / ln K, H the Shannon entropy in natural log with 0 ln 0 = 0: 1 for
+ * a one-hot P, 0 for the uniform one (a measure of concentration, not of
+ * calibrated correctness).  value, choice and confidence are host arrays of n
+ * entries; choice and confidence may be NULL.  Computed in double precision;
+ * no context or device is involved.
+ * Errors: JEV_EINVAL (n < 0, NULL probs/offsets/kinds/value, bad offsets,
+ * K outside [2, 64], a negative or non-finite probability, unknown kind);
+ * on error no output is written. */
+enum { JEV_ANSWER_NOUL = 0, JEV_ANSWER_CHOICE = 1, JEV_ANSWER_SCORE = 2 };
+int jev_answers(int32_t n, const float* probs, const int64_t* label_offsets, const int32_t* kinds, double* value,
+                int32_t* choice, double* confidence);
+
 const char* jev_last_error(void);
 
 #ifdef __cplusplus

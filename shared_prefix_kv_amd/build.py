@@ -25,6 +25,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "kernels.hip"),
     os.path.join(CSRC, "kernels", "gemm.hip"),
     os.path.join(CSRC, "host", "tree.cpp"),
+    os.path.join(CSRC, "host", "answers.cpp"),
     os.path.join(CSRC, "host", "api.cpp"),
 ]
 

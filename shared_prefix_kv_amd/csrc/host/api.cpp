@@ -33,6 +33,7 @@
 
 #include "../../../include/jev.h"
 #include "../kernels/launch.hpp"
+#include "answers.hpp"
 #include "tree.hpp"
 
 namespace {
@@ -549,6 +550,32 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
 extern "C" {
 
 const char* jev_last_error(void) { return g_err.c_str(); }
+
+int jev_answers(int32_t n, const float* probs, const int64_t* label_offsets, const int32_t* kinds, double* value,
+                int32_t* choice, double* confidence) {
+  if (n < 0) return fail(JEV_EINVAL, "n < 0");
+  if (n == 0) return JEV_OK;
+  if (!probs || !label_offsets || !kinds || !value) return fail(JEV_EINVAL, "NULL probs/offsets/kinds/value");
+  if (label_offsets[0] != 0) return fail(JEV_EINVAL, "label_offsets[0] != 0");
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t k = label_offsets[i + 1] - label_offsets[i];
+    if (k < JEV_MIN_LABELS || k > JEV_MAX_LABELS)
+      return fail(JEV_EINVAL, "branch " + std::to_string(i) + ": label count outside [2, 64]");
+    if (kinds[i] != JEV_ANSWER_NOUL && kinds[i] != JEV_ANSWER_CHOICE && kinds[i] != JEV_ANSWER_SCORE)
+      return fail(JEV_EINVAL, "branch " + std::to_string(i) + ": unknown answer kind");
+    for (int64_t j = label_offsets[i]; j < label_offsets[i + 1]; ++j)
+      if (!std::isfinite(probs[j]) || probs[j] < 0.f)
+        return fail(JEV_EINVAL, "branch " + std::to_string(i) + ": probability not finite and >= 0");
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const jev::Answer a = jev::answer(kinds[i], probs + label_offsets[i],
+                                      int32_t(label_offsets[i + 1] - label_offsets[i]));
+    value[i] = a.value;
+    if (choice) choice[i] = a.choice;
+    if (confidence) confidence[i] = a.confidence;
+  }
+  return JEV_OK;
+}
 
 size_t jev_workspace_bytes(const jev_model_desc* desc) {
   std::string why;

@@ -19,11 +19,13 @@ LIB_PATH = os.path.join(_HERE, "lib", "libjev.so")
 JEV_OK, JEV_EINVAL, JEV_ENOMEM, JEV_EHANDLE, JEV_EHIP, JEV_ESTATE = range(6)
 JEV_DTYPE_F32, JEV_DTYPE_BF16 = 0, 1
 JEV_TAP_ATTN, JEV_TAP_RESID = 0, 1
+JEV_ANSWER_NOUL, JEV_ANSWER_CHOICE, JEV_ANSWER_SCORE = 0, 1, 2
 _NAMES = {0: "JEV_OK", 1: "JEV_EINVAL", 2: "JEV_ENOMEM", 3: "JEV_EHANDLE", 4: "JEV_EHIP", 5: "JEV_ESTATE"}
 
 EXPORTED = ["jev_workspace_bytes", "jev_kv_pool_bytes", "jev_create", "jev_destroy", "jev_prefill_prefix",
             "jev_score_branches", "jev_score_candidates", "jev_free_pages", "jev_plan", "jev_page_table",
-            "jev_match", "jev_stats", "jev_debug_tap", "jev_profile", "jev_profile_read", "jev_last_error"]
+            "jev_match", "jev_stats", "jev_debug_tap", "jev_profile", "jev_profile_read", "jev_answers",
+            "jev_last_error"]
 KERNELS = ["embed", "rmsnorm", "qkv", "attn", "merge", "oproj", "readout"]
 
 
@@ -89,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.jev_debug_tap.argtypes = [vp, i32, i32, vp, i64]
         L.jev_profile.argtypes = [vp, ctypes.c_uint32]
         L.jev_profile_read.argtypes = [vp, P(LaunchRecord), i64, P(i64)]
+        L.jev_answers.argtypes = [i32, P(ctypes.c_float), P(i64), P(i32), P(ctypes.c_double), P(i32),
+                                  P(ctypes.c_double)]
         L.jev_last_error.restype = ctypes.c_char_p
         _lib = L
     return _lib
@@ -139,6 +143,30 @@ def upload_weights(w, device="cuda:0") -> dict:
     return {"embed": dev(w.embed), "unembed": dev(w.unembed), "final_norm": dev(w.final_norm),
             "attn_norm": [dev(a) for a in w.attn_norm], "wq": [dev(a) for a in w.wq],
             "wk": [dev(a) for a in w.wk], "wv": [dev(a) for a in w.wv], "wo": [dev(a) for a in w.wo]}
+
+
+def answers(probs, label_offsets, kinds):
+    """jev_answers: per branch (value, choice, confidence) from host label
+    distributions.  probs: float32 values (numpy, list or a torch tensor, which
+    is copied to the host); label_offsets: n+1 int64; kinds: n JEV_ANSWER_*.
+    Returns three numpy arrays: value (float64), choice (int32), confidence
+    (float64)."""
+    if hasattr(probs, "detach"):
+        probs = probs.detach().cpu().numpy()
+    p = np.ascontiguousarray(np.asarray(probs, dtype=np.float32))
+    off = _i64(label_offsets)
+    k = _i32(kinds)
+    n = len(k)
+    if len(off) != n + 1:
+        raise ValueError("label_offsets needs n + 1 entries")
+    value = np.zeros(n, dtype=np.float64)
+    choice = np.zeros(n, dtype=np.int32)
+    conf = np.zeros(n, dtype=np.float64)
+    if n:
+        _check(lib().jev_answers(n, _ptr(p, ctypes.c_float), _ptr(off, ctypes.c_int64), _ptr(k, ctypes.c_int32),
+                                 _ptr(value, ctypes.c_double), _ptr(choice, ctypes.c_int32),
+                                 _ptr(conf, ctypes.c_double)))
+    return value, choice, conf
 
 
 def _current_stream():

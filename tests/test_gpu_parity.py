@@ -77,6 +77,28 @@ def test_w1_shared_prefix_matches_oracle(w1):
     assert ctx.stats()["pages_in_use"] == 0
 
 
+def test_w1_answers_of_scored_branches(w1):
+    """jev_answers on the device-scored distributions vs the oracle's answer
+    functions on the oracle's distributions (every kind for every branch)."""
+    from oracle import answers as oa
+    from shared_prefix_kv_amd import jev
+    wl, inst, m, ref, ctx, _ = w1
+    (h,) = ctx.prefill_prefix([0], [inst.prefixes[0]])
+    br = inst.passes[0]
+    probs, loff = ctx.score_branches([h] * len(br), [b.tokens for b in br], [b.labels for b in br])
+    _sync()
+    ctx.free_pages([h])
+    n = len(br)
+    for kind, f in ((jev.JEV_ANSWER_NOUL, oa.noul), (jev.JEV_ANSWER_SCORE, oa.score)):
+        val, choice, conf = jev.answers(probs, loff, [kind] * n)
+        for i in range(n):
+            assert abs(val[i] - f(ref[i])) <= len(ref[i]) * TOL_F32
+            assert abs(conf[i] - oa.confidence(ref[i])) <= 1e-3
+            top = sorted(ref[i], reverse=True)
+            if top[0] - top[1] > 1e-3:
+                assert choice[i] == oa.choice(ref[i])[0]
+
+
 def test_w1_unshared_and_candidate_paths_match_oracle(w1):
     wl, inst, m, ref, ctx, _ = w1
     seqs = inst.full_sequences(0)
