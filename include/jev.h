@@ -148,13 +148,29 @@ int jev_score_branches(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const
 /* Scores n candidates given as full token sequences (LLM2Jev shared-prefix page,
  * staged-submission section).  Each candidate is matched against the resident
  * prefixes (longest full-node match leaving at least one token), the rest are
- * grouped into a token-prefix tree and computed in staged rounds by tree depth;
- * every candidate is read out exactly once; probs as for jev_score_branches, in
- * input order.  Pages of the call's own tree nodes are released when it ends.
+ * grouped into a token-prefix tree and computed in staged rounds whose order
+ * is the context's plan mode (jev_set_plan_mode); every candidate is read out
+ * exactly once; probs as for jev_score_branches, in input order.  Pages of the
+ * call's own tree nodes are released when it ends.
  * Errors: as jev_score_branches. */
 int jev_score_candidates(jev_ctx* ctx, int32_t n, const int32_t* tokens, const int64_t* tok_offsets,
                          const int32_t* label_ids, const int64_t* label_offsets, float* probs,
                          void* hip_stream);
+
+/* Round order of jev_score_candidates and jev_plan on this context (LLM2Jev
+ * shared-prefix page, staged-submission section).
+ *  JEV_PLAN_DEPTH (the default): round k computes every new tree node at depth
+ *    k; a shared prefix is computed as a node of its own before the candidates
+ *    that continue it.
+ *  JEV_PLAN_CANDIDATE_FIRST: the page's own order.  Each round takes every node
+ *    whose parent is already computed; a node without children is computed with
+ *    all its candidates, while a shared node is built by one real candidate, its
+ *    smallest index, whose path down to its own read-out is computed (and read
+ *    out) in that round.  No candidate waits on a separate warmup node.
+ * Both orders compute every node once and give the same probabilities.
+ * Errors: JEV_EINVAL (NULL ctx, unknown mode). */
+enum { JEV_PLAN_DEPTH = 0, JEV_PLAN_CANDIDATE_FIRST = 1 };
+int jev_set_plan_mode(jev_ctx* ctx, int32_t mode);
 
 /* Drops one caller reference of each handle.  A prefix with no reference and
  * no resident child returns its pages to the pool (its parent may follow).
@@ -162,10 +178,15 @@ int jev_score_candidates(jev_ctx* ctx, int32_t n, const int32_t* tokens, const i
  * device work that read them.  Errors: JEV_EHANDLE (nothing is released then). */
 int jev_free_pages(jev_ctx* ctx, int32_t n, const jev_prefix* handles);
 
-/* Host-only: the staged-round plan jev_score_candidates would execute now,
- * serialised as int32 (format in the design doc; identical to the oracle's planner).
- * out may be NULL to query *out_len.  Errors: JEV_EINVAL, JEV_ENOMEM (pool too
- * small for the plan; the plan is not returned). */
+/* Host-only: the staged-round plan jev_score_candidates would execute now (in
+ * the context's plan mode), serialised as int32: the round count; per round,
+ * its node count and per node: id, parent id (-1: continues the resident
+ * anchor), anchor handle, tree depth, smallest candidate index, segment start
+ * (relative to the anchor), segment length, page count, the page ids, read-out
+ * count, the read-out candidate indices; then the candidate count and per
+ * candidate: anchor handle, tokens matched in the resident tree, id of its
+ * read-out node.  out may be NULL to query *out_len.  Errors: JEV_EINVAL,
+ * JEV_ENOMEM (pool too small for the plan; the plan is not returned). */
 int jev_plan(jev_ctx* ctx, int32_t n, const int32_t* tokens, const int64_t* tok_offsets,
              int32_t* out, int64_t cap, int64_t* out_len);
 

@@ -5,8 +5,7 @@ Test infrastructure only (see the package docstring).
 Model (the synthetic configurations; the pages use a trained Qwen model whose
 weights are not available here): embedding -> L x [RMSNorm -> causal
 self-attention with RoPE and grouped KV heads -> residual add] -> RMSNorm ->
-unembedding.  Readings taken where the pages say nothing (each is listed in
-DESIGN.md):
+unembedding.  Readings taken where the pages say nothing:
 
 * RMSNorm: y = x / sqrt(mean(x^2) + eps) * g, eps = 1e-6, g = ones.
 * RoPE: rotate-half pairing (i, i + dh/2), inverse frequency theta^(-2i/dh),

@@ -13,7 +13,7 @@ rounds following the token tree; its Radix Cache section says reuse is keyed
 on the exact token prefix and that each candidate's last scored position is
 always computed.  Page size 16 tokens.
 
-Readings (the pages leave these open; listed in the design doc):
+Readings (the pages leave these open):
 
 * Trie: compressed, token-granular, over each candidate's tokens after its
   resident match.  A node is a maximal token run shared by the same set of
@@ -22,8 +22,16 @@ Readings (the pages leave these open; listed in the design doc):
   and whose own run is shorter than one page, is removed; its tokens are
   prepended to each child.  Short accidental common runs therefore never add a
   round.
-* Rounds: level-synchronous by depth under the anchor (round k computes every
-  new node at depth k).
+* Rounds, mode "depth": level-synchronous by depth under the anchor (round k
+  computes every new node at depth k).
+* Rounds, mode "candidate_first" (the staged-submission section's own
+  example order): a candidate is submitted in a round when the first node on
+  its path that is not yet computed either has no children (nothing there for
+  others to reuse) or is a shared node of which it is the smallest candidate
+  (it builds that prefix for the others).  A submitted candidate computes
+  every node of its path not yet computed; a candidate is scored in the round
+  its read-out node is computed.  Nodes of a round are in (depth, smallest
+  candidate) order.
 * Canonical order: (depth, smallest candidate index through the node); node
   ids are ranks in that order.
 * Pages: free ids in a min-heap; each new node takes ceil(len/16) lowest ids at
@@ -259,7 +267,45 @@ class Plan:
         return out
 
 
-def plan_candidates(tree: ResidentTree, seqs: Sequence[Sequence[int]]) -> Plan:
+def _paths(tops: List[PlanNode]) -> Dict[int, List[PlanNode]]:
+    """Candidate -> its nodes from the top-level node down to its read-out node."""
+    out: Dict[int, List[PlanNode]] = {}
+
+    def walk(node: PlanNode, above: List[PlanNode]) -> None:
+        here = above + [node]
+        for c in node.readout:
+            out[c] = here
+        for ch in node.children:
+            walk(ch, here)
+
+    for t in tops:
+        walk(t, [])
+    return out
+
+
+def _rounds_candidate_first(tops: List[PlanNode]) -> List[List[PlanNode]]:
+    paths = _paths(tops)
+    computed: set = set()
+    pending = sorted(paths)
+    rounds: List[List[PlanNode]] = []
+    while pending:
+        submitted = []
+        for c in pending:
+            first = next(x for x in paths[c] if id(x) not in computed)
+            if not first.children or first.cand_min == c:
+                submitted.append(c)
+        new: Dict[int, PlanNode] = {}
+        for c in submitted:
+            for x in paths[c]:
+                if id(x) not in computed:
+                    new[id(x)] = x
+        computed |= set(new)
+        rounds.append(sorted(new.values(), key=lambda x: (x.depth, x.cand_min)))
+        pending = [c for c in pending if id(paths[c][-1]) not in computed]
+    return rounds
+
+
+def plan_candidates(tree: ResidentTree, seqs: Sequence[Sequence[int]], mode: str = "depth") -> Plan:
     """Plans the staged rounds of a call and assigns pages (all-or-nothing).
 
     Pages of nodes without children are returned to the pool at the end of
@@ -279,7 +325,7 @@ def plan_candidates(tree: ResidentTree, seqs: Sequence[Sequence[int]]) -> Plan:
     tops: List[PlanNode] = []
     for h, cs in by_anchor.items():
         tops += _dissolve(_build(cs, 0, rel, h))
-    # depth levels
+    # depth levels (and parents)
     levels: List[List[PlanNode]] = []
     frontier = sorted(tops, key=lambda x: x.cand_min)
     d = 1
@@ -294,6 +340,10 @@ def plan_candidates(tree: ResidentTree, seqs: Sequence[Sequence[int]]) -> Plan:
                 nxt.append(ch)
         frontier = nxt
         d += 1
+    if mode == "candidate_first":
+        levels = _rounds_candidate_first(tops)
+    elif mode != "depth":
+        raise ValueError(mode)
     nid = 0
     for lvl in levels:
         for x in lvl:

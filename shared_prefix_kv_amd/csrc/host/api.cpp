@@ -156,6 +156,7 @@ struct jev_ctx {
   jev_model_desc desc{};
   bool dry = true;
   bool dead = false;
+  jev::PlanMode plan_mode = jev::PlanMode::DEPTH;
   jev::ModelDims dims{};
   std::vector<jev::LayerW> layers;
   const void* embed = nullptr;
@@ -801,7 +802,7 @@ int jev_score_candidates(jev_ctx* ctx, int32_t n, const int32_t* tokens, const i
     if (tok_offsets[i + 1] - tok_offsets[i] > ctx->desc.max_positions)
       return fail(JEV_EINVAL, "candidate " + std::to_string(i) + " runs past max_positions");
   jev::Plan plan;
-  if (!jev::plan_candidates(*ctx->tree, &ctx->pages, n, tokens, tok_offsets, &plan))
+  if (!jev::plan_candidates(*ctx->tree, &ctx->pages, n, tokens, tok_offsets, &plan, ctx->plan_mode))
     return fail(JEV_ENOMEM, "not enough free KV pages for the plan");
   // rounds
   std::vector<std::vector<RNode>> rounds(plan.rounds.size());
@@ -855,6 +856,13 @@ int jev_score_candidates(jev_ctx* ctx, int32_t n, const int32_t* tokens, const i
   return run_rounds(ctx, rds, hb, probs, reinterpret_cast<hipStream_t>(hip_stream));
 }
 
+int jev_set_plan_mode(jev_ctx* ctx, int32_t mode) {
+  if (!ctx) return fail(JEV_EINVAL, "ctx is NULL");
+  if (mode != JEV_PLAN_DEPTH && mode != JEV_PLAN_CANDIDATE_FIRST) return fail(JEV_EINVAL, "unknown plan mode");
+  ctx->plan_mode = mode == JEV_PLAN_DEPTH ? jev::PlanMode::DEPTH : jev::PlanMode::CANDIDATE_FIRST;
+  return JEV_OK;
+}
+
 int jev_free_pages(jev_ctx* ctx, int32_t n, const jev_prefix* handles) {
   if (!ctx) return fail(JEV_EINVAL, "ctx is NULL");
   if (n < 0 || (n > 0 && !handles)) return fail(JEV_EINVAL, "bad handle array");
@@ -876,7 +884,7 @@ int jev_plan(jev_ctx* ctx, int32_t n, const int32_t* tokens, const int64_t* tok_
   if (!ctx || !out_len) return fail(JEV_EINVAL, "NULL ctx/out_len");
   if (int rc = check_segments(ctx, n, tokens, tok_offsets, "candidates")) return rc;
   jev::Plan plan;
-  if (n > 0 && !jev::plan_candidates(*ctx->tree, &ctx->pages, n, tokens, tok_offsets, &plan))
+  if (n > 0 && !jev::plan_candidates(*ctx->tree, &ctx->pages, n, tokens, tok_offsets, &plan, ctx->plan_mode))
     return fail(JEV_ENOMEM, "not enough free KV pages for the plan");
   std::vector<int32_t> s = n > 0 ? plan.serialize() : std::vector<int32_t>{0, 0};
   *out_len = int64_t(s.size());

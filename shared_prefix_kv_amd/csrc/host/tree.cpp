@@ -204,7 +204,7 @@ struct Builder {
 }  // namespace
 
 bool plan_candidates(const ResidentTree& tree, PagePool* pool, int32_t n, const int32_t* tok,
-                     const int64_t* off, Plan* plan) {
+                     const int64_t* off, Plan* plan, PlanMode mode) {
   *plan = Plan();
   std::vector<const int32_t*> rel(n);
   std::vector<int64_t> len(n);
@@ -236,24 +236,72 @@ bool plan_candidates(const ResidentTree& tree, PagePool* pool, int32_t n, const 
     std::vector<int32_t> t = B.dissolve(B.build(by_anchor[g], 0, anchor_order[g]));
     tops.insert(tops.end(), t.begin(), t.end());
   }
-  // depth levels
+  // tree depth and parent links
   auto by_min = [&](int32_t x, int32_t y) {
     return plan->nodes[x].cand_min() < plan->nodes[y].cand_min();
   };
-  std::vector<int32_t> frontier = tops;
-  int32_t depth = 1;
-  while (!frontier.empty()) {
-    std::sort(frontier.begin(), frontier.end(), by_min);
-    for (int32_t i : frontier) plan->nodes[i].depth = depth;
-    plan->rounds.push_back(frontier);
-    std::vector<int32_t> next;
-    for (int32_t i : frontier)
-      for (int32_t c : plan->nodes[i].children) {
-        plan->nodes[c].parent = i;
-        next.push_back(c);
+  {
+    std::vector<int32_t> level = tops;
+    int32_t depth = 1;
+    while (!level.empty()) {
+      std::vector<int32_t> next;
+      for (int32_t i : level) {
+        plan->nodes[i].depth = depth;
+        for (int32_t c : plan->nodes[i].children) {
+          plan->nodes[c].parent = i;
+          next.push_back(c);
+        }
       }
+      level = std::move(next);
+      ++depth;
+    }
+  }
+  auto by_depth_min = [&](int32_t x, int32_t y) {
+    const PlanNode& a = plan->nodes[x];
+    const PlanNode& b = plan->nodes[y];
+    return a.depth != b.depth ? a.depth < b.depth : a.cand_min() < b.cand_min();
+  };
+  std::vector<int32_t> frontier = tops;
+  while (!frontier.empty()) {
+    std::vector<int32_t> round;
+    if (mode == PlanMode::DEPTH) {
+      round = frontier;
+    } else {
+      for (int32_t v : frontier) {
+        if (plan->nodes[v].children.empty()) {
+          round.push_back(v);
+          continue;
+        }
+        // the builder: the node's smallest candidate, down its own path
+        const int32_t bc = plan->nodes[v].cand_min();
+        int32_t x = v;
+        for (;;) {
+          round.push_back(x);
+          const PlanNode& nx = plan->nodes[x];
+          if (std::find(nx.readout.begin(), nx.readout.end(), bc) != nx.readout.end()) break;
+          int32_t down = -1;
+          for (int32_t ch : nx.children) {
+            const auto& cs = plan->nodes[ch].cands;
+            if (std::binary_search(cs.begin(), cs.end(), bc)) {
+              down = ch;
+              break;
+            }
+          }
+          x = down;
+        }
+      }
+    }
+    std::sort(round.begin(), round.end(), by_depth_min);
+    // next: children of this round's nodes that it did not compute
+    std::vector<char> in_round(plan->nodes.size(), 0);
+    for (int32_t i : round) in_round[i] = 1;
+    std::vector<int32_t> next;
+    for (int32_t i : round)
+      for (int32_t c : plan->nodes[i].children)
+        if (!in_round[c]) next.push_back(c);
+    std::sort(next.begin(), next.end(), by_min);
+    plan->rounds.push_back(std::move(round));
     frontier = std::move(next);
-    ++depth;
   }
   int32_t id = 0;
   for (auto& rnd : plan->rounds)

@@ -6,7 +6,7 @@
 // submitted in rounds so that a shared prefix exists before the candidates that
 // reuse it (same page, staged-submission section).  Page size 16 tokens.
 //
-// Rules (the pages leave them open; the same rules are stated in the design doc):
+// Rules (the pages leave them open):
 //  * page allocation: lowest free ids first; every node starts on a fresh page;
 //  * the candidate tree is a compressed, token-granular trie below each
 //    candidate's resident match; a node with children, where no candidate
@@ -149,7 +149,19 @@ struct Plan {
 // untouched) if the pool cannot hold the plan.  Either way the pool ends as it
 // started: the plan's pages live only for the call, and device work of a later
 // call that re-uses them is stream-ordered after this call's.
+// Round orders of a candidate plan.  DEPTH: round k computes the nodes at
+// tree depth k.  CANDIDATE_FIRST (LLM2Jev shared-prefix page,
+// staged-submission section: a real candidate is scored first to build the
+// shared prefix, then the candidates that reuse it are submitted; deeper forks
+// take further rounds and independent branches share one): each round takes
+// every node whose parent is computed; a node without children is computed
+// with all its candidates, while a node with children is computed by one
+// builder, its smallest candidate, whose whole remaining path down to its own
+// read-out node is computed in that round too.  Within a round nodes are in
+// (tree depth, smallest candidate) order.
+enum class PlanMode { DEPTH = 0, CANDIDATE_FIRST = 1 };
+
 bool plan_candidates(const ResidentTree& tree, PagePool* pool, int32_t n, const int32_t* tok,
-                     const int64_t* off, Plan* plan);
+                     const int64_t* off, Plan* plan, PlanMode mode = PlanMode::DEPTH);
 
 }  // namespace jev

@@ -20,12 +20,13 @@ JEV_OK, JEV_EINVAL, JEV_ENOMEM, JEV_EHANDLE, JEV_EHIP, JEV_ESTATE = range(6)
 JEV_DTYPE_F32, JEV_DTYPE_BF16 = 0, 1
 JEV_TAP_ATTN, JEV_TAP_RESID = 0, 1
 JEV_ANSWER_NOUL, JEV_ANSWER_CHOICE, JEV_ANSWER_SCORE = 0, 1, 2
+JEV_PLAN_DEPTH, JEV_PLAN_CANDIDATE_FIRST = 0, 1
 _NAMES = {0: "JEV_OK", 1: "JEV_EINVAL", 2: "JEV_ENOMEM", 3: "JEV_EHANDLE", 4: "JEV_EHIP", 5: "JEV_ESTATE"}
 
 EXPORTED = ["jev_workspace_bytes", "jev_kv_pool_bytes", "jev_create", "jev_destroy", "jev_prefill_prefix",
             "jev_score_branches", "jev_score_candidates", "jev_free_pages", "jev_plan", "jev_page_table",
             "jev_match", "jev_stats", "jev_debug_tap", "jev_profile", "jev_profile_read", "jev_answers",
-            "jev_last_error"]
+            "jev_set_plan_mode", "jev_last_error"]
 KERNELS = ["embed", "rmsnorm", "qkv", "attn", "merge", "oproj", "readout"]
 
 
@@ -91,6 +92,7 @@ def lib() -> ctypes.CDLL:
         L.jev_debug_tap.argtypes = [vp, i32, i32, vp, i64]
         L.jev_profile.argtypes = [vp, ctypes.c_uint32]
         L.jev_profile_read.argtypes = [vp, P(LaunchRecord), i64, P(i64)]
+        L.jev_set_plan_mode.argtypes = [vp, i32]
         L.jev_answers.argtypes = [i32, P(ctypes.c_float), P(i64), P(i32), P(ctypes.c_double), P(i32),
                                   P(ctypes.c_double)]
         L.jev_last_error.restype = ctypes.c_char_p
@@ -251,6 +253,10 @@ class Context:
     def free_pages(self, handles: Sequence[int]) -> None:
         h = _i64(handles)
         _check(lib().jev_free_pages(self.ctx, len(h), _ptr(h, ctypes.c_int64)))
+
+    def set_plan_mode(self, mode: int) -> None:
+        """JEV_PLAN_DEPTH or JEV_PLAN_CANDIDATE_FIRST (jev_set_plan_mode)."""
+        _check(lib().jev_set_plan_mode(self.ctx, mode))
 
     def plan(self, seqs) -> List[int]:
         flat, off = _segments(seqs)

@@ -3,7 +3,7 @@
 This module only draws numbers.  It holds none of the scoring arithmetic, and
 both the oracle and the GPU path take their inputs from it.
 
-Recipe (also stated in the design doc):
+Recipe:
 
 * Weights.  Every weight tensor is filled in row-major order, in chunks of
   ``CHUNK`` elements.  Chunk ``c`` of tensor ``t`` of workload ``w`` is
