@@ -172,6 +172,27 @@ int jev_score_candidates(jev_ctx* ctx, int32_t n, const int32_t* tokens, const i
 enum { JEV_PLAN_DEPTH = 0, JEV_PLAN_CANDIDATE_FIRST = 1 };
 int jev_set_plan_mode(jev_ctx* ctx, int32_t mode);
 
+/* What happens to a prefix whose last caller reference is dropped
+ * (openjev-multimodal performance page, repeated-state section: the KV at the
+ * end of a state is kept for the next request that repeats it, and several
+ * states can be kept and used in turn).
+ *  JEV_CACHE_RELEASE (the default): its pages return to the pool at once
+ *    (once it has no resident child either).
+ *  JEV_CACHE_LRU: it stays resident as a cached prefix.  jev_prefill_prefix of
+ *    the same segment under the same parent re-references it with no
+ *    compute.  A call that is short of free pages evicts cached prefixes that
+ *    have no resident children, least recently used first (ties: the smallest
+ *    handle), never one on the path of a prefix the call uses; it fails with
+ *    JEV_ENOMEM (evicting nothing) if that cannot make room.  An eviction made
+ *    for a call stays even if the call then fails a later capacity check.  A
+ *    prefix is used by a call that creates, re-references, scores under or
+ *    releases a prefix on whose path it lies (jev_plan changes nothing; it
+ *    reports the plan, evictions included, that scoring would run).
+ * Setting JEV_CACHE_RELEASE evicts every cached prefix that can go.
+ * Errors: JEV_EINVAL (NULL ctx, unknown policy). */
+enum { JEV_CACHE_RELEASE = 0, JEV_CACHE_LRU = 1 };
+int jev_set_cache_policy(jev_ctx* ctx, int32_t policy);
+
 /* Drops one caller reference of each handle.  A prefix with no reference and
  * no resident child returns its pages to the pool (its parent may follow).
  * Pages are re-used only by later calls, which the library orders after the
@@ -207,8 +228,11 @@ typedef struct {
   int32_t rounds;           /* rounds of the last call */
   int32_t pages_in_use;
   int32_t pages_total;
-  int32_t resident_prefixes;
+  int32_t resident_prefixes;  /* resident prefixes, cached ones included */
   int64_t calls;
+  int32_t cached_prefixes;    /* resident prefixes without caller references (cache policy) */
+  int32_t cached_pages;       /* pages they hold (counted in pages_in_use) */
+  int64_t evictions;          /* cached prefixes evicted so far */
 } jev_stats_t;
 
 int jev_stats(jev_ctx* ctx, jev_stats_t* out);

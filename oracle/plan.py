@@ -87,6 +87,7 @@ class ResNode:
     start: int             # logical position of the first token
     refs: int = 1
     children: List[int] = field(default_factory=list)   # handles, creation order
+    last_use: int = 0     # stamp of the last call that used the node
 
 
 class ResidentTree:
@@ -97,6 +98,8 @@ class ResidentTree:
         self.nodes: Dict[int, ResNode] = {}
         self.root_children: List[int] = []
         self.next_handle = 1
+        self.keep = False      # cache policy: keep prefixes whose last reference is dropped
+        self.evictions = 0
 
     def _children(self, parent: int) -> List[int]:
         return self.root_children if parent == 0 else self.nodes[parent].children
@@ -159,15 +162,49 @@ class ResidentTree:
         return None
 
     def release(self, h: int) -> None:
-        """Drops one caller reference; frees nodes left with no reference and no child."""
+        """Drops one caller reference; without the cache policy, frees nodes
+        left with no reference and no child."""
         n = self.nodes[h]
         n.refs -= 1
+        if self.keep:
+            return
         while n is not None and n.refs == 0 and not n.children:
             self.pool.release(n.pages)
             del self.nodes[n.handle]
             sib = self._children(n.parent)
             sib.remove(n.handle)
             n = self.nodes.get(n.parent)
+
+    # ---- cache policy (openjev-multimodal performance page, repeated-state
+    # section: a state's KV is kept for the next request that repeats it, and
+    # several states can be kept and used in turn).  Reading: a cached prefix
+    # (no caller reference) without resident children may be evicted when a
+    # call is short of pages, least recently used first, ties to the smallest
+    # handle, never one on the path of a prefix the call uses.
+
+    def path(self, h: int) -> List[int]:
+        out = []
+        while h != 0:
+            out.append(h)
+            h = self.nodes[h].parent
+        return out
+
+    def stamp(self, handles: Sequence[int], t: int) -> None:
+        for h in handles:
+            for x in self.path(h):
+                self.nodes[x].last_use = t
+
+    def victim(self, pinned: set) -> Optional[int]:
+        cands = [n for n in self.nodes.values() if n.refs == 0 and not n.children and n.handle not in pinned]
+        if not cands:
+            return None
+        return min(cands, key=lambda n: (n.last_use, n.handle)).handle
+
+    def evict(self, h: int) -> None:
+        n = self.nodes.pop(h)
+        self.pool.release(n.pages)
+        self._children(n.parent).remove(h)
+        self.evictions += 1
 
     def match(self, seq: Sequence[int]) -> Tuple[int, int]:
         """Deepest resident node whose whole path is a prefix of seq with at
@@ -387,3 +424,100 @@ def branch_pages(tree: ResidentTree, parents: Sequence[int],
     for p in out:
         tree.pool.release(p)
     return out
+
+
+class Session:
+    """Call-level model of the host library's resident state: the tree, the
+    cache policy, the plan mode and one recency stamp per call."""
+
+    def __init__(self, n_pages: int, mode: str = "depth", keep: bool = False):
+        self.tree = ResidentTree(PagePool(n_pages))
+        self.tree.keep = keep
+        self.mode = mode
+        self.clock = 0
+
+    def _copy(self) -> "ResidentTree":
+        import copy
+        return copy.deepcopy(self.tree)
+
+    def _room(self, pinned: set, fits) -> None:
+        """Evicts cached prefixes (found on a copy first) until fits(tree)."""
+        if fits(self.tree):
+            return
+        if not self.tree.keep:
+            raise PoolExhausted(0)
+        t = self._copy()
+        victims = []
+        while not fits(t):
+            v = t.victim(pinned)
+            if v is None:
+                raise PoolExhausted(0)
+            t.evict(v)
+            victims.append(v)
+        for v in victims:
+            self.tree.evict(v)
+
+    def _pins(self, handles: Sequence[int]) -> set:
+        return {x for h in handles for x in self.tree.path(h)}
+
+    def prefill(self, items: Sequence[Tuple[int, Sequence[int]]]) -> List[int]:
+        used = []
+        for parent, toks in items:
+            used.append(parent)
+            c = self.tree._find_child(parent, tuple(int(t) for t in toks))
+            if c is not None:
+                used.append(c)
+
+        def fits(t: ResidentTree) -> bool:
+            need, seen = 0, set()
+            for parent, toks in items:
+                key = (parent, tuple(int(x) for x in toks))
+                if t._find_child(parent, key[1]) is None and key not in seen:
+                    seen.add(key)
+                    need += n_pages_for(len(toks))
+            return need <= t.pool.n_free()
+
+        self._room(self._pins(used), fits)
+        out = self.tree.prefill(items)
+        self.clock += 1
+        self.tree.stamp(out, self.clock)
+        return out
+
+    def release(self, handles: Sequence[int]) -> None:
+        self.clock += 1
+        for h in handles:
+            self.tree.stamp([h], self.clock)
+            self.tree.release(h)
+
+    def _plan_pins(self, tree: ResidentTree, seqs) -> set:
+        return {x for s in seqs for x in tree.path(tree.match(s)[0])}
+
+    def plan(self, seqs) -> Plan:
+        """The plan scoring would run now, evictions included; changes nothing."""
+        t = self._copy()
+        pins = self._plan_pins(t, seqs)
+        while True:
+            try:
+                return plan_candidates(t, seqs, self.mode)
+            except PoolExhausted:
+                v = t.victim(pins) if t.keep else None
+                if v is None:
+                    raise
+                t.evict(v)
+
+    def set_keep(self, keep: bool) -> None:
+        self.tree.keep = keep
+        if not keep:
+            while True:
+                v = self.tree.victim(set())
+                if v is None:
+                    break
+                self.tree.evict(v)
+
+    def stats(self) -> Dict[str, int]:
+        nodes = self.tree.nodes.values()
+        return {"pages_in_use": self.tree.pool.n_pages - self.tree.pool.n_free(),
+                "resident_prefixes": len(self.tree.nodes),
+                "cached_prefixes": sum(1 for n in nodes if n.refs == 0),
+                "cached_pages": sum(len(n.pages) for n in nodes if n.refs == 0),
+                "evictions": self.tree.evictions}

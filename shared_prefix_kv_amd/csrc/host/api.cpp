@@ -157,6 +157,7 @@ struct jev_ctx {
   bool dry = true;
   bool dead = false;
   jev::PlanMode plan_mode = jev::PlanMode::DEPTH;
+  uint64_t clock = 0;  // stamp of the last call (cache recency)
   jev::ModelDims dims{};
   std::vector<jev::LayerW> layers;
   const void* embed = nullptr;
@@ -203,6 +204,55 @@ int check_alive(jev_ctx* ctx) {
   if (!ctx) return fail(JEV_EINVAL, "ctx is NULL");
   if (ctx->dead) return fail(JEV_EHIP, "context is unusable after an earlier HIP failure");
   return JEV_OK;
+}
+
+// Handles on the root..h paths of `hs`: prefixes a call uses, never evicted by it.
+std::set<int64_t> path_set(const jev::ResidentTree& t, const std::vector<int64_t>& hs) {
+  std::set<int64_t> out;
+  for (int64_t h : hs)
+    for (; h != 0 && !out.count(h); h = t.node(h).parent) out.insert(h);
+  return out;
+}
+
+// Makes room for a call that does not fit: with the cache policy on, evicts
+// cached prefixes (least recently used first, none in `pinned`) until
+// fits(tree, pool) holds.  The victims are found on copies and applied only if
+// they suffice; otherwise JEV_ENOMEM and nothing changes.
+template <typename Fits>
+int make_room(jev_ctx* ctx, const std::set<int64_t>& pinned, Fits fits, const char* what) {
+  if (fits(*ctx->tree, ctx->pages)) return JEV_OK;  // a plan trial leaves the pool as it found it
+  if (!ctx->tree->keep()) return fail(JEV_ENOMEM, what);
+  jev::PagePool pool = ctx->pages;
+  jev::ResidentTree tree = *ctx->tree;
+  tree.rebind(&pool);
+  std::vector<int64_t> victims;
+  while (!fits(tree, pool)) {
+    const int64_t v = tree.evict_one(pinned);
+    if (v == 0) return fail(JEV_ENOMEM, what);
+    victims.push_back(v);
+  }
+  for (int64_t v : victims) ctx->tree->evict(v);
+  return JEV_OK;
+}
+
+// Resident prefixes the candidates of a plan continue (their match paths).
+std::set<int64_t> plan_pins(const jev::ResidentTree& t, int32_t n, const int32_t* tok, const int64_t* off) {
+  std::vector<int64_t> used;
+  for (int32_t c = 0; c < n; ++c) {
+    int64_t h, m;
+    t.match(tok + off[c], off[c + 1] - off[c], &h, &m);
+    used.push_back(h);
+  }
+  return path_set(t, used);
+}
+
+int make_room_for_plan(jev_ctx* ctx, int32_t n, const int32_t* tok, const int64_t* off) {
+  return make_room(ctx, plan_pins(*ctx->tree, n, tok, off),
+                   [&](const jev::ResidentTree& t, jev::PagePool& p) {
+                     jev::Plan trial;
+                     return jev::plan_candidates(t, &p, n, tok, off, &trial, ctx->plan_mode);
+                   },
+                   "not enough free KV pages for the plan");
 }
 
 int check_segments(const jev_ctx* ctx, int32_t n, const int32_t* tokens, const int64_t* off, const char* what) {
@@ -683,7 +733,19 @@ int jev_prefill_prefix(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const
       return fail(JEV_EINVAL, "prefix " + std::to_string(i) + " runs past max_positions");
     items.push_back({parents[i], tokens + offsets[i], len});
   }
-  if (ctx->tree->prefill_need(items) > ctx->pages.n_free()) return fail(JEV_ENOMEM, "not enough free KV pages");
+  {
+    std::vector<int64_t> used;
+    for (const auto& it : items) {
+      used.push_back(it.parent);
+      if (int64_t c = ctx->tree->find_child(it.parent, it.tok, it.n)) used.push_back(c);
+    }
+    if (int rc = make_room(ctx, path_set(*ctx->tree, used),
+                           [&](const jev::ResidentTree& t, jev::PagePool& p) {
+                             return t.prefill_need(items) <= p.n_free();
+                           },
+                           "not enough free KV pages"))
+      return rc;
+  }
   // Simulate the allocation tree->prefill() will make (new nodes take the
   // lowest free ids in input order; an identical resident child or an earlier
   // identical item of this call creates nothing), so that descriptors are built
@@ -725,7 +787,11 @@ int jev_prefill_prefix(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const
   std::vector<int64_t> handles;
   std::vector<char> created;
   ctx->tree->prefill(items, &handles, &created);
-  for (int32_t i = 0; i < n; ++i) out_handles[i] = handles[i];
+  ctx->clock += 1;
+  for (int32_t i = 0; i < n; ++i) {
+    out_handles[i] = handles[i];
+    ctx->tree->touch_path(handles[i], ctx->clock);
+  }
   ctx->stats.logical_tokens = computed;
   ctx->stats.computed_tokens = computed;
   ctx->stats.cached_tokens = 0;
@@ -756,7 +822,13 @@ int jev_score_branches(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const
     need += jev::pages_for(len);
     logical += ctx->tree->end_pos(parents[i]) + len;
   }
-  if (need > ctx->pages.n_free()) return fail(JEV_ENOMEM, "not enough free KV pages");
+  const std::vector<int64_t> used(parents, parents + n);
+  if (int rc = make_room(ctx, path_set(*ctx->tree, used),
+                         [&](const jev::ResidentTree&, jev::PagePool& p) { return need <= p.n_free(); },
+                         "not enough free KV pages"))
+    return rc;
+  ctx->clock += 1;
+  for (int64_t h : used) ctx->tree->touch_path(h, ctx->clock);
   std::set<int32_t> snap = ctx->pages.snapshot();
   std::vector<RNode> rn;
   std::map<int64_t, std::vector<jev::PageRef>> anc_cache;
@@ -802,8 +874,11 @@ int jev_score_candidates(jev_ctx* ctx, int32_t n, const int32_t* tokens, const i
     if (tok_offsets[i + 1] - tok_offsets[i] > ctx->desc.max_positions)
       return fail(JEV_EINVAL, "candidate " + std::to_string(i) + " runs past max_positions");
   jev::Plan plan;
+  if (int rc = make_room_for_plan(ctx, n, tokens, tok_offsets)) return rc;
   if (!jev::plan_candidates(*ctx->tree, &ctx->pages, n, tokens, tok_offsets, &plan, ctx->plan_mode))
     return fail(JEV_ENOMEM, "not enough free KV pages for the plan");
+  ctx->clock += 1;
+  for (int64_t h : plan.anchors) ctx->tree->touch_path(h, ctx->clock);
   // rounds
   std::vector<std::vector<RNode>> rounds(plan.rounds.size());
   std::map<int64_t, std::vector<jev::PageRef>> anchor_pages;
@@ -863,6 +938,16 @@ int jev_set_plan_mode(jev_ctx* ctx, int32_t mode) {
   return JEV_OK;
 }
 
+int jev_set_cache_policy(jev_ctx* ctx, int32_t policy) {
+  if (!ctx) return fail(JEV_EINVAL, "ctx is NULL");
+  if (policy != JEV_CACHE_RELEASE && policy != JEV_CACHE_LRU) return fail(JEV_EINVAL, "unknown cache policy");
+  ctx->tree->set_keep(policy == JEV_CACHE_LRU);
+  if (policy == JEV_CACHE_RELEASE)
+    while (ctx->tree->evict_one({}) != 0) {
+    }
+  return JEV_OK;
+}
+
 int jev_free_pages(jev_ctx* ctx, int32_t n, const jev_prefix* handles) {
   if (!ctx) return fail(JEV_EINVAL, "ctx is NULL");
   if (n < 0 || (n > 0 && !handles)) return fail(JEV_EINVAL, "bad handle array");
@@ -875,7 +960,11 @@ int jev_free_pages(jev_ctx* ctx, int32_t n, const jev_prefix* handles) {
   }
   for (auto& kv : count)
     if (ctx->tree->node(kv.first).refs < kv.second) return fail(JEV_EHANDLE, "handle released more times than held");
-  for (int32_t i = 0; i < n; ++i) ctx->tree->release(handles[i]);
+  ctx->clock += 1;
+  for (int32_t i = 0; i < n; ++i) {
+    ctx->tree->touch_path(handles[i], ctx->clock);
+    ctx->tree->release(handles[i]);
+  }
   return JEV_OK;
 }
 
@@ -884,8 +973,18 @@ int jev_plan(jev_ctx* ctx, int32_t n, const int32_t* tokens, const int64_t* tok_
   if (!ctx || !out_len) return fail(JEV_EINVAL, "NULL ctx/out_len");
   if (int rc = check_segments(ctx, n, tokens, tok_offsets, "candidates")) return rc;
   jev::Plan plan;
-  if (n > 0 && !jev::plan_candidates(*ctx->tree, &ctx->pages, n, tokens, tok_offsets, &plan, ctx->plan_mode))
-    return fail(JEV_ENOMEM, "not enough free KV pages for the plan");
+  if (n > 0) {
+    // what jev_score_candidates would do, evictions included, on copies
+    jev::PagePool pool = ctx->pages;
+    jev::ResidentTree tree = *ctx->tree;
+    tree.rebind(&pool);
+    const std::set<int64_t> pinned = plan_pins(tree, n, tokens, tok_offsets);
+    bool ok;
+    while (!(ok = jev::plan_candidates(tree, &pool, n, tokens, tok_offsets, &plan, ctx->plan_mode)) &&
+           tree.keep() && tree.evict_one(pinned) != 0) {
+    }
+    if (!ok) return fail(JEV_ENOMEM, "not enough free KV pages for the plan");
+  }
   std::vector<int32_t> s = n > 0 ? plan.serialize() : std::vector<int32_t>{0, 0};
   *out_len = int64_t(s.size());
   if (!out) return JEV_OK;
@@ -921,6 +1020,9 @@ int jev_stats(jev_ctx* ctx, jev_stats_t* out) {
   ctx->stats.pages_total = ctx->pages.n_total();
   ctx->stats.pages_in_use = ctx->pages.n_total() - ctx->pages.n_free();
   ctx->stats.resident_prefixes = ctx->tree->size();
+  ctx->stats.cached_prefixes = ctx->tree->cached_count();
+  ctx->stats.cached_pages = ctx->tree->cached_pages();
+  ctx->stats.evictions = ctx->tree->evictions();
   *out = ctx->stats;
   return JEV_OK;
 }

@@ -84,6 +84,7 @@ void ResidentTree::prefill(const std::vector<PrefillItem>& items, std::vector<in
 void ResidentTree::release(int64_t h) {
   ResNode* n = &nodes_.at(h);
   n->refs -= 1;
+  if (keep_) return;
   while (n != nullptr && n->refs == 0 && n->children.empty()) {
     pool_->release(n->pages);
     int64_t parent = n->parent;
@@ -92,6 +93,53 @@ void ResidentTree::release(int64_t h) {
     nodes_.erase(n->handle);
     n = parent == 0 ? nullptr : &nodes_.at(parent);
   }
+}
+
+void ResidentTree::touch_path(int64_t h, uint64_t stamp) {
+  for (; h != 0; h = nodes_.at(h).parent) nodes_.at(h).last_use = stamp;
+}
+
+int64_t ResidentTree::evict_one(const std::set<int64_t>& pinned) {
+  int64_t best = 0;
+  uint64_t best_use = 0;
+  for (const auto& kv : nodes_) {  // ascending handles: the first of equal stamps wins
+    const ResNode& n = kv.second;
+    if (n.refs != 0 || !n.children.empty() || pinned.count(n.handle)) continue;
+    if (best == 0 || n.last_use < best_use) {
+      best = n.handle;
+      best_use = n.last_use;
+    }
+  }
+  if (best != 0) evict(best);
+  return best;
+}
+
+void ResidentTree::evict(int64_t h) {
+  ResNode& n = nodes_.at(h);
+  pool_->release(n.pages);
+  auto& sib = children_mut(n.parent);
+  sib.erase(std::find(sib.begin(), sib.end(), h));
+  nodes_.erase(h);
+  evictions_ += 1;
+}
+
+int32_t ResidentTree::cached_count() const {
+  int32_t k = 0;
+  for (const auto& kv : nodes_) k += kv.second.refs == 0;
+  return k;
+}
+
+int32_t ResidentTree::cached_pages() const {
+  int32_t k = 0;
+  for (const auto& kv : nodes_)
+    if (kv.second.refs == 0) k += int32_t(kv.second.pages.size());
+  return k;
+}
+
+int32_t ResidentTree::pages_held() const {
+  int32_t k = 0;
+  for (const auto& kv : nodes_) k += int32_t(kv.second.pages.size());
+  return k;
 }
 
 void ResidentTree::match(const int32_t* seq, int64_t n, int64_t* handle, int64_t* matched) const {

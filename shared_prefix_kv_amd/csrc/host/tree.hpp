@@ -69,6 +69,7 @@ struct ResNode {
   std::vector<int32_t> pages;
   int64_t start = 0;   // logical position of tokens[0]
   int64_t refs = 1;
+  uint64_t last_use = 0;           // stamp of the last call that used the node
   std::vector<int64_t> children;  // creation order
 };
 
@@ -78,9 +79,20 @@ struct PageRef {
   int32_t valid;
 };
 
+// Cache policy of unreferenced prefixes (openjev-multimodal performance page,
+// repeated-state section: a state's KV is kept for the next request, and
+// several states can be kept and used in turn).  With keep() set, a prefix
+// whose last caller reference is dropped stays resident as a cached prefix; a
+// call that is short of pages evicts cached prefixes that have no children,
+// least recently used first (ties: the smallest handle), never one on the
+// path of a prefix the call uses.  A node's last use is the stamp of the last
+// call that created, re-referenced, scored under or released a prefix whose
+// path contains it.
 class ResidentTree {
  public:
   explicit ResidentTree(PagePool* pool) : pool_(pool) {}
+  // Points a copy of the tree at a copy of its pool (for dry runs).
+  void rebind(PagePool* pool) { pool_ = pool; }
 
   bool has(int64_t h) const { return h == 0 || nodes_.count(h) != 0; }
   const ResNode& node(int64_t h) const { return nodes_.at(h); }
@@ -100,8 +112,23 @@ class ResidentTree {
   // whether it is new.  Caller has checked prefill_need() against the pool.
   void prefill(const std::vector<PrefillItem>& items, std::vector<int64_t>* out,
                std::vector<char>* created);
-  // Drops one reference; frees nodes with no reference and no child.
+  // Drops one reference; without keep(), frees nodes with no reference and no child.
   void release(int64_t h);
+  void set_keep(bool keep) { keep_ = keep; }
+  bool keep() const { return keep_; }
+  // Marks every node on the root..h path as used at `stamp`.
+  void touch_path(int64_t h, uint64_t stamp);
+  // Evicts the least recently used cached node without children that is not
+  // in `pinned`; returns its handle, or 0 if there is none.
+  int64_t evict_one(const std::set<int64_t>& pinned);
+  // Evicts node h (a cached node without children).
+  void evict(int64_t h);
+  int64_t evictions() const { return evictions_; }
+  int32_t cached_count() const;
+  int32_t cached_pages() const;
+  int32_t pages_held() const;
+  // The child of `parent` whose segment is exactly tok[0..n), or 0.
+  int64_t find_child(int64_t parent, const int32_t* tok, int64_t n) const;
   // Deepest full-node match leaving >= 1 token.
   void match(const int32_t* seq, int64_t n, int64_t* handle, int64_t* matched) const;
 
@@ -112,12 +139,13 @@ class ResidentTree {
   std::vector<int64_t>& children_mut(int64_t parent) {
     return parent == 0 ? root_children_ : nodes_.at(parent).children;
   }
-  int64_t find_child(int64_t parent, const int32_t* tok, int64_t n) const;
 
   PagePool* pool_;
   std::map<int64_t, ResNode> nodes_;
   std::vector<int64_t> root_children_;
   int64_t next_handle_ = 1;
+  bool keep_ = false;
+  int64_t evictions_ = 0;
 };
 
 struct PlanNode {

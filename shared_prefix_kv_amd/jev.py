@@ -21,12 +21,13 @@ JEV_DTYPE_F32, JEV_DTYPE_BF16 = 0, 1
 JEV_TAP_ATTN, JEV_TAP_RESID = 0, 1
 JEV_ANSWER_NOUL, JEV_ANSWER_CHOICE, JEV_ANSWER_SCORE = 0, 1, 2
 JEV_PLAN_DEPTH, JEV_PLAN_CANDIDATE_FIRST = 0, 1
+JEV_CACHE_RELEASE, JEV_CACHE_LRU = 0, 1
 _NAMES = {0: "JEV_OK", 1: "JEV_EINVAL", 2: "JEV_ENOMEM", 3: "JEV_EHANDLE", 4: "JEV_EHIP", 5: "JEV_ESTATE"}
 
 EXPORTED = ["jev_workspace_bytes", "jev_kv_pool_bytes", "jev_create", "jev_destroy", "jev_prefill_prefix",
             "jev_score_branches", "jev_score_candidates", "jev_free_pages", "jev_plan", "jev_page_table",
             "jev_match", "jev_stats", "jev_debug_tap", "jev_profile", "jev_profile_read", "jev_answers",
-            "jev_set_plan_mode", "jev_last_error"]
+            "jev_set_plan_mode", "jev_set_cache_policy", "jev_last_error"]
 KERNELS = ["embed", "rmsnorm", "qkv", "attn", "merge", "oproj", "readout"]
 
 
@@ -58,7 +59,8 @@ class LaunchRecord(ctypes.Structure):
 class Stats(ctypes.Structure):
     _fields_ = [("logical_tokens", ctypes.c_int64), ("computed_tokens", ctypes.c_int64),
                 ("cached_tokens", ctypes.c_int64), ("rounds", ctypes.c_int32), ("pages_in_use", ctypes.c_int32),
-                ("pages_total", ctypes.c_int32), ("resident_prefixes", ctypes.c_int32), ("calls", ctypes.c_int64)]
+                ("pages_total", ctypes.c_int32), ("resident_prefixes", ctypes.c_int32), ("calls", ctypes.c_int64),
+                ("cached_prefixes", ctypes.c_int32), ("cached_pages", ctypes.c_int32), ("evictions", ctypes.c_int64)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -93,6 +95,7 @@ def lib() -> ctypes.CDLL:
         L.jev_profile.argtypes = [vp, ctypes.c_uint32]
         L.jev_profile_read.argtypes = [vp, P(LaunchRecord), i64, P(i64)]
         L.jev_set_plan_mode.argtypes = [vp, i32]
+        L.jev_set_cache_policy.argtypes = [vp, i32]
         L.jev_answers.argtypes = [i32, P(ctypes.c_float), P(i64), P(i32), P(ctypes.c_double), P(i32),
                                   P(ctypes.c_double)]
         L.jev_last_error.restype = ctypes.c_char_p
@@ -257,6 +260,10 @@ class Context:
     def set_plan_mode(self, mode: int) -> None:
         """JEV_PLAN_DEPTH or JEV_PLAN_CANDIDATE_FIRST (jev_set_plan_mode)."""
         _check(lib().jev_set_plan_mode(self.ctx, mode))
+
+    def set_cache_policy(self, policy: int) -> None:
+        """JEV_CACHE_RELEASE or JEV_CACHE_LRU (jev_set_cache_policy)."""
+        _check(lib().jev_set_cache_policy(self.ctx, policy))
 
     def plan(self, seqs) -> List[int]:
         flat, off = _segments(seqs)

@@ -99,6 +99,40 @@ def test_w1_answers_of_scored_branches(w1):
                 assert choice[i] == oa.choice(ref[i])[0]
 
 
+def test_w1_rotating_states_under_the_lru_cache(w1):
+    """Three 128-token states in turn through a pool that holds two of them
+    plus the branch pages (openjev-multimodal performance page, repeated-state
+    section).  A cached state is re-used with no compute, an evicted one is
+    recomputed into re-used pages, and every scoring matches the oracle."""
+    from shared_prefix_kv_amd import jev
+    wl, inst, m, ref, _, wd = w1
+    P = inst.prefixes[0]
+    rng = np.random.default_rng(77)
+    others = [list(rng.integers(0, wl.model.vocab, len(P))) for _ in range(2)]
+    ctx, _ = device_context(1, n_pages=2 * 8 + 4, max_pos=1024, max_tok=1024, weights_dev=wd)
+    ctx.set_cache_policy(jev.JEV_CACHE_LRU)
+    br = inst.passes[0]
+
+    def score_p():
+        (h,) = ctx.prefill_prefix([0], [P])
+        computed = ctx.stats()["computed_tokens"]
+        probs, loff = ctx.score_branches([h] * len(br), [b.tokens for b in br], [b.labels for b in br])
+        _sync()
+        assert max_abs(split_probs(probs, loff), ref) <= TOL_F32
+        ctx.free_pages([h])
+        return computed
+
+    assert score_p() == len(P)                  # cold
+    assert score_p() == 0                       # cached: no compute
+    for s in others:                            # the second one evicts P
+        (h,) = ctx.prefill_prefix([0], [s])
+        ctx.free_pages([h])
+    assert ctx.stats()["evictions"] == 1
+    assert score_p() == len(P)                  # recomputed, evicting the oldest other state
+    assert ctx.stats()["evictions"] == 2 and ctx.stats()["cached_prefixes"] == 2
+    assert score_p() == 0
+
+
 def test_w1_unshared_and_candidate_paths_match_oracle(w1):
     wl, inst, m, ref, ctx, _ = w1
     seqs = inst.full_sequences(0)
