@@ -285,12 +285,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __syncthreads();  // page list
   pw = sP[min(lane, tile.n_pages - 1)];
   if (nst > 0) {
+    // K and V of step 0 and K of step 1 in flight together (one load latency)
     gload_k(0, rkA);
     gload_v(0, rvA);
+    gload_k(1, rkB);
     sstore_k(0, rkA);
     sstore_v(0, rvA);
-    gload_k(1, rkA);
-    sstore_k(1, rkA);
+    sstore_k(1, rkB);
     // staged for the first step's stores: K of step 2, V of step 1
     gload_k(2, rkA);
     gload_v(1, rvA);
