@@ -299,6 +299,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __syncthreads();
   f32x16 SA, SB;
   if (nst > 0) SA = qk(0);
+  // step 0 stores K of step 2 into K buffer 0: every wave has to be done
+  // reading K of step 0 from it first (once per tile)
+  if (nst > 2) __syncthreads();
   // One step: stores K of step st+2 and V of step st+1 from (kst, vst), loads
   // K of step st+3 and V of step st+2 into (kld, vld), turns S_in (scores of
   // step st) into probabilities and leaves the scores of step st+1 in S_out.
