@@ -147,7 +147,11 @@ int jev_score_branches(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const
 
 /* Scores n candidates given as full token sequences (LLM2Jev shared-prefix page,
  * staged-submission section).  Each candidate is matched against the resident
- * prefixes (longest full-node match leaving at least one token), the rest are
+ * prefixes (longest full-node match leaving at least one token; where it leaves
+ * a resident node inside it after at least one whole page, that node is split
+ * at the last page boundary before the divergence and the candidate reuses the
+ * pages before it (the split stays; the node's handle keeps the rest and still
+ * names the whole prefix)), the rest are
  * grouped into a token-prefix tree and computed in staged rounds whose order
  * is the context's plan mode (jev_set_plan_mode); every candidate is read out
  * exactly once; probs as for jev_score_branches, in input order.  Pages of the

@@ -41,6 +41,13 @@ Readings (the pages leave these open):
 * Resident match: walk resident nodes from the root, taking the longest child
   segment that matches in full and still leaves at least one token (the last
   scored position must be computed).
+* Reuse inside a resident node (a scoring or planning call over full
+  candidates): where no child continues in full, the child sharing the
+  longest run rounded down to whole pages (at least one page, leaving at
+  least one token; ties to the earliest created) is split at that page
+  boundary, and the candidate continues the first part.  The split keeps the
+  original handle, references and children on the second part.  Candidates are
+  resolved in input order, each on the tree the earlier ones left.
 """
 from __future__ import annotations
 
@@ -205,6 +212,43 @@ class ResidentTree:
         self.pool.release(n.pages)
         self._children(n.parent).remove(h)
         self.evictions += 1
+
+    def split(self, h: int, at: int) -> int:
+        """First `at` tokens (whole pages) of node h become a new node in its
+        place; h keeps the rest below it.  Returns the new handle."""
+        tail = self.nodes[h]
+        nh = self.next_handle
+        self.next_handle += 1
+        head = ResNode(nh, tail.parent, tail.tokens[:at], tail.pages[:at // PAGE], tail.start, refs=0,
+                       children=[h], last_use=tail.last_use)
+        sib = self._children(tail.parent)
+        sib[sib.index(h)] = nh
+        tail.parent = nh
+        tail.tokens = tail.tokens[at:]
+        tail.pages = tail.pages[at // PAGE:]
+        tail.start += at
+        self.nodes[nh] = head
+        return nh
+
+    def match_split(self, seq: Sequence[int]) -> Tuple[int, int]:
+        """match(), then page-aligned reuse inside the child that shares the
+        longest whole-page run below it (splitting that child)."""
+        h, pos = self.match(seq)
+        rest = [int(t) for t in seq[pos:len(seq) - 1]]     # the last token is always computed
+        choice, reuse = None, 0
+        for c in self._children(h):
+            t = self.nodes[c].tokens
+            common = 0
+            for a, b in zip(t, rest):
+                if a != b:
+                    break
+                common += 1
+            pages = common // PAGE * PAGE
+            if PAGE <= pages < len(t) and pages > reuse:
+                choice, reuse = c, pages
+        if choice is None:
+            return h, pos
+        return self.split(choice, reuse), pos + reuse
 
     def match(self, seq: Sequence[int]) -> Tuple[int, int]:
         """Deepest resident node whose whole path is a prefix of seq with at
@@ -413,6 +457,17 @@ def plan_candidates(tree: ResidentTree, seqs: Sequence[Sequence[int]], mode: str
     return Plan(levels, anchors, alen, readout_node, released)
 
 
+def plan_with_reuse(tree: ResidentTree, seqs: Sequence[Sequence[int]], mode: str = "depth") -> Plan:
+    """The plan of a scoring call, on a copy of the tree: anchors resolved with
+    reuse inside resident nodes (splits), then plan_candidates.  The given
+    tree and its pool are left unchanged."""
+    import copy
+    t = copy.deepcopy(tree)
+    for s in seqs:
+        t.match_split(s)
+    return plan_candidates(t, seqs, mode)
+
+
 def branch_pages(tree: ResidentTree, parents: Sequence[int],
                  suffixes: Sequence[Sequence[int]]) -> List[List[int]]:
     """Pages of one explicit scoring call: each branch is a new leaf under its
@@ -493,8 +548,11 @@ class Session:
         return {x for s in seqs for x in tree.path(tree.match(s)[0])}
 
     def plan(self, seqs) -> Plan:
-        """The plan scoring would run now, evictions included; changes nothing."""
+        """The plan scoring would run now, splits and evictions included;
+        changes nothing."""
         t = self._copy()
+        for s in seqs:
+            t.match_split(s)
         pins = self._plan_pins(t, seqs)
         while True:
             try:

@@ -246,13 +246,24 @@ std::set<int64_t> plan_pins(const jev::ResidentTree& t, int32_t n, const int32_t
   return path_set(t, used);
 }
 
-int make_room_for_plan(jev_ctx* ctx, int32_t n, const int32_t* tok, const int64_t* off) {
-  return make_room(ctx, plan_pins(*ctx->tree, n, tok, off),
-                   [&](const jev::ResidentTree& t, jev::PagePool& p) {
-                     jev::Plan trial;
-                     return jev::plan_candidates(t, &p, n, tok, off, &trial, ctx->plan_mode);
-                   },
-                   "not enough free KV pages for the plan");
+// The tree work of a candidate call, on copies of the tree and pool: each
+// candidate in input order takes its anchor (splitting a resident node at a
+// page boundary where it diverges inside it), then cached prefixes are evicted
+// (cache policy) until the plan fits.  The caller commits the copies or drops
+// them.
+int stage_candidates(jev_ctx* ctx, int32_t n, const int32_t* tok, const int64_t* off, jev::PagePool* pool,
+                     jev::ResidentTree* tree, jev::Plan* plan) {
+  *pool = ctx->pages;
+  *tree = *ctx->tree;
+  tree->rebind(pool);
+  for (int32_t c = 0; c < n; ++c) {
+    int64_t h, m;
+    tree->match_split(tok + off[c], off[c + 1] - off[c], &h, &m);
+  }
+  const std::set<int64_t> pinned = plan_pins(*tree, n, tok, off);
+  while (!jev::plan_candidates(*tree, pool, n, tok, off, plan, ctx->plan_mode))
+    if (!tree->keep() || tree->evict_one(pinned) == 0) return fail(JEV_ENOMEM, "not enough free KV pages for the plan");
+  return JEV_OK;
 }
 
 int check_segments(const jev_ctx* ctx, int32_t n, const int32_t* tokens, const int64_t* off, const char* what) {
@@ -874,9 +885,14 @@ int jev_score_candidates(jev_ctx* ctx, int32_t n, const int32_t* tokens, const i
     if (tok_offsets[i + 1] - tok_offsets[i] > ctx->desc.max_positions)
       return fail(JEV_EINVAL, "candidate " + std::to_string(i) + " runs past max_positions");
   jev::Plan plan;
-  if (int rc = make_room_for_plan(ctx, n, tokens, tok_offsets)) return rc;
-  if (!jev::plan_candidates(*ctx->tree, &ctx->pages, n, tokens, tok_offsets, &plan, ctx->plan_mode))
-    return fail(JEV_ENOMEM, "not enough free KV pages for the plan");
+  {
+    jev::PagePool pool;
+    jev::ResidentTree tree(&pool);
+    if (int rc = stage_candidates(ctx, n, tokens, tok_offsets, &pool, &tree, &plan)) return rc;
+    ctx->pages = pool;
+    *ctx->tree = std::move(tree);
+    ctx->tree->rebind(&ctx->pages);
+  }
   ctx->clock += 1;
   for (int64_t h : plan.anchors) ctx->tree->touch_path(h, ctx->clock);
   // rounds
@@ -974,16 +990,10 @@ int jev_plan(jev_ctx* ctx, int32_t n, const int32_t* tokens, const int64_t* tok_
   if (int rc = check_segments(ctx, n, tokens, tok_offsets, "candidates")) return rc;
   jev::Plan plan;
   if (n > 0) {
-    // what jev_score_candidates would do, evictions included, on copies
-    jev::PagePool pool = ctx->pages;
-    jev::ResidentTree tree = *ctx->tree;
-    tree.rebind(&pool);
-    const std::set<int64_t> pinned = plan_pins(tree, n, tokens, tok_offsets);
-    bool ok;
-    while (!(ok = jev::plan_candidates(tree, &pool, n, tokens, tok_offsets, &plan, ctx->plan_mode)) &&
-           tree.keep() && tree.evict_one(pinned) != 0) {
-    }
-    if (!ok) return fail(JEV_ENOMEM, "not enough free KV pages for the plan");
+    // what jev_score_candidates would do (splits and evictions included), on copies
+    jev::PagePool pool;
+    jev::ResidentTree tree(&pool);
+    if (int rc = stage_candidates(ctx, n, tokens, tok_offsets, &pool, &tree, &plan)) return rc;
   }
   std::vector<int32_t> s = n > 0 ? plan.serialize() : std::vector<int32_t>{0, 0};
   *out_len = int64_t(s.size());

@@ -95,6 +95,51 @@ void ResidentTree::release(int64_t h) {
   }
 }
 
+int64_t ResidentTree::split(int64_t h, int64_t at) {
+  ResNode& tail = nodes_.at(h);
+  const int64_t nh = next_handle_++;
+  ResNode head;
+  head.handle = nh;
+  head.parent = tail.parent;
+  head.tokens.assign(tail.tokens.begin(), tail.tokens.begin() + at);
+  head.pages.assign(tail.pages.begin(), tail.pages.begin() + at / kPage);
+  head.start = tail.start;
+  head.refs = 0;
+  head.last_use = tail.last_use;
+  head.children.push_back(h);
+  auto& sib = children_mut(tail.parent);
+  *std::find(sib.begin(), sib.end(), h) = nh;
+  tail.parent = nh;
+  tail.tokens.erase(tail.tokens.begin(), tail.tokens.begin() + at);
+  tail.pages.erase(tail.pages.begin(), tail.pages.begin() + at / kPage);
+  tail.start += at;
+  nodes_.emplace(nh, std::move(head));
+  return nh;
+}
+
+void ResidentTree::match_split(const int32_t* seq, int64_t n, int64_t* handle, int64_t* matched) {
+  int64_t h, pos;
+  match(seq, n, &h, &pos);
+  int64_t best = 0, best_at = 0;
+  for (int64_t c : children(h)) {
+    const std::vector<int32_t>& t = nodes_.at(c).tokens;
+    const int64_t lim = std::min<int64_t>(int64_t(t.size()), n - 1 - pos);
+    int64_t l = 0;
+    while (l < lim && t[size_t(l)] == seq[pos + l]) ++l;
+    const int64_t at = l / kPage * kPage;
+    if (at >= kPage && at < int64_t(t.size()) && at > best_at) {
+      best = c;
+      best_at = at;
+    }
+  }
+  if (best != 0) {
+    h = split(best, best_at);
+    pos += best_at;
+  }
+  *handle = h;
+  *matched = pos;
+}
+
 void ResidentTree::touch_path(int64_t h, uint64_t stamp) {
   for (; h != 0; h = nodes_.at(h).parent) nodes_.at(h).last_use = stamp;
 }

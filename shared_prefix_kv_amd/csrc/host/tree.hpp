@@ -129,6 +129,18 @@ class ResidentTree {
   int32_t pages_held() const;
   // The child of `parent` whose segment is exactly tok[0..n), or 0.
   int64_t find_child(int64_t parent, const int32_t* tok, int64_t n) const;
+  // Splits node h after its first `at` tokens (a multiple of the page size,
+  // inside the node): a new node takes h's place under its parent with the
+  // first at / 16 pages and no reference; h keeps its handle, references and
+  // children with the rest and becomes the new node's child.  Returns the new
+  // handle.
+  int64_t split(int64_t h, int64_t at);
+  // Anchor of a candidate with reuse inside resident nodes: full-node matches
+  // as in match(); where none continues, the child sharing the longest
+  // page-aligned run (at least one page, leaving >= 1 token; ties: the
+  // earliest created) is split at that page boundary and its first part is
+  // the anchor.
+  void match_split(const int32_t* seq, int64_t n, int64_t* handle, int64_t* matched);
   // Deepest full-node match leaving >= 1 token.
   void match(const int32_t* seq, int64_t n, int64_t* handle, int64_t* matched) const;
 

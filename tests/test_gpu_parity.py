@@ -133,6 +133,33 @@ def test_w1_rotating_states_under_the_lru_cache(w1):
     assert score_p() == 0
 
 
+def test_w1_candidates_reuse_whole_pages_inside_a_resident_prefix(w1):
+    """Candidates that leave the resident 128-token prefix at token 100 reuse
+    its first six pages (the node is split at token 96) and compute the rest;
+    results match the oracle from scratch and the prefix's handle still maps
+    to its own pages."""
+    wl, inst, m, ref, ctx, _ = w1
+    P = inst.prefixes[0]
+    (h,) = ctx.prefill_prefix([0], [P])
+    pages_before = ctx.page_table(h)
+    rng = np.random.default_rng(91)
+    seqs = [[int(t) for t in P[:100]] + [int(t) for t in rng.integers(0, wl.model.vocab, 12 + 5 * i)] for i in range(3)]
+    labels = [b.labels for b in inst.passes[0][:3]]
+    probs, loff = ctx.score_candidates(seqs, labels)
+    _sync()
+    want = om.score_from_scratch(m, seqs, labels)
+    assert max_abs(split_probs(probs, loff), want) <= TOL_F32
+    st = ctx.stats()
+    assert st["cached_tokens"] == 3 * 96
+    # the 4 shared tokens 96..99 are less than a page: that node is dissolved
+    # into the candidates, each computing tokens 96..end
+    assert st["computed_tokens"] == sum(len(s) - 96 for s in seqs)
+    assert ctx.page_table(h) == pages_before
+    assert st["resident_prefixes"] == 2                                   # head (96) + the caller's tail
+    ctx.free_pages([h])
+    assert ctx.stats()["pages_in_use"] == 0 and ctx.stats()["resident_prefixes"] == 0
+
+
 def test_w1_unshared_and_candidate_paths_match_oracle(w1):
     wl, inst, m, ref, ctx, _ = w1
     seqs = inst.full_sequences(0)
@@ -402,6 +429,23 @@ def test_w2_attention_output_matches_oracle(w2):
     print("w2 layer-0 attention max row rel err", err)
     assert err <= 2e-2
     ctx.free_pages([h])
+
+
+def test_w2_repeated_calls_are_bitwise_identical(w2):
+    """Same prefix and branches prefilled and scored again: the kernels have no
+    order-dependent reductions, so any difference is a race (e.g. an LDS buffer
+    overwritten before every wave has read it)."""
+    wl, inst, g, ctx, _ = w2
+    br = inst.passes[0]
+    runs = []
+    for _ in range(4):
+        (h,) = ctx.prefill_prefix([0], [inst.prefixes[0]])
+        probs, loff = ctx.score_branches([h] * 5, [b.tokens for b in br], [b.labels for b in br])
+        _sync()
+        runs.append(probs.float().cpu().numpy().copy())
+        ctx.free_pages([h])
+    for r in runs[1:]:
+        assert np.array_equal(r, runs[0])
 
 
 def test_w3_staged_rounds_match_oracle(w2):

@@ -47,7 +47,7 @@ def test_plan_of_each_config_matches_oracle(idx):
     seqs = [s for s, _ in inst.full_sequences(0)]
     ctx = dry(wl, 4096)
     tree = op.ResidentTree(op.PagePool(4096))
-    assert ctx.plan(seqs) == op.plan_candidates(tree, seqs).serialize()
+    assert ctx.plan(seqs) == op.plan_with_reuse(tree, seqs).serialize()
 
 
 @pytest.mark.parametrize("seed", range(60))
@@ -71,7 +71,7 @@ def test_plan_random_tries_bit_exact(seed):
         (h,) = ctx.prefill_prefix([0], [base[:k]])
         assert tree.prefill([(0, base[:k])]) == [h]
     try:
-        want = op.plan_candidates(tree, seqs).serialize()
+        want = op.plan_with_reuse(tree, seqs).serialize()
     except op.PoolExhausted:
         with pytest.raises(jev.JevError) as e:
             ctx.plan(seqs)
@@ -116,7 +116,7 @@ def test_tree_of_prefixes_path_pages_and_match():
     tree = op.ResidentTree(op.PagePool(64))
     (oa,) = tree.prefill([(0, list(range(20)))])
     (ob,) = tree.prefill([(oa, list(range(20, 25)))])
-    assert ctx.plan(seqs) == op.plan_candidates(tree, seqs).serialize()
+    assert ctx.plan(seqs) == op.plan_with_reuse(tree, seqs).serialize()
     # releasing the parent first keeps it alive for its child
     ctx.free_pages([a])
     assert ctx.stats()["resident_prefixes"] == 2

@@ -110,7 +110,7 @@ def test_plan_random_tries_bit_exact(seed):
         (h,) = ctx.prefill_prefix([0], [base[:k]])
         assert tree.prefill([(0, base[:k])]) == [h]
     try:
-        want = op.plan_candidates(tree, seqs, "candidate_first")
+        want = op.plan_with_reuse(tree, seqs, "candidate_first")
     except op.PoolExhausted:
         with pytest.raises(jev.JevError) as e:
             ctx.plan(seqs)
