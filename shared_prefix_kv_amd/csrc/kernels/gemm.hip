@@ -256,9 +256,9 @@ __device__ __forceinline__ void xcd_tile(int b, int n_blocks, int m_tiles, int* 
 // the 16 rows touched by one 16-lane fragment read (or one 16-lane write) fall
 // in different bank groups; the stores of the next stage are spread between
 // the MFMAs of the current one.  One barrier per 128-byte K stage.  With SPLIT,
-// blockIdx.y selects a slice of K and partial sums are added (agent-scope fp32
-// atomics) into an fp32 [M][N] scratch; split_epilogue (next launch) runs the
-// epilogue on the sums over all CUs and clears the scratch for the next use.
+// blockIdx.y selects a slice of K and the fp32 partial tile is stored to its
+// own [256][N] scratch slice; split_epilogue (next launch) sums the slices and
+// runs the epilogue.
 template <typename T, int BN, int EPI, bool SPLIT, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_kernel(const T* __restrict__ A, int M, int K, int N, ColMap cm,
                                                    QkvOut qo, ResOut ro, float* __restrict__ scratch) {
@@ -453,28 +453,247 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM
   }
 }
 
+// --------------------------------------------------- large GEMM, direct loads
+// LDS unit of 16-byte chunk j of stage row R in the direct-load layout: rows of
+// 8 units (128 bytes, unpadded), chunk slots XOR-swizzled by (R / 2) mod 8, so
+// that the 16 lanes of a fragment read (16 consecutive rows, one chunk) fall in
+// 16 distinct bank groups.
+__device__ __forceinline__ int dl_unit(int R, int j) { return R * 8 + (j ^ ((R >> 1) & 7)); }
+
+// Waits until at most N vector memory operations of this wave are outstanding
+// and all of its LDS operations are done, then joins the workgroup barrier.
+// The direct loads below are vector memory operations that write LDS, so after
+// the barrier every wave's loads up to that point have landed.
+template <int N>
+__device__ __forceinline__ void vm_lds_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Scheduling groups of one k-step region: NMF MFMAs, with the region's NRD LDS
+// fragment reads two per MFMA from the first one on (the next region starts
+// by waiting for all of them), then NV direct loads spread over the MFMAs after
+// those.  (A direct load writes LDS, so the scheduler keeps it after LDS reads
+// that precede it in program order: the reads are issued first.)
+template <int NMF, int NRD, int NV, int M_ = 0>
+__device__ __forceinline__ void dl_groups() {
+  if constexpr (M_ < NMF) {
+    constexpr int RS = (NRD + 1) / 2;  // MFMAs that take reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int r = M_ < RS ? (2 * M_ + 2 <= NRD ? 2 : NRD - 2 * M_) : 0;
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+    constexpr int NT = NMF - RS > 0 ? NMF - RS : 1;  // MFMAs that take loads
+    constexpr int q = M_ - (NMF - NT);
+    constexpr int v = q < 0 ? 0 : (NV * (q + 1)) / NT - (NV * q) / NT;
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);
+    dl_groups<NMF, NRD, NV, M_ + 1>();
+  }
+}
+
+// Large bf16 GEMM (prefill projections): one 256 x BN tile per workgroup of
+// four waves, one wave per SIMD; wave w owns rows [64w, 64w+64) and all BN
+// columns (2 x BN/32 MFMA 32x32 blocks, accumulators in the unified register
+// file).  Both operands go from global memory straight into LDS
+// (global_load_lds, 16 bytes per lane: each instruction fills 8 stage rows of
+// 128 bytes, lane l writing slot l of that 1 KB and loading the chunk that the
+// swizzle puts there), NSTG stages deep: the loads of stage k + NSTG - 1 are
+// issued, between the MFMAs, when stage k starts, into the buffer of stage
+// k - 1.  Near the end they reload the last stage into that buffer, which no
+// later stage reads, so every wait count is static and the loop body has no
+// branch (a branch would make the compiler wait for all LDS reads where its
+// paths join).  One barrier per 64-wide K
+// stage, placed before the MFMAs of the stage's last k-step: after it the wave
+// reads the first fragments of the next stage, and those 10 MFMAs cover the
+// read latency, so the MFMA pipe does not drain at stage boundaries.  Same
+// tile order, epilogue and split-K convention as gemm_kernel (with SPLIT,
+// blockIdx.y takes a slice of K and the fp32 partial tile goes to its own
+// scratch slice); every output accumulates over K in the same order, so the
+// results are bitwise those of gemm_kernel.
+template <int BN, int EPI, int NSTG, bool SPLIT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_dl_kernel(
+    const bf16s* __restrict__ A, int M, int K, int N, ColMap cm, QkvOut qo, ResOut ro, float* __restrict__ scratch) {
+  using T = bf16s;
+  using MF = Mfma<T>;
+  using frag = typename MF::frag;
+  constexpr int BM = 256, NW = 4, NTH = 256;
+  constexpr int CH = 8;                    // bf16 per 16-byte chunk
+  constexpr int BK = 64;                   // K per stage (128 bytes)
+  constexpr int KS = BK / MF::KSTEP;       // 4 k-steps per stage
+  constexpr int NRB = 2, TN = BN / 32;
+  constexpr int NL = (BM + BN) / 8;        // 1 KB loads per stage
+  constexpr int LPW = NL / NW;             // loads per wave per stage
+  constexpr int STAGE = (BM + BN) * 8;     // 16-byte units
+  constexpr int LDS_MAIN = NSTG * STAGE;
+  constexpr int LDS_EPI = SPLIT ? 0 : 128 * (BN + 4) / 4;
+  constexpr int LDS_UNITS = LDS_MAIN > LDS_EPI ? LDS_MAIN : LDS_EPI;
+  constexpr int VM_AHEAD = (NSTG - 2) * LPW;  // loads allowed in flight at a stage barrier
+  static_assert(KS == 4 && BN % 32 == 0 && NL % NW == 0 && (NSTG == 2 || NSTG == 3), "tile");
+  static_assert(LDS_UNITS * 16 <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(16))) u32x4 smem[LDS_UNITS];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;
+  const int c = lane & 31, hh = lane >> 5;
+  const int rowA0 = 64 * wave;
+  int mt, nt;
+  if (SPLIT) {
+    mt = 0;
+    nt = blockIdx.x;
+  } else {
+    xcd_tile(blockIdx.x, gridDim.x, (M + BM - 1) / BM, &mt, &nt);
+  }
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int KTall = K / BK;
+  const int kt0 = SPLIT ? (KTall * (int)blockIdx.y) / (int)gridDim.y : 0;
+  const int KT = SPLIT ? (KTall * ((int)blockIdx.y + 1)) / (int)gridDim.y - kt0 : KTall;
+
+  // this wave's loads: load i fills stage rows 8 li .. 8 li + 7, li = wave + NW i
+  const T* src[LPW];
+  {
+    const int lr = lane >> 3, lp = lane & 7;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int li = wave + NW * i;
+      const int R = 8 * li + lr;
+      const int j = lp ^ ((R >> 1) & 7);
+      src[i] = (R < BM ? A + (size_t)min(m0 + R, M - 1) * K : weight_row<T>(cm, BN, n0 + R - BM, K)) +
+               (size_t)kt0 * BK + j * CH;
+    }
+  }
+  // loads [I0, I1) of stage min(kt, KT - 1) into LDS buffer buf
+  auto issue = [&](int kt, int buf, int I0, int I1) __attribute__((always_inline)) {
+    const size_t koff = (size_t)min(kt, KT - 1) * BK;
+    u32x4* dst = smem + buf * STAGE + 64 * wave;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      if (i < I0 || i >= I1) continue;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src[i] + koff),
+                                       (__attribute__((address_space(3))) void*)(dst + 64 * NW * i), 16, 0, 0);
+    }
+  };
+
+  f32x16 acc[NRB][TN];
+#pragma unroll
+  for (int i = 0; i < NRB; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  auto frags = [&](const u32x4* st, int s, frag* fa, frag* fb) __attribute__((always_inline)) {
+    const int j = 2 * s + hh;  // chunk of this lane's 8 k elements
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) fa[i] = MF::load(&st[dl_unit(rowA0 + 32 * i + c, j)]);
+#pragma unroll
+    for (int t = 0; t < TN; ++t) fb[t] = MF::load(&st[dl_unit(BM + 32 * t + c, j)]);
+  };
+  auto mma = [&](const frag* fa, const frag* fb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NRB; ++i)
+#pragma unroll
+      for (int t = 0; t < TN; ++t) acc[i][t] = MF::mma(fa[i], fb[t], acc[i][t]);
+  };
+  // loads of a stage, spread over the three k-step regions before the barrier
+  constexpr int P1 = (LPW + 2) / 3, P2 = P1 + (LPW - P1 + 1) / 2;
+
+#pragma unroll
+  for (int p = 0; p < NSTG - 1; ++p) issue(p, p, 0, LPW);
+  vm_lds_barrier<VM_AHEAD>();  // stage 0 landed
+  frag fa0[NRB], fb0[TN], fa1[NRB], fb1[TN];
+  frags(smem, 0, fa0, fb0);
+  int buf = 0, ibuf = NSTG - 1;  // buffers of stage kt and of stage kt + NSTG - 1
+  for (int kt = 0; kt < KT; ++kt) {
+    const u32x4* st = smem + buf * STAGE;
+    // loads of stage kt + NSTG - 1 go into the buffer of stage kt - 1, which
+    // every wave finished reading before the barrier that ended that stage
+    frags(st, 1, fa1, fb1);
+    issue(kt + NSTG - 1, ibuf, 0, P1);
+    mma(fa0, fb0);
+    dl_groups<NRB * TN, NRB + TN, P1>();
+    __builtin_amdgcn_sched_barrier(0);
+    frags(st, 2, fa0, fb0);
+    issue(kt + NSTG - 1, ibuf, P1, P2);
+    mma(fa1, fb1);
+    dl_groups<NRB * TN, NRB + TN, P2 - P1>();
+    __builtin_amdgcn_sched_barrier(0);
+    frags(st, 3, fa1, fb1);
+    issue(kt + NSTG - 1, ibuf, P2, LPW);
+    mma(fa0, fb0);
+    dl_groups<NRB * TN, NRB + TN, LPW - P2>();
+    __builtin_amdgcn_sched_barrier(0);
+    // stage kt + 1 landed (the loads of stage kt + 2 may still be in flight);
+    // on the last stage the reads below fetch unused values
+    vm_lds_barrier<VM_AHEAD>();
+    buf = buf + 1 == NSTG ? 0 : buf + 1;
+    ibuf = ibuf + 1 == NSTG ? 0 : ibuf + 1;
+    frags(smem + buf * STAGE, 0, fa0, fb0);
+    mma(fa1, fb1);
+    dl_groups<NRB * TN, NRB + TN, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  vm_lds_barrier<0>();  // every load and read of the main loop done
+  if constexpr (SPLIT) {
+    float* part = scratch + (size_t)blockIdx.y * BM * N;
+#pragma unroll
+    for (int i = 0; i < NRB; ++i)
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = rowA0 + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (m < M) part[(size_t)m * N + n0 + 32 * t + c] = acc[i][t][r];
+        }
+    return;
+  }
+  float* stile = reinterpret_cast<float*>(smem);
+  constexpr int LD = BN + 4;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (rowA0 / 128 == half) {
+#pragma unroll
+      for (int i = 0; i < NRB; ++i)
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = rowA0 % 128 + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+            stile[row * LD + 32 * t + c] = acc[i][t][r];
+          }
+    }
+    __syncthreads();
+    if (m0 + 128 * half < M) tile_epilogue<T, EPI>(stile, LD, 128, m0 + 128 * half, M, nt, BN, cm, qo, ro, tid, NTH);
+    __syncthreads();
+  }
+}
+
 // Epilogue of a split-K GEMM: block (column tile of 128, 16 rows) sums the
-// `splits` partial slices into slice 0, then runs the epilogue on it.
+// `splits` partial slices in slice order into an LDS tile (all of a thread's
+// slice loads in flight at once), then runs the epilogue on it.
 template <typename T, int EPI>
-__global__ __launch_bounds__(256) void split_epilogue(float* __restrict__ scratch, int splits, int M, int N, ColMap cm,
-                                                      QkvOut qo, ResOut ro) {
-  constexpr int BN = 128, RB = 16;
+__global__ __launch_bounds__(256) void split_epilogue(const float* __restrict__ scratch, int splits, int M, int N,
+                                                      ColMap cm, QkvOut qo, ResOut ro) {
+  constexpr int BN = 128, RB = 16, LD = BN + 4;
+  __shared__ __attribute__((aligned(16))) float stile[RB * LD];
   const int nt = blockIdx.x, r0 = blockIdx.y * RB;
   const int rows = min(RB, M - r0);
-  float* tile = scratch + (size_t)r0 * N + nt * BN;
+  const float* tile = scratch + (size_t)r0 * N + nt * BN;
   const size_t slice = (size_t)256 * N;
   for (int e = threadIdx.x; e < rows * (BN / 4); e += 256) {
     const int r = e / (BN / 4), q4 = e % (BN / 4);
-    float4* p = reinterpret_cast<float4*>(tile + (size_t)r * N + 4 * q4);
-    float4 v = *p;
-    for (int y = 1; y < splits; ++y) {
-      const float4 w = *reinterpret_cast<const float4*>(tile + y * slice + (size_t)r * N + 4 * q4);
-      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
-    }
-    *p = v;
+    float4 w[kMaxSplits];
+#pragma unroll
+    for (int y = 0; y < kMaxSplits; ++y)
+      if (y < splits) w[y] = *reinterpret_cast<const float4*>(tile + y * slice + (size_t)r * N + 4 * q4);
+    float4 v = w[0];
+#pragma unroll
+    for (int y = 1; y < kMaxSplits; ++y)
+      if (y < splits) {
+        v.x += w[y].x; v.y += w[y].y; v.z += w[y].z; v.w += w[y].w;
+      }
+    *reinterpret_cast<float4*>(&stile[r * LD + 4 * q4]) = v;
   }
   __syncthreads();
-  tile_epilogue<T, EPI>(tile, N, rows, r0, M, nt, BN, cm, qo, ro, threadIdx.x, 256);
+  tile_epilogue<T, EPI>(stile, LD, rows, r0, M, nt, BN, cm, qo, ro, threadIdx.x, 256);
 }
 
 }  // namespace dev
@@ -500,8 +719,18 @@ hipError_t gemm_dispatch(const ModelDims& m, const GemmWs& ws, const void* A, in
     int S = g_gemm_tuning.splits > 0 ? g_gemm_tuning.splits : std::max(1, 256 / tiles);
     S = std::max(1, std::min({S, kMaxSplits, KT / 2 > 0 ? KT / 2 : 1}));
     if ((size_t)S * 256 * N > ws.partial_elems) return hipErrorInvalidValue;
-    JEV_LAUNCH((dev::gemm_kernel<T, BN, EPI, true, 4, 2>), dim3(tiles, S), dim3(512), 0, s, a, M, K, N, cm,
-                       qo, ro, ws.partial);
+    bool done = false;
+    if constexpr (sizeof(T) == 2) {
+      // bf16: four waves, operands loaded straight into LDS
+      if (g_gemm_tuning.large != 1 && K % 64 == 0) {
+        JEV_LAUNCH((dev::gemm_dl_kernel<BN, EPI, 3, true>), dim3(tiles, S), dim3(256), 0, s, a, M, K, N, cm, qo,
+                   ro, ws.partial);
+        done = true;
+      }
+    }
+    if (!done)
+      JEV_LAUNCH((dev::gemm_kernel<T, BN, EPI, true, 4, 2>), dim3(tiles, S), dim3(512), 0, s, a, M, K, N, cm,
+                         qo, ro, ws.partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     JEV_LAUNCH((dev::split_epilogue<T, EPI>), dim3(tiles, (M + 15) / 16), dim3(256), 0, s, ws.partial, S, M,
@@ -519,6 +748,21 @@ hipError_t gemm_dispatch(const ModelDims& m, const GemmWs& ws, const void* A, in
   if (g_gemm_tuning.bn == 128 || g_gemm_tuning.bn == 160) bn = g_gemm_tuning.bn;
   if (N % bn) return hipErrorInvalidValue;
   dim3 grid((N / bn) * mt);
+  if constexpr (sizeof(T) == 2) {
+    // bf16: four waves, operands loaded straight into LDS
+    const int kind = g_gemm_tuning.large == 0 ? 3 : g_gemm_tuning.large;
+    if (kind >= 2 && K % 64 == 0) {
+      if (bn == 160 && kind == 2)
+        JEV_LAUNCH((dev::gemm_dl_kernel<160, EPI, 2, false>), grid, dim3(256), 0, s, a, M, K, N, cm, qo, ro, nullptr);
+      else if (bn == 160)
+        JEV_LAUNCH((dev::gemm_dl_kernel<160, EPI, 3, false>), grid, dim3(256), 0, s, a, M, K, N, cm, qo, ro, nullptr);
+      else if (kind == 2)
+        JEV_LAUNCH((dev::gemm_dl_kernel<128, EPI, 2, false>), grid, dim3(256), 0, s, a, M, K, N, cm, qo, ro, nullptr);
+      else
+        JEV_LAUNCH((dev::gemm_dl_kernel<128, EPI, 3, false>), grid, dim3(256), 0, s, a, M, K, N, cm, qo, ro, nullptr);
+      return hipGetLastError();
+    }
+  }
   // eight waves (two per SIMD): 8 x 1 over a 160-wide tile, 4 x 2 over 128
   if (bn == 160)
     JEV_LAUNCH((dev::gemm_kernel<T, 160, EPI, false, 8, 1>), grid, dim3(512), 0, s, a, M, K, N, cm, qo, ro,
