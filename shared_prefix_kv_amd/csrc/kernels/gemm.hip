@@ -6,11 +6,13 @@
 // bound.  Branch scoring: M = suffix tokens of all branches (a few hundred),
 // bound by streaming the weights once.
 //
-// One kernel, gemm_kernel (below): 256-row x BN-column tiles, 4 waves of 64
-// rows; BN = 160 where it makes the tile count fit the 256 CUs (QKV at 2,000
-// rows: 8 x 32 tiles), else 128.  Up to 256 rows (branch scoring) it splits K
-// over several workgroups per column tile so that the weights stream from
-// every CU.
+// Tiles of 256 rows x BN columns; BN = 160 where it makes the tile count fit
+// the 256 CUs (QKV at 2,000 rows: 8 x 32 tiles), else 128.  Up to 256 rows
+// (branch scoring) K is split over several workgroups per column tile so that
+// the weights stream from every CU.  Full-K bf16 tiles run gemm_dl_kernel
+// (four waves, operands loaded straight into LDS three stages deep); the
+// split-K tiles and float32 run gemm_kernel (register-staged loads, eight
+// waves).
 //
 // Epilogues run on an fp32 tile staged in LDS (full K) or in the fp32 scratch
 // (split K), so their element mapping is independent of the MFMA layout:
@@ -278,7 +280,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM
   constexpr int RS = 9;                // LDS row stride, 16-byte units
   constexpr int STAGE = (BM + BN) * RS;
   constexpr int LDS_MAIN = 2 * STAGE;
-  constexpr int LDS_EPI = SPLIT ? 0 : 128 * (BN + 4) / 4;
+  constexpr int LDS_EPI = 128 * (BN + 4) / 4;
   constexpr int LDS_UNITS = LDS_MAIN > LDS_EPI ? LDS_MAIN : LDS_EPI;
   static_assert(BM % (WM * 32) == 0 && BN % (WN * 32) == 0 && BM % RPL == 0, "tile");
   __shared__ __attribute__((aligned(16))) u32x4 smem[LDS_UNITS];
@@ -504,13 +506,13 @@ __device__ __forceinline__ void dl_groups() {
 // stage, placed before the MFMAs of the stage's last k-step: after it the wave
 // reads the first fragments of the next stage, and those 10 MFMAs cover the
 // read latency, so the MFMA pipe does not drain at stage boundaries.  Same
-// tile order, epilogue and split-K convention as gemm_kernel (with SPLIT,
-// blockIdx.y takes a slice of K and the fp32 partial tile goes to its own
-// scratch slice); every output accumulates over K in the same order, so the
-// results are bitwise those of gemm_kernel.
-template <int BN, int EPI, int NSTG, bool SPLIT>
+// tile order and epilogue as gemm_kernel; every output accumulates over K in
+// the same order, so the results are bitwise those of gemm_kernel.  (With K
+// split over workgroups the loop is ~10 stages long, and this kernel measured
+// slower than gemm_kernel there: the split-K GEMMs keep gemm_kernel.)
+template <int BN, int EPI, int NSTG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_dl_kernel(
-    const bf16s* __restrict__ A, int M, int K, int N, ColMap cm, QkvOut qo, ResOut ro, float* __restrict__ scratch) {
+    const bf16s* __restrict__ A, int M, int K, int N, ColMap cm, QkvOut qo, ResOut ro) {
   using T = bf16s;
   using MF = Mfma<T>;
   using frag = typename MF::frag;
@@ -523,7 +525,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int LPW = NL / NW;             // loads per wave per stage
   constexpr int STAGE = (BM + BN) * 8;     // 16-byte units
   constexpr int LDS_MAIN = NSTG * STAGE;
-  constexpr int LDS_EPI = SPLIT ? 0 : 128 * (BN + 4) / 4;
+  constexpr int LDS_EPI = 128 * (BN + 4) / 4;
   constexpr int LDS_UNITS = LDS_MAIN > LDS_EPI ? LDS_MAIN : LDS_EPI;
   constexpr int VM_AHEAD = (NSTG - 2) * LPW;  // loads allowed in flight at a stage barrier
   static_assert(KS == 4 && BN % 32 == 0 && NL % NW == 0 && (NSTG == 2 || NSTG == 3), "tile");
@@ -535,16 +537,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int c = lane & 31, hh = lane >> 5;
   const int rowA0 = 64 * wave;
   int mt, nt;
-  if (SPLIT) {
-    mt = 0;
-    nt = blockIdx.x;
-  } else {
-    xcd_tile(blockIdx.x, gridDim.x, (M + BM - 1) / BM, &mt, &nt);
-  }
+  xcd_tile(blockIdx.x, gridDim.x, (M + BM - 1) / BM, &mt, &nt);
   const int m0 = mt * BM, n0 = nt * BN;
-  const int KTall = K / BK;
-  const int kt0 = SPLIT ? (KTall * (int)blockIdx.y) / (int)gridDim.y : 0;
-  const int KT = SPLIT ? (KTall * ((int)blockIdx.y + 1)) / (int)gridDim.y - kt0 : KTall;
+  const int KT = K / BK;
 
   // this wave's loads: load i fills stage rows 8 li .. 8 li + 7, li = wave + NW i
   const T* src[LPW];
@@ -555,8 +550,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const int li = wave + NW * i;
       const int R = 8 * li + lr;
       const int j = lp ^ ((R >> 1) & 7);
-      src[i] = (R < BM ? A + (size_t)min(m0 + R, M - 1) * K : weight_row<T>(cm, BN, n0 + R - BM, K)) +
-               (size_t)kt0 * BK + j * CH;
+      src[i] = (R < BM ? A + (size_t)min(m0 + R, M - 1) * K : weight_row<T>(cm, BN, n0 + R - BM, K)) + j * CH;
     }
   }
   // loads [I0, I1) of stage min(kt, KT - 1) into LDS buffer buf
@@ -631,22 +625,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  vm_lds_barrier<0>();  // every load and read of the main loop done
-  if constexpr (SPLIT) {
-    float* part = scratch + (size_t)blockIdx.y * BM * N;
-#pragma unroll
-    for (int i = 0; i < NRB; ++i)
-#pragma unroll
-      for (int t = 0; t < TN; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = rowA0 + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (m < M) part[(size_t)m * N + n0 + 32 * t + c] = acc[i][t][r];
-        }
-    return;
-  }
   float* stile = reinterpret_cast<float*>(smem);
   constexpr int LD = BN + 4;
+  vm_lds_barrier<0>();  // every load and read of the main loop done
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     if (rowA0 / 128 == half) {
@@ -719,18 +700,8 @@ hipError_t gemm_dispatch(const ModelDims& m, const GemmWs& ws, const void* A, in
     int S = g_gemm_tuning.splits > 0 ? g_gemm_tuning.splits : std::max(1, 256 / tiles);
     S = std::max(1, std::min({S, kMaxSplits, KT / 2 > 0 ? KT / 2 : 1}));
     if ((size_t)S * 256 * N > ws.partial_elems) return hipErrorInvalidValue;
-    bool done = false;
-    if constexpr (sizeof(T) == 2) {
-      // bf16: four waves, operands loaded straight into LDS
-      if (g_gemm_tuning.large != 1 && K % 64 == 0) {
-        JEV_LAUNCH((dev::gemm_dl_kernel<BN, EPI, 3, true>), dim3(tiles, S), dim3(256), 0, s, a, M, K, N, cm, qo,
-                   ro, ws.partial);
-        done = true;
-      }
-    }
-    if (!done)
-      JEV_LAUNCH((dev::gemm_kernel<T, BN, EPI, true, 4, 2>), dim3(tiles, S), dim3(512), 0, s, a, M, K, N, cm,
-                         qo, ro, ws.partial);
+    JEV_LAUNCH((dev::gemm_kernel<T, BN, EPI, true, 4, 2>), dim3(tiles, S), dim3(512), 0, s, a, M, K, N, cm,
+                       qo, ro, ws.partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     JEV_LAUNCH((dev::split_epilogue<T, EPI>), dim3(tiles, (M + 15) / 16), dim3(256), 0, s, ws.partial, S, M,
@@ -753,13 +724,13 @@ hipError_t gemm_dispatch(const ModelDims& m, const GemmWs& ws, const void* A, in
     const int kind = g_gemm_tuning.large == 0 ? 3 : g_gemm_tuning.large;
     if (kind >= 2 && K % 64 == 0) {
       if (bn == 160 && kind == 2)
-        JEV_LAUNCH((dev::gemm_dl_kernel<160, EPI, 2, false>), grid, dim3(256), 0, s, a, M, K, N, cm, qo, ro, nullptr);
+        JEV_LAUNCH((dev::gemm_dl_kernel<160, EPI, 2>), grid, dim3(256), 0, s, a, M, K, N, cm, qo, ro);
       else if (bn == 160)
-        JEV_LAUNCH((dev::gemm_dl_kernel<160, EPI, 3, false>), grid, dim3(256), 0, s, a, M, K, N, cm, qo, ro, nullptr);
+        JEV_LAUNCH((dev::gemm_dl_kernel<160, EPI, 3>), grid, dim3(256), 0, s, a, M, K, N, cm, qo, ro);
       else if (kind == 2)
-        JEV_LAUNCH((dev::gemm_dl_kernel<128, EPI, 2, false>), grid, dim3(256), 0, s, a, M, K, N, cm, qo, ro, nullptr);
+        JEV_LAUNCH((dev::gemm_dl_kernel<128, EPI, 2>), grid, dim3(256), 0, s, a, M, K, N, cm, qo, ro);
       else
-        JEV_LAUNCH((dev::gemm_dl_kernel<128, EPI, 3, false>), grid, dim3(256), 0, s, a, M, K, N, cm, qo, ro, nullptr);
+        JEV_LAUNCH((dev::gemm_dl_kernel<128, EPI, 3>), grid, dim3(256), 0, s, a, M, K, N, cm, qo, ro);
       return hipGetLastError();
     }
   }
