@@ -50,6 +50,9 @@ constexpr int kMaxChunks = jev::kMaxAncParts;  // prefix chunks per sibling grou
 // pairs than the GPU has CUs (otherwise every CU already holds work)
 constexpr int64_t kSplitTilesBelow = 256;
 constexpr int kRowsPerTile = 128;
+// attention rounds whose longest tile has at least this many pages run two
+// wave groups per workgroup
+constexpr int32_t kTwoGroupPages = 48;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -148,6 +151,7 @@ struct RoundDesc {
   int64_t part_slots = 0;
   double attn_pairs = 0;  // visible (query row, key) pairs of one layer
   int64_t n_part_rows = 0;
+  int32_t attn_groups = 1;  // wave groups per attention workgroup
 };
 
 }  // namespace
@@ -483,6 +487,9 @@ int build_round(jev_ctx* ctx, std::vector<RNode>& nodes, std::vector<int32_t>& h
   std::stable_sort(tiles.begin(), tiles.end(),
                    [](const jev::AttnTile& a, const jev::AttnTile& b) { return a.n_pages > b.n_pages; });
   rd->n_tiles = int32_t(tiles.size());
+  // a round whose longest tile has many steps splits every tile's steps over
+  // two wave groups, halving the chain that sets the kernel's length
+  rd->attn_groups = (!tiles.empty() && tiles.front().n_pages >= kTwoGroupPages) ? 2 : 1;
   rd->off_tiles = push(int64_t(tiles.size()) * 8);
   std::memcpy(hb.data() + rd->off_tiles, tiles.data(), tiles.size() * sizeof(jev::AttnTile));
   rd->n_merge = int32_t(merges.size());
@@ -581,7 +588,8 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
       }));
       HIPCHK(timed(JEV_K_ATTN, l, rd.T, 4.0 * m.dh * rd.attn_pairs, 0, [&] {
         return jev::launch_attention(m, l, reinterpret_cast<const jev::AttnTile*>(dd + rd.off_tiles), rd.n_tiles,
-                                     dd + rd.off_plist, dd + rd.off_pos, q, ctx->pool, o, part_o, part_lse, s);
+                                     dd + rd.off_plist, dd + rd.off_pos, q, ctx->pool, o, part_o, part_lse,
+                                     rd.attn_groups, s);
       }));
       if (rd.n_merge > 0)
         HIPCHK(timed(JEV_K_MERGE, l, rd.n_merge, 0, 0, [&] {

@@ -107,9 +107,11 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x, c
 }
 
 // ------------------------------------------------------------------ attention
-// Block = 4 waves = 128 query rows (tokens_per_tile x G heads of one KV head);
-// wave w owns rows [32w, 32w+32).  Per step two pages (32 keys) of K and V go
-// through LDS.  S^T = K Q^T (keys as MFMA rows, query rows as columns) keeps a
+// A wave group = 4 waves = 128 query rows (tokens_per_tile x G heads of one KV
+// head); wave w owns rows [32w, 32w+32).  Per step two pages (32 keys) of K and
+// V go through LDS.  A workgroup has one group, or two that take the two
+// halves of the tile's steps and merge their softmax states at the end (the
+// chain of a long causal tile halves; the CU holds the same eight waves).  S^T = K Q^T (keys as MFMA rows, query rows as columns) keeps a
 // query row's softmax statistics in one lane column, so that O^T = V^T P^T
 // rescales per lane with no cross-lane traffic besides the two half-waves.
 template <typename T>
@@ -146,8 +148,8 @@ constexpr float RESCALE_SLACK = 8.0f;
 // Longest page list of one attention tile (the host checks max_positions).
 constexpr int kMaxTilePages = 4096;
 
-template <typename T, int DH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(const AttnTile* __restrict__ tiles,
+template <typename T, int DH, int GROUPS>
+__global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(const AttnTile* __restrict__ tiles,
                                                    const int32_t* __restrict__ plist,
                                                    const int32_t* __restrict__ tok_pos, const T* __restrict__ q,
                                                    const T* __restrict__ pool, T* __restrict__ o,
@@ -164,10 +166,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int VCPR = 16 / CH;           // 16-byte chunks per V^T row of a page
   constexpr int NDB = DH / 32;
   static_assert(PAGE_CHUNKS == 256, "two pages per step = 512 chunks = 2 per thread");
-  __shared__ __attribute__((aligned(16))) T sK[2][32 * DH];
-  __shared__ __attribute__((aligned(16))) T sV[2][DH * 32];
-  // the tile's page list, page id * 32 + valid keys (read once per workgroup)
-  __shared__ int32_t sP[kMaxTilePages];
+  static_assert(GROUPS == 1 || GROUPS == 2, "one or two wave groups");
+  // Per wave group: K and V double buffers.  Then the tile's page list, page
+  // id * 32 + valid keys (read once per workgroup).  With two groups the
+  // buffers are reused after the loop for group 1's state (NDB * 16 + 2
+  // floats per thread).
+  constexpr int KV_BYTES = 2 * 32 * DH * (int)sizeof(T);
+  constexpr int XCH_BYTES = GROUPS > 1 ? (DH / 32 * 16 + 2) * 256 * 4 : 0;
+  constexpr int MAIN_BYTES = GROUPS * 2 * KV_BYTES + kMaxTilePages * 4;
+  __shared__ __attribute__((aligned(16))) char lds[MAIN_BYTES > XCH_BYTES ? MAIN_BYTES : XCH_BYTES];
+  int32_t* const sP = reinterpret_cast<int32_t*>(lds + GROUPS * 2 * KV_BYTES);
+  // per-group barrier counters (two groups): each wave adds 1 per barrier
+  __shared__ int gbar[2];
+  if (GROUPS > 1 && threadIdx.x < 2) gbar[threadIdx.x] = 0;
 
   // one workgroup per (tile, KV head); the KV head is the fast index, so that
   // neighbouring workgroups read the same pages (whose KV heads are adjacent)
@@ -176,7 +187,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int i = threadIdx.x; i < tile.n_pages; i += blockDim.x)
     sP[i] = plist[2 * (tile.page_off + i)] * 32 + plist[2 * (tile.page_off + i) + 1];
   const int G = hq / hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 31, hh = lane >> 5;
+  // wave group: with two, group g takes the g-th half of the tile's steps
+  const int grp = GROUPS > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 8) : 0;
+  T (*const sK)[32 * DH] = reinterpret_cast<T (*)[32 * DH]>(lds + grp * 2 * KV_BYTES);
+  T (*const sV)[DH * 32] = reinterpret_cast<T (*)[DH * 32]>(lds + grp * 2 * KV_BYTES + KV_BYTES);
+  const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6, c = lane & 31, hh = lane >> 5;
+  // Barrier of the step pipeline.  One group: the workgroup barrier.  Two:
+  // each group waits for its own four waves only (an LDS counter), so that
+  // the groups drift out of phase like two workgroups and overlap one's MFMAs
+  // with the other's exponentials; a shared barrier kept them in lockstep.
+  // The wait is bounded: past the limit a wave goes on (it cannot happen
+  // while every wave of a group runs the same steps).
+  int gtarget = 0;
+  auto step_sync = [&]() __attribute__((always_inline)) {
+    if constexpr (GROUPS == 1) {
+      __syncthreads();
+    } else {
+      gtarget += 4;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      if (lane == 0) __hip_atomic_fetch_add(&gbar[grp], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      for (int spin = 0; spin < (1 << 22); ++spin) {
+        const int seen = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(&gbar[grp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        if (seen >= gtarget) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+  };
   const int row = wave * 32 + c;
   const int ti = row / G, hg = row % G;
   const bool row_ok = ti < tile.n_tok;
@@ -196,7 +234,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   const T* kvbase = pool + layer_base + (size_t)kvh * 2 * PAGE_ELEMS;
-  const int nst = (tile.n_pages + 1) >> 1;
+  // steps of two pages: this group's first global step s0 and the loop count
+  // nst (the same for both groups, so that their barriers pair up; a group's
+  // steps past the tile's end have every key masked)
+  const int nst_all = (tile.n_pages + 1) >> 1;
+  const int nst = (nst_all + GROUPS - 1) / GROUPS;
+  const int s0 = grp * nst;
 
   // loop-invariant LDS offsets
   int koff[NKS];
@@ -222,8 +265,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // unrolled by two), so no register copy waits for loads still in flight.
   u32x4 rkA[2], rvA[2], rkB[2], rvB[2];
   // A window of 64 page-list entries, one per lane (entries pw_base + lane),
-  // read by readlane: a step needs entries 2st .. 2st+7, so the window is
-  // moved every 16 steps and page ids cost no memory access in between.
+  // read by readlane: a step needs entries 2st .. 2st+7 (global step st), so
+  // the window is moved every 16 steps and page ids cost no memory access in
+  // between.  Page indexes are clamped to the tile's last page, and so is the
+  // window's base.
   int pw = 0, pw_base = 0;
   auto page_entry = [&](int lp) -> int {
     return __builtin_amdgcn_readlane(pw, min(lp, tile.n_pages - 1) - pw_base);
@@ -237,13 +282,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint32_t pg = (uint32_t)page_entry(lp) >> 5;
     return reinterpret_cast<const T*>(kvbytes + (uint64_t)pg * page_bytes);
   };
+  // K or V of this group's step st (global step s0 + st)
   auto gload_k = [&](int st, u32x4* dst) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dst[i] = reinterpret_cast<const u32x4*>(page_ptr(2 * st + i))[tid];
+    for (int i = 0; i < 2; ++i) dst[i] = reinterpret_cast<const u32x4*>(page_ptr(2 * (s0 + st) + i))[tid];
   };
   auto gload_v = [&](int st, u32x4* dst) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dst[i] = reinterpret_cast<const u32x4*>(page_ptr(2 * st + i) + PAGE_ELEMS)[tid];
+    for (int i = 0; i < 2; ++i)
+      dst[i] = reinterpret_cast<const u32x4*>(page_ptr(2 * (s0 + st) + i) + PAGE_ELEMS)[tid];
   };
   auto sstore_k = [&](int buf, const u32x4* rk) {
 #pragma unroll
@@ -283,7 +330,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   float mrun = kNegInf, lrun = 0.f;
 
   __syncthreads();  // page list
-  pw = sP[min(lane, tile.n_pages - 1)];
+  pw_base = min(2 * s0, tile.n_pages - 1);
+  pw = sP[min(pw_base + lane, tile.n_pages - 1)];
   if (nst > 0) {
     // K and V of step 0 and K of step 1 in flight together (one load latency)
     gload_k(0, rkA);
@@ -296,12 +344,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     gload_k(2, rkA);
     gload_v(1, rvA);
   }
-  __syncthreads();
+  step_sync();
   f32x16 SA, SB;
   if (nst > 0) SA = qk(0);
   // step 0 stores K of step 2 into K buffer 0: every wave has to be done
   // reading K of step 0 from it first (once per tile)
-  if (nst > 2) __syncthreads();
+  if (nst > 2) step_sync();
   // One step: stores K of step st+2 and V of step st+1 from (kst, vst), loads
   // K of step st+3 and V of step st+2 into (kld, vld), turns S_in (scores of
   // step st) into probabilities and leaves the scores of step st+1 in S_out.
@@ -309,7 +357,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                   f32x16& S_out) __attribute__((always_inline)) {
     const int buf = st & 1;
     if (st > 0 && (st & 15) == 0) {
-      pw_base = 2 * st;
+      pw_base = min(2 * (s0 + st), tile.n_pages - 1);
       pw = sP[min(pw_base + lane, tile.n_pages - 1)];
     }
     // loads for the next step's stores
@@ -318,8 +366,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     f32x16& S = S_in;  // consumed here: masked in place
     // mask only where needed: partial pages, or keys past the wave's first query
-    const int lp0 = 2 * st;
-    const int v0 = page_entry(lp0) & 31;
+    const int lp0 = 2 * (s0 + st);
+    const int v0 = (lp0 < tile.n_pages) ? (page_entry(lp0) & 31) : 0;
     const int v1 = (lp0 + 1 < tile.n_pages) ? (page_entry(lp0 + 1) & 31) : 0;
     const bool mask = (v0 < 16) || (v1 < 16) || (tile.causal && tile.kv_pos0 + 16 * lp0 + 31 > qmin);
     if (mask) {
@@ -410,11 +458,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     if (st + 2 < nst) sstore_k(buf, kst);
     if (st + 1 < nst) sstore_v(buf ^ 1, vst);
-    __syncthreads();
+    step_sync();
   };
   for (int st = 0; st < nst; st += 2) {
     step(st, rkA, rvA, rkB, rvB, SA, SB);
     if (st + 1 < nst) step(st + 1, rkB, rvB, rkA, rvA, SB, SA);
+  }
+
+  if constexpr (GROUPS > 1) {
+    // group 1 leaves its running maximum, sum and unnormalised output in LDS
+    // (element k of thread tid at k * 256 + tid); group 0 rescales both to
+    // the larger maximum and adds them (the softmax over the union of the
+    // two key ranges)
+    float* const xo = reinterpret_cast<float*>(lds);
+    constexpr int NX = NDB * 16;
+    __syncthreads();  // both groups done with their buffers (the groups sync separately in the loop)
+    if (grp == 1) {
+#pragma unroll
+      for (int b = 0; b < NDB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[(b * 16 + r) * 256 + tid] = oacc[b][r];
+      xo[NX * 256 + tid] = mrun;
+      xo[(NX + 1) * 256 + tid] = lrun;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = xo[NX * 256 + tid], l1 = xo[(NX + 1) * 256 + tid];
+    const float mn = fmaxf(mrun, m1);
+    const float a0 = (mrun == kNegInf) ? 0.f : exp2f(mrun - mn);
+    const float a1 = (m1 == kNegInf) ? 0.f : exp2f(m1 - mn);
+    lrun = lrun * a0 + l1 * a1;
+#pragma unroll
+    for (int b = 0; b < NDB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[b][r] = oacc[b][r] * a0 + xo[(b * 16 + r) * 256 + tid] * a1;
+    mrun = mn;
   }
 
   if (!row_ok) return;
@@ -585,22 +663,31 @@ hipError_t launch_rmsnorm(const ModelDims& m, const void* x, const void* g, int3
 
 hipError_t launch_attention(const ModelDims& m, int32_t layer, const AttnTile* tiles, int32_t n_tiles,
                             const int32_t* page_list, const int32_t* tok_pos, const void* qbuf, const void* pool,
-                            void* o, float* part_o, float* part_lse, hipStream_t s) {
+                            void* o, float* part_o, float* part_lse, int32_t groups, hipStream_t s) {
   if (n_tiles <= 0) return hipSuccess;
+  if (groups != 1 && groups != 2) return hipErrorInvalidValue;
   const size_t layer_base = (size_t)layer * m.n_pages * m.hkv * 2 * 16 * m.dh;
   const float scale_log2 = float(1.4426950408889634 / std::sqrt((double)m.dh));
   dim3 grid(n_tiles * m.hkv);
+  const dim3 block(256 * groups);
+#define JEV_ATTN(T_, DH_, G_)                                                                              \
+  JEV_LAUNCH((dev::attn_kernel<T_, DH_, G_>), grid, block, 0, s, tiles, page_list, tok_pos,                 \
+             reinterpret_cast<const T_*>(qbuf), reinterpret_cast<const T_*>(pool), reinterpret_cast<T_*>(o), \
+             part_o, part_lse, m.hq, m.hkv, layer_base, scale_log2)
   if (m.dtype == 1 && m.dh == 128) {
-    JEV_LAUNCH((dev::attn_kernel<bf16s, 128>), grid, dim3(256), 0, s, tiles, page_list, tok_pos,
-                       reinterpret_cast<const bf16s*>(qbuf), reinterpret_cast<const bf16s*>(pool),
-                       reinterpret_cast<bf16s*>(o), part_o, part_lse, m.hq, m.hkv, layer_base, scale_log2);
+    if (groups == 2)
+      JEV_ATTN(bf16s, 128, 2);
+    else
+      JEV_ATTN(bf16s, 128, 1);
   } else if (m.dtype == 0 && m.dh == 64) {
-    JEV_LAUNCH((dev::attn_kernel<float, 64>), grid, dim3(256), 0, s, tiles, page_list, tok_pos,
-                       reinterpret_cast<const float*>(qbuf), reinterpret_cast<const float*>(pool),
-                       reinterpret_cast<float*>(o), part_o, part_lse, m.hq, m.hkv, layer_base, scale_log2);
+    if (groups == 2)
+      JEV_ATTN(float, 64, 2);
+    else
+      JEV_ATTN(float, 64, 1);
   } else {
     return hipErrorInvalidValue;
   }
+#undef JEV_ATTN
   return hipGetLastError();
 }
 

@@ -94,10 +94,12 @@ hipError_t launch_rmsnorm(const ModelDims& m, const void* x, const void* g, int3
 hipError_t launch_qkv(const ModelDims& m, const LayerW& w, int32_t layer, const void* h, int32_t T,
                       const int32_t* pos, const int32_t* kvslot, const float* rope, void* qbuf,
                       void* pool, const GemmWs& ws, hipStream_t s);
-// attention tiles (grid n_tiles x Hkv)
+// attention tiles (grid n_tiles x Hkv); groups = wave groups per workgroup (1
+// or 2: two split every tile's steps in halves, for rounds with long tiles)
 hipError_t launch_attention(const ModelDims& m, int32_t layer, const AttnTile* tiles, int32_t n_tiles,
                             const int32_t* page_list, const int32_t* tok_pos, const void* qbuf,
-                            const void* pool, void* o, float* part_o, float* part_lse, hipStream_t s);
+                            const void* pool, void* o, float* part_o, float* part_lse, int32_t groups,
+                            hipStream_t s);
 hipError_t launch_merge(const ModelDims& m, const MergeItem* items, int32_t n_items, const float* part_o,
                         const float* part_lse, void* o, hipStream_t s);
 // x += o Wo^T (stored)
