@@ -45,7 +45,8 @@ enum {
   JEV_ENOMEM = 2,  /* not enough free KV pages or workspace for the whole call */
   JEV_EHANDLE = 3, /* unknown or already released prefix handle */
   JEV_EHIP = 4,    /* a HIP call failed; the context is dead */
-  JEV_ESTATE = 5   /* operation not available on this context (e.g. device work on a planning-only context) */
+  JEV_ESTATE = 5,  /* operation not available on this context (e.g. device work on a planning-only context) */
+  JEV_EPENDING = 6 /* a scheduled request has not finished yet */
 };
 
 enum { JEV_DTYPE_F32 = 0, JEV_DTYPE_BF16 = 1 };
@@ -301,6 +302,59 @@ int jev_profile_read(jev_ctx* ctx, jev_launch_record* out, int64_t cap, int64_t*
 enum { JEV_ANSWER_NOUL = 0, JEV_ANSWER_CHOICE = 1, JEV_ANSWER_SCORE = 2 };
 int jev_answers(int32_t n, const float* probs, const int64_t* label_offsets, const int32_t* kinds, double* value,
                 int32_t* choice, double* confidence);
+
+/* ---------------------------------------------------------------------------
+ * Round-level continuous batching of requests from many callers (shared-prefix
+ * scoring article, "next steps" section: cross-request continuous batching
+ * for throughput).  A request is a set of candidates as for
+ * jev_score_candidates.  Callers on any thread submit requests; one driver
+ * thread calls jev_sched_step.  Each step: the requests submitted since the
+ * previous step join the active ones; the unfinished candidates of all active
+ * requests (in submission order, then candidate order) are planned together
+ * as one scoring call in depth rounds (shared prefixes across requests are
+ * computed once, reuse inside resident prefixes and the cache policy as for
+ * jev_score_candidates), and only the plan's first round runs.  That round's
+ * nodes with children become resident prefixes held by the scheduler, so the
+ * next step continues below them; candidates read out in the round are done.
+ * Held prefixes that no unfinished candidate of a started request passes
+ * through are then released.  Admission: jev_sched_submit refuses a request
+ * that does not fit an empty pool of the context's size on its own
+ * (JEV_ENOMEM); when a step's plan does not fit, the newest requests that have
+ * not started yet wait for a later step, until it fits.  Every step therefore advances each active request by
+ * one level of its candidate tree, and new requests join at their first level
+ * in the same GPU round.  Probabilities equal those of scoring each request
+ * alone, up to the rounding order of the bf16 kernels.
+ *
+ * The scheduler belongs to its context: destroy it before the context, and
+ * make no other call on the context while jev_sched_step runs. */
+typedef struct jev_sched jev_sched;
+enum { JEV_SCHED_QUEUED = 0, JEV_SCHED_ACTIVE = 1, JEV_SCHED_FINISHED = 2 };
+int jev_sched_create(jev_ctx* ctx, jev_sched** out);
+/* Waits for the context's last work, releases the held prefixes and frees the
+ * scheduler; requests not collected are dropped. */
+int jev_sched_destroy(jev_sched* s);
+/* Thread-safe.  Queues a request of n >= 1 candidates (arguments as for
+ * jev_score_candidates; copied, so the caller's arrays may be reused at once)
+ * and returns its ticket.  Errors: JEV_EINVAL (as jev_score_candidates). */
+int jev_sched_submit(jev_sched* s, int32_t n, const int32_t* tokens, const int64_t* tok_offsets,
+                     const int32_t* label_ids, const int64_t* label_offsets, int64_t* ticket);
+/* Runs one round on hip_stream (NULL: the default stream) and waits for it.
+ * If plan_out is not NULL it receives the plan the round was taken from, in
+ * jev_plan's format (candidates numbered in this step's order), and *plan_n
+ * its length in int32 words (plan_cap is its capacity).  An idle step (no
+ * unfinished candidate) does nothing and sets *plan_n = 0.  On a planning-only
+ * context the tree work is done and no kernel runs.  Errors: JEV_ENOMEM (the
+ * step's plan does not fit; nothing changes and the requests stay queued or
+ * active), JEV_EINVAL (plan_out too small), JEV_EHIP. */
+int jev_sched_step(jev_sched* s, void* hip_stream, int32_t* plan_out, int64_t plan_cap, int64_t* plan_n);
+/* Thread-safe: *state = JEV_SCHED_QUEUED, _ACTIVE or _FINISHED.
+ * Errors: JEV_EHANDLE (unknown ticket, or a result already collected). */
+int jev_sched_status(jev_sched* s, int64_t ticket, int32_t* state);
+/* Thread-safe: copies a finished request's probabilities (host float32, in
+ * its label_offsets layout; cap = entries available) and forgets the request.
+ * Errors: JEV_EPENDING (queued or active), JEV_EHANDLE (unknown or collected),
+ * JEV_ESTATE (planning-only context), JEV_EINVAL (probs NULL or too small). */
+int jev_sched_result(jev_sched* s, int64_t ticket, float* probs, int64_t cap);
 
 const char* jev_last_error(void);
 

@@ -81,6 +81,14 @@ class PagePool:
         for p in pages:
             heapq.heappush(self.free, p)
 
+    def take(self, pages: Sequence[int]) -> None:
+        """Marks the given free ids as used."""
+        gone = set(pages)
+        if not gone <= set(self.free):
+            raise ValueError("page not free")
+        self.free = [p for p in self.free if p not in gone]
+        heapq.heapify(self.free)
+
     def n_free(self) -> int:
         return len(self.free)
 
@@ -167,6 +175,16 @@ class ResidentTree:
             if self.nodes[c].tokens == toks:
                 return c
         return None
+
+    def adopt(self, parent: int, toks: Sequence[int], pages: Sequence[int]) -> int:
+        """A new node continuing `parent` whose K/V are already in `pages`
+        (free ids, taken here); one reference."""
+        self.pool.take(pages)
+        h = self.next_handle
+        self.next_handle += 1
+        self.nodes[h] = ResNode(h, parent, tuple(int(t) for t in toks), list(pages), self.end_pos(parent))
+        self._children(parent).append(h)
+        return h
 
     def release(self, h: int) -> None:
         """Drops one caller reference; without the cache policy, frees nodes
@@ -579,3 +597,132 @@ class Session:
                 "cached_prefixes": sum(1 for n in nodes if n.refs == 0),
                 "cached_pages": sum(len(n.pages) for n in nodes if n.refs == 0),
                 "evictions": self.tree.evictions}
+
+
+class Scheduler:
+    """Round-level continuous batching of requests on one session (the shared-
+    prefix scoring article's "next steps" name cross-request continuous
+    batching for throughput; this is the reading built here).
+
+    A request is a list of candidates.  Each step: the requests submitted since
+    the last step join the active ones; the unfinished candidates of all active
+    requests (request order, then candidate order) are planned together like
+    one scoring call (reuse inside resident nodes, depth rounds, evictions
+    under the cache policy), and only the first round runs.  Its nodes with
+    children become resident nodes held by the scheduler, so that the next
+    step continues below them; candidates read out in that round are done.
+    Held nodes that no unfinished candidate of a started request passes
+    through (by its resident match) are then released, oldest first; a
+    request still waiting pins nothing, since it might never fit beside what
+    it would pin.  Every step therefore advances each
+    active request by one level of its candidate tree, and new requests join
+    at their first level in the same GPU round.
+
+    Admission: a request that does not fit an empty pool on its own is
+    refused at submission.  When a step's plan does not fit, the newest
+    request that has not taken part in a step yet is left out of it (it waits
+    for a later step), until the plan fits; if the started requests alone do
+    not fit, the step fails and changes nothing."""
+
+    def __init__(self, session: Session):
+        self.s = session
+        self.queued: List[Tuple[int, List[List[int]]]] = []
+        self.active: List[dict] = []
+        self.done_tickets: List[int] = []
+        self.held: List[int] = []
+        self.next_ticket = 1
+
+    def submit(self, seqs: Sequence[Sequence[int]]) -> int:
+        alone = ResidentTree(PagePool(self.s.tree.pool.n_pages))
+        plan_candidates(alone, seqs, "depth")            # raises PoolExhausted
+        t = self.next_ticket
+        self.next_ticket += 1
+        self.queued.append((t, [[int(x) for x in q] for q in seqs]))
+        return t
+
+    def status(self, ticket: int) -> int:
+        """0 queued, 1 active, 2 finished."""
+        if any(t == ticket for t, _ in self.queued):
+            return 0
+        if any(r["ticket"] == ticket for r in self.active):
+            return 1
+        if ticket in self.done_tickets:
+            return 2
+        raise KeyError(ticket)
+
+    def _stage(self, seqs):
+        """A scoring call's tree work on a copy: splits in candidate order, the
+        plan, evictions under the cache policy (none in the candidates' paths)."""
+        import copy
+        t = copy.deepcopy(self.s.tree)
+        for q in seqs:
+            t.match_split(q)
+        pins = {x for q in seqs for x in t.path(t.match(q)[0])}
+        while True:
+            try:
+                return t, plan_candidates(t, seqs, "depth")
+            except PoolExhausted:
+                v = t.victim(pins) if t.keep else None
+                if v is None:
+                    raise
+                t.evict(v)
+
+    def step(self) -> Optional[Plan]:
+        """Runs one round; returns the plan it was taken from (None if idle)."""
+        import copy
+        for t, seqs in self.queued:
+            self.active.append({"ticket": t, "seqs": seqs, "done": [False] * len(seqs), "started": False})
+        self.queued = []
+        incl = [True] * len(self.active)
+        while True:
+            cands = [(ri, ci) for ri, r in enumerate(self.active) if incl[ri] for ci in range(len(r["seqs"]))
+                     if not r["done"][ci]]
+            if not cands:
+                return None
+            seqs = [self.active[ri]["seqs"][ci] for ri, ci in cands]
+            try:
+                t, plan = self._stage(seqs)
+                break
+            except PoolExhausted:
+                later = [ri for ri in range(len(self.active)) if incl[ri] and not self.active[ri]["started"]]
+                if not later:
+                    raise
+                incl[later[-1]] = False
+        for ri in range(len(self.active)):
+            if incl[ri]:
+                self.active[ri]["started"] = True
+        self.s.tree = t
+        self.s.clock += 1
+        t.stamp(plan.anchors, self.s.clock)
+        made = []
+        for x in plan.rounds[0]:
+            if x.children:
+                c0 = x.cand_min
+                off = plan.anchor_len[c0]
+                made.append(t.adopt(x.anchor, seqs[c0][off + x.a:off + x.b], x.pages))
+        t.stamp(made, self.s.clock)
+        self.held += made
+        for x in plan.rounds[0]:
+            for c in x.readout:
+                ri, ci = cands[c]
+                self.active[ri]["done"][ci] = True
+        still = []
+        for r in self.active:
+            if all(r["done"]):
+                self.done_tickets.append(r["ticket"])
+            else:
+                still.append(r)
+        self.active = still
+        needed = set()
+        for r in self.active:
+            for ci, q in enumerate(r["seqs"]):
+                if r["started"] and not r["done"][ci]:
+                    needed |= set(t.path(t.match(q)[0]))
+        keep_held = []
+        for h in self.held:
+            if h in needed:
+                keep_held.append(h)
+            else:
+                t.release(h)
+        self.held = keep_held
+        return plan

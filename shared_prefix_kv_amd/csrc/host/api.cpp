@@ -27,6 +27,7 @@
 #include <cstring>
 #include <map>
 #include <memory>
+#include <mutex>
 #include <set>
 #include <string>
 #include <vector>
@@ -256,7 +257,7 @@ std::set<int64_t> plan_pins(const jev::ResidentTree& t, int32_t n, const int32_t
 // (cache policy) until the plan fits.  The caller commits the copies or drops
 // them.
 int stage_candidates(jev_ctx* ctx, int32_t n, const int32_t* tok, const int64_t* off, jev::PagePool* pool,
-                     jev::ResidentTree* tree, jev::Plan* plan) {
+                     jev::ResidentTree* tree, jev::Plan* plan, jev::PlanMode mode) {
   *pool = ctx->pages;
   *tree = *ctx->tree;
   tree->rebind(pool);
@@ -265,7 +266,7 @@ int stage_candidates(jev_ctx* ctx, int32_t n, const int32_t* tok, const int64_t*
     tree->match_split(tok + off[c], off[c + 1] - off[c], &h, &m);
   }
   const std::set<int64_t> pinned = plan_pins(*tree, n, tok, off);
-  while (!jev::plan_candidates(*tree, pool, n, tok, off, plan, ctx->plan_mode))
+  while (!jev::plan_candidates(*tree, pool, n, tok, off, plan, mode))
     if (!tree->keep() || tree->evict_one(pinned) == 0) return fail(JEV_ENOMEM, "not enough free KV pages for the plan");
   return JEV_OK;
 }
@@ -881,6 +882,50 @@ int jev_score_branches(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const
   return run_rounds(ctx, rds, hb, probs, reinterpret_cast<hipStream_t>(hip_stream));
 }
 
+// The nodes of round r of a candidate plan, as the executor takes them;
+// returns their token count.  Candidate c's labels are
+// label_ids[label_offsets[c] ..) and its probabilities go to probs at the same
+// offsets.
+static int64_t plan_round_nodes(const jev::ResidentTree& tree, const jev::Plan& plan, size_t r, const int32_t* tokens,
+                         const int64_t* tok_offsets, const int32_t* label_ids, const int64_t* label_offsets,
+                         std::map<int64_t, std::vector<jev::PageRef>>* anchor_pages, std::vector<RNode>* out) {
+  int64_t computed = 0;
+  for (int32_t idx : plan.rounds[r]) {
+    const jev::PlanNode& x = plan.nodes[idx];
+    RNode nd;
+    const int32_t c0 = x.cand_min();
+    const int64_t alen = plan.anchor_len[c0];
+    // group: parent node id within the plan, or the anchor handle (negated, offset)
+    nd.group = x.parent >= 0 ? int64_t(plan.nodes[x.parent].id) : -1 - x.anchor;
+    if (x.anchor != 0) {
+      auto it = anchor_pages->find(x.anchor);
+      if (it == anchor_pages->end()) it = anchor_pages->emplace(x.anchor, tree.path_pages(x.anchor)).first;
+      nd.anc = it->second;
+    }
+    // plan ancestors, root first
+    std::vector<int32_t> chain;
+    for (int32_t p = x.parent; p >= 0; p = plan.nodes[p].parent) chain.push_back(p);
+    for (auto it = chain.rbegin(); it != chain.rend(); ++it) {
+      const jev::PlanNode& a = plan.nodes[*it];
+      const int64_t L = a.b - a.a;
+      for (size_t pi = 0; pi < a.pages.size(); ++pi) {
+        const int64_t v = L - int64_t(jev::kPage) * int64_t(pi);
+        nd.anc.push_back(jev::PageRef{a.pages[pi], int32_t(v < jev::kPage ? v : jev::kPage)});
+      }
+    }
+    nd.tok = tokens + tok_offsets[c0] + alen + x.a;
+    nd.n = x.b - x.a;
+    nd.start = alen + x.a;
+    nd.pages = x.pages;
+    for (int32_t c : x.readout)
+      nd.reads.push_back(ReadSpec{c, label_ids + label_offsets[c], int32_t(label_offsets[c + 1] - label_offsets[c]),
+                                  label_offsets[c]});
+    computed += nd.n;
+    out->push_back(std::move(nd));
+  }
+  return computed;
+}
+
 int jev_score_candidates(jev_ctx* ctx, int32_t n, const int32_t* tokens, const int64_t* tok_offsets,
                          const int32_t* label_ids, const int64_t* label_offsets, float* probs, void* hip_stream) {
   if (int rc = check_alive(ctx)) return rc;
@@ -896,7 +941,7 @@ int jev_score_candidates(jev_ctx* ctx, int32_t n, const int32_t* tokens, const i
   {
     jev::PagePool pool;
     jev::ResidentTree tree(&pool);
-    if (int rc = stage_candidates(ctx, n, tokens, tok_offsets, &pool, &tree, &plan)) return rc;
+    if (int rc = stage_candidates(ctx, n, tokens, tok_offsets, &pool, &tree, &plan, ctx->plan_mode)) return rc;
     ctx->pages = pool;
     *ctx->tree = std::move(tree);
     ctx->tree->rebind(&ctx->pages);
@@ -908,41 +953,9 @@ int jev_score_candidates(jev_ctx* ctx, int32_t n, const int32_t* tokens, const i
   std::map<int64_t, std::vector<jev::PageRef>> anchor_pages;
   int64_t computed = 0, logical = 0;
   for (int32_t c = 0; c < n; ++c) logical += tok_offsets[c + 1] - tok_offsets[c];
-  for (size_t r = 0; r < plan.rounds.size(); ++r) {
-    for (int32_t idx : plan.rounds[r]) {
-      const jev::PlanNode& x = plan.nodes[idx];
-      RNode nd;
-      const int32_t c0 = x.cand_min();
-      const int64_t alen = plan.anchor_len[c0];
-      // group: parent node id within the plan, or the anchor handle (negated, offset)
-      nd.group = x.parent >= 0 ? int64_t(plan.nodes[x.parent].id) : -1 - x.anchor;
-      if (x.anchor != 0) {
-        auto it = anchor_pages.find(x.anchor);
-        if (it == anchor_pages.end()) it = anchor_pages.emplace(x.anchor, ctx->tree->path_pages(x.anchor)).first;
-        nd.anc = it->second;
-      }
-      // plan ancestors, root first
-      std::vector<int32_t> chain;
-      for (int32_t p = x.parent; p >= 0; p = plan.nodes[p].parent) chain.push_back(p);
-      for (auto it = chain.rbegin(); it != chain.rend(); ++it) {
-        const jev::PlanNode& a = plan.nodes[*it];
-        const int64_t L = a.b - a.a;
-        for (size_t pi = 0; pi < a.pages.size(); ++pi) {
-          const int64_t v = L - int64_t(jev::kPage) * int64_t(pi);
-          nd.anc.push_back(jev::PageRef{a.pages[pi], int32_t(v < jev::kPage ? v : jev::kPage)});
-        }
-      }
-      nd.tok = tokens + tok_offsets[c0] + alen + x.a;
-      nd.n = x.b - x.a;
-      nd.start = alen + x.a;
-      nd.pages = x.pages;
-      for (int32_t c : x.readout)
-        nd.reads.push_back(ReadSpec{c, label_ids + label_offsets[c],
-                                    int32_t(label_offsets[c + 1] - label_offsets[c]), label_offsets[c]});
-      computed += nd.n;
-      rounds[r].push_back(std::move(nd));
-    }
-  }
+  for (size_t r = 0; r < plan.rounds.size(); ++r)
+    computed += plan_round_nodes(*ctx->tree, plan, r, tokens, tok_offsets, label_ids, label_offsets, &anchor_pages,
+                                 &rounds[r]);
   std::vector<int32_t> hb;
   std::vector<RoundDesc> rds(rounds.size());
   for (size_t r = 0; r < rounds.size(); ++r)
@@ -953,6 +966,282 @@ int jev_score_candidates(jev_ctx* ctx, int32_t n, const int32_t* tokens, const i
   ctx->stats.rounds = int32_t(rounds.size());
   ctx->stats.calls += 1;
   return run_rounds(ctx, rds, hb, probs, reinterpret_cast<hipStream_t>(hip_stream));
+}
+
+// ----------------------------------------------------------------- scheduler
+// Round-level continuous batching (see jev.h).  submit/status/result take the
+// mutex and touch only the request lists; step is the single driver of the
+// context.
+
+struct jev_sched {
+  jev_ctx* ctx = nullptr;
+  std::mutex mu;
+  struct Req {
+    int64_t ticket = 0;
+    std::vector<int32_t> tok, lab;
+    std::vector<int64_t> off, loff;
+    std::vector<char> done;
+    std::vector<float> probs;  // host, in label_offsets layout
+    bool started = false;      // took part in a step
+  };
+  std::vector<std::unique_ptr<Req>> queued;            // submitted, not yet stepped
+  std::vector<std::unique_ptr<Req>> active;            // step thread only
+  std::map<int64_t, std::unique_ptr<Req>> finished;    // until their result is taken
+  std::set<int64_t> active_tickets;                    // under mu
+  std::vector<int64_t> held;                           // resident handles the scheduler holds
+  int64_t next_ticket = 1;
+  int32_t n_pages = 0;  // the context's page count (fixed at creation)
+  float* dprobs = nullptr;
+  int64_t dprobs_cap = 0;
+};
+
+int jev_sched_create(jev_ctx* ctx, jev_sched** out) {
+  if (int rc = check_alive(ctx)) return rc;
+  if (!out) return fail(JEV_EINVAL, "NULL out");
+  auto* s = new jev_sched();
+  s->ctx = ctx;
+  s->n_pages = ctx->pages.n_total();
+  *out = s;
+  return JEV_OK;
+}
+
+int jev_sched_destroy(jev_sched* s) {
+  if (!s) return JEV_OK;
+  jev_ctx* ctx = s->ctx;
+  int rc = JEV_OK;
+  if (!ctx->dry && ctx->have_last && hipEventSynchronize(ctx->last_done) != hipSuccess)
+    rc = fail(JEV_EHIP, "sync failed");
+  for (int64_t h : s->held) ctx->tree->release(h);
+  if (s->dprobs) (void)hipFree(s->dprobs);
+  delete s;
+  return rc;
+}
+
+int jev_sched_submit(jev_sched* s, int32_t n, const int32_t* tokens, const int64_t* tok_offsets,
+                     const int32_t* label_ids, const int64_t* label_offsets, int64_t* ticket) {
+  if (!s || !ticket) return fail(JEV_EINVAL, "NULL scheduler or ticket");
+  const jev_ctx* ctx = s->ctx;
+  if (n < 1) return fail(JEV_EINVAL, "a request needs at least one candidate");
+  if (int rc = check_segments(ctx, n, tokens, tok_offsets, "candidates")) return rc;
+  if (int rc = check_labels(ctx, n, label_ids, label_offsets)) return rc;
+  for (int32_t i = 0; i < n; ++i)
+    if (tok_offsets[i + 1] - tok_offsets[i] > ctx->desc.max_positions)
+      return fail(JEV_EINVAL, "candidate " + std::to_string(i) + " runs past max_positions");
+  {
+    // a request that cannot run even alone on an empty pool would wait forever
+    jev::PagePool pool(s->n_pages);
+    jev::ResidentTree tree(&pool);
+    jev::Plan plan;
+    if (!jev::plan_candidates(tree, &pool, n, tokens, tok_offsets, &plan, jev::PlanMode::DEPTH))
+      return fail(JEV_ENOMEM, "the request does not fit the page pool even alone");
+  }
+  auto r = std::make_unique<jev_sched::Req>();
+  r->tok.assign(tokens, tokens + tok_offsets[n]);
+  r->off.assign(tok_offsets, tok_offsets + n + 1);
+  r->lab.assign(label_ids, label_ids + label_offsets[n]);
+  r->loff.assign(label_offsets, label_offsets + n + 1);
+  r->done.assign(size_t(n), 0);
+  r->probs.assign(size_t(label_offsets[n]), 0.f);
+  std::lock_guard<std::mutex> lk(s->mu);
+  r->ticket = s->next_ticket++;
+  *ticket = r->ticket;
+  s->queued.push_back(std::move(r));
+  return JEV_OK;
+}
+
+int jev_sched_status(jev_sched* s, int64_t ticket, int32_t* state) {
+  if (!s || !state) return fail(JEV_EINVAL, "NULL scheduler or state");
+  std::lock_guard<std::mutex> lk(s->mu);
+  for (const auto& r : s->queued)
+    if (r->ticket == ticket) return *state = JEV_SCHED_QUEUED, JEV_OK;
+  if (s->active_tickets.count(ticket)) return *state = JEV_SCHED_ACTIVE, JEV_OK;
+  if (s->finished.count(ticket)) return *state = JEV_SCHED_FINISHED, JEV_OK;
+  return fail(JEV_EHANDLE, "unknown or collected ticket " + std::to_string(ticket));
+}
+
+int jev_sched_result(jev_sched* s, int64_t ticket, float* probs, int64_t cap) {
+  if (!s) return fail(JEV_EINVAL, "NULL scheduler");
+  std::lock_guard<std::mutex> lk(s->mu);
+  auto it = s->finished.find(ticket);
+  if (it == s->finished.end()) {
+    for (const auto& r : s->queued)
+      if (r->ticket == ticket) return fail(JEV_EPENDING, "request " + std::to_string(ticket) + " not finished");
+    if (s->active_tickets.count(ticket)) return fail(JEV_EPENDING, "request " + std::to_string(ticket) + " not finished");
+    return fail(JEV_EHANDLE, "unknown or collected ticket " + std::to_string(ticket));
+  }
+  if (s->ctx->dry) return fail(JEV_ESTATE, "no scores on a planning-only context");
+  const std::vector<float>& p = it->second->probs;
+  if (!probs || cap < int64_t(p.size())) return fail(JEV_EINVAL, "probs NULL or cap below the request's label count");
+  std::memcpy(probs, p.data(), p.size() * sizeof(float));
+  s->finished.erase(it);
+  return JEV_OK;
+}
+
+int jev_sched_step(jev_sched* s, void* hip_stream, int32_t* plan_out, int64_t plan_cap, int64_t* plan_n) {
+  if (!s) return fail(JEV_EINVAL, "NULL scheduler");
+  jev_ctx* ctx = s->ctx;
+  if (int rc = check_alive(ctx)) return rc;
+  if (plan_n) *plan_n = 0;
+  {
+    std::lock_guard<std::mutex> lk(s->mu);
+    for (auto& r : s->queued) {
+      s->active_tickets.insert(r->ticket);
+      s->active.push_back(std::move(r));
+    }
+    s->queued.clear();
+  }
+  // this step's candidates: unfinished ones of the included requests, in
+  // order.  All active requests are included; while the plan does not fit,
+  // the newest request that has not started yet waits for a later step.
+  struct Ref {
+    size_t req;
+    int32_t cand;
+  };
+  std::vector<char> incl(s->active.size(), 1);
+  std::vector<Ref> refs;
+  std::vector<int32_t> tok, lab;
+  std::vector<int64_t> off, loff;
+  jev::Plan plan;
+  jev::PagePool pool;
+  jev::ResidentTree tree(&pool);
+  for (;;) {
+    refs.clear();
+    tok.clear();
+    lab.clear();
+    off.assign(1, 0);
+    loff.assign(1, 0);
+    for (size_t ri = 0; ri < s->active.size(); ++ri) {
+      if (!incl[ri]) continue;
+      const auto& r = *s->active[ri];
+      for (int32_t c = 0; c + 1 < int32_t(r.off.size()); ++c) {
+        if (r.done[size_t(c)]) continue;
+        refs.push_back(Ref{ri, c});
+        tok.insert(tok.end(), r.tok.begin() + r.off[size_t(c)], r.tok.begin() + r.off[size_t(c) + 1]);
+        off.push_back(int64_t(tok.size()));
+        lab.insert(lab.end(), r.lab.begin() + r.loff[size_t(c)], r.lab.begin() + r.loff[size_t(c) + 1]);
+        loff.push_back(int64_t(lab.size()));
+      }
+    }
+    if (refs.empty()) return JEV_OK;
+    const int rc = stage_candidates(ctx, int32_t(refs.size()), tok.data(), off.data(), &pool, &tree, &plan,
+                                    jev::PlanMode::DEPTH);
+    if (rc == JEV_OK) break;
+    if (rc != JEV_ENOMEM) return rc;
+    size_t drop = s->active.size();
+    for (size_t ri = s->active.size(); ri-- > 0;)
+      if (incl[ri] && !s->active[ri]->started) {
+        drop = ri;
+        break;
+      }
+    if (drop == s->active.size()) return rc;  // the started requests alone do not fit
+    incl[drop] = 0;
+  }
+  if (plan_out) {
+    const std::vector<int32_t> img = plan.serialize();
+    if (plan_cap < int64_t(img.size())) return fail(JEV_EINVAL, "plan_out too small");
+    std::copy(img.begin(), img.end(), plan_out);
+    if (plan_n) *plan_n = int64_t(img.size());
+  }
+  // the first round, against the staged tree (anchors may be split heads)
+  std::vector<RNode> rn;
+  std::map<int64_t, std::vector<jev::PageRef>> anchor_pages;
+  const int64_t computed =
+      plan_round_nodes(tree, plan, 0, tok.data(), off.data(), lab.data(), loff.data(), &anchor_pages, &rn);
+  std::vector<int32_t> hb;
+  std::vector<RoundDesc> rds(1);
+  if (!ctx->dry) {
+    if (int rc = build_round(ctx, rn, hb, &rds[0])) return rc;
+    if (int64_t(hb.size()) > ctx->L.desc_ints)
+      return fail(JEV_ENOMEM, "call descriptors exceed the workspace descriptor region");
+    if (s->dprobs_cap < loff.back()) {
+      if (s->dprobs) HIPCHK(hipFree(s->dprobs));
+      s->dprobs = nullptr;
+      s->dprobs_cap = 0;
+      if (hipMalloc(reinterpret_cast<void**>(&s->dprobs), size_t(loff.back()) * sizeof(float)) != hipSuccess)
+        return fail(JEV_ENOMEM, "device buffer for the step's probabilities");
+      s->dprobs_cap = loff.back();
+    }
+  }
+  // commit: the staged tree and pool, then the round's nodes with children
+  // become resident nodes held by the scheduler
+  ctx->pages = pool;
+  *ctx->tree = std::move(tree);
+  ctx->tree->rebind(&ctx->pages);
+  ctx->clock += 1;
+  for (int64_t h : plan.anchors) ctx->tree->touch_path(h, ctx->clock);
+  for (size_t ri = 0; ri < s->active.size(); ++ri)
+    if (incl[ri]) s->active[ri]->started = true;
+  for (int32_t idx : plan.rounds[0]) {
+    const jev::PlanNode& x = plan.nodes[idx];
+    if (x.children.empty()) continue;
+    const int32_t c0 = x.cand_min();
+    const int64_t h =
+        ctx->tree->adopt(x.anchor, tok.data() + off[c0] + plan.anchor_len[c0] + x.a, x.b - x.a, x.pages);
+    if (h == 0) {
+      ctx->dead = true;
+      return fail(JEV_ESTATE, "internal: a planned page is not free");
+    }
+    ctx->tree->touch_path(h, ctx->clock);
+    s->held.push_back(h);
+  }
+  int64_t logical = 0;
+  for (int32_t idx : plan.rounds[0])
+    for (int32_t c : plan.nodes[idx].readout) logical += off[c + 1] - off[c];
+  ctx->stats.logical_tokens = logical;
+  ctx->stats.computed_tokens = computed;
+  ctx->stats.cached_tokens = logical - computed;
+  ctx->stats.rounds = 1;
+  ctx->stats.calls += 1;
+  if (!ctx->dry) {
+    const hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+    if (int rc = run_rounds(ctx, rds, hb, s->dprobs, st)) return rc;
+    std::vector<float> hp(size_t(loff.back()));
+    HIPCHK(hipMemcpyAsync(hp.data(), s->dprobs, hp.size() * sizeof(float), hipMemcpyDeviceToHost, st));
+    HIPCHK(hipStreamSynchronize(st));
+    for (int32_t idx : plan.rounds[0])
+      for (int32_t c : plan.nodes[idx].readout) {
+        auto& r = *s->active[refs[size_t(c)].req];
+        const int32_t rc_ = refs[size_t(c)].cand;
+        std::copy(hp.begin() + loff[c], hp.begin() + loff[c + 1], r.probs.begin() + r.loff[size_t(rc_)]);
+      }
+  }
+  for (int32_t idx : plan.rounds[0])
+    for (int32_t c : plan.nodes[idx].readout) s->active[refs[size_t(c)].req]->done[size_t(refs[size_t(c)].cand)] = 1;
+  {
+    std::vector<std::unique_ptr<jev_sched::Req>> still;
+    std::lock_guard<std::mutex> lk(s->mu);
+    for (auto& r : s->active) {
+      bool all = true;
+      for (char d : r->done) all = all && d;
+      if (all) {
+        s->active_tickets.erase(r->ticket);
+        s->finished.emplace(r->ticket, std::move(r));
+      } else {
+        still.push_back(std::move(r));
+      }
+    }
+    s->active = std::move(still);
+  }
+  // release held nodes that no unfinished candidate of a started request
+  // passes through (a waiting request does not pin them: it might never fit
+  // beside them)
+  std::set<int64_t> needed;
+  for (const auto& r : s->active)
+    for (int32_t c = 0; r->started && c + 1 < int32_t(r->off.size()); ++c) {
+      if (r->done[size_t(c)]) continue;
+      int64_t h, m;
+      ctx->tree->match(r->tok.data() + r->off[size_t(c)], r->off[size_t(c) + 1] - r->off[size_t(c)], &h, &m);
+      for (; h != 0 && !needed.count(h); h = ctx->tree->node(h).parent) needed.insert(h);
+    }
+  std::vector<int64_t> keep;
+  for (int64_t h : s->held) {
+    if (needed.count(h))
+      keep.push_back(h);
+    else
+      ctx->tree->release(h);
+  }
+  s->held = std::move(keep);
+  return JEV_OK;
 }
 
 int jev_set_plan_mode(jev_ctx* ctx, int32_t mode) {
@@ -1001,7 +1290,7 @@ int jev_plan(jev_ctx* ctx, int32_t n, const int32_t* tokens, const int64_t* tok_
     // what jev_score_candidates would do (splits and evictions included), on copies
     jev::PagePool pool;
     jev::ResidentTree tree(&pool);
-    if (int rc = stage_candidates(ctx, n, tokens, tok_offsets, &pool, &tree, &plan)) return rc;
+    if (int rc = stage_candidates(ctx, n, tokens, tok_offsets, &pool, &tree, &plan, ctx->plan_mode)) return rc;
   }
   std::vector<int32_t> s = n > 0 ? plan.serialize() : std::vector<int32_t>{0, 0};
   *out_len = int64_t(s.size());

@@ -81,6 +81,20 @@ void ResidentTree::prefill(const std::vector<PrefillItem>& items, std::vector<in
   }
 }
 
+int64_t ResidentTree::adopt(int64_t parent, const int32_t* tok, int64_t n, const std::vector<int32_t>& pages) {
+  if (!pool_->take(pages)) return 0;
+  const int64_t h = next_handle_++;
+  ResNode nd;
+  nd.handle = h;
+  nd.parent = parent;
+  nd.tokens.assign(tok, tok + n);
+  nd.pages = pages;
+  nd.start = end_pos(parent);
+  nodes_.emplace(h, std::move(nd));
+  children_mut(parent).push_back(h);
+  return h;
+}
+
 void ResidentTree::release(int64_t h) {
   ResNode* n = &nodes_.at(h);
   n->refs -= 1;

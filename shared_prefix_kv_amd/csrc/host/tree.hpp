@@ -54,6 +54,13 @@ class PagePool {
   void release(const std::vector<int32_t>& pages) {
     for (int32_t p : pages) free_.insert(p);
   }
+  // Marks the given ids as used; false (and no change) if one is not free.
+  bool take(const std::vector<int32_t>& pages) {
+    for (int32_t p : pages)
+      if (!free_.count(p)) return false;
+    for (int32_t p : pages) free_.erase(p);
+    return true;
+  }
   std::set<int32_t> snapshot() const { return free_; }
   void restore(std::set<int32_t> s) { free_ = std::move(s); }
 
@@ -112,6 +119,10 @@ class ResidentTree {
   // whether it is new.  Caller has checked prefill_need() against the pool.
   void prefill(const std::vector<PrefillItem>& items, std::vector<int64_t>* out,
                std::vector<char>* created);
+  // A new node continuing `parent` with tokens tok[0..n) whose K/V are
+  // already in `pages` (free ids, taken from the pool here); one reference.
+  // Returns its handle, or 0 if a page is not free.
+  int64_t adopt(int64_t parent, const int32_t* tok, int64_t n, const std::vector<int32_t>& pages);
   // Drops one reference; without keep(), frees nodes with no reference and no child.
   void release(int64_t h);
   void set_keep(bool keep) { keep_ = keep; }

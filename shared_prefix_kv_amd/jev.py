@@ -9,25 +9,28 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import List, Optional, Sequence, Tuple
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libjev.so")
 
-JEV_OK, JEV_EINVAL, JEV_ENOMEM, JEV_EHANDLE, JEV_EHIP, JEV_ESTATE = range(6)
+JEV_OK, JEV_EINVAL, JEV_ENOMEM, JEV_EHANDLE, JEV_EHIP, JEV_ESTATE, JEV_EPENDING = range(7)
 JEV_DTYPE_F32, JEV_DTYPE_BF16 = 0, 1
 JEV_TAP_ATTN, JEV_TAP_RESID = 0, 1
 JEV_ANSWER_NOUL, JEV_ANSWER_CHOICE, JEV_ANSWER_SCORE = 0, 1, 2
 JEV_PLAN_DEPTH, JEV_PLAN_CANDIDATE_FIRST = 0, 1
 JEV_CACHE_RELEASE, JEV_CACHE_LRU = 0, 1
-_NAMES = {0: "JEV_OK", 1: "JEV_EINVAL", 2: "JEV_ENOMEM", 3: "JEV_EHANDLE", 4: "JEV_EHIP", 5: "JEV_ESTATE"}
+JEV_SCHED_QUEUED, JEV_SCHED_ACTIVE, JEV_SCHED_FINISHED = 0, 1, 2
+_NAMES = {0: "JEV_OK", 1: "JEV_EINVAL", 2: "JEV_ENOMEM", 3: "JEV_EHANDLE", 4: "JEV_EHIP", 5: "JEV_ESTATE",
+          6: "JEV_EPENDING"}
 
 EXPORTED = ["jev_workspace_bytes", "jev_kv_pool_bytes", "jev_create", "jev_destroy", "jev_prefill_prefix",
             "jev_score_branches", "jev_score_candidates", "jev_free_pages", "jev_plan", "jev_page_table",
             "jev_match", "jev_stats", "jev_debug_tap", "jev_profile", "jev_profile_read", "jev_answers",
-            "jev_set_plan_mode", "jev_set_cache_policy", "jev_last_error"]
+            "jev_set_plan_mode", "jev_set_cache_policy", "jev_sched_create", "jev_sched_destroy",
+            "jev_sched_submit", "jev_sched_step", "jev_sched_status", "jev_sched_result", "jev_last_error"]
 KERNELS = ["embed", "rmsnorm", "qkv", "attn", "merge", "oproj", "readout"]
 
 
@@ -98,6 +101,12 @@ def lib() -> ctypes.CDLL:
         L.jev_set_cache_policy.argtypes = [vp, i32]
         L.jev_answers.argtypes = [i32, P(ctypes.c_float), P(i64), P(i32), P(ctypes.c_double), P(i32),
                                   P(ctypes.c_double)]
+        L.jev_sched_create.argtypes = [vp, P(vp)]
+        L.jev_sched_destroy.argtypes = [vp]
+        L.jev_sched_submit.argtypes = [vp, i32, P(i32), P(i64), P(i32), P(i64), P(i64)]
+        L.jev_sched_step.argtypes = [vp, vp, P(i32), i64, P(i64)]
+        L.jev_sched_status.argtypes = [vp, i64, P(i32)]
+        L.jev_sched_result.argtypes = [vp, i64, P(ctypes.c_float), i64]
         L.jev_last_error.restype = ctypes.c_char_p
         _lib = L
     return _lib
@@ -330,6 +339,63 @@ class Context:
                 return _NullTensor()
             probs = torch.empty(n, dtype=torch.float32, device=self.pool.device)
         return probs
+
+
+class Scheduler:
+    """Round-level continuous batching on a context (jev_sched_*): submit() from
+    any thread, step() from one driver thread, result() once finished."""
+
+    def __init__(self, ctx: Context):
+        self.owner = ctx
+        s = ctypes.c_void_p()
+        _check(lib().jev_sched_create(ctx.ctx, ctypes.byref(s)))
+        self.s = s
+        self._loff: Dict[int, np.ndarray] = {}
+
+    def close(self) -> None:
+        if self.s:
+            _check(lib().jev_sched_destroy(self.s))
+            self.s = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def submit(self, seqs, labels) -> int:
+        flat, off = _segments(seqs)
+        lflat, loff = _segments(labels)
+        t = ctypes.c_int64()
+        _check(lib().jev_sched_submit(self.s, len(seqs), _ptr(flat, ctypes.c_int32), _ptr(off, ctypes.c_int64),
+                                      _ptr(lflat, ctypes.c_int32), _ptr(loff, ctypes.c_int64), ctypes.byref(t)))
+        self._loff[t.value] = loff
+        return t.value
+
+    def step(self, stream=None, want_plan: bool = False) -> Optional[List[int]]:
+        """One round; with want_plan, the plan it was taken from (jev_plan format)."""
+        n = ctypes.c_int64()
+        st = stream or self.owner._stream()
+        if not want_plan:
+            _check(lib().jev_sched_step(self.s, st, None, 0, ctypes.byref(n)))
+            return None
+        cap = 1 << 20
+        buf = np.zeros(cap, dtype=np.int32)
+        _check(lib().jev_sched_step(self.s, st, _ptr(buf, ctypes.c_int32), cap, ctypes.byref(n)))
+        return [int(v) for v in buf[:n.value]]
+
+    def status(self, ticket: int) -> int:
+        st = ctypes.c_int32()
+        _check(lib().jev_sched_status(self.s, ticket, ctypes.byref(st)))
+        return st.value
+
+    def result(self, ticket: int) -> List[np.ndarray]:
+        """Per candidate, its label probabilities (host float32)."""
+        loff = self._loff[ticket]
+        out = np.zeros(int(loff[-1]), dtype=np.float32)
+        _check(lib().jev_sched_result(self.s, ticket, _ptr(out, ctypes.c_float), len(out)))
+        del self._loff[ticket]
+        return [out[loff[i]:loff[i + 1]] for i in range(len(loff) - 1)]
 
 
 class _NullTensor:

@@ -172,6 +172,35 @@ def test_w1_unshared_and_candidate_paths_match_oracle(w1):
     assert ctx.stats()["rounds"] == 2 and ctx.stats()["pages_in_use"] == 0
 
 
+def test_w1_scheduler_requests_match_oracle(w1):
+    """Three requests through the scheduler: two submitted together, one (new
+    branches over the same prefix plus a second state) after the first step.
+    Each request's distributions match the oracle from scratch."""
+    from shared_prefix_kv_amd import jev
+    wl, inst, m, ref, ctx, _ = w1
+    seqs = inst.full_sequences(0)
+    P = inst.prefixes[0]
+    rng = np.random.default_rng(5)
+    third = [[int(t) for t in P] + [int(t) for t in rng.integers(0, wl.model.vocab, 9 + i)] for i in range(2)]
+    third.append([int(t) for t in rng.integers(0, wl.model.vocab, 40)])
+    lab3 = [b.labels for b in inst.passes[0][:3]]
+    sch = jev.Scheduler(ctx)
+    ta = sch.submit([s for s, _ in seqs[:2]], [l for _, l in seqs[:2]])
+    tb = sch.submit([s for s, _ in seqs[2:]], [l for _, l in seqs[2:]])
+    sch.step()
+    tc = sch.submit(third, lab3)
+    for _ in range(10):
+        if all(sch.status(t) == jev.JEV_SCHED_FINISHED for t in (ta, tb, tc)):
+            break
+        sch.step()
+    got_ab = sch.result(ta) + sch.result(tb)
+    assert max_abs(got_ab, ref) <= TOL_F32
+    want_c = om.score_from_scratch(m, third, lab3)
+    assert max_abs(sch.result(tc), want_c) <= TOL_F32
+    sch.close()
+    assert ctx.stats()["pages_in_use"] == 0
+
+
 def test_w1_attention_output_matches_oracle(w1):
     wl, inst, m, ref, ctx, _ = w1
     (h,) = ctx.prefill_prefix([0], [inst.prefixes[0]])
@@ -476,6 +505,33 @@ def test_w3_staged_rounds_match_oracle(w2):
     st = ctx.stats()
     assert st["rounds"] == 3 and st["computed_tokens"] == 800 + 120 + 240
     assert st["pages_in_use"] == 0
+
+
+def test_w3_requests_through_the_continuous_batching_scheduler(w2):
+    """Workload 3's candidates as two requests, the second submitted after the
+    first step: every distribution matches the stored oracle values, and the
+    scheduler leaves no page behind."""
+    from shared_prefix_kv_amd import jev
+    g = golden(3)
+    inst = make_instance(workload(3))
+    ctx, _ = device_context(3, n_pages=1024, max_pos=4096, max_tok=4096)
+    sch = jev.Scheduler(ctx)
+    C, L = inst.candidates, inst.cand_labels
+    h = len(C) // 2
+    t1 = sch.submit(C[:h], L[:h])
+    sch.step()
+    t2 = sch.submit(C[h:], L[h:])
+    steps = 1
+    while sch.status(t1) != jev.JEV_SCHED_FINISHED or sch.status(t2) != jev.JEV_SCHED_FINISHED:
+        sch.step()
+        steps += 1
+        assert steps < 20
+    got = sch.result(t1) + sch.result(t2)
+    err = max_abs(got, g["passes"][0]["probs"])
+    print("w3 scheduler max abs err", err, "steps", steps)
+    assert err <= TOL_BF16_E2E
+    sch.close()
+    assert ctx.stats()["pages_in_use"] == 0
 
 
 # ------------------------------------------------------------------ workload 4 (batch of requests)
