@@ -156,7 +156,9 @@ int jev_score_branches(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const
  * grouped into a token-prefix tree and computed in staged rounds whose order
  * is the context's plan mode (jev_set_plan_mode); every candidate is read out
  * exactly once; probs as for jev_score_branches, in input order.  Pages of the
- * call's own tree nodes are released when it ends.
+ * call's own tree nodes are released when it ends; with JEV_CACHE_LRU the
+ * nodes its candidates share stay as cached prefixes instead (automatic
+ * checkpoints of a repeated state, evicted least recently used first).
  * Errors: as jev_score_branches. */
 int jev_score_candidates(jev_ctx* ctx, int32_t n, const int32_t* tokens, const int64_t* tok_offsets,
                          const int32_t* label_ids, const int64_t* label_offsets, float* probs,

@@ -965,6 +965,32 @@ int jev_score_candidates(jev_ctx* ctx, int32_t n, const int32_t* tokens, const i
   ctx->stats.cached_tokens = logical - computed;
   ctx->stats.rounds = int32_t(rounds.size());
   ctx->stats.calls += 1;
+  if (ctx->tree->keep()) {
+    // Automatic checkpoints (cache policy on): the call's nodes with children,
+    // i.e. the prefixes its candidates share, stay resident as cached
+    // prefixes (no reference) holding the pages the call writes, so a later
+    // call over the same state reuses them.  Parents come before
+    // children.  Done once nothing can fail before the rounds run.
+    std::vector<int64_t> handle_of(plan.nodes.size(), 0);
+    std::vector<int64_t> made;
+    for (const auto& rnd : plan.rounds)
+      for (int32_t idx : rnd) {
+        const jev::PlanNode& x = plan.nodes[idx];
+        if (x.children.empty()) continue;
+        const int64_t parent = x.parent >= 0 ? handle_of[size_t(x.parent)] : x.anchor;
+        const int32_t c0 = x.cand_min();
+        const int64_t h = ctx->tree->adopt(parent, tokens + tok_offsets[c0] + plan.anchor_len[c0] + x.a, x.b - x.a,
+                                           x.pages);
+        if (h == 0) {
+          ctx->dead = true;
+          return fail(JEV_ESTATE, "internal: a planned page is not free");
+        }
+        handle_of[size_t(idx)] = h;
+        ctx->tree->touch_path(h, ctx->clock);
+        made.push_back(h);
+      }
+    for (int64_t h : made) ctx->tree->release(h);
+  }
   return run_rounds(ctx, rds, hb, probs, reinterpret_cast<hipStream_t>(hip_stream));
 }
 

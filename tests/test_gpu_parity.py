@@ -201,6 +201,33 @@ def test_w1_scheduler_requests_match_oracle(w1):
     assert ctx.stats()["pages_in_use"] == 0
 
 
+def test_w1_candidate_calls_checkpoint_a_repeated_state(w1):
+    """Cache policy on: the state that a call's candidates share stays cached,
+    and a second call over the same state computes only its own tokens; both
+    match the oracle.  Switching the policy off frees everything."""
+    from shared_prefix_kv_amd import jev
+    wl, inst, m, ref, _, wd = w1
+    rng = np.random.default_rng(11)
+    S = [int(t) for t in rng.integers(0, wl.model.vocab, 70)]
+    q1 = [S + [int(t) for t in rng.integers(0, wl.model.vocab, 5 + i)] for i in range(3)]
+    q2 = [S + [int(t) for t in rng.integers(0, wl.model.vocab, 3 + i)] for i in range(2)]
+    lab = [b.labels for b in inst.passes[0][:3]]
+    ctx, _ = device_context(1, n_pages=64, max_pos=1024, max_tok=1024, weights_dev=wd)
+    ctx.set_cache_policy(jev.JEV_CACHE_LRU)
+    p1, l1 = ctx.score_candidates(q1, lab)
+    _sync()
+    assert max_abs(split_probs(p1, l1), om.score_from_scratch(m, q1, lab)) <= TOL_F32
+    assert ctx.stats()["cached_prefixes"] == 1 and ctx.stats()["cached_pages"] == 5
+    p2, l2 = ctx.score_candidates(q2, lab[:2])
+    _sync()
+    assert max_abs(split_probs(p2, l2), om.score_from_scratch(m, q2, lab[:2])) <= TOL_F32
+    st = ctx.stats()
+    assert st["computed_tokens"] == sum(len(q) - len(S) for q in q2)
+    assert st["cached_tokens"] == 2 * len(S)
+    ctx.set_cache_policy(jev.JEV_CACHE_RELEASE)
+    assert ctx.stats()["pages_in_use"] == 0
+
+
 def test_w1_attention_output_matches_oracle(w1):
     wl, inst, m, ref, ctx, _ = w1
     (h,) = ctx.prefill_prefix([0], [inst.prefixes[0]])

@@ -232,3 +232,28 @@ def test_concurrent_submitters():
         sch.step()
     assert all(sch.status(t) == jev.JEV_SCHED_FINISHED for t in tickets)
     assert ctx.stats()["pages_in_use"] == 0
+
+
+def test_repeated_state_is_checkpointed_under_the_cache_policy():
+    """A state shared by a request's candidates stays cached after the request
+    (cache policy on): a later request over the same state computes only its
+    own tokens, in one step.  With the policy off it is recomputed."""
+    S = [int(t) for t in np.random.default_rng(3).integers(0, VOCAB, 70)]
+    for keep in (True, False):
+        ctx = dry(64)
+        if keep:
+            ctx.set_cache_policy(jev.JEV_CACHE_LRU)
+        sch = jev.Scheduler(ctx)
+        a = sch.submit([S + [1, 2], S + [3]], labels(2))
+        sch.step()
+        sch.step()
+        assert sch.status(a) == jev.JEV_SCHED_FINISHED
+        b = sch.submit([S + [4, 5, 6], S + [7]], labels(2))
+        sch.step()
+        if keep:
+            assert sch.status(b) == jev.JEV_SCHED_FINISHED
+            assert ctx.stats()["computed_tokens"] == 3 + 1
+            assert ctx.stats()["cached_prefixes"] == 1 and ctx.stats()["cached_pages"] == 5
+        else:
+            assert sch.status(b) == jev.JEV_SCHED_ACTIVE
+            assert ctx.stats()["computed_tokens"] == len(S)
