@@ -579,11 +579,14 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
     const double T = rd.T;
     HIPCHK(timed(JEV_K_EMBED, -1, rd.T, 0, 2 * T * D * E + 4 * T,
                  [&] { return jev::launch_embed(m, ctx->embed, tok, rd.T, x, s); }));
+    bool h_ready = false;  // h of this layer already written by the previous projection
     for (int l = 0; l < m.n_layers; ++l) {
       const jev::LayerW& w = ctx->layers[l];
       if (int rc = tap(JEV_TAP_RESID, l, x, rd.T, size_t(m.d))) return rc;
-      HIPCHK(timed(JEV_K_RMSNORM, l, rd.T, 0, (2 * T + 1) * D * E,
-                   [&] { return jev::launch_rmsnorm(m, x, w.norm, rd.T, h, s); }));
+      if (!h_ready)
+        HIPCHK(timed(JEV_K_RMSNORM, l, rd.T, 0, (2 * T + 1) * D * E,
+                     [&] { return jev::launch_rmsnorm(m, x, w.norm, rd.T, h, s); }));
+      h_ready = false;
       HIPCHK(timed(JEV_K_QKV, l, rd.T, 2 * T * NQKV * D, (T * D + NQKV * D + T * NQKV) * E, [&] {
         return jev::launch_qkv(m, w, l, h, rd.T, dd + rd.off_pos, dd + rd.off_slot, rope, q, ctx->pool, gws, s);
       }));
@@ -598,8 +601,20 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
                                    part_o, part_lse, o, s);
         }));
       if (int rc = tap(JEV_TAP_ATTN, l, o, rd.T, size_t(m.hq) * m.dh)) return rc;
-      HIPCHK(timed(JEV_K_OPROJ, l, rd.T, 2 * T * D * HD, (T * HD + D * HD + 2 * T * D) * E,
-                   [&] { return jev::launch_oproj(m, w, o, rd.T, x, gws, s); }));
+      if (rd.T <= jev::kSplitRows && l + 1 < m.n_layers) {
+        // split-K projection whose residual epilogue also writes the next
+        // layer's normalised input (one launch fewer per layer)
+        HIPCHK(timed(JEV_K_OPROJ, l, rd.T, 2 * T * D * HD, (T * HD + D * HD + 2 * T * D) * E, [&] {
+          int32_t splits = 0;
+          const hipError_t e = jev::launch_oproj_split(m, w, o, rd.T, gws, &splits, s);
+          if (e != hipSuccess) return e;
+          return jev::launch_split_res_norm(m, gws.partial, splits, rd.T, x, ctx->layers[l + 1].norm, h, s);
+        }));
+        h_ready = true;
+      } else {
+        HIPCHK(timed(JEV_K_OPROJ, l, rd.T, 2 * T * D * HD, (T * HD + D * HD + 2 * T * D) * E,
+                     [&] { return jev::launch_oproj(m, w, o, rd.T, x, gws, s); }));
+      }
     }
     if (int rc = tap(JEV_TAP_RESID, m.n_layers, x, rd.T, size_t(m.d))) return rc;
     if (rd.n_read > 0)

@@ -687,18 +687,24 @@ GemmTuning g_gemm_tuning{};
 
 namespace {
 
+// K splits of a split-K GEMM with `tiles` column tiles: tiles x splits fill
+// the CUs once, at most kMaxSplits, and every split keeps >= 2 K stages.
+int split_count(int tiles, int K, int elt_bytes) {
+  const int KT = K / (8 * (16 / elt_bytes));
+  int S = g_gemm_tuning.splits > 0 ? g_gemm_tuning.splits : std::max(1, 256 / tiles);
+  return std::max(1, std::min({S, kMaxSplits, KT / 2 > 0 ? KT / 2 : 1}));
+}
+
 template <typename T, int EPI>
 hipError_t gemm_dispatch(const ModelDims& m, const GemmWs& ws, const void* A, int M, int K, int N,
                          const dev::ColMap& cm, const dev::QkvOut& qo, const dev::ResOut& ro, hipStream_t s) {
   const T* a = reinterpret_cast<const T*>(A);
-  if (M <= 256) {
+  if (M <= kSplitRows) {
     // split K so that the column tiles times the splits fill the CUs once
     constexpr int BN = 128;
     if (N % BN) return hipErrorInvalidValue;
     const int tiles = N / BN;
-    const int KT = K / (8 * (16 / int(sizeof(T))));
-    int S = g_gemm_tuning.splits > 0 ? g_gemm_tuning.splits : std::max(1, 256 / tiles);
-    S = std::max(1, std::min({S, kMaxSplits, KT / 2 > 0 ? KT / 2 : 1}));
+    const int S = split_count(tiles, K, int(sizeof(T)));
     if ((size_t)S * 256 * N > ws.partial_elems) return hipErrorInvalidValue;
     JEV_LAUNCH((dev::gemm_kernel<T, BN, EPI, true, 4, 2>), dim3(tiles, S), dim3(512), 0, s, a, M, K, N, cm,
                        qo, ro, ws.partial);
@@ -759,6 +765,26 @@ hipError_t launch_qkv(const ModelDims& m, const LayerW& w, int32_t layer, const 
   dev::ResOut ro{nullptr, 0};
   if (m.dtype == 1) return gemm_dispatch<bf16s, dev::EPI_QKV>(m, ws, h, T_, m.d, N, cm, qo, ro, s);
   return gemm_dispatch<float, dev::EPI_QKV>(m, ws, h, T_, m.d, N, cm, qo, ro, s);
+}
+
+hipError_t launch_oproj_split(const ModelDims& m, const LayerW& w, const void* o, int32_t T_, const GemmWs& ws,
+                              int32_t* splits, hipStream_t s) {
+  if (T_ <= 0 || T_ > kSplitRows) return hipErrorInvalidValue;
+  dev::ColMap cm{w.wo, nullptr, nullptr, 0, 0, m.dh, 0};
+  const int K = m.hq * m.dh, N = m.d;
+  constexpr int BN = 128;
+  if (N % BN) return hipErrorInvalidValue;
+  const int tiles = N / BN;
+  const int S = split_count(tiles, K, m.dtype == 1 ? 2 : 4);
+  if ((size_t)S * 256 * N > ws.partial_elems) return hipErrorInvalidValue;
+  *splits = S;
+  if (m.dtype == 1)
+    JEV_LAUNCH((dev::gemm_kernel<bf16s, BN, dev::EPI_RES, true, 4, 2>), dim3(tiles, S), dim3(512), 0, s,
+               reinterpret_cast<const bf16s*>(o), T_, K, N, cm, dev::QkvOut{}, dev::ResOut{}, ws.partial);
+  else
+    JEV_LAUNCH((dev::gemm_kernel<float, BN, dev::EPI_RES, true, 4, 2>), dim3(tiles, S), dim3(512), 0, s,
+               reinterpret_cast<const float*>(o), T_, K, N, cm, dev::QkvOut{}, dev::ResOut{}, ws.partial);
+  return hipGetLastError();
 }
 
 hipError_t launch_oproj(const ModelDims& m, const LayerW& w, const void* o, int32_t T_, void* x, const GemmWs& ws,

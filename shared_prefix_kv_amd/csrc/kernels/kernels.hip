@@ -106,6 +106,58 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x, c
   }
 }
 
+// Residual epilogue of a split-K projection fused with the next layer's norm:
+// one block per row.  x = x + (p_0 + p_1 + ... + p_{S-1}) summed in slice
+// order and rounded to T (as split_epilogue's residual epilogue does), then h
+// = RMSNorm(x) * g with the rows's elements, squares and block sum in
+// rmsnorm_kernel's order: both outputs are bitwise those of the two kernels.
+template <typename T>
+__global__ __launch_bounds__(256) void split_res_norm_kernel(const float* __restrict__ part, int splits, int d,
+                                                             T* __restrict__ x, const T* __restrict__ g, float eps,
+                                                             T* __restrict__ h) {
+  constexpr int CH = 16 / sizeof(T);
+  constexpr int MAXV = 4;
+  __shared__ float scratch[4];
+  const size_t slice = (size_t)256 * d;
+  T* xr = x + (size_t)blockIdx.x * d;
+  const float* pr = part + (size_t)blockIdx.x * d;
+  T* hr = h + (size_t)blockIdx.x * d;
+  float v[MAXV][CH];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) {
+    const int i = (threadIdx.x + 256 * j) * CH;
+    if (i < d) {
+      float xs[CH], acc[CH];
+      load16<T>(xr + i, xs);
+#pragma unroll
+      for (int e = 0; e < CH; ++e) acc[e] = pr[i + e];
+      for (int y = 1; y < splits; ++y)
+#pragma unroll
+        for (int e = 0; e < CH; ++e) acc[e] += pr[y * slice + i + e];
+#pragma unroll
+      for (int e = 0; e < CH; ++e) {
+        const T r = from_f32<T>(xs[e] + acc[e]);
+        xr[i + e] = r;
+        v[j][e] = to_f32(r);
+        ss += v[j][e] * v[j][e];
+      }
+    }
+  }
+  ss = block_sum256(ss, scratch);
+  const float r = 1.0f / sqrtf(ss / float(d) + eps);
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) {
+    const int i = (threadIdx.x + 256 * j) * CH;
+    if (i < d) {
+      float gg[CH];
+      load16<T>(g + i, gg);
+#pragma unroll
+      for (int e = 0; e < CH; ++e) hr[i + e] = from_f32<T>(v[j][e] * r * gg[e]);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ attention
 // A wave group = 4 waves = 128 query rows (tokens_per_tile x G heads of one KV
 // head); wave w owns rows [32w, 32w+32).  Per step two pages (32 keys) of K and
@@ -657,6 +709,17 @@ hipError_t launch_rmsnorm(const ModelDims& m, const void* x, const void* g, int3
   JEV_DISPATCH_T(m, {
     JEV_LAUNCH(dev::rmsnorm_kernel<T>, dim3(T_), dim3(256), 0, s, reinterpret_cast<const T*>(x),
                        reinterpret_cast<const T*>(g), m.d, m.eps, reinterpret_cast<T*>(h));
+  })
+  return hipGetLastError();
+}
+
+hipError_t launch_split_res_norm(const ModelDims& m, const float* partial, int32_t splits, int32_t T_, void* x,
+                                 const void* g, void* h, hipStream_t s) {
+  if (T_ <= 0) return hipSuccess;
+  if (T_ > kSplitRows || splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
+  JEV_DISPATCH_T(m, {
+    JEV_LAUNCH(dev::split_res_norm_kernel<T>, dim3(T_), dim3(256), 0, s, partial, splits, m.d,
+               reinterpret_cast<T*>(x), reinterpret_cast<const T*>(g), m.eps, reinterpret_cast<T*>(h));
   })
   return hipGetLastError();
 }

@@ -54,6 +54,8 @@ struct LayerW {
 // Scratch of the projection GEMMs with at most 256 rows: one fp32 [256][N]
 // partial tile per K split (up to kMaxSplits), overwritten by every launch.
 constexpr int kMaxSplits = 8;
+// GEMMs with at most this many rows split K over workgroups (branch scoring).
+constexpr int kSplitRows = 256;
 struct GemmWs {
   float* partial;
   size_t partial_elems;
@@ -94,6 +96,16 @@ hipError_t launch_rmsnorm(const ModelDims& m, const void* x, const void* g, int3
 hipError_t launch_qkv(const ModelDims& m, const LayerW& w, int32_t layer, const void* h, int32_t T,
                       const int32_t* pos, const int32_t* kvslot, const float* rope, void* qbuf,
                       void* pool, const GemmWs& ws, hipStream_t s);
+// Residual projection of a round of at most kSplitRows rows without its
+// epilogue: the split-K partial tiles go to ws.partial (slice y at
+// y * 256 * d), *splits receives their count.  launch_split_res_norm adds them.
+hipError_t launch_oproj_split(const ModelDims& m, const LayerW& w, const void* o, int32_t T, const GemmWs& ws,
+                              int32_t* splits, hipStream_t s);
+// x += sum of the split partial tiles (slice order), then h = RMSNorm(x) * g:
+// the residual epilogue of the projection fused with the next layer's norm,
+// bitwise equal to the two separate kernels.
+hipError_t launch_split_res_norm(const ModelDims& m, const float* partial, int32_t splits, int32_t T, void* x,
+                                 const void* g, void* h, hipStream_t s);
 // attention tiles (grid n_tiles x Hkv); groups = wave groups per workgroup (1
 // or 2: two split every tile's steps in halves, for rounds with long tiles)
 hipError_t launch_attention(const ModelDims& m, int32_t layer, const AttnTile* tiles, int32_t n_tiles,
