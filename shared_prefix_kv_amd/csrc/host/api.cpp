@@ -577,9 +577,11 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
   for (const RoundDesc& rd : rds) {
     const int32_t* tok = dd + rd.off_tok;
     const double T = rd.T;
-    HIPCHK(timed(JEV_K_EMBED, -1, rd.T, 0, 2 * T * D * E + 4 * T,
-                 [&] { return jev::launch_embed(m, ctx->embed, tok, rd.T, x, s); }));
-    bool h_ready = false;  // h of this layer already written by the previous projection
+    // the embedding gather also writes layer 0's normalised input
+    HIPCHK(timed(JEV_K_EMBED, -1, rd.T, 0, 3 * T * D * E + 4 * T, [&] {
+      return jev::launch_embed_norm(m, ctx->embed, tok, rd.T, ctx->layers[0].norm, x, h, s);
+    }));
+    bool h_ready = true;  // h of this layer already written (by the gather or the previous projection)
     for (int l = 0; l < m.n_layers; ++l) {
       const jev::LayerW& w = ctx->layers[l];
       if (int rc = tap(JEV_TAP_RESID, l, x, rd.T, size_t(m.d))) return rc;

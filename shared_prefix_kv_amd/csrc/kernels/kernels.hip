@@ -1,7 +1,7 @@
 // gfx950 kernels of the shared-prefix scoring path (the projection GEMMs are
 // in gemm.hip).
 //
-//  embed      x[t] = E[token t]
+//  embed+norm x[t] = E[token t], h = RMSNorm(x) * g of the first layer
 //  rmsnorm    h = x / sqrt(mean x^2 + eps) * g  (fp32 math, stored)
 //  attention  paged attention of packed query rows (token x query head of one
 //             KV head) against a page list; causal over a node's own pages,
@@ -27,17 +27,6 @@ namespace jev {
 namespace dev {
 
 constexpr float kNegInf = -INFINITY;
-
-// ------------------------------------------------------------------ embed
-template <typename T>
-__global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ E, const int32_t* __restrict__ tok,
-                                                    int d, T* __restrict__ x) {
-  const int t = blockIdx.x;
-  const u32x4* src = reinterpret_cast<const u32x4*>(E + (size_t)tok[t] * d);
-  u32x4* dst = reinterpret_cast<u32x4*>(x + (size_t)t * d);
-  const int n = d * int(sizeof(T)) / 16;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = src[i];
-}
 
 // block-wide sum over 256 threads
 __device__ __forceinline__ float block_sum256(float v, float* scratch) {
@@ -88,6 +77,46 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x, c
     const int i = (threadIdx.x + 256 * j) * CH;
     if (i < d) {
       load16<T>(xr + i, v[j]);
+#pragma unroll
+      for (int e = 0; e < CH; ++e) ss += v[j][e] * v[j][e];
+    }
+  }
+  ss = block_sum256(ss, scratch);
+  const float r = 1.0f / sqrtf(ss / float(d) + eps);
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) {
+    const int i = (threadIdx.x + 256 * j) * CH;
+    if (i < d) {
+      float gg[CH];
+      load16<T>(g + i, gg);
+#pragma unroll
+      for (int e = 0; e < CH; ++e) hr[i + e] = from_f32<T>(v[j][e] * r * gg[e]);
+    }
+  }
+}
+
+// Embedding gather fused with layer 0's norm: one block per token; x = E[tok]
+// and h = RMSNorm(x) * g with rmsnorm_kernel's element and reduction order
+// (bitwise those of the two kernels).
+template <typename T>
+__global__ __launch_bounds__(256) void embed_norm_kernel(const T* __restrict__ E, const int32_t* __restrict__ tok,
+                                                         int d, const T* __restrict__ g, float eps, T* __restrict__ x,
+                                                         T* __restrict__ h) {
+  constexpr int CH = 16 / sizeof(T);
+  constexpr int MAXV = 4;
+  __shared__ float scratch[4];
+  const T* er = E + (size_t)tok[blockIdx.x] * d;
+  T* xr = x + (size_t)blockIdx.x * d;
+  T* hr = h + (size_t)blockIdx.x * d;
+  float v[MAXV][CH];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) {
+    const int i = (threadIdx.x + 256 * j) * CH;
+    if (i < d) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(er + i);
+      *reinterpret_cast<u32x4*>(xr + i) = raw;
+      load16<T>(er + i, v[j]);
 #pragma unroll
       for (int e = 0; e < CH; ++e) ss += v[j][e] * v[j][e];
     }
@@ -694,21 +723,21 @@ using dev::bf16s;
     __VA_ARGS__                     \
   }
 
-hipError_t launch_embed(const ModelDims& m, const void* embed, const int32_t* tok, int32_t T_, void* x,
-                        hipStream_t s) {
-  if (T_ <= 0) return hipSuccess;
-  JEV_DISPATCH_T(m, {
-    JEV_LAUNCH(dev::embed_kernel<T>, dim3(T_), dim3(256), 0, s, reinterpret_cast<const T*>(embed), tok,
-                       m.d, reinterpret_cast<T*>(x));
-  })
-  return hipGetLastError();
-}
-
 hipError_t launch_rmsnorm(const ModelDims& m, const void* x, const void* g, int32_t T_, void* h, hipStream_t s) {
   if (T_ <= 0) return hipSuccess;
   JEV_DISPATCH_T(m, {
     JEV_LAUNCH(dev::rmsnorm_kernel<T>, dim3(T_), dim3(256), 0, s, reinterpret_cast<const T*>(x),
                        reinterpret_cast<const T*>(g), m.d, m.eps, reinterpret_cast<T*>(h));
+  })
+  return hipGetLastError();
+}
+
+hipError_t launch_embed_norm(const ModelDims& m, const void* embed, const int32_t* tok, int32_t T_, const void* g,
+                             void* x, void* h, hipStream_t s) {
+  if (T_ <= 0) return hipSuccess;
+  JEV_DISPATCH_T(m, {
+    JEV_LAUNCH(dev::embed_norm_kernel<T>, dim3(T_), dim3(256), 0, s, reinterpret_cast<const T*>(embed), tok, m.d,
+               reinterpret_cast<const T*>(g), m.eps, reinterpret_cast<T*>(x), reinterpret_cast<T*>(h));
   })
   return hipGetLastError();
 }

@@ -85,9 +85,6 @@ struct GemmTuning {
 };
 extern GemmTuning g_gemm_tuning;
 
-// x[t] = E[tok[t]]
-hipError_t launch_embed(const ModelDims& m, const void* embed, const int32_t* tok, int32_t T, void* x,
-                        hipStream_t s);
 // h = RMSNorm(x) * g, stored
 hipError_t launch_rmsnorm(const ModelDims& m, const void* x, const void* g, int32_t T, void* h,
                           hipStream_t s);
@@ -96,6 +93,10 @@ hipError_t launch_rmsnorm(const ModelDims& m, const void* x, const void* g, int3
 hipError_t launch_qkv(const ModelDims& m, const LayerW& w, int32_t layer, const void* h, int32_t T,
                       const int32_t* pos, const int32_t* kvslot, const float* rope, void* qbuf,
                       void* pool, const GemmWs& ws, hipStream_t s);
+// x = E[tok], then h = RMSNorm(x) * g (the first layer's norm), with the same
+// arithmetic as launch_rmsnorm on the gathered rows.
+hipError_t launch_embed_norm(const ModelDims& m, const void* embed, const int32_t* tok, int32_t T, const void* g,
+                             void* x, void* h, hipStream_t s);
 // Residual projection of a round of at most kSplitRows rows without its
 // epilogue: the split-K partial tiles go to ws.partial (slice y at
 // y * 256 * d), *splits receives their count.  launch_split_res_norm adds them.
