@@ -221,6 +221,11 @@ class Context:
 
     def close(self) -> None:
         if self.ctx:
+            # schedulers belong to the context: destroy them first
+            for ref in getattr(self, "_scheds", []):
+                sch = ref()
+                if sch is not None:
+                    sch.close()
             _check(lib().jev_destroy(self.ctx))
             self.ctx = ctypes.c_void_p()
 
@@ -346,11 +351,15 @@ class Scheduler:
     any thread, step() from one driver thread, result() once finished."""
 
     def __init__(self, ctx: Context):
+        import weakref
         self.owner = ctx
         s = ctypes.c_void_p()
         _check(lib().jev_sched_create(ctx.ctx, ctypes.byref(s)))
         self.s = s
         self._loff: Dict[int, np.ndarray] = {}
+        if not hasattr(ctx, "_scheds"):
+            ctx._scheds = []
+        ctx._scheds.append(weakref.ref(self))
 
     def close(self) -> None:
         if self.s:

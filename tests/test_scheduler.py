@@ -257,3 +257,24 @@ def test_repeated_state_is_checkpointed_under_the_cache_policy():
         else:
             assert sch.status(b) == jev.JEV_SCHED_ACTIVE
             assert ctx.stats()["computed_tokens"] == len(S)
+
+
+def test_closing_the_context_first_closes_its_schedulers():
+    ctx = dry(64)
+    sch = jev.Scheduler(ctx)
+    t = sch.submit([[1, 2, 3], [1, 2, 4]], labels(2))
+    sch.step()
+    ctx.close()                                   # destroys the scheduler first
+    assert not sch.s
+    sch.close()                                   # no-op
+    ctx2 = dry(64)
+    sch2 = jev.Scheduler(ctx2)
+    t2 = sch2.submit([[5, 6]], labels(1))
+    sch2.step()
+    assert sch2.status(t2) == jev.JEV_SCHED_FINISHED
+    with pytest.raises(jev.JevError) as e:
+        sch2.result(t2)                           # planning-only context: no scores
+    assert e.value.code == jev.JEV_ESTATE
+    with pytest.raises(jev.JevError) as e:
+        sch2.status(t + 100)
+    assert e.value.code == jev.JEV_EHANDLE
