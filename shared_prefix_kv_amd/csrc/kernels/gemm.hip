@@ -688,10 +688,12 @@ GemmTuning g_gemm_tuning{};
 namespace {
 
 // K splits of a split-K GEMM with `tiles` column tiles: tiles x splits fill
-// the CUs once, at most kMaxSplits, and every split keeps >= 2 K stages.
+// the CUs at most once, at most 6 (measured at 240 rows: more splits cost more
+// in partial-slice traffic than the extra CUs bring), and every split keeps
+// >= 2 K stages.
 int split_count(int tiles, int K, int elt_bytes) {
   const int KT = K / (8 * (16 / elt_bytes));
-  int S = g_gemm_tuning.splits > 0 ? g_gemm_tuning.splits : std::max(1, 256 / tiles);
+  int S = g_gemm_tuning.splits > 0 ? g_gemm_tuning.splits : std::min(6, std::max(1, 256 / tiles));
   return std::max(1, std::min({S, kMaxSplits, KT / 2 > 0 ? KT / 2 : 1}));
 }
 

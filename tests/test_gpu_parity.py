@@ -28,6 +28,7 @@ pytestmark = pytest.mark.gpu
 TOL_F32 = 1e-5
 TOL_BF16 = 1e-3          # well-conditioned bf16 checks
 TOL_BF16_E2E = 1e-2      # end to end, bf16 storage (derived; see module docstring)
+ORDER_FLOOR = 3.2e-3     # bf16 models: what a change of accumulation order alone moves (module docstring)
 TAP_ATTN, TAP_RESID = 0, 1
 
 
@@ -528,10 +529,17 @@ def test_w3_staged_rounds_match_oracle(w2):
     err2 = max_abs(split_probs(probs2, loff2), g["passes"][0]["probs"])
     print("w3 candidate-first max abs err", err2)
     assert err2 <= TOL_BF16_E2E
-    assert max_abs(split_probs(probs2, loff2), split_probs(probs, loff)) <= 1e-3
+    # the two orders run the same nodes in other round compositions, i.e. the
+    # GEMMs accumulate in other orders: they may differ by the models'
+    # accumulation-order floor (TOL_BF16_E2E's derivation), not more
+    assert max_abs(split_probs(probs2, loff2), split_probs(probs, loff)) <= ORDER_FLOOR
     st = ctx.stats()
     assert st["rounds"] == 3 and st["computed_tokens"] == 800 + 120 + 240
     assert st["pages_in_use"] == 0
+    # the same call again: bitwise the same (a race would show here)
+    probs3, loff3 = ctx.score_candidates(inst.candidates, inst.cand_labels)
+    _sync()
+    assert np.array_equal(probs3.cpu().numpy(), probs2.cpu().numpy())
 
 
 def test_w3_requests_through_the_continuous_batching_scheduler(w2):
