@@ -72,7 +72,7 @@ WsLayout layout(const jev_model_desc& d) {
   const int G = d.n_q_heads / d.n_kv_heads;
   const int64_t tt = kRowsPerTile / G;
   // partial rows: own tiles plus prefix-chunk tiles of a round, per KV head
-  // (the chunk count is chosen so that tiles x chunks x Hkv stays near 512)
+  // (the chunk count is chosen so that tiles x chunks x Hkv stays within 512)
   L.part_rows = int64_t(kRowsPerTile) * (int64_t(d.n_kv_heads) * (2 * ((T + tt - 1) / tt) + 64) + 1024);
   L.desc_ints = 32 * T + 4 * int64_t(d.max_positions) + (1 << 18);
   const size_t e = elt_size(d);
@@ -378,10 +378,15 @@ int build_round(jev_ctx* ctx, std::vector<RNode>& nodes, std::vector<int32_t>& h
       anc_qtiles += (g.t1 - g.t0 + TT - 1) / TT;
       min_anc_pages = std::min(min_anc_pages, g.anc_pages);
     }
+  int64_t own_qtiles = 0;
+  for (auto& nd : nodes) own_qtiles += (nd.n + TT - 1) / TT;
   int64_t n_chunks = 1;
   if (anc_qtiles > 0) {
-    const int64_t want = 512;
-    n_chunks = (want + anc_qtiles * ctx->desc.n_kv_heads - 1) / (anc_qtiles * ctx->desc.n_kv_heads);
+    // as many chunks as fit, with the own tiles, in one wave of the 512
+    // workgroup slots (two per CU): a second, partial wave would add a
+    // whole chunk's steps for a few tiles
+    const int64_t slots = 512 - own_qtiles * ctx->desc.n_kv_heads;
+    n_chunks = slots / (anc_qtiles * ctx->desc.n_kv_heads);
     n_chunks = std::max<int64_t>(1, std::min<int64_t>({n_chunks, kMaxChunks, min_anc_pages / 8}));
   }
 
