@@ -81,7 +81,8 @@ extern thread_local LaunchTiming g_launch_timing;
 struct GemmTuning {
   int splits;  // split-K count of the skinny GEMM (0 = automatic)
   int bn;      // column tile of the large GEMM (0 = automatic)
-  int large;   // large bf16 GEMM kernel: 0 = automatic, 1 = register staging, 2/3 = direct loads, 2/3 stages
+  int large;   // large bf16 GEMM kernel: 0 = automatic (4), 1 = register staging, 2/3 = direct loads, 2/3
+               // stages, 4 = direct loads by loader waves
 };
 extern GemmTuning g_gemm_tuning;
 
