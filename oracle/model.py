@@ -17,6 +17,16 @@ unembedding.  Readings taken where the pages say nothing:
   RMSNorm output.  Logits, log-probabilities and label probabilities are not
   rounded.
 
+Contractions (the projections, q.k, p.v and the unembedding) accumulate in
+float32 by default, as the method's "fp32 accumulate" asks.  The ``gemm``
+field selects another accumulation, used only to measure how far a change of
+summation order alone moves the result (the reproducibility floor that the
+bf16 parity bars are derived from): "fp64" (float64 products and sums, then
+the same storage rounding), "fp32_krev" (float32, contraction index run in
+reverse) and "fp32_khalves" (float32, the two halves of the contraction
+summed separately, then added).  All of them are faithful implementations of
+the same definition.
+
 Scoring (jdon.com openjev-sglang article, "prefill-only" section and
 "inference flow" steps 4-5): run the whole prompt once, take the
 log-probabilities over the full vocabulary at the last position, read them at
@@ -42,6 +52,8 @@ class OracleModel:
 
     mode: "bf16" (emulate bf16 storage, fp32 GEMMs), "f32" (fp32 storage and
     GEMMs) or "f64" (everything float64, no rounding; invariant tests).
+    gemm: accumulation of the contractions ("fp32", "fp64", "fp32_krev",
+    "fp32_khalves"; see the module docstring).  Ignored in "f64" mode.
     """
     n_layers: int
     d: int
@@ -60,23 +72,44 @@ class OracleModel:
     wo: List[np.ndarray]
     attn_norm: List[np.ndarray]
     final_norm: np.ndarray
+    gemm: str = "fp32"
 
     @property
     def gemm_dtype(self):
-        return np.float64 if self.mode == "f64" else np.float32
+        return np.float64 if (self.mode == "f64" or self.gemm == "fp64") else np.float32
 
 
-def from_weights(w, mode: Optional[str] = None) -> OracleModel:
+GEMM_ORDERS = ("fp32", "fp64", "fp32_krev", "fp32_khalves")
+
+
+def from_weights(w, mode: Optional[str] = None, gemm: str = "fp32") -> OracleModel:
     """Builds the oracle's float view of ``synth.Weights``."""
     s = w.shape
     mode = mode or ("bf16" if s.dtype == "bf16" else "f32")
+    if gemm not in GEMM_ORDERS:
+        raise ValueError(f"unknown accumulation {gemm!r}")
     conv = (lambda a: bits_to_f32(a)) if a_is_bits(w) else (lambda a: np.asarray(a, np.float32))
-    cast = (lambda a: conv(a).astype(np.float64)) if mode == "f64" else conv
+    wide = mode == "f64" or gemm == "fp64"
+    cast = (lambda a: conv(a).astype(np.float64)) if wide else conv
     return OracleModel(
         s.n_layers, s.d, s.hq, s.hkv, s.dh, s.vocab, s.rope_theta, s.eps, mode,
         cast(w.embed), cast(w.unembed),
         [cast(a) for a in w.wq], [cast(a) for a in w.wk], [cast(a) for a in w.wv],
-        [cast(a) for a in w.wo], [cast(a) for a in w.attn_norm], cast(w.final_norm))
+        [cast(a) for a in w.wo], [cast(a) for a in w.attn_norm], cast(w.final_norm), gemm)
+
+
+def contract(m: OracleModel, a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """a [..., k] times b [k, n]: products and sums in the model's accumulation
+    (float32 by default; see the module docstring for the alternatives)."""
+    gd = m.gemm_dtype
+    a = np.asarray(a, gd)
+    b = np.asarray(b, gd)
+    if gd == np.float64 or m.gemm == "fp32":
+        return a @ b
+    if m.gemm == "fp32_krev":
+        return np.ascontiguousarray(a[..., ::-1]) @ np.ascontiguousarray(b[::-1])
+    half = a.shape[-1] // 2
+    return a[..., :half] @ b[:half] + a[..., half:] @ b[half:]
 
 
 def a_is_bits(w) -> bool:
@@ -126,7 +159,6 @@ def attention(m: OracleModel, q: np.ndarray, k: np.ndarray, v: np.ndarray,
     """
     nq, hq, dh = q.shape
     group = hq // k.shape[1]
-    gd = m.gemm_dtype
     scale = 1.0 / math.sqrt(dh)
     out = np.zeros((nq, hq, dh), dtype=np.float64)
     q_pos = np.asarray(q_pos, np.int64)
@@ -134,20 +166,20 @@ def attention(m: OracleModel, q: np.ndarray, k: np.ndarray, v: np.ndarray,
 
     def head(j: int) -> None:
         kh = j // group
-        kj = np.ascontiguousarray(k[:, kh, :], dtype=gd)
-        vj = np.ascontiguousarray(v[:, kh, :], dtype=gd)
+        kj = np.ascontiguousarray(k[:, kh, :], dtype=m.gemm_dtype)
+        vj = np.ascontiguousarray(v[:, kh, :], dtype=m.gemm_dtype)
         for t0 in range(0, nq, q_chunk):
             t1 = min(nq, t0 + q_chunk)
-            qj = np.ascontiguousarray(q[t0:t1, j, :], dtype=gd)
+            qj = np.ascontiguousarray(q[t0:t1, j, :], dtype=m.gemm_dtype)
             # keys no query of this chunk can see contribute nothing; skip them
             ks = np.nonzero(k_pos <= q_pos[t0:t1].max())[0]
-            s = (qj @ kj[ks].T).astype(np.float64) * scale
+            s = contract(m, qj, kj[ks].T).astype(np.float64) * scale
             visible = k_pos[None, ks] <= q_pos[t0:t1, None]
             s = np.where(visible, s, -np.inf)
             mx = s.max(axis=1, keepdims=True)
             p = np.exp(s - mx)
             p /= p.sum(axis=1, keepdims=True)
-            out[t0:t1, j, :] = (p.astype(gd) @ vj[ks]).astype(np.float64)
+            out[t0:t1, j, :] = contract(m, p, vj[ks]).astype(np.float64)
 
     if hq == 1 or nq * k.shape[0] < (1 << 16):
         for j in range(hq):
@@ -159,9 +191,8 @@ def attention(m: OracleModel, q: np.ndarray, k: np.ndarray, v: np.ndarray,
 
 
 def _gemm(m: OracleModel, a: np.ndarray, w: np.ndarray) -> np.ndarray:
-    """a [n, in] times w[out, in]^T in the model's GEMM precision."""
-    gd = m.gemm_dtype
-    return np.asarray(a, gd) @ np.asarray(w, gd).T
+    """a [n, in] times w[out, in]^T in the model's accumulation."""
+    return contract(m, a, w.T)
 
 
 def layer_qkv(m: OracleModel, l: int, x: np.ndarray, positions: np.ndarray):

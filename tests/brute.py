@@ -4,6 +4,21 @@ Written with plain lists and the math module, independent of the numpy
 oracle, so that a transposed operand, a wrong head mapping or a dropped term
 in either shows up as a mismatch.  Weights are the [out, in] row-major
 matrices of ``synth.Weights`` converted to nested lists of floats.
+
+bf16 storage: ``forward_last(..., round_at=...)`` rounds values to bfloat16
+(8 significant bits, round to nearest, ties to even, straight from the float64
+value) at the named points, so that the oracle's bf16 mode can be pinned point
+by point:
+
+  "norm"   RMSNorm output of each block
+  "qk"     q and k after RoPE
+  "v"      v
+  "attn"   attention output (all heads of a token)
+  "resid"  residual stream after each add
+  "final"  final RMSNorm output
+
+"qk_before_rope" rounds q and k before RoPE instead: a plausible misreading,
+used to show that the pin tells the two apart.
 """
 from __future__ import annotations
 
@@ -12,6 +27,19 @@ from typing import List, Sequence
 
 Vec = List[float]
 Mat = List[List[float]]
+
+
+STORE_POINTS = ("norm", "qk", "v", "attn", "resid", "final")
+
+
+def bf16(x: float) -> float:
+    """Nearest bfloat16 value of x: frexp gives x = m * 2**e with
+    0.5 <= |m| < 1, so m * 256 carries the 8 significant bits; Python's round()
+    takes the nearest integer with ties to even."""
+    if x == 0.0 or not math.isfinite(x):
+        return x
+    m, e = math.frexp(x)
+    return math.ldexp(round(m * 256.0), e - 8)
 
 
 def matvec(w: Mat, x: Vec) -> Vec:
@@ -38,23 +66,30 @@ def rope_vec(x: Vec, pos: int, theta: float) -> Vec:
 
 
 def forward_last(tokens: Sequence[int], E: Mat, U: Mat, layers, g_final: Vec,
-                 hq: int, hkv: int, dh: int, theta: float, eps: float) -> Vec:
+                 hq: int, hkv: int, dh: int, theta: float, eps: float,
+                 round_at: Sequence[str] = ()) -> Vec:
     """Returns log-probabilities over the vocabulary at the last position.
 
-    layers: list of dicts with keys g, wq, wk, wv, wo (nested lists)."""
+    layers: list of dicts with keys g, wq, wk, wv, wo (nested lists).
+    round_at: storage points rounded to bf16 (module docstring)."""
+    def r(point: str, vec: Vec) -> Vec:
+        return [bf16(a) for a in vec] if point in round_at else vec
+
     n = len(tokens)
     x = [list(E[t]) for t in tokens]
     group = hq // hkv
     for L in layers:
         qs, ks, vs = [], [], []
         for t in range(n):
-            h = rms(x[t], L["g"], eps)
+            h = r("norm", rms(x[t], L["g"], eps))
             q = matvec(L["wq"], h)
             k = matvec(L["wk"], h)
             v = matvec(L["wv"], h)
-            qs.append([rope_vec(q[j * dh:(j + 1) * dh], t, theta) for j in range(hq)])
-            ks.append([rope_vec(k[j * dh:(j + 1) * dh], t, theta) for j in range(hkv)])
-            vs.append([v[j * dh:(j + 1) * dh] for j in range(hkv)])
+            qs.append([r("qk", rope_vec(r("qk_before_rope", q[j * dh:(j + 1) * dh]), t, theta))
+                       for j in range(hq)])
+            ks.append([r("qk", rope_vec(r("qk_before_rope", k[j * dh:(j + 1) * dh]), t, theta))
+                       for j in range(hkv)])
+            vs.append([r("v", v[j * dh:(j + 1) * dh]) for j in range(hkv)])
         newx = []
         for t in range(n):
             att = []
@@ -66,10 +101,10 @@ def forward_last(tokens: Sequence[int], E: Mat, U: Mat, layers, g_final: Vec,
                 w = [math.exp(s - mx) for s in sc]
                 z = sum(w)
                 att += [sum(w[u] * vs[u][kv][e] for u in range(t + 1)) / z for e in range(dh)]
-            y = matvec(L["wo"], att)
-            newx.append([x[t][i] + y[i] for i in range(len(y))])
+            y = matvec(L["wo"], r("attn", att))
+            newx.append(r("resid", [x[t][i] + y[i] for i in range(len(y))]))
         x = newx
-    hfin = rms(x[-1], g_final, eps)
+    hfin = r("final", rms(x[-1], g_final, eps))
     z = matvec(U, hfin)
     mx = max(z)
     lse = mx + math.log(sum(math.exp(v - mx) for v in z))

@@ -232,3 +232,123 @@ def test_bf16_mode_rounds_at_storage_points():
     assert np.array_equal(round_bf16(hb), hb)
     hf = om.final_hidden(mf, toks)
     assert np.max(np.abs(hb - hf)) < 0.05 * np.max(np.abs(hf))
+
+
+# ---------------------------------------------------------------- bf16 storage points
+def _bf16_pin_model(index=106):
+    """Tiny bf16 model, float64 products and sums (so that the only roundings
+    are the storage points), weights scaled by 16 (a power of two keeps them
+    bf16 values) to make every storage rounding change the result."""
+    wl = tiny_workload(index=index, dtype="bf16", d=16, hq=4, hkv=2, dh=8, vocab=23)
+    m = om.from_weights(make_weights(wl), gemm="fp64")
+    assert m.mode == "bf16" and m.gemm_dtype == np.float64
+    m.embed *= 16.0
+    m.unembed *= 16.0
+    for lst in (m.wq, m.wk, m.wv, m.wo):
+        for a in lst:
+            a *= 16.0
+    return m
+
+
+def _brute_bf16(m, tokens, round_at):
+    layers = [dict(g=_lists(m.attn_norm[l]), wq=_lists(m.wq[l]), wk=_lists(m.wk[l]),
+                   wv=_lists(m.wv[l]), wo=_lists(m.wo[l])) for l in range(m.n_layers)]
+    return np.asarray(brute.forward_last(tokens, _lists(m.embed), _lists(m.unembed), layers,
+                                         _lists(m.final_norm), m.hq, m.hkv, m.dh, m.theta, m.eps,
+                                         round_at=round_at))
+
+
+BF16_TOKENS = [3, 7, 0, 22, 3, 5, 19]
+
+
+def test_brute_bf16_rounding_is_ieee_round_to_nearest_even():
+    x = np.random.default_rng(12).standard_normal(5000).astype(np.float32) * 5
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(np.array([brute.bf16(float(v)) for v in x], np.float32), ref)
+    assert brute.bf16(1.0 + 2 ** -8) == 1.0 and brute.bf16(1.0 + 3 * 2 ** -8) == 1.0 + 2 ** -6
+    assert brute.bf16(255.5) == 256.0 and brute.bf16(-1.0 - 2 ** -7 - 2 ** -30) == -1.0 - 2 ** -7
+
+
+def test_bf16_mode_matches_brute_force_storage_points():
+    """The oracle's bf16 mode rounds exactly at the reading's storage points:
+    RMSNorm outputs, q and k after RoPE, v, the attention output, the residual
+    stream after each add, the final norm output (and nowhere else)."""
+    m = _bf16_pin_model()
+    got = om.full_logprobs(m, om.final_hidden(m, BF16_TOKENS))
+    ref = _brute_bf16(m, BF16_TOKENS, brute.STORE_POINTS)
+    assert np.allclose(got, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("change", ["drop:" + p for p in brute.STORE_POINTS] + ["qk_before_rope"])
+def test_bf16_pin_tells_every_storage_point_apart(change):
+    """Each storage point left out, or q/k rounded before RoPE instead of
+    after, moves the brute-force result far beyond the pin's 1e-12: the pin
+    above would catch that mistake in the oracle."""
+    m = _bf16_pin_model()
+    got = om.full_logprobs(m, om.final_hidden(m, BF16_TOKENS))
+    if change == "qk_before_rope":
+        pts = [p for p in brute.STORE_POINTS if p != "qk"] + ["qk_before_rope"]
+    else:
+        pts = [p for p in brute.STORE_POINTS if p != change.split(":")[1]]
+    assert np.max(np.abs(got - _brute_bf16(m, BF16_TOKENS, pts))) > 1e-7
+
+
+@pytest.mark.parametrize("order", om.GEMM_ORDERS)
+def test_contractions_within_the_float_error_bound(order):
+    """Every accumulation of ``contract`` is the exact product within the
+    classical bound |err| <= gamma_k * sum |a_i b_i|, gamma_k = k u / (1 - k u),
+    with u the unit roundoff of its precision (2^-24 float32, 2^-53 float64)."""
+    wl = tiny_workload(index=107)
+    m = om.from_weights(make_weights(wl), gemm=order)
+    rng = np.random.default_rng(13)
+    a = rng.standard_normal((7, 300)).astype(np.float32)
+    b = rng.standard_normal((300, 9)).astype(np.float32)
+    exact = a.astype(np.float64) @ b.astype(np.float64)
+    got = np.asarray(om.contract(m, a, b), np.float64)
+    u = 2.0 ** -53 if order == "fp64" else 2.0 ** -24
+    k = a.shape[1]
+    gamma = k * u / (1 - k * u)
+    bound = gamma * (np.abs(a).astype(np.float64) @ np.abs(b).astype(np.float64))
+    assert np.all(np.abs(got - exact) <= bound)
+    if order != "fp64":
+        assert np.max(np.abs(got - exact)) > 0      # it really is a float32 accumulation
+
+
+def test_attention_query_chunks_and_skipped_keys():
+    """Queries processed in chunks of 3 with the keys a chunk cannot see skipped
+    give the unchunked result and the pure-Python definition; the case is a
+    suffix over cached keys (queries at positions 6..16, keys 0..16)."""
+    m = _m64(hq=4, hkv=2, dh=8)
+    rng = np.random.default_rng(14)
+    nk, nq = 17, 11
+    k = rng.standard_normal((nk, 2, 8)) * 2
+    v = rng.standard_normal((nk, 2, 8))
+    q = rng.standard_normal((nq, 4, 8)) * 2
+    qp, kp = np.arange(nk - nq, nk), np.arange(nk)
+    full = om.attention(m, q, k, v, qp, kp)
+    chunked = om.attention(m, q, k, v, qp, kp, q_chunk=3)
+    assert np.allclose(chunked, full, rtol=0, atol=1e-13)
+    for t in range(nq):
+        for j in range(4):
+            g = j // 2
+            vis = [u for u in range(nk) if kp[u] <= qp[t]]
+            sc = [sum(q[t, j, e] * k[u, g, e] for e in range(8)) / math.sqrt(8) for u in vis]
+            mx = max(sc)
+            w = [math.exp(s - mx) for s in sc]
+            ref = [sum(w[i] * v[u, g, e] for i, u in enumerate(vis)) / sum(w) for e in range(8)]
+            assert np.allclose(chunked[t, j], ref, rtol=0, atol=1e-13)
+
+
+def test_attention_threaded_heads_match_single_head_calls():
+    """Above 65,536 query-key pairs the heads run on a thread pool; each head
+    equals the same head computed alone."""
+    m = _m64(hq=4, hkv=2, dh=4)
+    rng = np.random.default_rng(15)
+    n = 260
+    q = rng.standard_normal((n, 4, 4))
+    k, v = rng.standard_normal((n, 2, 4)), rng.standard_normal((n, 2, 4))
+    out = om.attention(m, q, k, v, np.arange(n), np.arange(n))
+    for j in range(4):
+        single = om.attention(m, q[:, j:j + 1], k[:, j // 2:j // 2 + 1], v[:, j // 2:j // 2 + 1],
+                              np.arange(n), np.arange(n))
+        assert np.array_equal(out[:, j], single[:, 0])
