@@ -174,7 +174,10 @@ int jev_score_candidates(jev_ctx* ctx, int32_t n, const int32_t* tokens, const i
  *    all its candidates, while a shared node is built by one real candidate, its
  *    smallest index, whose path down to its own read-out is computed (and read
  *    out) in that round.  No candidate waits on a separate warmup node.
- * Both orders compute every node once and give the same probabilities.
+ * Both orders compute every node once.  Their probabilities agree to the
+ * accumulation-order floor, not bitwise: a round of at most 256 tokens splits
+ * the K dimension of its projections over workgroups and a larger round does
+ * not, so a node's K/V can be summed in another order in another round.
  * Errors: JEV_EINVAL (NULL ctx, unknown mode). */
 enum { JEV_PLAN_DEPTH = 0, JEV_PLAN_CANDIDATE_FIRST = 1 };
 int jev_set_plan_mode(jev_ctx* ctx, int32_t mode);

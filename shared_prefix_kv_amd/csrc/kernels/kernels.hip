@@ -465,7 +465,10 @@ __global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2,
     for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, S[r]);
     mloc = xor32_max(mloc) * scale_log2;
     if (__any(mloc > mrun + RESCALE_SLACK)) {
-      const float mnew = fmaxf(mrun, mloc);
+      // each row moves its own maximum only when it exceeds the slack itself
+      // (alpha = 1 exactly otherwise), so a row's rounding never depends on
+      // the other rows of its wave
+      const float mnew = (mloc > mrun + RESCALE_SLACK) ? mloc : mrun;
       const float alpha = (mnew == kNegInf) ? 1.f : exp2f(mrun - mnew);
       lrun *= alpha;
 #pragma unroll
@@ -490,12 +493,21 @@ __global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2,
     }
     lsum = xor32_sum(lsum);
     lrun += lsum;
-    frag pb[16 / KL];
+    // bf16: P = P_hi + P_lo, both bf16 (P_hi the upper 16 bits of the fp32
+    // value, P_lo its exact remainder rounded to nearest), so that the PV
+    // product sees P to ~16 significant bits, not the 8 of one bf16 rounding
+    // (that rounding alone moved label probabilities several times further
+    // than any change of summation order does).
+    frag pb[16 / KL], pl[16 / KL];
 #pragma unroll
     for (int tt = 0; tt < 16 / KL; ++tt) {
       if constexpr (KL == 8) {
 #pragma unroll
-        for (int sidx = 0; sidx < 8; ++sidx) pb[tt][sidx] = (__bf16)p[8 * tt + sidx];
+        for (int sidx = 0; sidx < 8; ++sidx) {
+          const uint32_t u = __float_as_uint(p[8 * tt + sidx]);
+          pb[tt][sidx] = __builtin_bit_cast(__bf16, uint16_t(u >> 16));
+          pl[tt][sidx] = (__bf16)(p[8 * tt + sidx] - __uint_as_float(u & 0xFFFF0000u));
+        }
       } else {
         pb[tt] = p[tt];
       }
@@ -503,37 +515,44 @@ __global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2,
     // O^T += V^T P^T; MFMA tt covers keys {8j + 4*hh + i : 4j + i in [tt*KL, tt*KL+KL)}
 #pragma unroll
     for (int tt = 0; tt < 16 / KL; ++tt) {
+      frag va[NDB];
 #pragma unroll
       for (int b = 0; b < NDB; ++b) {
         const int d = 32 * b + c;
-        frag va;
         if constexpr (KL == 8) {
           // keys 16tt + {4hh..4hh+3, 8+4hh..8+4hh+3}: quads hh, hh+2 of half tt,
           // stored at quad slots 2hh, 2hh+1 = unit 2tt + hh
-          va = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(&sV[buf][0])[vq_unit(d, 2 * tt + hh)]);
+          va[b] = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(&sV[buf][0])[vq_unit(d, 2 * tt + hh)]);
         } else {
           const int key = 8 * (tt >> 2) + 4 * hh + (tt & 3);
-          va = MF::load(&sV[buf][v_off(d, key)]);
+          va[b] = MF::load(&sV[buf][v_off(d, key)]);
         }
-        oacc[b] = MF::mma(va, pb[tt], oacc[b]);
+        oacc[b] = MF::mma(va[b], pb[tt], oacc[b]);
+      }
+      if constexpr (KL == 8) {
+#pragma unroll
+        for (int b = 0; b < NDB; ++b) oacc[b] = MF::mma(va[b], pl[tt], oacc[b]);
       }
     }
     if constexpr (KL == 8) {
       // Order of the branch-free block: 2 K-fragment reads ahead; per S MFMA
-      // ~7 VALU and the next K read, plus, over the last four, the V reads of
-      // the first PV half; then per PV MFMA one V read four ahead.
+      // ~10 VALU (exponentials, row sums, the P_hi / P_lo split) and the next
+      // K read, plus, over the last four, the V reads of the first PV block;
+      // then the PV MFMAs (hi then lo per 16 keys) with the V reads of the
+      // second block spread over the first half.
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
       for (int i = 0; i < NKS; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
         if (i + 2 < NKS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         if (i >= NKS - NDB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
 #pragma unroll
-      for (int i = 0; i < 2 * NDB; ++i) {
+      for (int i = 0; i < 4 * NDB; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i + NDB < 2 * NDB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (i < 2 * NDB && (i & 1) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
       }
     }
 

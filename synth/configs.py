@@ -68,21 +68,27 @@ class TreeSpec:
 
 @dataclass(frozen=True)
 class Workload:
-    index: int        # 1-based position in the list below; also the seed root
+    index: int        # 1-based position in the lists below
     name: str
     model: ModelShape
     requests: Tuple[Request, ...] = ()
     tree: Optional[TreeSpec] = None
     passes: int = 1   # >1: later passes draw fresh suffixes over the resident prefix
+    seed: Optional[int] = None  # seed root (default: the index)
 
     @property
     def kind(self) -> str:
         return "tree" if self.tree is not None else "prefix_branches"
 
+    @property
+    def seed_index(self) -> int:
+        return self.index if self.seed is None else self.seed
+
 
 TINY_F32 = ModelShape(n_layers=1, d=256, hq=4, hkv=4, dh=64, vocab=1024, dtype="f32")
 QWEN_LIKE_4L = ModelShape(n_layers=4, d=4096, hq=32, hkv=4, dh=128, vocab=151936, dtype="bf16")
 LONG_8L = ModelShape(n_layers=8, d=4096, hq=32, hkv=8, dh=128, vocab=151936, dtype="bf16")
+QWEN_LIKE_1L = ModelShape(n_layers=1, d=4096, hq=32, hkv=4, dh=128, vocab=151936, dtype="bf16")
 
 # Yes/no label ids of the worked example in the jdon.com article
 # (prefill-only section): "yes" = 9891, "no" = 2201.
@@ -106,8 +112,32 @@ WORKLOADS: List[Workload] = [
 ]
 
 
+# Parity-only cases (never timed):
+# 6  workload 2 cut to its first block: the same seed, so the same tokens,
+#    labels, embedding, unembedding and block-0 weights, run by the same
+#    kernel instances; its accumulation-order floor lies below 1e-3;
+# 7  workload 3's tree and 8 workload 4's batch on the tiny float32 model
+#    (the other reading of "same model shapes as config 1");
+# 9  a 2,100-token prefix on the tiny float32 model: a round whose longest
+#    attention tile has more than 48 pages (two wave groups per workgroup) and
+#    whose long causal tiles are split in two.
+PARITY_WORKLOADS: List[Workload] = [
+    Workload(6, "prefix2000_x5x48_yesno_1block", QWEN_LIKE_1L,
+             requests=(Request(prefix_len=2000, n_branches=5, suffix_len=48, k_labels=2,
+                               fixed_labels=YES_NO_IDS),), seed=2),
+    Workload(7, "tree800_2x60_3x40_tiny_f32", TINY_F32,
+             tree=TreeSpec(root_len=800, child_lens=(60, 60), leaves_per_child=(3, 3),
+                           leaf_len=40, k_labels=2)),
+    Workload(8, "batch16_prefix1200_x8x64_k64_tiny_f32", TINY_F32,
+             requests=tuple(Request(prefix_len=1200, n_branches=8, suffix_len=64, k_labels=64)
+                            for _ in range(16))),
+    Workload(9, "prefix2100_x4x20_tiny_f32", TINY_F32,
+             requests=(Request(prefix_len=2100, n_branches=4, suffix_len=20, k_labels=3),)),
+]
+
+
 def workload(index_or_name) -> Workload:
-    for w in WORKLOADS:
+    for w in WORKLOADS + PARITY_WORKLOADS:
         if w.index == index_or_name or w.name == index_or_name:
             return w
     raise KeyError(index_or_name)

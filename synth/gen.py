@@ -6,7 +6,8 @@ both the oracle and the GPU path take their inputs from it.
 Recipe:
 
 * Weights.  Every weight tensor is filled in row-major order, in chunks of
-  ``CHUNK`` elements.  Chunk ``c`` of tensor ``t`` of workload ``w`` is
+  ``CHUNK`` elements.  Chunk ``c`` of tensor ``t`` of workload ``w`` (its seed
+  root: the workload's index unless it names another) is
   ``np.random.default_rng([w, 0, t, c]).standard_normal(n, float32)`` times
   ``float32(init_std)``.  bf16 workloads round each value once to bf16
   (round-to-nearest-even) and store the 16-bit patterns (``uint16``); the f32
@@ -97,14 +98,14 @@ def make_weights(wl: Workload, with_embed: bool = True) -> Weights:
     bf = m.dtype == "bf16"
     std = m.init_std
     ones = (np.full(m.d, 0x3F80, dtype=np.uint16) if bf else np.ones(m.d, dtype=np.float32))
-    emb = _fill((m.vocab, m.d), wl.index, TID_E, std, bf) if with_embed else None
-    unemb = _fill((m.vocab, m.d), wl.index, TID_U, std, bf) if with_embed else None
+    emb = _fill((m.vocab, m.d), wl.seed_index, TID_E, std, bf) if with_embed else None
+    unemb = _fill((m.vocab, m.d), wl.seed_index, TID_U, std, bf) if with_embed else None
     wq, wk, wv, wo = [], [], [], []
     for l in range(m.n_layers):
-        wq.append(_fill((m.hq * m.dh, m.d), wl.index, tid_layer(l, "wq"), std, bf))
-        wk.append(_fill((m.hkv * m.dh, m.d), wl.index, tid_layer(l, "wk"), std, bf))
-        wv.append(_fill((m.hkv * m.dh, m.d), wl.index, tid_layer(l, "wv"), std, bf))
-        wo.append(_fill((m.d, m.hq * m.dh), wl.index, tid_layer(l, "wo"), std, bf))
+        wq.append(_fill((m.hq * m.dh, m.d), wl.seed_index, tid_layer(l, "wq"), std, bf))
+        wk.append(_fill((m.hkv * m.dh, m.d), wl.seed_index, tid_layer(l, "wk"), std, bf))
+        wv.append(_fill((m.hkv * m.dh, m.d), wl.seed_index, tid_layer(l, "wv"), std, bf))
+        wo.append(_fill((m.d, m.hq * m.dh), wl.seed_index, tid_layer(l, "wo"), std, bf))
     return Weights(m, emb, unemb, wq, wk, wv, wo,
                    [ones.copy() for _ in range(m.n_layers)], ones.copy())
 
@@ -138,8 +139,8 @@ class Instance:
 
 def make_instance(wl: Workload) -> Instance:
     V = wl.model.vocab
-    tok_rng = np.random.default_rng([wl.index, 1])
-    lab_rng = np.random.default_rng([wl.index, 2])
+    tok_rng = np.random.default_rng([wl.seed_index, 1])
+    lab_rng = np.random.default_rng([wl.seed_index, 2])
 
     def draw_tokens(n: int) -> np.ndarray:
         return tok_rng.integers(0, V, size=n, dtype=np.int64).astype(np.int32)

@@ -60,3 +60,38 @@ def row_rel_err(got, ref):
     num = np.linalg.norm(g - r, axis=-1)
     den = np.maximum(np.linalg.norm(r, axis=-1), 1e-6)
     return float(np.max(num / den))
+
+
+# ------------------------------------------------------------------ parity report
+# Every parity check records its worst error and its bar here before it
+# asserts; the terminal summary (tests/conftest.py) prints the table, so a
+# quiet run still shows the numbers.
+PARITY_LOG = []
+
+
+def record(what, err, bar):
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0].split("::")[-1]
+    PARITY_LOG.append((test, what, float(err), float(bar)))
+    print(f"{what}: {err:.3e} (bar {bar:.1e})", flush=True)
+
+
+def stored_bars(g, pass_index=0):
+    """Per-branch bars of a stored workload: max(1e-3, 3 * spread), the spread
+    being how far the oracle's own probabilities move under other accumulation
+    orders (tests/golden/make_golden.py)."""
+    from tests.golden.make_golden import bars
+    ps = g["passes"][pass_index]
+    assert "spread" in ps and ps.get("by_order"), "stored oracle values carry no spread"
+    return bars(ps["spread"])
+
+
+def check_branches(what, got, ref, bars):
+    """Asserts |got_b - ref_b|_inf <= bars[b] for every branch b; records the
+    worst error, the worst error relative to its bar and that bar."""
+    errs = [float(np.max(np.abs(np.asarray(a) - np.asarray(b)))) for a, b in zip(got, ref)]
+    assert len(errs) == len(bars) and len(errs) > 0
+    worst = max(range(len(errs)), key=lambda i: errs[i] / bars[i])
+    record(f"{what} (worst branch {worst}, max err {max(errs):.2e})", errs[worst], bars[worst])
+    bad = [(i, e, b) for i, (e, b) in enumerate(zip(errs, bars)) if e > b]
+    assert not bad, f"{what}: branches over their bars (branch, err, bar): {bad[:8]}"
+    return errs

@@ -4,18 +4,18 @@ A 32,768-token prefix over 8 blocks (8 KV heads) is prefilled once; two passes
 of 64 fresh 128-token branches are scored against it while it stays resident
 (openjev-multimodal performance page, repeated-state section).  The oracle
 recomputed a seeded subset of branches of each pass from scratch
-(tests/golden/probs_w5.json); the bar is the bf16 end-to-end one.
+(tests/golden/probs_w5.json); each is held to its own bar, max(1e-3, 3 x the
+spread of the oracle's probabilities under other accumulation orders).
 """
 import numpy as np
 import pytest
 import torch
 
 from synth import make_instance, workload
-from tests.gpu_common import device_context, golden, max_abs, split_probs
+from tests.gpu_common import check_branches, device_context, golden, split_probs, stored_bars
 
 pytestmark = pytest.mark.gpu
 
-TOL_BF16_E2E = 1e-2
 
 
 def test_w5_resident_prefix_two_passes_match_oracle():
@@ -33,9 +33,8 @@ def test_w5_resident_prefix_two_passes_match_oracle():
         torch.cuda.synchronize()
         got = split_probs(probs, loff)
         sel = g["passes"][p]["branches"]
-        err = max_abs([got[b] for b in sel], g["passes"][p]["probs"])
-        print(f"w5 pass {p} branches {sel}: max abs err {err:.3e}")
-        assert err <= TOL_BF16_E2E
+        check_branches(f"w5 pass {p} branches {sel} vs oracle", [got[b] for b in sel], g["passes"][p]["probs"],
+                       stored_bars(g, p))
         st = ctx.stats()
         assert st["computed_tokens"] == 64 * 128 and st["cached_tokens"] == 64 * P
         assert st["pages_in_use"] == P // 16

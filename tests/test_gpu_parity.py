@@ -8,11 +8,18 @@ Bars:
   layer is fed the GPU's own layer input (teacher forcing), and label
   probabilities within 1e-3 absolute when the oracle reads out the GPU's own
   final hidden state;
-* bf16 workloads end to end (oracle from scratch vs GPU): 1e-2 absolute.  The
-  1e-3 bar is below the reproducibility floor of these random-weight bf16
-  models: the oracle itself moves by up to 3.2e-3 when only its GEMM
-  accumulation changes from float32 to float64, because bf16 rounding flips
-  cascade through the layers; 1e-2 is three times that floor.
+* bf16 workloads end to end (oracle from scratch vs GPU): every branch within
+  max(1e-3, 3 * spread), where the spread is how far the oracle's own
+  probabilities of that branch move when only its accumulation order changes
+  (float64, reversed or halved float32 sums; tests/golden/make_golden.py).
+  A bf16 rounding that one order puts on one side of a tie and another order
+  on the other carries through the blocks of these random-weight models, so
+  no implementation with another summation order can be held below that
+  floor.  Workload 2 cut to one block has a floor below 1e-3 and is held to
+  the benchmark spec's 1e-3 itself.
+* Two GPU runs of the same nodes in other round compositions (other plan
+  orders, the scheduler) accumulate in other orders too; they are held to
+  the same per-branch bars against each other.
 """
 import numpy as np
 import pytest
@@ -20,20 +27,31 @@ import torch
 
 from oracle import model as om
 from synth import make_instance, workload
-from tests.gpu_common import (device_context, golden, host_weights, max_abs, row_rel_err,
-                              split_probs)
+from tests.gpu_common import (check_branches, device_context, golden, host_weights, max_abs,
+                              record, row_rel_err, split_probs, stored_bars)
 
 pytestmark = pytest.mark.gpu
 
 TOL_F32 = 1e-5
-TOL_BF16 = 1e-3          # well-conditioned bf16 checks
-TOL_BF16_E2E = 1e-2      # end to end, bf16 storage (derived; see module docstring)
-ORDER_FLOOR = 3.2e-3     # bf16 models: what a change of accumulation order alone moves (module docstring)
+TOL_BF16 = 1e-3          # well-conditioned bf16 checks and the one-block workload
+TOL_ROW = 2e-2           # bf16 attention / residual rows, relative
 TAP_ATTN, TAP_RESID = 0, 1
 
 
 def _sync():
     torch.cuda.synchronize()
+
+
+def close(what, got, ref, bar):
+    err = max_abs(got, ref)
+    record(what, err, bar)
+    assert err <= bar
+
+
+def close_rows(what, got, ref, bar):
+    err = row_rel_err(got, ref)
+    record(what + " (rel)", err, bar)
+    assert err <= bar
 
 
 def oracle_attention_layer0(m, prefix, suffixes):
@@ -71,7 +89,7 @@ def test_w1_shared_prefix_matches_oracle(w1):
     probs, loff = ctx.score_branches([h] * len(br), [b.tokens for b in br], [b.labels for b in br])
     _sync()
     got = split_probs(probs, loff)
-    assert max_abs(got, ref) <= TOL_F32
+    close("w1 shared prefix", got, ref, TOL_F32)
     st = ctx.stats()
     assert st["computed_tokens"] == 64 and st["logical_tokens"] == 4 * 144
     ctx.free_pages([h])
@@ -119,7 +137,7 @@ def test_w1_rotating_states_under_the_lru_cache(w1):
         computed = ctx.stats()["computed_tokens"]
         probs, loff = ctx.score_branches([h] * len(br), [b.tokens for b in br], [b.labels for b in br])
         _sync()
-        assert max_abs(split_probs(probs, loff), ref) <= TOL_F32
+        close("w1 rotating states", split_probs(probs, loff), ref, TOL_F32)
         ctx.free_pages([h])
         return computed
 
@@ -149,7 +167,7 @@ def test_w1_candidates_reuse_whole_pages_inside_a_resident_prefix(w1):
     probs, loff = ctx.score_candidates(seqs, labels)
     _sync()
     want = om.score_from_scratch(m, seqs, labels)
-    assert max_abs(split_probs(probs, loff), want) <= TOL_F32
+    close("w1 mid-node reuse", split_probs(probs, loff), want, TOL_F32)
     st = ctx.stats()
     assert st["cached_tokens"] == 3 * 96
     # the 4 shared tokens 96..99 are less than a page: that node is dissolved
@@ -166,10 +184,10 @@ def test_w1_unshared_and_candidate_paths_match_oracle(w1):
     seqs = inst.full_sequences(0)
     probs, loff = ctx.score_branches([0] * len(seqs), [s for s, _ in seqs], [l for _, l in seqs])
     _sync()
-    assert max_abs(split_probs(probs, loff), ref) <= TOL_F32
+    close("w1 unshared", split_probs(probs, loff), ref, TOL_F32)
     probs, loff = ctx.score_candidates([s for s, _ in seqs], [l for _, l in seqs])
     _sync()
-    assert max_abs(split_probs(probs, loff), ref) <= TOL_F32
+    close("w1 candidates", split_probs(probs, loff), ref, TOL_F32)
     assert ctx.stats()["rounds"] == 2 and ctx.stats()["pages_in_use"] == 0
 
 
@@ -195,9 +213,9 @@ def test_w1_scheduler_requests_match_oracle(w1):
             break
         sch.step()
     got_ab = sch.result(ta) + sch.result(tb)
-    assert max_abs(got_ab, ref) <= TOL_F32
+    close("w1 scheduler requests a+b", got_ab, ref, TOL_F32)
     want_c = om.score_from_scratch(m, third, lab3)
-    assert max_abs(sch.result(tc), want_c) <= TOL_F32
+    close("w1 scheduler request c", sch.result(tc), want_c, TOL_F32)
     sch.close()
     assert ctx.stats()["pages_in_use"] == 0
 
@@ -217,11 +235,11 @@ def test_w1_candidate_calls_checkpoint_a_repeated_state(w1):
     ctx.set_cache_policy(jev.JEV_CACHE_LRU)
     p1, l1 = ctx.score_candidates(q1, lab)
     _sync()
-    assert max_abs(split_probs(p1, l1), om.score_from_scratch(m, q1, lab)) <= TOL_F32
+    close("w1 checkpoint call 1", split_probs(p1, l1), om.score_from_scratch(m, q1, lab), TOL_F32)
     assert ctx.stats()["cached_prefixes"] == 1 and ctx.stats()["cached_pages"] == 5
     p2, l2 = ctx.score_candidates(q2, lab[:2])
     _sync()
-    assert max_abs(split_probs(p2, l2), om.score_from_scratch(m, q2, lab[:2])) <= TOL_F32
+    close("w1 checkpoint call 2", split_probs(p2, l2), om.score_from_scratch(m, q2, lab[:2]), TOL_F32)
     st = ctx.stats()
     assert st["computed_tokens"] == sum(len(q) - len(S) for q in q2)
     assert st["cached_tokens"] == 2 * len(S)
@@ -241,7 +259,7 @@ def test_w1_attention_output_matches_oracle(w1):
     ctx.debug_tap()
     got = tap.cpu().numpy().reshape(T, m.hq, m.dh)
     want = oracle_attention_layer0(m, inst.prefixes[0], [b.tokens for b in br])
-    assert row_rel_err(got, want) <= 1e-4
+    close_rows("w1 layer-0 attention rows", got, want, 1e-4)
     ctx.free_pages([h])
 
 
@@ -257,12 +275,12 @@ def test_w1_ragged_and_edge_cases(w1):
     probs, loff = ctx.score_branches([h] * 5, sufs, labs)
     _sync()
     ref = om.score_from_scratch(m, [pre + s for s in sufs], labs)
-    assert max_abs(split_probs(probs, loff), ref) <= TOL_F32
+    close("w1 ragged suffixes", split_probs(probs, loff), ref, TOL_F32)
     (h1,) = ctx.prefill_prefix([0], [[5]])
     probs, loff = ctx.score_branches([h1], [[9]], [[1, 2, 3]])
     _sync()
     ref = om.score_from_scratch(m, [[5, 9]], [[1, 2, 3]])
-    assert max_abs(split_probs(probs, loff), ref) <= TOL_F32
+    close("w1 one-token prefix", split_probs(probs, loff), ref, TOL_F32)
     ctx.free_pages([h, h1])
 
 
@@ -279,10 +297,8 @@ def test_w1_long_prefix_split_causal_tiles(w1):
     probs, loff = ctx.score_branches([h] * 3, sufs, labs)
     _sync()
     ref = om.score_from_scratch(m, [pre + s for s in sufs], labs)
-    err = max_abs(split_probs(probs, loff), ref)
     ctx.free_pages([h])
-    print("w1 long prefix max abs err", err)
-    assert err <= TOL_F32
+    close("w1 600-token prefix", split_probs(probs, loff), ref, TOL_F32)
 
 
 def test_w1_nested_prefixes_candidates_and_errors(w1):
@@ -303,7 +319,7 @@ def test_w1_nested_prefixes_candidates_and_errors(w1):
     _sync()
     full = [(A + B if p == hb else A) + s for p, s in zip(parents, sufs)]
     ref = om.score_from_scratch(m, full, labs)
-    assert max_abs(split_probs(probs, loff), ref) <= TOL_F32
+    close("w1 nested prefixes", split_probs(probs, loff), ref, TOL_F32)
     st = ctx.stats()
     assert st["computed_tokens"] == sum(len(s) for s in sufs)
     assert st["cached_tokens"] == sum(len(f) - len(s) for f, s in zip(full, sufs))
@@ -318,7 +334,7 @@ def test_w1_nested_prefixes_candidates_and_errors(w1):
     _sync()
     got = split_probs(probs, loff)
     ref = om.score_from_scratch(m, cands, clabs)
-    assert max_abs(got, ref) <= TOL_F32
+    close("w1 staged candidates", got, ref, TOL_F32)
     assert np.array_equal(got[0], got[1])
 
     in_use = ctx.stats()["pages_in_use"]
@@ -340,7 +356,7 @@ def test_w1_nested_prefixes_candidates_and_errors(w1):
     probs, loff = ctx.score_branches([hb], [sufs[1]], [labs[1]])        # still works
     _sync()
     ref = om.score_from_scratch(m, [A + B + sufs[1]], [labs[1]])
-    assert max_abs(split_probs(probs, loff), ref) <= TOL_F32
+    close("w1 after errors", split_probs(probs, loff), ref, TOL_F32)
     ctx.free_pages([hb, ha])
     assert ctx.stats()["pages_in_use"] == 0
 
@@ -364,7 +380,7 @@ def test_w1_out_of_pages_leaves_state_unchanged():
     probs, loff = ctx.score_branches([ha], sufs[:1], labs[:1])
     _sync()
     ref = om.score_from_scratch(m, [A + sufs[0]], labs[:1])
-    assert max_abs(split_probs(probs, loff), ref) <= TOL_F32
+    close("w1 out of pages", split_probs(probs, loff), ref, TOL_F32)
     ctx.free_pages([ha])
     assert ctx.stats()["pages_in_use"] == 0
     ctx.close()
@@ -387,12 +403,9 @@ def test_w2_shared_prefix_matches_oracle(w2):
     probs, loff = ctx.score_branches([h] * 5, [b.tokens for b in br], [b.labels for b in br])
     _sync()
     got = split_probs(probs, loff)
-    ref = g["passes"][0]["probs"]
-    err = max_abs(got, ref)
-    print("w2 shared max abs err", err)
     pages = ctx.page_table(h)[0]
     ctx.free_pages([h])
-    assert err <= TOL_BF16_E2E
+    check_branches("w2 shared prefix vs oracle", got, g["passes"][0]["probs"], stored_bars(g))
     assert pages == list(range(125))
 
 
@@ -401,21 +414,27 @@ def test_w2_unshared_matches_oracle(w2):
     seqs = inst.full_sequences(0)
     probs, loff = ctx.score_branches([0] * 5, [s for s, _ in seqs], [l for _, l in seqs])
     _sync()
-    err = max_abs(split_probs(probs, loff), g["passes"][0]["probs"])
-    print("w2 unshared max abs err", err)
-    assert err <= TOL_BF16_E2E
+    check_branches("w2 unshared vs oracle", split_probs(probs, loff), g["passes"][0]["probs"],
+                   stored_bars(g))
 
 
 def teacher_forced_check(ctx, m, prefix, branches, layers):
     """Runs prefill + scoring with taps on every layer, then re-runs each oracle
-    layer on the GPU's own input of that layer and compares."""
+    layer on the GPU's own input of that layer and compares, for the prefix
+    round (causal prefill attention, prefill output projection) and for the
+    branch round (cascade attention, branch projections).  Returns the worst
+    attention-row and residual-row errors of each round and the readout
+    error."""
     P = len(prefix)
     T = sum(len(b.tokens) for b in branches)
     dev = "cuda:0"
     dt = torch.bfloat16
-    pre_x = [torch.zeros((P, m.d), dtype=dt, device=dev) for _ in range(layers)]
-    for l in range(layers):
+    pre_x = [torch.zeros((P, m.d), dtype=dt, device=dev) for _ in range(layers + 1)]
+    pre_att = [torch.zeros((P, m.hq * m.dh), dtype=dt, device=dev) for _ in range(layers)]
+    for l in range(layers + 1):
         ctx.debug_tap(TAP_RESID, l, pre_x[l])
+    for l in range(layers):
+        ctx.debug_tap(TAP_ATTN, l, pre_att[l])
     (h,) = ctx.prefill_prefix([0], [prefix])
     _sync()
     ctx.debug_tap()
@@ -430,10 +449,17 @@ def teacher_forced_check(ctx, m, prefix, branches, layers):
     _sync()
     ctx.debug_tap()
     npf = lambda t: t.float().cpu().numpy()
-    worst_att = worst_res = 0.0
+    worst = {"prefix attention": 0.0, "prefix residual": 0.0, "branch attention": 0.0,
+             "branch residual": 0.0}
+    pos_p = np.arange(P)
     for l in range(layers):
         xp = npf(pre_x[l])
-        _, kp, vp = om.layer_qkv(m, l, xp, np.arange(P))
+        qp, kp, vp = om.layer_qkv(m, l, xp, pos_p)
+        a_pre = om.store(m, om.attention(m, qp, kp, vp, pos_p, pos_p))
+        g_pre = npf(pre_att[l]).reshape(P, m.hq, m.dh)
+        worst["prefix attention"] = max(worst["prefix attention"], row_rel_err(g_pre, a_pre))
+        worst["prefix residual"] = max(worst["prefix residual"],
+                                       row_rel_err(npf(pre_x[l + 1]), om.layer_out(m, l, xp, g_pre)))
         xs = npf(suf_x[l])
         o_ref = []
         t0 = 0
@@ -446,9 +472,10 @@ def teacher_forced_check(ctx, m, prefix, branches, layers):
             o_ref.append(om.store(m, a))
             t0 += n
         o_ref = np.concatenate(o_ref)
-        worst_att = max(worst_att, row_rel_err(npf(att[l]).reshape(T, m.hq, m.dh), o_ref))
-        x_next = om.layer_out(m, l, xs, npf(att[l]).reshape(T, m.hq, m.dh))
-        worst_res = max(worst_res, row_rel_err(npf(suf_x[l + 1]), x_next))
+        g_att = npf(att[l]).reshape(T, m.hq, m.dh)
+        worst["branch attention"] = max(worst["branch attention"], row_rel_err(g_att, o_ref))
+        worst["branch residual"] = max(worst["branch residual"],
+                                       row_rel_err(npf(suf_x[l + 1]), om.layer_out(m, l, xs, g_att)))
     # readout of the GPU's own final residual stream
     xl = npf(suf_x[layers])
     last = np.cumsum([len(b.tokens) for b in branches]) - 1
@@ -457,15 +484,17 @@ def teacher_forced_check(ctx, m, prefix, branches, layers):
     ref = [om.label_softmax(lp[i, np.asarray(b.labels)]) for i, b in enumerate(branches)]
     err_read = max_abs(split_probs(probs, loff), ref)
     ctx.free_pages([h])
-    return worst_att, worst_res, err_read
+    return worst, err_read
 
 
 def test_w2_teacher_forced_layers_and_readout(w2):
     wl, inst, g, ctx, _ = w2
     m = om.from_weights(host_weights(2))
-    att, res, rd = teacher_forced_check(ctx, m, inst.prefixes[0], inst.passes[0], wl.model.n_layers)
-    print(f"w2 teacher-forced: attention {att:.2e}, residual {res:.2e}, readout {rd:.2e}")
-    assert att <= 2e-2 and res <= 2e-2
+    worst, rd = teacher_forced_check(ctx, m, inst.prefixes[0], inst.passes[0], wl.model.n_layers)
+    for what, err in worst.items():
+        record(f"w2 teacher-forced {what} rows (rel)", err, TOL_ROW)
+    record("w2 teacher-forced readout of own final state", rd, TOL_BF16)
+    assert all(err <= TOL_ROW for err in worst.values())
     assert rd <= TOL_BF16
 
 
@@ -482,9 +511,7 @@ def test_w2_attention_output_matches_oracle(w2):
     ctx.debug_tap()
     got = tap.float().cpu().numpy().reshape(T, 32, 128)
     want = oracle_attention_layer0(m, inst.prefixes[0], [b.tokens for b in br])
-    err = row_rel_err(got, want)
-    print("w2 layer-0 attention max row rel err", err)
-    assert err <= 2e-2
+    close_rows("w2 layer-0 attention rows", got, want, TOL_ROW)
     ctx.free_pages([h])
 
 
@@ -514,9 +541,8 @@ def test_w3_staged_rounds_match_oracle(w2):
     ctx, _ = device_context(3, n_pages=1024, max_pos=4096, max_tok=4096)
     probs, loff = ctx.score_candidates(inst.candidates, inst.cand_labels)
     _sync()
-    err = max_abs(split_probs(probs, loff), g["passes"][0]["probs"])
-    print("w3 staged max abs err", err)
-    assert err <= TOL_BF16_E2E
+    bars = stored_bars(g)
+    check_branches("w3 depth rounds vs oracle", split_probs(probs, loff), g["passes"][0]["probs"], bars)
     st = ctx.stats()
     assert st["rounds"] == 3 and st["computed_tokens"] == 800 + 120 + 240
     assert st["pages_in_use"] == 0
@@ -526,13 +552,14 @@ def test_w3_staged_rounds_match_oracle(w2):
     ctx.set_plan_mode(jev.JEV_PLAN_CANDIDATE_FIRST)
     probs2, loff2 = ctx.score_candidates(inst.candidates, inst.cand_labels)
     _sync()
-    err2 = max_abs(split_probs(probs2, loff2), g["passes"][0]["probs"])
-    print("w3 candidate-first max abs err", err2)
-    assert err2 <= TOL_BF16_E2E
-    # the two orders run the same nodes in other round compositions, i.e. the
-    # GEMMs accumulate in other orders: they may differ by the models'
-    # accumulation-order floor (TOL_BF16_E2E's derivation), not more
-    assert max_abs(split_probs(probs2, loff2), split_probs(probs, loff)) <= ORDER_FLOOR
+    check_branches("w3 candidate-first vs oracle", split_probs(probs2, loff2), g["passes"][0]["probs"],
+                   bars)
+    # the two orders run the same nodes in other round compositions; a round
+    # of at most 256 rows splits its projections' K over workgroups, a larger
+    # one does not, so the K/V of a node can accumulate in another order: the
+    # two runs are held to each other like two faithful orders of the oracle
+    check_branches("w3 candidate-first vs depth rounds", split_probs(probs2, loff2),
+                   split_probs(probs, loff), bars)
     st = ctx.stats()
     assert st["rounds"] == 3 and st["computed_tokens"] == 800 + 120 + 240
     assert st["pages_in_use"] == 0
@@ -562,9 +589,7 @@ def test_w3_requests_through_the_continuous_batching_scheduler(w2):
         steps += 1
         assert steps < 20
     got = sch.result(t1) + sch.result(t2)
-    err = max_abs(got, g["passes"][0]["probs"])
-    print("w3 scheduler max abs err", err, "steps", steps)
-    assert err <= TOL_BF16_E2E
+    check_branches(f"w3 scheduler ({steps} steps) vs oracle", got, g["passes"][0]["probs"], stored_bars(g))
     sch.close()
     assert ctx.stats()["pages_in_use"] == 0
 
@@ -585,14 +610,134 @@ def test_w4_batch_of_requests_matches_oracle():
                                      [b.labels for b in br])
     _sync()
     got = split_probs(probs, loff)
-    err = max_abs(got, g["passes"][0]["probs"])
-    print("w4 max abs err", err)
     st = ctx.stats()
     ctx.free_pages(hs)
-    assert err <= TOL_BF16_E2E
+    check_branches("w4 batch of requests vs oracle", got, g["passes"][0]["probs"], stored_bars(g))
     assert all(len(t) == 75 for t in tables)
     assert len({p for t in tables for p in t}) == 16 * 75
     assert st["computed_tokens"] == 128 * 64 and st["logical_tokens"] == 128 * (1200 + 64)
     assert ctx.stats()["pages_in_use"] == 0
     for p in got:
         assert abs(float(np.sum(p)) - 1.0) < 1e-4 and len(p) == 64
+
+
+# ------------------------------------------------------------------ workload 2 cut to one block
+def test_w6_one_block_bf16_held_to_1e3():
+    """Workload 2's first block alone (same seed: the same tokens, labels,
+    embedding, unembedding and block-0 weights; the same kernel instances).
+    With one block the oracle's own accumulation-order spread stays below
+    1e-3 (at most 6.3e-4), so every branch is held to the benchmark spec's 1e-3
+    itself, shared and unshared."""
+    g = golden(6)
+    assert max(g["passes"][0]["spread"]) < TOL_BF16
+    inst = make_instance(workload(6))
+    ctx, _ = device_context(6, n_pages=1024, max_pos=4096, max_tok=10240)
+    br = inst.passes[0]
+    (h,) = ctx.prefill_prefix([0], [inst.prefixes[0]])
+    probs, loff = ctx.score_branches([h] * 5, [b.tokens for b in br], [b.labels for b in br])
+    _sync()
+    ctx.free_pages([h])
+    check_branches("w6 one block, shared prefix vs oracle", split_probs(probs, loff), g["passes"][0]["probs"],
+                   [TOL_BF16] * 5)
+    seqs = inst.full_sequences(0)
+    probs, loff = ctx.score_branches([0] * 5, [s for s, _ in seqs], [l for _, l in seqs])
+    _sync()
+    check_branches("w6 one block, unshared vs oracle", split_probs(probs, loff), g["passes"][0]["probs"],
+                   [TOL_BF16] * 5)
+    ctx.close()
+
+
+# ------------------------------------------------------------------ workloads 3 and 4 on the tiny float32 model
+def test_w7_tiny_tree_rounds_plan_orders_and_scheduler_float32():
+    """Workload 3's tree (800 -> 2 x 60 -> 3 x 40 each) on the float32 model:
+    depth rounds, the page's candidate-first rounds and the continuous-batching
+    scheduler all match the oracle from scratch within 1e-5."""
+    from shared_prefix_kv_amd import jev
+    wl = workload(7)
+    inst = make_instance(wl)
+    m = om.from_weights(host_weights(7))
+    ref = om.score_from_scratch(m, inst.candidates, inst.cand_labels)
+    ctx, _ = device_context(7, n_pages=256, max_pos=2048, max_tok=2048)
+    runs = []
+    for mode in (jev.JEV_PLAN_DEPTH, jev.JEV_PLAN_CANDIDATE_FIRST):
+        ctx.set_plan_mode(mode)
+        probs, loff = ctx.score_candidates(inst.candidates, inst.cand_labels)
+        _sync()
+        runs.append(split_probs(probs, loff))
+        close(f"w7 tiny tree, plan mode {mode}", runs[-1], ref, TOL_F32)
+        st = ctx.stats()
+        assert st["rounds"] == 3 and st["computed_tokens"] == 800 + 120 + 240
+        assert st["pages_in_use"] == 0
+    close("w7 tiny tree, candidate-first vs depth", runs[1], runs[0], 2 * TOL_F32)
+    ctx.set_plan_mode(jev.JEV_PLAN_DEPTH)
+    sch = jev.Scheduler(ctx)
+    C, L = inst.candidates, inst.cand_labels
+    t1 = sch.submit(C[:4], L[:4])
+    sch.step()
+    t2 = sch.submit(C[4:], L[4:])
+    for _ in range(10):
+        if sch.status(t1) == jev.JEV_SCHED_FINISHED and sch.status(t2) == jev.JEV_SCHED_FINISHED:
+            break
+        sch.step()
+    close("w7 tiny tree, scheduler", sch.result(t1) + sch.result(t2), ref, TOL_F32)
+    sch.close()
+    assert ctx.stats()["pages_in_use"] == 0
+    ctx.close()
+
+
+def test_w8_tiny_batch_of_requests_float32():
+    """Workload 4's batch (16 prefixes of 1,200 tokens, 8 branches of 64 tokens
+    each, 64 labels per branch) on the float32 model, against the oracle from
+    scratch within 1e-5; every branch sees only its own request's pages."""
+    wl = workload(8)
+    inst = make_instance(wl)
+    m = om.from_weights(host_weights(8))
+    seqs = inst.full_sequences(0)
+    ref = om.score_from_scratch(m, [s for s, _ in seqs], [l for _, l in seqs])
+    ctx, _ = device_context(8, n_pages=2048, max_pos=1536, max_tok=20480)
+    hs = ctx.prefill_prefix([0] * len(inst.prefixes), inst.prefixes)
+    tables = [ctx.page_table(h)[0] for h in hs]
+    br = inst.passes[0]
+    probs, loff = ctx.score_branches([hs[b.request] for b in br], [b.tokens for b in br],
+                                     [b.labels for b in br])
+    _sync()
+    got = split_probs(probs, loff)
+    close("w8 tiny batch of requests", got, ref, TOL_F32)
+    assert tables == [list(range(75 * r, 75 * r + 75)) for r in range(16)]
+    st = ctx.stats()
+    assert st["computed_tokens"] == 128 * 64 and st["logical_tokens"] == 128 * (1200 + 64)
+    ctx.free_pages(hs)
+    assert ctx.stats()["pages_in_use"] == 0
+    ctx.close()
+
+
+def test_w9_tiny_long_prefix_two_wave_groups_and_split_tiles_float32():
+    """A 2,100-token prefix on the float32 model: the prefill round's longest
+    causal tile has 132 pages, so the attention runs two wave groups per
+    workgroup, and its long tiles are split into an unmasked and a causal page
+    chunk merged by LSE.  Prefill attention rows within 1e-4 relative and the
+    branches' probabilities within 1e-5 of the oracle."""
+    wl = workload(9)
+    inst = make_instance(wl)
+    m = om.from_weights(host_weights(9))
+    P = inst.prefixes[0]
+    ctx, _ = device_context(9, n_pages=512, max_pos=4096, max_tok=4096)
+    tap = torch.zeros((len(P), m.hq * m.dh), dtype=torch.float32, device="cuda:0")
+    ctx.debug_tap(TAP_ATTN, 0, tap)
+    (h,) = ctx.prefill_prefix([0], [P])
+    _sync()
+    ctx.debug_tap()
+    pos = np.arange(len(P))
+    x = om.store(m, m.embed[np.asarray(P)])
+    q, k, v = om.layer_qkv(m, 0, x, pos)
+    want = om.store(m, om.attention(m, q, k, v, pos, pos))
+    close_rows("w9 prefill attention rows (two wave groups, split tiles)",
+               tap.cpu().numpy().reshape(len(P), m.hq, m.dh), want, 1e-4)
+    br = inst.passes[0]
+    probs, loff = ctx.score_branches([h] * len(br), [b.tokens for b in br], [b.labels for b in br])
+    _sync()
+    seqs = inst.full_sequences(0)
+    ref = om.score_from_scratch(m, [s for s, _ in seqs], [l for _, l in seqs])
+    close("w9 tiny long prefix branches", split_probs(probs, loff), ref, TOL_F32)
+    ctx.free_pages([h])
+    ctx.close()
