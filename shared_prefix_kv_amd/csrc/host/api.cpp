@@ -155,6 +155,16 @@ struct RoundDesc {
   int32_t attn_groups = 1;  // wave groups per attention workgroup
 };
 
+// Device scratch of a call's kernels: attention partial states (rows of dh
+// floats plus their log2-sum-exp) and the split-K partial tiles of the
+// branch-round projections.
+struct Scratch {
+  float* part_o;
+  float* part_lse;
+  int64_t part_rows;
+  jev::GemmWs gemm;
+};
+
 }  // namespace
 
 struct jev_ctx {
@@ -211,6 +221,12 @@ int check_alive(jev_ctx* ctx) {
   return JEV_OK;
 }
 
+Scratch ws_scratch(const jev_ctx* ctx) {
+  return Scratch{reinterpret_cast<float*>(ctx->ws + ctx->L.part_o), reinterpret_cast<float*>(ctx->ws + ctx->L.part_lse),
+                 ctx->L.part_rows,
+                 jev::GemmWs{reinterpret_cast<float*>(ctx->ws + ctx->L.gemm_part), ctx->L.gemm_part_elems}};
+}
+
 // Handles on the root..h paths of `hs`: prefixes a call uses, never evicted by it.
 std::set<int64_t> path_set(const jev::ResidentTree& t, const std::vector<int64_t>& hs) {
   std::set<int64_t> out;
@@ -219,25 +235,32 @@ std::set<int64_t> path_set(const jev::ResidentTree& t, const std::vector<int64_t
   return out;
 }
 
-// Makes room for a call that does not fit: with the cache policy on, evicts
-// cached prefixes (least recently used first, none in `pinned`) until
-// fits(tree, pool) holds.  The victims are found on copies and applied only if
-// they suffice; otherwise JEV_ENOMEM and nothing changes.
+// Cached prefixes a call must evict to fit (cache policy on): least recently
+// used first, none in `pinned`, found on copies of the tree and pool until
+// fits(tree, pool) holds.  Nothing changes here; JEV_ENOMEM if they do not
+// suffice.  The caller applies them together with the rest of its changes,
+// once every check of the call has passed.
 template <typename Fits>
-int make_room(jev_ctx* ctx, const std::set<int64_t>& pinned, Fits fits, const char* what) {
+int find_room(jev_ctx* ctx, const std::set<int64_t>& pinned, Fits fits, const char* what,
+              std::vector<int64_t>* victims) {
+  victims->clear();
   if (fits(*ctx->tree, ctx->pages)) return JEV_OK;  // a plan trial leaves the pool as it found it
   if (!ctx->tree->keep()) return fail(JEV_ENOMEM, what);
   jev::PagePool pool = ctx->pages;
   jev::ResidentTree tree = *ctx->tree;
   tree.rebind(&pool);
-  std::vector<int64_t> victims;
   while (!fits(tree, pool)) {
     const int64_t v = tree.evict_one(pinned);
     if (v == 0) return fail(JEV_ENOMEM, what);
-    victims.push_back(v);
+    victims->push_back(v);
   }
-  for (int64_t v : victims) ctx->tree->evict(v);
   return JEV_OK;
+}
+
+// Stages the pages of a call's victims as free in the pool (the caller
+// restores its snapshot after simulating its page allocation).
+void release_victim_pages(jev_ctx* ctx, const std::vector<int64_t>& victims) {
+  for (int64_t v : victims) ctx->pages.release(ctx->tree->node(v).pages);
 }
 
 // Resident prefixes the candidates of a plan continue (their match paths).
@@ -520,9 +543,12 @@ int build_round(jev_ctx* ctx, std::vector<RNode>& nodes, std::vector<int32_t>& h
 
 // Copies the descriptors of a call to the device and runs its rounds.
 int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vector<int32_t>& hb, float* probs,
-               hipStream_t s) {
+               hipStream_t s, const Scratch& sc) {
   if (int64_t(hb.size()) > ctx->L.desc_ints)
     return fail(JEV_ENOMEM, "call descriptors exceed the workspace descriptor region");
+  for (const RoundDesc& rd : rds)
+    if (rd.part_slots * ctx->desc.n_kv_heads * kRowsPerTile > sc.part_rows)
+      return fail(JEV_ENOMEM, "round needs more partial-state rows than the scratch holds");
   if (ctx->have_last && s != ctx->last_stream) HIPCHK(hipStreamWaitEvent(s, ctx->last_done, 0));
   if (ctx->have_last) HIPCHK(hipEventSynchronize(ctx->desc_copied));
   std::memcpy(ctx->desc_host, hb.data(), hb.size() * sizeof(int32_t));
@@ -535,9 +561,9 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
   void* q = ctx->ws + ctx->L.q;
   void* o = ctx->ws + ctx->L.o;
   float* rope = reinterpret_cast<float*>(ctx->ws + ctx->L.rope);
-  float* part_o = reinterpret_cast<float*>(ctx->ws + ctx->L.part_o);
-  float* part_lse = reinterpret_cast<float*>(ctx->ws + ctx->L.part_lse);
-  const jev::GemmWs gws{reinterpret_cast<float*>(ctx->ws + ctx->L.gemm_part), ctx->L.gemm_part_elems};
+  float* part_o = sc.part_o;
+  float* part_lse = sc.part_lse;
+  const jev::GemmWs gws = sc.gemm;
   const size_t elt = size_t(elt_size(ctx->desc));
   // times one launch with events when its kind is being profiled
   auto timed = [&](int kind, int layer, int64_t rows, double flops, double bytes, auto&& launch) -> hipError_t {
@@ -775,26 +801,28 @@ int jev_prefill_prefix(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const
       return fail(JEV_EINVAL, "prefix " + std::to_string(i) + " runs past max_positions");
     items.push_back({parents[i], tokens + offsets[i], len});
   }
+  std::vector<int64_t> victims;
   {
     std::vector<int64_t> used;
     for (const auto& it : items) {
       used.push_back(it.parent);
       if (int64_t c = ctx->tree->find_child(it.parent, it.tok, it.n)) used.push_back(c);
     }
-    if (int rc = make_room(ctx, path_set(*ctx->tree, used),
+    if (int rc = find_room(ctx, path_set(*ctx->tree, used),
                            [&](const jev::ResidentTree& t, jev::PagePool& p) {
                              return t.prefill_need(items) <= p.n_free();
                            },
-                           "not enough free KV pages"))
+                           "not enough free KV pages", &victims))
       return rc;
   }
-  // Simulate the allocation tree->prefill() will make (new nodes take the
-  // lowest free ids in input order; an identical resident child or an earlier
-  // identical item of this call creates nothing), so that descriptors are built
-  // and checked before any state changes.
+  // Simulate the allocation tree->prefill() will make after the evictions
+  // (new nodes take the lowest free ids in input order; an identical resident
+  // child or an earlier identical item of this call creates nothing), so that
+  // descriptors are built and checked before any state changes.
   std::vector<RNode> rn;
   {
     std::set<int32_t> snap = ctx->pages.snapshot();
+    release_victim_pages(ctx, victims);
     std::vector<size_t> made;  // indices of items that create a node
     for (int32_t i = 0; i < n; ++i) {
       const auto& it = items[i];
@@ -825,7 +853,9 @@ int jev_prefill_prefix(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const
     if (int64_t(hb.size()) > ctx->L.desc_ints)
       return fail(JEV_ENOMEM, "call descriptors exceed the workspace descriptor region");
   }
-  // commit the tree change, then run (the tree allocates the same lowest ids)
+  // commit the evictions and the tree change, then run (the tree allocates the
+  // same lowest ids)
+  for (int64_t v : victims) ctx->tree->evict(v);
   std::vector<int64_t> handles;
   std::vector<char> created;
   ctx->tree->prefill(items, &handles, &created);
@@ -840,14 +870,19 @@ int jev_prefill_prefix(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const
   ctx->stats.rounds = rn.empty() ? 0 : 1;
   ctx->stats.calls += 1;
   if (!rn.empty() && !ctx->dry) {
-    if (int rc = run_rounds(ctx, rds, hb, nullptr, reinterpret_cast<hipStream_t>(hip_stream))) return rc;
+    if (int rc = run_rounds(ctx, rds, hb, nullptr, reinterpret_cast<hipStream_t>(hip_stream), ws_scratch(ctx)))
+      return rc;
   }
   return JEV_OK;
 }
 
-int jev_score_branches(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const int32_t* tokens,
-                       const int64_t* tok_offsets, const int32_t* label_ids, const int64_t* label_offsets,
-                       float* probs, void* hip_stream) {
+namespace {
+
+// jev_score_branches: everything is checked and every descriptor built
+// before any state changes.
+int score_branches(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const int32_t* tokens,
+                   const int64_t* tok_offsets, const int32_t* label_ids, const int64_t* label_offsets, float* probs,
+                   void* hip_stream) {
   if (int rc = check_alive(ctx)) return rc;
   if (int rc = check_segments(ctx, n, tokens, tok_offsets, "branches")) return rc;
   if (n == 0) return JEV_OK;
@@ -865,13 +900,15 @@ int jev_score_branches(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const
     logical += ctx->tree->end_pos(parents[i]) + len;
   }
   const std::vector<int64_t> used(parents, parents + n);
-  if (int rc = make_room(ctx, path_set(*ctx->tree, used),
+  std::vector<int64_t> victims;
+  if (int rc = find_room(ctx, path_set(*ctx->tree, used),
                          [&](const jev::ResidentTree&, jev::PagePool& p) { return need <= p.n_free(); },
-                         "not enough free KV pages"))
+                         "not enough free KV pages", &victims))
     return rc;
-  ctx->clock += 1;
-  for (int64_t h : used) ctx->tree->touch_path(h, ctx->clock);
+  // branch pages live for this call only: allocated on the pool as it will be
+  // after the evictions, then the pool is restored
   std::set<int32_t> snap = ctx->pages.snapshot();
+  release_victim_pages(ctx, victims);
   std::vector<RNode> rn;
   std::map<int64_t, std::vector<jev::PageRef>> anc_cache;
   int64_t computed = 0;
@@ -892,16 +929,31 @@ int jev_score_branches(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const
     computed += nd.n;
     rn.push_back(std::move(nd));
   }
-  ctx->pages.restore(std::move(snap));  // branch pages live for this call only
+  ctx->pages.restore(std::move(snap));
   std::vector<int32_t> hb;
   std::vector<RoundDesc> rds(1);
   if (int rc = build_round(ctx, rn, hb, &rds[0])) return rc;
+  if (int64_t(hb.size()) > ctx->L.desc_ints)
+    return fail(JEV_ENOMEM, "call descriptors exceed the workspace descriptor region");
+  const Scratch sc = ws_scratch(ctx);
+  // commit: evictions, recency, statistics
+  for (int64_t v : victims) ctx->tree->evict(v);
+  ctx->clock += 1;
+  for (int64_t h : used) ctx->tree->touch_path(h, ctx->clock);
   ctx->stats.logical_tokens = logical;
   ctx->stats.computed_tokens = computed;
   ctx->stats.cached_tokens = logical - computed;
   ctx->stats.rounds = 1;
   ctx->stats.calls += 1;
-  return run_rounds(ctx, rds, hb, probs, reinterpret_cast<hipStream_t>(hip_stream));
+  return run_rounds(ctx, rds, hb, probs, reinterpret_cast<hipStream_t>(hip_stream), sc);
+}
+
+}  // namespace
+
+int jev_score_branches(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const int32_t* tokens,
+                       const int64_t* tok_offsets, const int32_t* label_ids, const int64_t* label_offsets,
+                       float* probs, void* hip_stream) {
+  return score_branches(ctx, n, parents, tokens, tok_offsets, label_ids, label_offsets, probs, hip_stream);
 }
 
 // The nodes of round r of a candidate plan, as the executor takes them;
@@ -959,29 +1011,31 @@ int jev_score_candidates(jev_ctx* ctx, int32_t n, const int32_t* tokens, const i
   for (int32_t i = 0; i < n; ++i)
     if (tok_offsets[i + 1] - tok_offsets[i] > ctx->desc.max_positions)
       return fail(JEV_EINVAL, "candidate " + std::to_string(i) + " runs past max_positions");
+  // the tree work (splits, evictions, the plan) on copies; the rounds and
+  // their descriptors are built against the copies, which are committed only
+  // once every check has passed
   jev::Plan plan;
-  {
-    jev::PagePool pool;
-    jev::ResidentTree tree(&pool);
-    if (int rc = stage_candidates(ctx, n, tokens, tok_offsets, &pool, &tree, &plan, ctx->plan_mode)) return rc;
-    ctx->pages = pool;
-    *ctx->tree = std::move(tree);
-    ctx->tree->rebind(&ctx->pages);
-  }
-  ctx->clock += 1;
-  for (int64_t h : plan.anchors) ctx->tree->touch_path(h, ctx->clock);
-  // rounds
+  jev::PagePool pool;
+  jev::ResidentTree tree(&pool);
+  if (int rc = stage_candidates(ctx, n, tokens, tok_offsets, &pool, &tree, &plan, ctx->plan_mode)) return rc;
   std::vector<std::vector<RNode>> rounds(plan.rounds.size());
   std::map<int64_t, std::vector<jev::PageRef>> anchor_pages;
   int64_t computed = 0, logical = 0;
   for (int32_t c = 0; c < n; ++c) logical += tok_offsets[c + 1] - tok_offsets[c];
   for (size_t r = 0; r < plan.rounds.size(); ++r)
-    computed += plan_round_nodes(*ctx->tree, plan, r, tokens, tok_offsets, label_ids, label_offsets, &anchor_pages,
+    computed += plan_round_nodes(tree, plan, r, tokens, tok_offsets, label_ids, label_offsets, &anchor_pages,
                                  &rounds[r]);
   std::vector<int32_t> hb;
   std::vector<RoundDesc> rds(rounds.size());
   for (size_t r = 0; r < rounds.size(); ++r)
     if (int rc = build_round(ctx, rounds[r], hb, &rds[r])) return rc;
+  if (int64_t(hb.size()) > ctx->L.desc_ints)
+    return fail(JEV_ENOMEM, "call descriptors exceed the workspace descriptor region");
+  ctx->pages = pool;
+  *ctx->tree = std::move(tree);
+  ctx->tree->rebind(&ctx->pages);
+  ctx->clock += 1;
+  for (int64_t h : plan.anchors) ctx->tree->touch_path(h, ctx->clock);
   ctx->stats.logical_tokens = logical;
   ctx->stats.computed_tokens = computed;
   ctx->stats.cached_tokens = logical - computed;
@@ -1013,7 +1067,7 @@ int jev_score_candidates(jev_ctx* ctx, int32_t n, const int32_t* tokens, const i
       }
     for (int64_t h : made) ctx->tree->release(h);
   }
-  return run_rounds(ctx, rds, hb, probs, reinterpret_cast<hipStream_t>(hip_stream));
+  return run_rounds(ctx, rds, hb, probs, reinterpret_cast<hipStream_t>(hip_stream), ws_scratch(ctx));
 }
 
 // ----------------------------------------------------------------- scheduler
@@ -1242,7 +1296,7 @@ int jev_sched_step(jev_sched* s, void* hip_stream, int32_t* plan_out, int64_t pl
   ctx->stats.calls += 1;
   if (!ctx->dry) {
     const hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
-    if (int rc = run_rounds(ctx, rds, hb, s->dprobs, st)) return rc;
+    if (int rc = run_rounds(ctx, rds, hb, s->dprobs, st, ws_scratch(ctx))) return rc;
     std::vector<float> hp(size_t(loff.back()));
     HIPCHK(hipMemcpyAsync(hp.data(), s->dprobs, hp.size() * sizeof(float), hipMemcpyDeviceToHost, st));
     HIPCHK(hipStreamSynchronize(st));

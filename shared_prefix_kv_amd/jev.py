@@ -251,10 +251,10 @@ class Context:
         flat, off = _segments(suffixes)
         lflat, loff = _segments(labels)
         probs = self._probs(probs, int(loff[-1]))
-        _check(lib().jev_score_branches(self.ctx, len(suffixes), _ptr(par, ctypes.c_int64),
-                                        _ptr(flat, ctypes.c_int32), _ptr(off, ctypes.c_int64),
-                                        _ptr(lflat, ctypes.c_int32), _ptr(loff, ctypes.c_int64),
-                                        ctypes.c_void_p(probs.data_ptr()), stream or self._stream()))
+        fn = lib().jev_score_branches
+        _check(fn(self.ctx, len(suffixes), _ptr(par, ctypes.c_int64), _ptr(flat, ctypes.c_int32),
+                  _ptr(off, ctypes.c_int64), _ptr(lflat, ctypes.c_int32), _ptr(loff, ctypes.c_int64),
+                  ctypes.c_void_p(probs.data_ptr()), stream or self._stream()))
         return probs, loff
 
     def score_candidates(self, seqs, labels, probs=None, stream=None):

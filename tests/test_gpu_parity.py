@@ -386,6 +386,45 @@ def test_w1_out_of_pages_leaves_state_unchanged():
     ctx.close()
 
 
+def test_w1_calls_that_fail_late_change_nothing():
+    """Calls that pass every early check but fail when their round is built
+    (more tokens than max_round_tokens) leave the tree, the pool, the cached
+    prefixes and the statistics as they were, even where they would have
+    evicted a cached prefix or split a resident one first."""
+    from shared_prefix_kv_amd import jev
+    wl = workload(1)
+    m = om.from_weights(host_weights(1))
+    ctx, _ = device_context(1, n_pages=10, max_pos=1024, max_tok=64)
+    ctx.set_cache_policy(jev.JEV_CACHE_LRU)
+    rng = np.random.default_rng(81)
+    A = [int(t) for t in rng.integers(0, 1024, 48)]                       # 3 pages, cached below
+    P = [int(t) for t in rng.integers(0, 1024, 16)]                       # 1 page, referenced
+    (ha,) = ctx.prefill_prefix([0], [A])
+    (hp,) = ctx.prefill_prefix([0], [P])
+    ctx.free_pages([ha])
+    before = ctx.stats()
+    assert before["cached_prefixes"] == 1 and before["pages_in_use"] == 4
+    # 100 tokens: 7 pages, so A would be evicted first; 100 rows > 64
+    long_suffix = [int(t) for t in rng.integers(0, 1024, 100)]
+    with pytest.raises(jev.JevError) as e:
+        ctx.score_branches([hp], [long_suffix], [[1, 2]])
+    assert e.value.code == jev.JEV_ENOMEM
+    # three candidates leaving A at token 40: A would be split at 32 tokens,
+    # and the round holds 3 x 28 = 84 > 64 rows
+    cands = [A[:40] + [int(t) for t in rng.integers(0, 1024, 20)] for _ in range(3)]
+    with pytest.raises(jev.JevError) as e:
+        ctx.score_candidates(cands, [[1, 2]] * 3)
+    assert e.value.code == jev.JEV_ENOMEM
+    assert ctx.stats() == before
+    assert ctx.match(A + [7]) == (ha, len(A))                               # A resident, whole, not split
+    probs, loff = ctx.score_branches([hp], [long_suffix[:20]], [[1, 2]])   # still works
+    _sync()
+    close("w1 after late failures", split_probs(probs, loff),
+          om.score_from_scratch(m, [P + long_suffix[:20]], [[1, 2]]), TOL_F32)
+    ctx.free_pages([hp])
+    ctx.close()
+
+
 # ------------------------------------------------------------------ workload 2 (bf16, headline)
 @pytest.fixture(scope="module")
 def w2():
