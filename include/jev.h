@@ -146,6 +146,22 @@ int jev_score_branches(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const
                        const int64_t* tok_offsets, const int32_t* label_ids,
                        const int64_t* label_offsets, float* probs, void* hip_stream);
 
+/* jev_score_branches for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, results and errors; the kernels' scratch (the
+ * attention partial states and the split-K partial tiles) lives in a 96 MiB
+ * file-scope device array instead of the context's workspace, one copy per GPU
+ * the library runs on, held until the process ends.  The call makes no
+ * hipMalloc/hipFree and no allocating library call (profiling records of
+ * jev_profile are not taken on this path).  A call whose round needs more
+ * partial-state rows than the array holds fails with JEV_ENOMEM before
+ * anything changes.  Every call on one GPU shares that GPU's array and finds
+ * it as the previous call left it: calls that overlap on one GPU (contexts
+ * driven on different streams at once) race. */
+int jev_score_branches_noalloc(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const int32_t* tokens,
+                               const int64_t* tok_offsets, const int32_t* label_ids,
+                               const int64_t* label_offsets, float* probs, void* hip_stream);
+
 /* Scores n candidates given as full token sequences (LLM2Jev shared-prefix page,
  * staged-submission section).  Each candidate is matched against the resident
  * prefixes (longest full-node match leaving at least one token; where it leaves

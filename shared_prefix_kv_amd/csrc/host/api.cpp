@@ -163,6 +163,7 @@ struct Scratch {
   float* part_lse;
   int64_t part_rows;
   jev::GemmWs gemm;
+  bool no_alloc;  // the call may not create anything (profiling records are skipped)
 };
 
 }  // namespace
@@ -181,6 +182,7 @@ struct jev_ctx {
   char* pool = nullptr;
   WsLayout L{};
   char* ws = nullptr;
+  char* static_scratch = nullptr;  // this device's copy of the file-scope scratch array
   int32_t* desc_host = nullptr;  // pinned staging
   hipEvent_t desc_copied = nullptr;
   hipEvent_t last_done = nullptr;
@@ -224,7 +226,64 @@ int check_alive(jev_ctx* ctx) {
 Scratch ws_scratch(const jev_ctx* ctx) {
   return Scratch{reinterpret_cast<float*>(ctx->ws + ctx->L.part_o), reinterpret_cast<float*>(ctx->ws + ctx->L.part_lse),
                  ctx->L.part_rows,
-                 jev::GemmWs{reinterpret_cast<float*>(ctx->ws + ctx->L.gemm_part), ctx->L.gemm_part_elems}};
+                 jev::GemmWs{reinterpret_cast<float*>(ctx->ws + ctx->L.gemm_part), ctx->L.gemm_part_elems}, false};
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------- static scratch
+// Scratch of jev_score_branches_noalloc: a file-scope device array, one copy
+// per GPU the library runs on, held until the process ends.  On the host its
+// name is only a stand-in symbol, never a device address: jev_create looks up
+// the current device's copy once with hipGetSymbolAddress, and every use goes
+// through that pointer (kernel arguments).
+constexpr size_t kNoAllocScratchBytes = size_t(96) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's copy of the scratch array (looked up once per device).
+int device_scratch(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(JEV_EHIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(JEV_EHIP, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(JEV_EHIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return JEV_OK;
+}
+
+// The static scratch laid out for a call: the split-K partial tiles first
+// (sized like the workspace's), then as many attention partial-state rows as
+// fit; JEV_ENOMEM if the call's rounds need more rows.
+int static_scratch_for(const jev_ctx* ctx, const std::vector<RoundDesc>& rds, Scratch* out) {
+  if (!ctx->static_scratch) return fail(JEV_ESTATE, "no static scratch on this context");
+  const size_t gemm_bytes = align256(ctx->L.gemm_part_elems * sizeof(float));
+  const size_t row_bytes = size_t(ctx->desc.head_dim + 1) * sizeof(float);
+  if (gemm_bytes + 512 + row_bytes > kNoAllocScratchBytes)
+    return fail(JEV_ENOMEM, "model too large for the 96 MiB static scratch");
+  const int64_t rows = int64_t((kNoAllocScratchBytes - gemm_bytes - 512) / row_bytes);
+  int64_t need = 0;
+  for (const RoundDesc& rd : rds) need = std::max<int64_t>(need, rd.part_slots * ctx->desc.n_kv_heads * kRowsPerTile);
+  if (need > rows)
+    return fail(JEV_ENOMEM, "round needs " + std::to_string(need) + " partial-state rows; the 96 MiB static scratch holds " +
+                                std::to_string(rows));
+  char* base = ctx->static_scratch;
+  const size_t o_bytes = align256(size_t(rows) * ctx->desc.head_dim * sizeof(float));
+  *out = Scratch{reinterpret_cast<float*>(base + gemm_bytes), reinterpret_cast<float*>(base + gemm_bytes + o_bytes),
+                 rows, jev::GemmWs{reinterpret_cast<float*>(base), ctx->L.gemm_part_elems}, true};
+  return JEV_OK;
 }
 
 // Handles on the root..h paths of `hs`: prefixes a call uses, never evicted by it.
@@ -567,7 +626,7 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
   const size_t elt = size_t(elt_size(ctx->desc));
   // times one launch with events when its kind is being profiled
   auto timed = [&](int kind, int layer, int64_t rows, double flops, double bytes, auto&& launch) -> hipError_t {
-    if (!(ctx->prof_mask & (1u << kind))) return launch();
+    if (sc.no_alloc || !(ctx->prof_mask & (1u << kind))) return launch();
     jev_ctx::Prof p;
     p.rec = jev_launch_record{kind, layer, rows, flops, bytes, 0.f};
     for (hipEvent_t* e : {&p.e0, &p.e1}) {
@@ -746,6 +805,7 @@ int jev_create(const jev_model_desc* desc, const jev_weights* weights, void* kv_
     }
     ctx->pool = reinterpret_cast<char*>(kv_pool);
     ctx->ws = reinterpret_cast<char*>(workspace);
+    if (int rc = device_scratch(&ctx->static_scratch)) return rc;
     HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&ctx->desc_host), size_t(ctx->L.desc_ints) * sizeof(int32_t),
                          hipHostMallocDefault));
     HIPCHK(hipEventCreateWithFlags(&ctx->desc_copied, hipEventDisableTiming));
@@ -878,11 +938,11 @@ int jev_prefill_prefix(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const
 
 namespace {
 
-// jev_score_branches: everything is checked and every descriptor built
-// before any state changes.
+// jev_score_branches and its allocation-free variant: everything is checked
+// and every descriptor built before any state changes.
 int score_branches(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const int32_t* tokens,
                    const int64_t* tok_offsets, const int32_t* label_ids, const int64_t* label_offsets, float* probs,
-                   void* hip_stream) {
+                   void* hip_stream, bool noalloc) {
   if (int rc = check_alive(ctx)) return rc;
   if (int rc = check_segments(ctx, n, tokens, tok_offsets, "branches")) return rc;
   if (n == 0) return JEV_OK;
@@ -935,7 +995,9 @@ int score_branches(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const int
   if (int rc = build_round(ctx, rn, hb, &rds[0])) return rc;
   if (int64_t(hb.size()) > ctx->L.desc_ints)
     return fail(JEV_ENOMEM, "call descriptors exceed the workspace descriptor region");
-  const Scratch sc = ws_scratch(ctx);
+  Scratch sc = ws_scratch(ctx);
+  if (noalloc)
+    if (int rc = static_scratch_for(ctx, rds, &sc)) return rc;
   // commit: evictions, recency, statistics
   for (int64_t v : victims) ctx->tree->evict(v);
   ctx->clock += 1;
@@ -953,7 +1015,13 @@ int score_branches(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const int
 int jev_score_branches(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const int32_t* tokens,
                        const int64_t* tok_offsets, const int32_t* label_ids, const int64_t* label_offsets,
                        float* probs, void* hip_stream) {
-  return score_branches(ctx, n, parents, tokens, tok_offsets, label_ids, label_offsets, probs, hip_stream);
+  return score_branches(ctx, n, parents, tokens, tok_offsets, label_ids, label_offsets, probs, hip_stream, false);
+}
+
+int jev_score_branches_noalloc(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const int32_t* tokens,
+                               const int64_t* tok_offsets, const int32_t* label_ids, const int64_t* label_offsets,
+                               float* probs, void* hip_stream) {
+  return score_branches(ctx, n, parents, tokens, tok_offsets, label_ids, label_offsets, probs, hip_stream, true);
 }
 
 // The nodes of round r of a candidate plan, as the executor takes them;

@@ -27,7 +27,7 @@ _NAMES = {0: "JEV_OK", 1: "JEV_EINVAL", 2: "JEV_ENOMEM", 3: "JEV_EHANDLE", 4: "J
           6: "JEV_EPENDING"}
 
 EXPORTED = ["jev_workspace_bytes", "jev_kv_pool_bytes", "jev_create", "jev_destroy", "jev_prefill_prefix",
-            "jev_score_branches", "jev_score_candidates", "jev_free_pages", "jev_plan", "jev_page_table",
+            "jev_score_branches", "jev_score_branches_noalloc", "jev_score_candidates", "jev_free_pages", "jev_plan", "jev_page_table",
             "jev_match", "jev_stats", "jev_debug_tap", "jev_profile", "jev_profile_read", "jev_answers",
             "jev_set_plan_mode", "jev_set_cache_policy", "jev_sched_create", "jev_sched_destroy",
             "jev_sched_submit", "jev_sched_step", "jev_sched_status", "jev_sched_result", "jev_last_error"]
@@ -88,6 +88,7 @@ def lib() -> ctypes.CDLL:
         L.jev_destroy.argtypes = [vp]
         L.jev_prefill_prefix.argtypes = [vp, i32, P(i64), P(i32), P(i64), P(i64), vp]
         L.jev_score_branches.argtypes = [vp, i32, P(i64), P(i32), P(i64), P(i32), P(i64), vp, vp]
+        L.jev_score_branches_noalloc.argtypes = [vp, i32, P(i64), P(i32), P(i64), P(i32), P(i64), vp, vp]
         L.jev_score_candidates.argtypes = [vp, i32, P(i32), P(i64), P(i32), P(i64), vp, vp]
         L.jev_free_pages.argtypes = [vp, i32, P(i64)]
         L.jev_plan.argtypes = [vp, i32, P(i32), P(i64), P(i32), i64, P(i64)]
@@ -245,13 +246,14 @@ class Context:
                                         _ptr(out, ctypes.c_int64), stream or self._stream()))
         return [int(h) for h in out]
 
-    def score_branches(self, parents, suffixes, labels, probs=None, stream=None):
-        """Returns (probs device tensor [sum K] float32, label offsets)."""
+    def score_branches(self, parents, suffixes, labels, probs=None, stream=None, noalloc=False):
+        """Returns (probs device tensor [sum K] float32, label offsets).
+        noalloc: call jev_score_branches_noalloc (the caller passes probs)."""
         par = _i64(parents)
         flat, off = _segments(suffixes)
         lflat, loff = _segments(labels)
         probs = self._probs(probs, int(loff[-1]))
-        fn = lib().jev_score_branches
+        fn = lib().jev_score_branches_noalloc if noalloc else lib().jev_score_branches
         _check(fn(self.ctx, len(suffixes), _ptr(par, ctypes.c_int64), _ptr(flat, ctypes.c_int32),
                   _ptr(off, ctypes.c_int64), _ptr(lflat, ctypes.c_int32), _ptr(loff, ctypes.c_int64),
                   ctypes.c_void_p(probs.data_ptr()), stream or self._stream()))
