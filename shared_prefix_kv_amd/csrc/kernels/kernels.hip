@@ -257,10 +257,6 @@ __global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2,
   constexpr int MAIN_BYTES = GROUPS * 2 * KV_BYTES + kMaxTilePages * 4;
   __shared__ __attribute__((aligned(16))) char lds[MAIN_BYTES > XCH_BYTES ? MAIN_BYTES : XCH_BYTES];
   int32_t* const sP = reinterpret_cast<int32_t*>(lds + GROUPS * 2 * KV_BYTES);
-  // per-group barrier counters (two groups): each wave adds 1 per barrier
-  __shared__ int gbar[2];
-  if (GROUPS > 1 && threadIdx.x < 2) gbar[threadIdx.x] = 0;
-
   // one workgroup per (tile, KV head); the KV head is the fast index, so that
   // neighbouring workgroups read the same pages (whose KV heads are adjacent)
   const int kvh = blockIdx.x % hkv;
@@ -273,29 +269,9 @@ __global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2,
   T (*const sK)[32 * DH] = reinterpret_cast<T (*)[32 * DH]>(lds + grp * 2 * KV_BYTES);
   T (*const sV)[DH * 32] = reinterpret_cast<T (*)[DH * 32]>(lds + grp * 2 * KV_BYTES + KV_BYTES);
   const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6, c = lane & 31, hh = lane >> 5;
-  // Barrier of the step pipeline.  One group: the workgroup barrier.  Two:
-  // each group waits for its own four waves only (an LDS counter), so that
-  // the groups drift out of phase like two workgroups and overlap one's MFMAs
-  // with the other's exponentials; a shared barrier kept them in lockstep.
-  // The wait is bounded: past the limit a wave goes on (it cannot happen
-  // while every wave of a group runs the same steps).
-  int gtarget = 0;
-  auto step_sync = [&]() __attribute__((always_inline)) {
-    if constexpr (GROUPS == 1) {
-      __syncthreads();
-    } else {
-      gtarget += 4;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      if (lane == 0) __hip_atomic_fetch_add(&gbar[grp], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      for (int spin = 0; spin < (1 << 22); ++spin) {
-        const int seen = __builtin_amdgcn_readfirstlane(
-            __hip_atomic_load(&gbar[grp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
-        if (seen >= gtarget) break;
-        __builtin_amdgcn_s_sleep(1);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    }
-  };
+  // Barrier of the step pipeline: the workgroup barrier (with two groups every
+  // wave of both groups meets it; their halves are offset, see the loop).
+  auto step_sync = [&]() __attribute__((always_inline)) { __syncthreads(); };
   const int row = wave * 32 + c;
   const int ti = row / G, hg = row % G;
   const bool row_ok = ti < tile.n_tok;
@@ -319,8 +295,13 @@ __global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2,
   // nst (the same for both groups, so that their barriers pair up; a group's
   // steps past the tile's end have every key masked)
   const int nst_all = (tile.n_pages + 1) >> 1;
-  const int nst = (nst_all + GROUPS - 1) / GROUPS;
-  const int s0 = grp * nst;
+  const int nst_own = (nst_all + GROUPS - 1) / GROUPS;
+  const int s0 = grp * nst_own;
+  // pages of this group's steps (the rest of its steps are fully masked)
+  const int page_end = min(tile.n_pages, 2 * (s0 + nst_own));
+  // two groups: an even count, so that the ping-pong loop body (two steps)
+  // has no conditional half; the extra step, if any, is fully masked
+  const int nst = GROUPS > 1 ? (nst_own + 1) & ~1 : nst_own;
 
   // loop-invariant LDS offsets
   int koff[NKS];
@@ -430,26 +411,24 @@ __global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2,
   if (nst > 0) SA = qk(0);
   // step 0 stores K of step 2 into K buffer 0: every wave has to be done
   // reading K of step 0 from it first (once per tile)
-  if (nst > 2) step_sync();
-  // One step: stores K of step st+2 and V of step st+1 from (kst, vst), loads
-  // K of step st+3 and V of step st+2 into (kld, vld), turns S_in (scores of
-  // step st) into probabilities and leaves the scores of step st+1 in S_out.
-  auto step = [&](const int st, const u32x4* kst, const u32x4* vst, u32x4* kld, u32x4* vld, f32x16& S_in,
-                  f32x16& S_out) __attribute__((always_inline)) {
-    const int buf = st & 1;
+  if (GROUPS > 1 || nst > 2) step_sync();
+
+  // ---- pieces of a step (st = this group's step) ----
+  // page-list window: moved every 16 steps
+  auto window = [&](const int st) __attribute__((always_inline)) {
     if (st > 0 && (st & 15) == 0) {
       pw_base = min(2 * (s0 + st), tile.n_pages - 1);
       pw = sP[min(pw_base + lane, tile.n_pages - 1)];
     }
-    // loads for the next step's stores
-    gload_k(st + 3, kld);
-    gload_v(st + 2, vld);
-
-    f32x16& S = S_in;  // consumed here: masked in place
-    // mask only where needed: partial pages, or keys past the wave's first query
+  };
+  // First half of the softmax of step st's scores S (masked in place): the
+  // mask where needed (partial pages, keys past the wave's first query), the
+  // running maximum with its lazy rescale of the output and the sum; returns
+  // the offset that the exponentials subtract.
+  auto softmax_a = [&](const int st, f32x16& S) __attribute__((always_inline)) -> float {
     const int lp0 = 2 * (s0 + st);
-    const int v0 = (lp0 < tile.n_pages) ? (page_entry(lp0) & 31) : 0;
-    const int v1 = (lp0 + 1 < tile.n_pages) ? (page_entry(lp0 + 1) & 31) : 0;
+    const int v0 = (lp0 < page_end) ? (page_entry(lp0) & 31) : 0;
+    const int v1 = (lp0 + 1 < page_end) ? (page_entry(lp0 + 1) & 31) : 0;
     const bool mask = (v0 < 16) || (v1 < 16) || (tile.causal && tile.kv_pos0 + 16 * lp0 + 31 > qmin);
     if (mask) {
 #pragma unroll
@@ -477,13 +456,15 @@ __global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2,
         for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
       mrun = mnew;
     }
-    const float nm = (mrun == kNegInf) ? 0.f : -mrun;
-
-    // Branch-free from here: the S MFMAs of the next step (a dependent chain)
-    // are interleaved with this step's exponentials, so that one wave per
-    // SIMD keeps the MFMA and VALU pipes busy together. On the last step the
-    // product reads stale LDS and is never used.
-    S_out = qk(buf ^ 1);
+    return (mrun == kNegInf) ? 0.f : -mrun;
+  };
+  // Second half: the probabilities, their sum, and (bf16) P = P_hi + P_lo,
+  // both bf16 (P_hi the upper 16 bits of the fp32 value, P_lo its exact
+  // remainder rounded to nearest), so that the PV product sees P to ~16
+  // significant bits, not the 8 of one bf16 rounding (that rounding alone
+  // moved label probabilities several times further than any change of
+  // summation order does).
+  auto softmax_b = [&](const f32x16& S, const float nm, frag* pb, frag* pl) __attribute__((always_inline)) {
     float p[16];
     float lsum = 0.f;
 #pragma unroll
@@ -493,12 +474,6 @@ __global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2,
     }
     lsum = xor32_sum(lsum);
     lrun += lsum;
-    // bf16: P = P_hi + P_lo, both bf16 (P_hi the upper 16 bits of the fp32
-    // value, P_lo its exact remainder rounded to nearest), so that the PV
-    // product sees P to ~16 significant bits, not the 8 of one bf16 rounding
-    // (that rounding alone moved label probabilities several times further
-    // than any change of summation order does).
-    frag pb[16 / KL], pl[16 / KL];
 #pragma unroll
     for (int tt = 0; tt < 16 / KL; ++tt) {
       if constexpr (KL == 8) {
@@ -512,7 +487,10 @@ __global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2,
         pb[tt] = p[tt];
       }
     }
-    // O^T += V^T P^T; MFMA tt covers keys {8j + 4*hh + i : 4j + i in [tt*KL, tt*KL+KL)}
+  };
+  // O^T += V^T P^T from V buffer buf; MFMA tt covers keys
+  // {8j + 4*hh + i : 4j + i in [tt*KL, tt*KL+KL)}
+  auto pv = [&](const int buf, const frag* pb, const frag* pl) __attribute__((always_inline)) {
 #pragma unroll
     for (int tt = 0; tt < 16 / KL; ++tt) {
       frag va[NDB];
@@ -534,35 +512,147 @@ __global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2,
         for (int b = 0; b < NDB; ++b) oacc[b] = MF::mma(va[b], pl[tt], oacc[b]);
       }
     }
-    if constexpr (KL == 8) {
-      // Order of the branch-free block: 2 K-fragment reads ahead; per S MFMA
-      // ~10 VALU (exponentials, row sums, the P_hi / P_lo split) and the next
-      // K read, plus, over the last four, the V reads of the first PV block;
-      // then the PV MFMAs (hi then lo per 16 keys) with the V reads of the
-      // second block spread over the first half.
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-      for (int i = 0; i < NKS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
-        if (i + 2 < NKS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (i >= NKS - NDB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4 * NDB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i < 2 * NDB && (i & 1) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-      }
-    }
-
-    if (st + 2 < nst) sstore_k(buf, kst);
-    if (st + 1 < nst) sstore_v(buf ^ 1, vst);
-    step_sync();
   };
-  for (int st = 0; st < nst; st += 2) {
-    step(st, rkA, rvA, rkB, rvB, SA, SB);
-    if (st + 1 < nst) step(st + 1, rkB, rvB, rkA, rvA, SB, SA);
+
+  if constexpr (GROUPS == 1) {
+    // One step: stores K of step st+2 and V of step st+1 from (kst, vst), loads
+    // K of step st+3 and V of step st+2 into (kld, vld), turns S_in (scores of
+    // step st) into probabilities and leaves the scores of step st+1 in S_out.
+    auto step = [&](const int st, const u32x4* kst, const u32x4* vst, u32x4* kld, u32x4* vld, f32x16& S_in,
+                    f32x16& S_out) __attribute__((always_inline)) {
+      const int buf = st & 1;
+      window(st);
+      // loads for the next step's stores
+      gload_k(st + 3, kld);
+      gload_v(st + 2, vld);
+      const float nm = softmax_a(st, S_in);
+      // Branch-free from here: the S MFMAs of the next step (a dependent chain)
+      // are interleaved with this step's exponentials, so that one wave per
+      // SIMD keeps the MFMA and VALU pipes busy together. On the last step the
+      // product reads stale LDS and is never used.
+      S_out = qk(buf ^ 1);
+      frag pb[16 / KL], pl[16 / KL];
+      softmax_b(S_in, nm, pb, pl);
+      pv(buf, pb, pl);
+      if constexpr (KL == 8) {
+        // Order of the branch-free block: 2 K-fragment reads ahead; per S MFMA
+        // ~10 VALU (exponentials, row sums, the P_hi / P_lo split) and the next
+        // K read, plus, over the last four, the V reads of the first PV block;
+        // then the PV MFMAs (hi then lo per 16 keys) with the V reads of the
+        // second block spread over the first half.
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int i = 0; i < NKS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+          if (i + 2 < NKS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (i >= NKS - NDB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4 * NDB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i < 2 * NDB && (i & 1) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
+      }
+      if (st + 2 < nst) sstore_k(buf, kst);
+      if (st + 1 < nst) sstore_v(buf ^ 1, vst);
+      step_sync();
+    };
+    for (int st = 0; st < nst; st += 2) {
+      step(st, rkA, rvA, rkB, rvB, SA, SB);
+      if (st + 1 < nst) step(st + 1, rkB, rvB, rkA, rvA, SB, SA);
+    }
+  } else {
+    // Two groups in ping-pong: a step is split into a softmax half (VALU: the
+    // mask, maximum, exponentials, sum and P split of step st, then the LDS
+    // stores of K of step st+2 and V of step st+1) and a matrix half (MFMA:
+    // the scores of step st+1 and O += V P of step st, with the global loads
+    // of K of step st+3 and V of step st+2).  Group 1 runs one half behind
+    // group 0, and every half ends at the workgroup barrier, so that on each
+    // SIMD one wave issues MFMAs while the other works the VALU.  Both groups
+    // run the same number of halves and barriers.
+    frag pb[16 / KL], pl[16 / KL];
+    auto half_softmax = [&](const int st, f32x16& S_in, const u32x4* kst, const u32x4* vst)
+                            __attribute__((always_inline)) {
+      const int buf = st & 1;
+      window(st);
+      const float nm = softmax_a(st, S_in);
+      softmax_b(S_in, nm, pb, pl);
+      if (st + 2 < nst) sstore_k(buf, kst);
+      if (st + 1 < nst) sstore_v(buf ^ 1, vst);
+    };
+    auto half_mfma = [&](const int st, f32x16& S_out, u32x4* kld, u32x4* vld) __attribute__((always_inline)) {
+      const int buf = st & 1;
+      gload_k(st + 3, kld);
+      gload_v(st + 2, vld);
+      // keep the loads here, two halves ahead of the stores that use them
+      // (the compiler would otherwise sink them next to the stores)
+      asm volatile("" ::: "memory");
+      // on the last step the score product reads stale LDS and is never used
+      if constexpr (KL == 8) {
+        // every fragment read first; then the dependent score chain of step
+        // st+1 alternates with the independent O += V P_hi / V P_lo MFMAs of
+        // step st (per output block the same order as pv(): hi then lo for
+        // keys 0-15, then for keys 16-31)
+        frag kf[NKS], v0[NDB], v1[NDB];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) kf[ks] = MF::load(&sK[buf ^ 1][koff[ks]]);
+#pragma unroll
+        for (int b = 0; b < NDB; ++b) {
+          v0[b] = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(&sV[buf][0])[vq_unit(32 * b + c, hh)]);
+          v1[b] = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(&sV[buf][0])[vq_unit(32 * b + c, 2 + hh)]);
+        }
+        f32x16 S;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[r] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 2 * NDB; ++i) {
+          oacc[i % NDB] = MF::mma(v0[i % NDB], i < NDB ? pb[0] : pl[0], oacc[i % NDB]);
+          if (i < NKS) S = MF::mma(kf[i], qf[i], S);
+        }
+#pragma unroll
+        for (int i = 2 * NDB; i < NKS; ++i) S = MF::mma(kf[i], qf[i], S);
+#pragma unroll
+        for (int i = 0; i < 2 * NDB; ++i)
+          oacc[i % NDB] = MF::mma(v1[i % NDB], i < NDB ? pb[1] : pl[1], oacc[i % NDB]);
+        S_out = S;
+        // issue order: the global loads, the K and first V fragment reads,
+        // then two MFMAs at a time (the second V reads among the first),
+        // then the last eight
+        __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NKS + NDB, 0);
+#pragma unroll
+        for (int i = 0; i < NKS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          if (i >= 2 && i < 2 + NDB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NDB, 0);
+      } else {
+        S_out = qk(buf ^ 1);
+        pv(buf, pb, pl);
+      }
+    };
+    // the halves are kept apart for the scheduler as well: nothing moves
+    // across a half's barrier (MFMAs would otherwise drift into the softmax
+    // half, which the partner group needs for its own MFMAs)
+    auto half_sync = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (grp == 1) half_sync();
+    for (int st = 0; st < nst; st += 2) {
+      half_softmax(st, SA, rkA, rvA);
+      half_sync();
+      half_mfma(st, SB, rkB, rvB);
+      half_sync();
+      half_softmax(st + 1, SB, rkB, rvB);
+      half_sync();
+      half_mfma(st + 1, SA, rkA, rvA);
+      half_sync();
+    }
+    if (grp == 0) half_sync();
   }
 
   if constexpr (GROUPS > 1) {
