@@ -346,8 +346,12 @@ int jev_answers(int32_t n, const float* probs, const int64_t* label_offsets, con
  * in the same GPU round.  Probabilities equal those of scoring each request
  * alone, up to the rounding order of the bf16 kernels.
  *
- * The scheduler belongs to its context: destroy it before the context, and
- * make no other call on the context while jev_sched_step runs. */
+ * The scheduler belongs to its context: make no other call on the context
+ * while jev_sched_step runs.  Destroying the context first detaches its
+ * schedulers (their requests are dropped): later calls on them fail with
+ * JEV_ESTATE, jev_sched_status still answers, and jev_sched_destroy only frees
+ * them.  Destroying a context while another thread uses one of its schedulers
+ * is undefined. */
 typedef struct jev_sched jev_sched;
 enum { JEV_SCHED_QUEUED = 0, JEV_SCHED_ACTIVE = 1, JEV_SCHED_FINISHED = 2 };
 int jev_sched_create(jev_ctx* ctx, jev_sched** out);

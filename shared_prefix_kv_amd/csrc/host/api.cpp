@@ -204,6 +204,7 @@ struct jev_ctx {
   uint32_t prof_mask = 0;
   std::vector<Prof> prof;
   std::vector<hipEvent_t> prof_free;  // events kept for re-use
+  std::vector<jev_sched*> scheds;     // schedulers on this context (detached when it is destroyed)
 };
 
 namespace {
@@ -829,9 +830,15 @@ int jev_create(const jev_model_desc* desc, const jev_weights* weights, void* kv_
   return JEV_OK;
 }
 
+static void detach_sched(jev_sched* s);
+
 int jev_destroy(jev_ctx* ctx) {
   if (!ctx) return JEV_OK;
   int rc = JEV_OK;
+  // schedulers still alive lose their context (their handles stay valid until
+  // jev_sched_destroy, which then only frees them)
+  for (jev_sched* s : ctx->scheds) detach_sched(s);
+  ctx->scheds.clear();
   if (!ctx->dry) {
     if (ctx->have_last && hipEventSynchronize(ctx->last_done) != hipSuccess) rc = fail(JEV_EHIP, "sync failed");
     if (ctx->desc_host) (void)hipHostFree(ctx->desc_host);
@@ -1171,18 +1178,35 @@ int jev_sched_create(jev_ctx* ctx, jev_sched** out) {
   auto* s = new jev_sched();
   s->ctx = ctx;
   s->n_pages = ctx->pages.n_total();
+  ctx->scheds.push_back(s);
   *out = s;
   return JEV_OK;
+}
+
+// The context of s is going away: its device buffer is freed and it forgets
+// the context (the held prefixes go with the context's tree).
+static void detach_sched(jev_sched* s) {
+  jev_ctx* ctx = s->ctx;
+  if (!ctx) return;
+  if (!ctx->dry && ctx->have_last) (void)hipEventSynchronize(ctx->last_done);
+  if (s->dprobs) (void)hipFree(s->dprobs);
+  s->dprobs = nullptr;
+  s->dprobs_cap = 0;
+  s->held.clear();
+  s->ctx = nullptr;
 }
 
 int jev_sched_destroy(jev_sched* s) {
   if (!s) return JEV_OK;
   jev_ctx* ctx = s->ctx;
   int rc = JEV_OK;
-  if (!ctx->dry && ctx->have_last && hipEventSynchronize(ctx->last_done) != hipSuccess)
-    rc = fail(JEV_EHIP, "sync failed");
-  for (int64_t h : s->held) ctx->tree->release(h);
-  if (s->dprobs) (void)hipFree(s->dprobs);
+  if (ctx) {
+    if (!ctx->dry && ctx->have_last && hipEventSynchronize(ctx->last_done) != hipSuccess)
+      rc = fail(JEV_EHIP, "sync failed");
+    for (int64_t h : s->held) ctx->tree->release(h);
+    if (s->dprobs) (void)hipFree(s->dprobs);
+    ctx->scheds.erase(std::remove(ctx->scheds.begin(), ctx->scheds.end(), s), ctx->scheds.end());
+  }
   delete s;
   return rc;
 }
@@ -1191,6 +1215,7 @@ int jev_sched_submit(jev_sched* s, int32_t n, const int32_t* tokens, const int64
                      const int32_t* label_ids, const int64_t* label_offsets, int64_t* ticket) {
   if (!s || !ticket) return fail(JEV_EINVAL, "NULL scheduler or ticket");
   const jev_ctx* ctx = s->ctx;
+  if (!ctx) return fail(JEV_ESTATE, "the scheduler's context was destroyed");
   if (n < 1) return fail(JEV_EINVAL, "a request needs at least one candidate");
   if (int rc = check_segments(ctx, n, tokens, tok_offsets, "candidates")) return rc;
   if (int rc = check_labels(ctx, n, label_ids, label_offsets)) return rc;
@@ -1239,6 +1264,7 @@ int jev_sched_result(jev_sched* s, int64_t ticket, float* probs, int64_t cap) {
     if (s->active_tickets.count(ticket)) return fail(JEV_EPENDING, "request " + std::to_string(ticket) + " not finished");
     return fail(JEV_EHANDLE, "unknown or collected ticket " + std::to_string(ticket));
   }
+  if (!s->ctx) return fail(JEV_ESTATE, "the scheduler's context was destroyed");
   if (s->ctx->dry) return fail(JEV_ESTATE, "no scores on a planning-only context");
   const std::vector<float>& p = it->second->probs;
   if (!probs || cap < int64_t(p.size())) return fail(JEV_EINVAL, "probs NULL or cap below the request's label count");
@@ -1250,6 +1276,7 @@ int jev_sched_result(jev_sched* s, int64_t ticket, float* probs, int64_t cap) {
 int jev_sched_step(jev_sched* s, void* hip_stream, int32_t* plan_out, int64_t plan_cap, int64_t* plan_n) {
   if (!s) return fail(JEV_EINVAL, "NULL scheduler");
   jev_ctx* ctx = s->ctx;
+  if (!ctx) return fail(JEV_ESTATE, "the scheduler's context was destroyed");
   if (int rc = check_alive(ctx)) return rc;
   if (plan_n) *plan_n = 0;
   {

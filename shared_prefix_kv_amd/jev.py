@@ -14,7 +14,9 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "lib", "libjev.so")
+# JEV_LIB selects another build of the same library (the sanitizer build for
+# the CPU tests); the default is the in-tree libjev.so
+LIB_PATH = os.environ.get("JEV_LIB") or os.path.join(_HERE, "lib", "libjev.so")
 
 JEV_OK, JEV_EINVAL, JEV_ENOMEM, JEV_EHANDLE, JEV_EHIP, JEV_ESTATE, JEV_EPENDING = range(7)
 JEV_DTYPE_F32, JEV_DTYPE_BF16 = 0, 1

@@ -278,3 +278,33 @@ def test_closing_the_context_first_closes_its_schedulers():
     with pytest.raises(jev.JevError) as e:
         sch2.status(t + 100)
     assert e.value.code == jev.JEV_EHANDLE
+
+
+def test_destroying_the_context_first_detaches_its_schedulers():
+    """A context destroyed before its scheduler (as a garbage collector may
+    finalise them in either order) detaches it: later calls fail with
+    JEV_ESTATE instead of reading freed memory, and destroying the scheduler
+    still works.  Raw C ABI calls, so the binding's own ordering cannot help."""
+    import ctypes
+    L = jev.lib()
+    ctx = dry(64)
+    sch = jev.Scheduler(ctx)
+    t = sch.submit([[1, 2, 3, 4]], labels(1))
+    raw_ctx, raw_s = ctx.ctx, sch.s
+    assert L.jev_destroy(raw_ctx) == jev.JEV_OK
+    ctx.ctx = ctypes.c_void_p()              # the binding no longer owns it
+    state = ctypes.c_int32()
+    assert L.jev_sched_status(raw_s, t, ctypes.byref(state)) == jev.JEV_OK
+    tk = ctypes.c_int64()
+    flat = np.array([1, 2, 3], np.int32)
+    off = np.array([0, 3], np.int64)
+    lab = np.array([1, 2], np.int32)
+    loff = np.array([0, 2], np.int64)
+    P = lambda a, t_: a.ctypes.data_as(ctypes.POINTER(t_))
+    rc = L.jev_sched_submit(raw_s, 1, P(flat, ctypes.c_int32), P(off, ctypes.c_int64), P(lab, ctypes.c_int32),
+                            P(loff, ctypes.c_int64), ctypes.byref(tk))
+    assert rc == jev.JEV_ESTATE
+    n = ctypes.c_int64()
+    assert L.jev_sched_step(raw_s, None, None, 0, ctypes.byref(n)) == jev.JEV_ESTATE
+    assert L.jev_sched_destroy(raw_s) == jev.JEV_OK
+    sch.s = ctypes.c_void_p()
