@@ -24,8 +24,11 @@ summation order alone moves the result (the reproducibility floor that the
 bf16 parity bars are derived from): "fp64" (float64 products and sums, then
 the same storage rounding), "fp32_krev" (float32, contraction index run in
 reverse) and "fp32_khalves" (float32, the two halves of the contraction
-summed separately, then added).  All of them are faithful implementations of
-the same definition.
+summed separately, then added).  The ``elementwise`` field does the same for
+the steps between contractions (RMSNorm, RoPE, the attention softmax, the
+residual add): float64 by default, or "fp32" (RoPE angles still taken in
+float64 and rounded to float32, as a table would hold them).  All of these are
+faithful implementations of the same definition.
 
 Scoring (jdon.com openjev-sglang article, "prefill-only" section and
 "inference flow" steps 4-5): run the whole prompt once, take the
@@ -73,21 +76,28 @@ class OracleModel:
     attn_norm: List[np.ndarray]
     final_norm: np.ndarray
     gemm: str = "fp32"
+    elementwise: str = "fp64"
 
     @property
     def gemm_dtype(self):
         return np.float64 if (self.mode == "f64" or self.gemm == "fp64") else np.float32
 
+    @property
+    def ew_dtype(self):
+        return np.float32 if (self.elementwise == "fp32" and self.mode != "f64") else np.float64
+
 
 GEMM_ORDERS = ("fp32", "fp64", "fp32_krev", "fp32_khalves")
 
 
-def from_weights(w, mode: Optional[str] = None, gemm: str = "fp32") -> OracleModel:
+def from_weights(w, mode: Optional[str] = None, gemm: str = "fp32", elementwise: str = "fp64") -> OracleModel:
     """Builds the oracle's float view of ``synth.Weights``."""
     s = w.shape
     mode = mode or ("bf16" if s.dtype == "bf16" else "f32")
     if gemm not in GEMM_ORDERS:
         raise ValueError(f"unknown accumulation {gemm!r}")
+    if elementwise not in ("fp64", "fp32"):
+        raise ValueError(f"unknown elementwise precision {elementwise!r}")
     conv = (lambda a: bits_to_f32(a)) if a_is_bits(w) else (lambda a: np.asarray(a, np.float32))
     wide = mode == "f64" or gemm == "fp64"
     cast = (lambda a: conv(a).astype(np.float64)) if wide else conv
@@ -95,7 +105,7 @@ def from_weights(w, mode: Optional[str] = None, gemm: str = "fp32") -> OracleMod
         s.n_layers, s.d, s.hq, s.hkv, s.dh, s.vocab, s.rope_theta, s.eps, mode,
         cast(w.embed), cast(w.unembed),
         [cast(a) for a in w.wq], [cast(a) for a in w.wk], [cast(a) for a in w.wv],
-        [cast(a) for a in w.wo], [cast(a) for a in w.attn_norm], cast(w.final_norm), gemm)
+        [cast(a) for a in w.wo], [cast(a) for a in w.attn_norm], cast(w.final_norm), gemm, elementwise)
 
 
 def contract(m: OracleModel, a: np.ndarray, b: np.ndarray) -> np.ndarray:
@@ -125,23 +135,24 @@ def store(m: OracleModel, x: np.ndarray) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
-    """x / sqrt(mean(x^2) + eps) * g over the last axis, in float64."""
-    x64 = np.asarray(x, np.float64)
-    ms = np.mean(x64 * x64, axis=-1, keepdims=True)
-    return x64 / np.sqrt(ms + eps) * np.asarray(g, np.float64)
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float, dtype=np.float64) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * g over the last axis (float64 by default)."""
+    xd = np.asarray(x, dtype)
+    ms = np.mean(xd * xd, axis=-1, keepdims=True)
+    return xd / np.sqrt(ms + dtype(eps)) * np.asarray(g, dtype)
 
 
-def rope(x: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray:
-    """Rotate-half RoPE of x [n, heads, dh] at the given logical positions (float64)."""
+def rope(x: np.ndarray, positions: np.ndarray, theta: float, dtype=np.float64) -> np.ndarray:
+    """Rotate-half RoPE of x [n, heads, dh] at the given logical positions.
+    Angles in float64; the rotation in ``dtype`` (float64 by default)."""
     n, _, dh = x.shape
     half = dh // 2
     inv_freq = theta ** (-(2.0 * np.arange(half, dtype=np.float64)) / dh)
     ang = np.asarray(positions, np.float64)[:, None] * inv_freq[None, :]
-    c = np.cos(ang)[:, None, :]
-    s = np.sin(ang)[:, None, :]
-    x64 = np.asarray(x, np.float64)
-    x1, x2 = x64[..., :half], x64[..., half:]
+    c = np.cos(ang).astype(dtype)[:, None, :]
+    s = np.sin(ang).astype(dtype)[:, None, :]
+    xd = np.asarray(x, dtype)
+    x1, x2 = xd[..., :half], xd[..., half:]
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
 
 
@@ -173,9 +184,10 @@ def attention(m: OracleModel, q: np.ndarray, k: np.ndarray, v: np.ndarray,
             qj = np.ascontiguousarray(q[t0:t1, j, :], dtype=m.gemm_dtype)
             # keys no query of this chunk can see contribute nothing; skip them
             ks = np.nonzero(k_pos <= q_pos[t0:t1].max())[0]
-            s = contract(m, qj, kj[ks].T).astype(np.float64) * scale
+            ew = m.ew_dtype
+            s = contract(m, qj, kj[ks].T).astype(ew) * ew(scale)
             visible = k_pos[None, ks] <= q_pos[t0:t1, None]
-            s = np.where(visible, s, -np.inf)
+            s = np.where(visible, s, ew(-np.inf))
             mx = s.max(axis=1, keepdims=True)
             p = np.exp(s - mx)
             p /= p.sum(axis=1, keepdims=True)
@@ -198,12 +210,12 @@ def _gemm(m: OracleModel, a: np.ndarray, w: np.ndarray) -> np.ndarray:
 def layer_qkv(m: OracleModel, l: int, x: np.ndarray, positions: np.ndarray):
     """RMSNorm -> q, k, v projections -> RoPE on q and k; all stored-rounded."""
     n = x.shape[0]
-    h = store(m, rmsnorm(x, m.attn_norm[l], m.eps))
+    h = store(m, rmsnorm(x, m.attn_norm[l], m.eps, m.ew_dtype))
     q = _gemm(m, h, m.wq[l]).reshape(n, m.hq, m.dh)
     k = _gemm(m, h, m.wk[l]).reshape(n, m.hkv, m.dh)
     v = _gemm(m, h, m.wv[l]).reshape(n, m.hkv, m.dh)
-    q = store(m, rope(q, positions, m.theta))
-    k = store(m, rope(k, positions, m.theta))
+    q = store(m, rope(q, positions, m.theta, m.ew_dtype))
+    k = store(m, rope(k, positions, m.theta, m.ew_dtype))
     v = store(m, v)
     return q, k, v
 
@@ -213,7 +225,7 @@ def layer_out(m: OracleModel, l: int, x: np.ndarray, a: np.ndarray) -> np.ndarra
     n = x.shape[0]
     a = store(m, a).reshape(n, m.hq * m.dh)
     y = _gemm(m, a, m.wo[l])
-    return store(m, np.asarray(x, np.float64) + np.asarray(y, np.float64))
+    return store(m, np.asarray(x, m.ew_dtype) + np.asarray(y, m.ew_dtype))
 
 
 def final_hidden(m: OracleModel, tokens: Sequence[int]) -> np.ndarray:
@@ -227,7 +239,7 @@ def final_hidden(m: OracleModel, tokens: Sequence[int]) -> np.ndarray:
         q, k, v = layer_qkv(m, l, x, pos)
         a = attention(m, q, k, v, pos, pos)
         x = layer_out(m, l, x, a)
-    return store(m, rmsnorm(x[-1:], m.final_norm, m.eps))[0]
+    return store(m, rmsnorm(x[-1:], m.final_norm, m.eps, m.ew_dtype))[0]
 
 
 def full_logprobs(m: OracleModel, hidden: np.ndarray) -> np.ndarray:
@@ -295,4 +307,4 @@ def final_hidden_with_cache(m: OracleModel, cache, prefix_len: int,
         kc, vc = cache[l]
         a = attention(m, q, np.concatenate([kc, k]), np.concatenate([vc, v]), pos, kpos)
         x = layer_out(m, l, x, a)
-    return store(m, rmsnorm(x[-1:], m.final_norm, m.eps))[0]
+    return store(m, rmsnorm(x[-1:], m.final_norm, m.eps, m.ew_dtype))[0]

@@ -9,14 +9,15 @@ float32 accumulation; the output files ``probs_w<index>.json`` hold the
 probabilities with a fingerprint of the inputs so that a change of the
 generator is caught instead of silently comparing against stale values.
 
-Spread.  The same branches are recomputed with each alternative accumulation
-of ``oracle.model`` (float64 products and sums; float32 with the contraction
-index reversed; float32 over two halves of the contraction).  Every one is a
-faithful implementation of the same definition, so how far they move a
-branch's probabilities is the floor below which no implementation with
-another summation order can be held: a bf16 rounding that one order lands on
-one side of, another lands on the other, and random-weight bf16 models carry
-such flips through their blocks.  ``spread`` is, per branch, the largest
+Spread.  The same branches are recomputed with alternative arithmetic of
+``oracle.model``: float64 products and sums; float32 with the contraction
+index reversed; float32 over two halves of the contraction; float32 for the
+steps between contractions (RMSNorm, RoPE, softmax, residual add) as well.
+Every one is a faithful implementation of the same definition, so how far
+they move a branch's probabilities is the floor below which no
+implementation with another rounding order can be held: a bf16 rounding that
+one order lands on one side of, another lands on the other, and random-weight
+bf16 models carry such flips through their blocks.  ``spread`` is, per branch, the largest
 absolute change over the alternatives; the parity tests hold branch b to
 max(1e-3, 3 * spread[b]).  Orders already stored are kept when the
 fingerprint matches, so alternatives can be added one run at a time.
@@ -39,7 +40,10 @@ from oracle import model as om
 from synth import make_instance, make_weights, workload
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-ALT_ORDERS = ("fp64", "fp32_krev", "fp32_khalves")
+# alternative -> (accumulation of the contractions, precision between them)
+ALTERNATIVES = {"fp64": ("fp64", "fp64"), "fp32_krev": ("fp32_krev", "fp64"),
+                "fp32_khalves": ("fp32_khalves", "fp64"), "ew32": ("fp32", "fp32")}
+ALT_ORDERS = tuple(ALTERNATIVES)
 BAR_FLOOR = 1e-3
 BAR_FACTOR = 3.0
 
@@ -112,7 +116,8 @@ def main(indices, orders):
         for order in orders:
             if all(order in ps["by_order"] for ps in out["passes"]):
                 continue
-            m_alt = om.from_weights(w, gemm=order)
+            gemm, ew = ALTERNATIVES[order]
+            m_alt = om.from_weights(w, gemm=gemm, elementwise=ew)
             for p, ps in enumerate(out["passes"]):
                 if order not in ps["by_order"]:
                     ps["by_order"][order] = _score(m_alt, inst.full_sequences(p), ps["branches"],

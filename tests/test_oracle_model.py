@@ -352,3 +352,31 @@ def test_attention_threaded_heads_match_single_head_calls():
         single = om.attention(m, q[:, j:j + 1], k[:, j // 2:j // 2 + 1], v[:, j // 2:j // 2 + 1],
                               np.arange(n), np.arange(n))
         assert np.array_equal(out[:, j], single[:, 0])
+
+
+def test_float32_elementwise_steps_within_their_precision():
+    """The float32 variants of RMSNorm, RoPE and the attention softmax (used
+    only to measure the spread of faithful implementations) agree with the
+    float64 closed forms to float32 precision, and really are float32."""
+    rng = np.random.default_rng(16)
+    x = rng.standard_normal((6, 64))
+    g = rng.standard_normal(64)
+    y32 = om.rmsnorm(x.astype(np.float32), g, 1e-6, np.float32)
+    assert y32.dtype == np.float32
+    y64 = om.rmsnorm(x.astype(np.float32), g, 1e-6)
+    assert np.max(np.abs(y32 - y64) / np.maximum(np.abs(y64), 1e-3)) < 1e-5
+    assert np.max(np.abs(y32 - y64)) > 0
+    q = rng.standard_normal((5, 2, 16)).astype(np.float32)
+    r32 = om.rope(q, np.array([0, 3, 100, 4000, 32000]), 1e4, np.float32)
+    r64 = om.rope(q, np.array([0, 3, 100, 4000, 32000]), 1e4)
+    assert r32.dtype == np.float32 and np.max(np.abs(r32 - r64)) < 1e-5
+    w = make_weights(tiny_workload(index=108, dtype="bf16", d=16, hq=4, hkv=2, dh=8, vocab=23))
+    m32 = om.from_weights(w, elementwise="fp32")
+    m64 = om.from_weights(w, mode="f64")
+    assert m32.ew_dtype == np.float32
+    k = rng.standard_normal((9, 2, 8))
+    v = rng.standard_normal((9, 2, 8))
+    qq = rng.standard_normal((9, 4, 8))
+    a32 = om.attention(m32, qq, k, v, np.arange(9), np.arange(9))
+    a64 = om.attention(m64, qq, k, v, np.arange(9), np.arange(9))
+    assert np.max(np.abs(a32 - a64)) < 1e-5 and np.max(np.abs(a32 - a64)) > 0
