@@ -277,12 +277,13 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM
   constexpr int LA = BM / RPL;         // A chunks per thread per stage
   constexpr int LB = (BN + RPL - 1) / RPL;  // B chunks per thread per stage (the last may idle)
   constexpr int NST = LA + LB;         // LDS stores per thread per stage
+  constexpr bool B_FULL = BN % RPL == 0;  // every thread's B rows are inside the tile (lrow < RPL)
   constexpr int RS = 9;                // LDS row stride, 16-byte units
   constexpr int STAGE = (BM + BN) * RS;
   constexpr int LDS_MAIN = 2 * STAGE;
   constexpr int LDS_EPI = 128 * (BN + 4) / 4;
   constexpr int LDS_UNITS = LDS_MAIN > LDS_EPI ? LDS_MAIN : LDS_EPI;
-  static_assert(BM % (WM * 32) == 0 && BN % (WN * 32) == 0 && BM % RPL == 0, "tile");
+  static_assert(BM % (WM * 32) == 0 && BN % (WN * 32) == 0 && BM % RPL == 0 && KS % 2 == 0, "tile");
   __shared__ __attribute__((aligned(16))) u32x4 smem[LDS_UNITS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -331,7 +332,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM
     u32x4* sA_ = smem + (BUF) * STAGE;                                                      \
     u32x4* sB_ = sA_ + BM * RS;                                                             \
     _Pragma("unroll") for (int i = 0; i < LA; ++i) sA_[(lrow + RPL * i) * RS + lch] = RA[i]; \
-    _Pragma("unroll") for (int i = 0; i < LB; ++i) if (lrow + RPL * i < BN) sB_[(lrow + RPL * i) * RS + lch] = RB[i]; \
+    _Pragma("unroll") for (int i = 0; i < LB; ++i) if (B_FULL || lrow + RPL * i < BN) sB_[(lrow + RPL * i) * RS + lch] = RB[i]; \
   } while (0)
   // One stage of compute on LDS buffer BUF, with the next stage's staged
   // registers (RA, RB) written into the other buffer during it (W_ = 1).
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM
   do {                                                                                           \
     _Pragma("unroll") for (int q = (S_) * NST / KS; q < ((S_) + 1) * NST / KS; ++q) {            \
       if (q < LA) wA_[(lrow + RPL * q) * RS + lch] = RA[q < LA ? q : 0];                         \
-      else if (lrow + RPL * (q - LA) < BN) wB_[(lrow + RPL * (q - LA)) * RS + lch] = RB[q < LA ? 0 : q - LA]; \
+      else if (B_FULL || lrow + RPL * (q - LA) < BN) wB_[(lrow + RPL * (q - LA)) * RS + lch] = RB[q < LA ? 0 : q - LA]; \
     }                                                                                            \
   } while (0)
 #define G_GROUPS(NR_, NW_)                                                                       \
@@ -394,26 +395,87 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM
     }                                                                                            \
   } while (0)
 
+  // Split K: the stage barrier sits before the MFMAs of the stage's last
+  // k-step; after it each wave reads the first fragments of the next stage
+  // while those MFMAs run, so the MFMA pipe does not drain at every stage
+  // boundary (with ~10 stages per slice, a drained pipe per stage cost about
+  // a third of the loop).  All LDS writes of the next stage and all reads of
+  // this stage are issued before the barrier.
+#define G_PHASE_SPLIT(BUF, RA, RB)                                                               \
+  do {                                                                                           \
+    const u32x4* sA_ = smem + (BUF) * STAGE;                                                     \
+    const u32x4* sB_ = sA_ + BM * RS;                                                            \
+    u32x4* wA_ = smem + ((BUF) ^ 1) * STAGE;                                                     \
+    u32x4* wB_ = wA_ + BM * RS;                                                                  \
+    _Pragma("unroll") for (int s = 0; s < KS; s += 2) {                                          \
+      G_FRAGS(fa1, fb1, s + 1);                                                                  \
+      G_MMA(fa0, fb0);                                                                           \
+      G_WRITES(RA, RB, s);                                                                       \
+      G_GROUPS(NRB + TN, (s + 1) * NST / KS - s * NST / KS);                                     \
+      __builtin_amdgcn_sched_barrier(0);                                                         \
+      if (s + 2 < KS) {                                                                          \
+        G_FRAGS(fa0, fb0, s + 2);                                                                \
+        G_MMA(fa1, fb1);                                                                         \
+        G_WRITES(RA, RB, s + 1);                                                                 \
+        G_GROUPS(NRB + TN, (s + 2) * NST / KS - (s + 1) * NST / KS);                             \
+        __builtin_amdgcn_sched_barrier(0);                                                       \
+      } else {                                                                                   \
+        G_WRITES(RA, RB, s + 1);                                                                 \
+        __syncthreads();                                                                         \
+        {                                                                                        \
+          const u32x4* sA_ = smem + ((BUF) ^ 1) * STAGE;                                         \
+          const u32x4* sB_ = sA_ + BM * RS;                                                      \
+          G_FRAGS(fa0, fb0, 0);                                                                  \
+        }                                                                                        \
+        G_MMA(fa1, fb1);                                                                         \
+        G_GROUPS(NRB + TN, 0);                                                                   \
+        __builtin_amdgcn_sched_barrier(0);                                                       \
+      }                                                                                          \
+    }                                                                                            \
+  } while (0)
+
   G_LOAD(ra0, rb0, 0);
   G_LOAD(ra1, rb1, 1);
   G_STORE(ra0, rb0, 0);
   __syncthreads();
-  int kt = 0;
-  // two stages per trip keep the register sets static
-  for (; kt + 1 < KT; kt += 2) {
-    G_LOAD(ra0, rb0, kt + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    G_PHASE(0, ra1, rb1, 1);
-    __syncthreads();
-    G_LOAD(ra1, rb1, kt + 3);
-    __builtin_amdgcn_sched_barrier(0);
-    G_PHASE(1, ra0, rb0, 1);
-    __syncthreads();
+  if constexpr (SPLIT) {
+    frag fa0[NRB], fb0[TN], fa1[NRB], fb1[TN];
+    {
+      const u32x4* sA_ = smem;
+      const u32x4* sB_ = sA_ + BM * RS;
+      G_FRAGS(fa0, fb0, 0);
+    }
+    // the last stage's writes store a clamped copy of it into a buffer that
+    // no stage reads, and its post-barrier reads fetch unused values
+    int kt = 0;
+    for (; kt + 1 < KT; kt += 2) {
+      G_LOAD(ra0, rb0, kt + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      G_PHASE_SPLIT(0, ra1, rb1);
+      G_LOAD(ra1, rb1, kt + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      G_PHASE_SPLIT(1, ra0, rb0);
+    }
+    if (kt < KT) G_PHASE_SPLIT(0, ra1, rb1);
+  } else {
+    int kt = 0;
+    // two stages per trip keep the register sets static
+    for (; kt + 1 < KT; kt += 2) {
+      G_LOAD(ra0, rb0, kt + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      G_PHASE(0, ra1, rb1, 1);
+      __syncthreads();
+      G_LOAD(ra1, rb1, kt + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      G_PHASE(1, ra0, rb0, 1);
+      __syncthreads();
+    }
+    if (kt < KT) G_PHASE(0, ra1, rb1, 0);
   }
-  if (kt < KT) G_PHASE(0, ra1, rb1, 0);
 #undef G_LOAD
 #undef G_STORE
 #undef G_PHASE
+#undef G_PHASE_SPLIT
 #undef G_FRAGS
 #undef G_MMA
 #undef G_WRITES
