@@ -207,6 +207,75 @@ def summarize(d: str) -> int:
     return 0
 
 
+# Kernel instances that make up one launch of each timed kind on the headline
+# workload (the split-K GEMMs of the branch round include their epilogue).
+TRAFFIC_LAUNCHES = {
+    "qkv[2000 rows]": ["gemm_pc_kernel<160, 0>"],
+    "oproj[2000 rows]": ["gemm_pc_kernel<128, 1>"],
+    "attn[2000 rows]": ["attn_kernel<bf16s, 128, 2>"],
+    "attn[240 rows]": ["attn_kernel<bf16s, 128, 1>"],
+    "merge[240 rows]": ["merge_kernel<bf16s, 128>"],
+    "qkv[240 rows]": ["gemm_kernel<bf16s, 128, 0, true, 4, 2>", "split_epilogue<bf16s, 0>"],
+    "oproj[240 rows]": ["gemm_kernel<bf16s, 128, 1, true, 4, 2>", "split_res_norm_kernel<bf16s>"],
+}
+
+
+def write_traffic(fetch_dir: str, write_dir: str, copy_mib: int = 1024) -> int:
+    """profiles/traffic.json from a FETCH_SIZE and a WRITE_SIZE rocprofv3 run of
+    `bench.py --copy-calibration MIB`: mean KiB per dispatch of every kernel in
+    TRAFFIC_LAUNCHES, and the copy kernel's reading for the calibration."""
+    import csv
+    import glob
+
+    def short(name: str) -> str:
+        return name.split("(")[0].replace("void ", "").replace("jev::dev::", "")
+
+    def means(d: str, counter: str):
+        agg = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if r["Counter_Name"] != counter:
+                        continue
+                    k = (short(r["Kernel_Name"]), int(r.get("Grid_Size", 0) or 0))
+                    a = agg.setdefault(k, [0, 0.0])
+                    a[0] += 1
+                    a[1] += float(r["Counter_Value"])
+        return {k: v / n for k, (n, v) in agg.items()}
+
+    fetch, write = means(fetch_dir, "FETCH_SIZE"), means(write_dir, "WRITE_SIZE")
+    nbytes = copy_mib << 20
+    copy_grid = nbytes // 8192  # the runtime's copy kernel: 8 KiB per workgroup of the 1 GiB copy
+
+    def per_kernel(m, name):
+        vals = [v for (kn, g), v in m.items() if kn == name]
+        if len(vals) != 1:
+            raise SystemExit(f"{name}: {len(vals)} instances in the counter run")
+        return vals[0]
+
+    copy_f = [v for (kn, g), v in fetch.items() if kn == "__amd_rocclr_copyBuffer" and g == copy_grid]
+    copy_w = [v for (kn, g), v in write.items() if kn == "__amd_rocclr_copyBuffer" and g == copy_grid]
+    if not copy_f or not copy_w:
+        raise SystemExit("no calibration copy in the counter runs (bench.py --copy-calibration)")
+    sha = kernel_sources_sha()
+    out = {"about": "HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of bench.py on the "
+                    "headline workload (bench.py --write-traffic); a split-K launch counts the GEMM and its "
+                    "epilogue kernel",
+           "copy": {"bytes_read": nbytes, "bytes_written": nbytes, "fetch_kib": round(copy_f[0], 1),
+                    "write_kib": round(copy_w[0], 1)},
+           "kernels": {}}
+    for key, names in TRAFFIC_LAUNCHES.items():
+        out["kernels"][key] = {"fetch_kib": round(sum(per_kernel(fetch, n) for n in names), 1),
+                               "write_kib": round(sum(per_kernel(write, n) for n in names), 1),
+                               "kernel_sources_sha256": sha}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+    return 0
+
+
 def config_summary(idx: int, steps: int, warmup: int) -> dict:
     """Throughput of another workload, inputs resident in HBM before the timed
     region; the same one-GPU path as the headline line.
@@ -370,9 +439,13 @@ def main(argv=None) -> int:
                     help="after the run, copy a MIB-MiB buffer 3 times (counter calibration for traffic)")
     ap.add_argument("--summarize", metavar="DIR", default=None,
                     help="print a summary of the rocprofv3 CSV output under DIR and exit")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="write profiles/traffic.json from a FETCH_SIZE and a WRITE_SIZE rocprofv3 run and exit")
     args = ap.parse_args(argv)
     if args.summarize:
         return summarize(args.summarize)
+    if args.write_traffic:
+        return write_traffic(*args.write_traffic)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU sharding of this path is "
               f"a design note, not built", file=sys.stderr)

@@ -571,6 +571,34 @@ def test_w2_repeated_calls_are_bitwise_identical(w2):
         assert np.array_equal(r, runs[0])
 
 
+def test_w2_round_size_moves_a_branch_within_its_bar(w2):
+    """Round-composition variance, measured: the same five branches scored in
+    a round of their own (240 rows: split-K projections, 7 prefix chunks) and
+    with a sixth, 32-token branch that takes the round past 256 rows (full-K
+    projections, 6 prefix chunks).  Each of the five accumulates in another
+    order in the two rounds, so the two results are held to each other like
+    two faithful orders of the oracle (and each to the oracle)."""
+    wl, inst, g, ctx, _ = w2
+    br = inst.passes[0]
+    bars = stored_bars(g)
+    (h,) = ctx.prefill_prefix([0], [inst.prefixes[0]])
+    probs, loff = ctx.score_branches([h] * 5, [b.tokens for b in br], [b.labels for b in br])
+    _sync()
+    alone = split_probs(probs, loff)
+    extra = list(br[0].tokens[:32])
+    probs2, loff2 = ctx.score_branches([h] * 6, [b.tokens for b in br] + [extra],
+                                       [b.labels for b in br] + [br[0].labels])
+    _sync()
+    st = ctx.stats()
+    ctx.free_pages([h])
+    assert st["computed_tokens"] == 5 * 48 + 32
+    with_extra = split_probs(probs2, loff2)[:5]
+    check_branches("w2 same branches, 240-row vs 272-row round", with_extra, alone, bars)
+    check_branches("w2 272-row round vs oracle", with_extra, g["passes"][0]["probs"], bars)
+    # the rounds really took different paths: not bitwise equal
+    assert any(not np.array_equal(np.asarray(a), np.asarray(b)) for a, b in zip(with_extra, alone))
+
+
 def test_w3_staged_rounds_match_oracle(w2):
     """Workload 3 uses the same model shapes as workload 2 (weights of its own
     seed), submitted as full candidate sequences in staged rounds."""
