@@ -144,6 +144,37 @@ def measured_traffic(key: str):
     return round(rd + wr)
 
 
+def library_gemms() -> dict:
+    """Context for the GEMM rooflines: torch.matmul (the ROCm BLAS library) on
+    the projection shapes of the headline workload, bf16 operands drawn like
+    the weights (N(0, 0.02)) and the activations (N(0, 1)), median over 50
+    calls.  Not part of the scoring path."""
+    import numpy as np
+    import torch
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    res = {}
+    for M, N, K, name in ((2000, 5120, 4096, "qkv[2000 rows]"), (2000, 4096, 4096, "oproj[2000 rows]"),
+                          (240, 5120, 4096, "qkv[240 rows]"), (240, 4096, 4096, "oproj[240 rows]")):
+        a = torch.randn(M, K, device="cuda:0", generator=g).to(torch.bfloat16)
+        w = (torch.randn(N, K, device="cuda:0", generator=g) * 0.02).to(torch.bfloat16)
+        wt = w.t()
+        for _ in range(5):
+            torch.matmul(a, wt)
+        ts = []
+        for _ in range(50):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            torch.matmul(a, wt)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        us = float(np.median(ts))
+        res[name] = {"us": round(us, 2), "tflop_s": round(2.0 * M * N * K / us / 1e6, 1),
+                     "note": "plain GEMM, no RoPE / page-write / residual epilogue"}
+    return res
+
+
 def copy_calibration(mib: int) -> None:
     """A plain device-to-device copy of known size, for the HBM byte counters."""
     import torch
@@ -439,6 +470,8 @@ def main(argv=None) -> int:
                     help="after the run, copy a MIB-MiB buffer 3 times (counter calibration for traffic)")
     ap.add_argument("--summarize", metavar="DIR", default=None,
                     help="print a summary of the rocprofv3 CSV output under DIR and exit")
+    ap.add_argument("--library-gemms", action="store_true",
+                    help="add torch.matmul times of the projection shapes ('library_gemm', context only)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
                     help="write profiles/traffic.json from a FETCH_SIZE and a WRITE_SIZE rocprofv3 run and exit")
     args = ap.parse_args(argv)
@@ -593,6 +626,8 @@ def main(argv=None) -> int:
         cfgs[workload(c).name] = config_summary(c, args.config_steps, 2)
     if cfgs:
         out["configs"] = cfgs
+    if args.library_gemms:
+        out["library_gemm"] = library_gemms()
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration)
     print(json.dumps(out))
