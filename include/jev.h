@@ -259,9 +259,57 @@ typedef struct {
   int32_t cached_prefixes;    /* resident prefixes without caller references (cache policy) */
   int32_t cached_pages;       /* pages they hold (counted in pages_in_use) */
   int64_t evictions;          /* cached prefixes evicted so far */
+  /* Timing of the last call that ran device work, split like the pages' server
+   * timing (openjev-sglang article, response-header section: preparation,
+   * shared prefill, branch inference; openjev-multimodal performance page,
+   * server-side timing section). */
+  int32_t last_call_kind;     /* JEV_CALL_* (JEV_CALL_NONE before the first such call) */
+  uint32_t debug_flags;       /* jev_set_debug flags in force */
+  int64_t last_prepare_ns;    /* host: call entry to its first enqueue (checks, matching, plan, descriptors) */
+  int64_t last_enqueue_ns;    /* host: queueing its copies and kernels */
+  double last_prefill_ms;     /* device: its rounds without read-outs (shared prefixes); with
+                                 JEV_DEBUG_TIME_CALLS, else -1 */
+  double last_branch_ms;      /* device: its rounds with read-outs (branch inference); with
+                                 JEV_DEBUG_TIME_CALLS, else -1 */
 } jev_stats_t;
 
+enum { JEV_CALL_NONE = 0, JEV_CALL_PREFILL = 1, JEV_CALL_BRANCHES = 2, JEV_CALL_CANDIDATES = 3, JEV_CALL_SCHED_STEP = 4 };
+
+/* Host-only statistics.  With JEV_DEBUG_TIME_CALLS the device times need the
+ * last call's device work: jev_stats then waits for it.  Errors: JEV_EINVAL. */
 int jev_stats(jev_ctx* ctx, jev_stats_t* out);
+
+/* Debug modes (bit flags; 0 turns everything off):
+ *  - JEV_DEBUG_POISON_FREED_PAGES: every KV page that a call (or
+ *    jev_free_pages) leaves free after the call wrote or released it is filled
+ *    with the byte 0x7F in every layer, on the call's stream after its kernels
+ *    (jev_free_pages: the stream of the last call).  0x7F7F is a finite bf16
+ *    (and 0x7F7F7F7F a finite fp32) near the type's maximum: masked key slots
+ *    of a partly filled page still contribute exactly 0, while a kernel that
+ *    reads a freed page as valid keys produces non-finite scores, so
+ *    stale-page bugs show up as wrong (NaN) probabilities in any parity test.
+ *    Costs one fill launch per call; results are unchanged.
+ *  - JEV_DEBUG_TIME_CALLS: the device time of each call's rounds is recorded
+ *    with events (two fence-free event records per round) for jev_stats.
+ * Errors: JEV_EINVAL (unknown bit, NULL ctx). */
+enum { JEV_DEBUG_POISON_FREED_PAGES = 1, JEV_DEBUG_TIME_CALLS = 2 };
+int jev_set_debug(jev_ctx* ctx, uint32_t flags);
+
+/* Limits of a context (host-only; also on a planning-only context). */
+typedef struct {
+  int32_t page_tokens;          /* JEV_PAGE_TOKENS */
+  int32_t min_labels;           /* JEV_MIN_LABELS */
+  int32_t max_labels;           /* JEV_MAX_LABELS */
+  int32_t max_positions;        /* longest sequence (prefix + suffix), from the model description */
+  int32_t max_round_tokens;     /* most tokens computed in one round */
+  int32_t n_pages;              /* KV pages of the pool */
+  int32_t split_k_rows;         /* rounds of at most this many rows split the projections' K */
+  int32_t max_tile_pages;       /* longest key list of one attention tile */
+  int64_t noalloc_scratch_bytes;     /* static scratch of jev_score_branches_noalloc (per device) */
+  int64_t noalloc_partial_rows;      /* attention partial-state rows it holds for this model (0: dry context) */
+  int64_t workspace_partial_rows;    /* those the workspace holds */
+} jev_limits_t;
+int jev_limits(jev_ctx* ctx, jev_limits_t* out);
 
 /* Debug taps for parity tests.  Each call registers one tap (up to 16); a
  * NULL dst removes every tap.  what = JEV_TAP_ATTN: the attention output of

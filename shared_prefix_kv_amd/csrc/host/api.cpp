@@ -205,6 +205,14 @@ struct jev_ctx {
   std::vector<Prof> prof;
   std::vector<hipEvent_t> prof_free;  // events kept for re-use
   std::vector<jev_sched*> scheds;     // schedulers on this context (detached when it is destroyed)
+  // debug modes and call timing (jev_set_debug, jev_stats)
+  uint32_t debug = 0;
+  int32_t call_kind = JEV_CALL_NONE;       // kind of the call in progress
+  std::chrono::steady_clock::time_point call_t0{};
+  std::vector<int32_t> call_written;       // KV pages the last run_rounds wrote
+  std::vector<hipEvent_t> round_ev;        // round boundaries of the last timed call
+  std::vector<char> round_reads;           // per round of it: has read-outs
+  int32_t n_round_ev = 0;                  // events recorded by the last call (0: not timed)
 };
 
 namespace {
@@ -221,6 +229,47 @@ namespace {
 int check_alive(jev_ctx* ctx) {
   if (!ctx) return fail(JEV_EINVAL, "ctx is NULL");
   if (ctx->dead) return fail(JEV_EHIP, "context is unusable after an earlier HIP failure");
+  return JEV_OK;
+}
+
+// Start of an entry point that may run device work (timing of jev_stats).
+void begin_call(jev_ctx* ctx, int32_t kind) {
+  ctx->call_kind = kind;
+  ctx->call_t0 = std::chrono::steady_clock::now();
+}
+
+int64_t ns_since(std::chrono::steady_clock::time_point t0) {
+  return std::chrono::duration_cast<std::chrono::nanoseconds>(std::chrono::steady_clock::now() - t0).count();
+}
+
+// Free pages before a call, when its freed pages are to be poisoned.
+std::set<int32_t> poison_before(const jev_ctx* ctx) {
+  if (ctx->dry || !(ctx->debug & JEV_DEBUG_POISON_FREED_PAGES)) return {};
+  return ctx->pages.snapshot();
+}
+
+// JEV_DEBUG_POISON_FREED_PAGES: after a call's kernels, on its stream, fills
+// every page that is free now and that the call wrote (call_written) or freed
+// (free now, not free before).  Runs of consecutive ids are filled by one
+// launch each.
+int poison_after(jev_ctx* ctx, const std::set<int32_t>& before, const std::vector<int32_t>& written,
+                 hipStream_t s) {
+  if (ctx->dry || !(ctx->debug & JEV_DEBUG_POISON_FREED_PAGES)) return JEV_OK;
+  const std::set<int32_t> now = ctx->pages.snapshot();
+  std::set<int32_t> pages;
+  for (int32_t p : now)
+    if (!before.count(p)) pages.insert(p);
+  for (int32_t p : written)
+    if (now.count(p)) pages.insert(p);
+  for (auto it = pages.begin(); it != pages.end();) {
+    const int32_t first = *it;
+    int32_t count = 0;
+    while (it != pages.end() && *it == first + count) {
+      ++count;
+      ++it;
+    }
+    HIPCHK(jev::launch_poison_pages(ctx->dims, ctx->pool, first, count, s));
+  }
   return JEV_OK;
 }
 
@@ -268,13 +317,20 @@ int device_scratch(char** out) {
 // The static scratch laid out for a call: the split-K partial tiles first
 // (sized like the workspace's), then as many attention partial-state rows as
 // fit; JEV_ENOMEM if the call's rounds need more rows.
+// Attention partial-state rows the static scratch holds after the split-K
+// tiles (0 if those alone do not fit).
+int64_t noalloc_rows(const jev_ctx* ctx) {
+  const size_t gemm_bytes = align256(ctx->L.gemm_part_elems * sizeof(float));
+  const size_t row_bytes = size_t(ctx->desc.head_dim + 1) * sizeof(float);
+  if (gemm_bytes + 512 + row_bytes > kNoAllocScratchBytes) return 0;
+  return int64_t((kNoAllocScratchBytes - gemm_bytes - 512) / row_bytes);
+}
+
 int static_scratch_for(const jev_ctx* ctx, const std::vector<RoundDesc>& rds, Scratch* out) {
   if (!ctx->static_scratch) return fail(JEV_ESTATE, "no static scratch on this context");
   const size_t gemm_bytes = align256(ctx->L.gemm_part_elems * sizeof(float));
-  const size_t row_bytes = size_t(ctx->desc.head_dim + 1) * sizeof(float);
-  if (gemm_bytes + 512 + row_bytes > kNoAllocScratchBytes)
-    return fail(JEV_ENOMEM, "model too large for the 96 MiB static scratch");
-  const int64_t rows = int64_t((kNoAllocScratchBytes - gemm_bytes - 512) / row_bytes);
+  const int64_t rows = noalloc_rows(ctx);
+  if (rows == 0) return fail(JEV_ENOMEM, "model too large for the 96 MiB static scratch");
   int64_t need = 0;
   for (const RoundDesc& rd : rds) need = std::max<int64_t>(need, rd.part_slots * ctx->desc.n_kv_heads * kRowsPerTile);
   if (need > rows)
@@ -609,8 +665,22 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
   for (const RoundDesc& rd : rds)
     if (rd.part_slots * ctx->desc.n_kv_heads * kRowsPerTile > sc.part_rows)
       return fail(JEV_ENOMEM, "round needs more partial-state rows than the scratch holds");
+  const int64_t prepare_ns = ns_since(ctx->call_t0);
+  const auto enqueue_t0 = std::chrono::steady_clock::now();
+  // (the allocation-free entry point times a call only with events made earlier)
+  const bool timed_call = (ctx->debug & JEV_DEBUG_TIME_CALLS) != 0 &&
+                          !(sc.no_alloc && ctx->round_ev.size() < rds.size() + 1);
+  if (timed_call)
+    while (ctx->round_ev.size() < rds.size() + 1) {
+      hipEvent_t e = nullptr;
+      // read after the device work is done: no system-scope fence needed
+      HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
+      ctx->round_ev.push_back(e);
+    }
+  ctx->n_round_ev = 0;
   if (ctx->have_last && s != ctx->last_stream) HIPCHK(hipStreamWaitEvent(s, ctx->last_done, 0));
   if (ctx->have_last) HIPCHK(hipEventSynchronize(ctx->desc_copied));
+  if (timed_call) HIPCHK(hipEventRecord(ctx->round_ev[0], s));
   std::memcpy(ctx->desc_host, hb.data(), hb.size() * sizeof(int32_t));
   int32_t* dd = reinterpret_cast<int32_t*>(ctx->ws + ctx->L.desc);
   HIPCHK(hipMemcpyAsync(dd, ctx->desc_host, hb.size() * sizeof(int32_t), hipMemcpyHostToDevice, s));
@@ -665,7 +735,11 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
     return JEV_OK;
   };
   const double D = m.d, HD = double(m.hq) * m.dh, NQKV = double(m.hq + 2 * m.hkv) * m.dh, E = double(elt);
+  ctx->call_written.clear();
+  ctx->round_reads.clear();
   for (const RoundDesc& rd : rds) {
+    for (int64_t t = 0; t < rd.T; ++t) ctx->call_written.push_back(hb[size_t(rd.off_slot + t)] >> 4);
+    ctx->round_reads.push_back(rd.n_read > 0);
     const int32_t* tok = dd + rd.off_tok;
     const double T = rd.T;
     // the embedding gather also writes layer 0's normalised input
@@ -716,10 +790,15 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
                                    reinterpret_cast<const jev::ReadoutItem*>(dd + rd.off_read), rd.n_read,
                                    dd + rd.off_labels, probs, s);
       }));
+    if (timed_call) HIPCHK(hipEventRecord(ctx->round_ev[&rd - rds.data() + 1], s));
   }
+  if (timed_call) ctx->n_round_ev = int32_t(rds.size()) + 1;
   HIPCHK(hipEventRecord(ctx->last_done, s));
   ctx->have_last = true;
   ctx->last_stream = s;
+  ctx->stats.last_call_kind = ctx->call_kind;
+  ctx->stats.last_prepare_ns = prepare_ns;
+  ctx->stats.last_enqueue_ns = ns_since(enqueue_t0);
   return JEV_OK;
 }
 
@@ -849,6 +928,7 @@ int jev_destroy(jev_ctx* ctx) {
       (void)hipEventDestroy(p.e1);
     }
     for (hipEvent_t e : ctx->prof_free) (void)hipEventDestroy(e);
+    for (hipEvent_t e : ctx->round_ev) (void)hipEventDestroy(e);
   }
   delete ctx;
   return rc;
@@ -860,6 +940,8 @@ int jev_prefill_prefix(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const
   if (int rc = check_segments(ctx, n, tokens, offsets, "prefill")) return rc;
   if (n == 0) return JEV_OK;
   if (!parents || !out_handles) return fail(JEV_EINVAL, "NULL parents/out_handles");
+  begin_call(ctx, JEV_CALL_PREFILL);
+  const std::set<int32_t> free_before = poison_before(ctx);
   std::vector<jev::ResidentTree::PrefillItem> items;
   for (int32_t i = 0; i < n; ++i) {
     if (!ctx->tree->has(parents[i])) return fail(JEV_EHANDLE, "unknown parent handle " + std::to_string(parents[i]));
@@ -936,11 +1018,12 @@ int jev_prefill_prefix(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const
   ctx->stats.cached_tokens = 0;
   ctx->stats.rounds = rn.empty() ? 0 : 1;
   ctx->stats.calls += 1;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
   if (!rn.empty() && !ctx->dry) {
-    if (int rc = run_rounds(ctx, rds, hb, nullptr, reinterpret_cast<hipStream_t>(hip_stream), ws_scratch(ctx)))
-      return rc;
+    if (int rc = run_rounds(ctx, rds, hb, nullptr, st, ws_scratch(ctx))) return rc;
+    return poison_after(ctx, free_before, ctx->call_written, st);
   }
-  return JEV_OK;
+  return poison_after(ctx, free_before, {}, st);  // evictions only
 }
 
 namespace {
@@ -957,6 +1040,8 @@ int score_branches(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const int
   if (int rc = check_labels(ctx, n, label_ids, label_offsets)) return rc;
   if (ctx->dry) return fail(JEV_ESTATE, "scoring needs a device context");
   if (!probs) return fail(JEV_EINVAL, "NULL probs");
+  begin_call(ctx, JEV_CALL_BRANCHES);
+  const std::set<int32_t> free_before = poison_before(ctx);
   int64_t need = 0, logical = 0;
   for (int32_t i = 0; i < n; ++i) {
     if (!ctx->tree->has(parents[i])) return fail(JEV_EHANDLE, "unknown parent handle " + std::to_string(parents[i]));
@@ -1014,7 +1099,9 @@ int score_branches(jev_ctx* ctx, int32_t n, const jev_prefix* parents, const int
   ctx->stats.cached_tokens = logical - computed;
   ctx->stats.rounds = 1;
   ctx->stats.calls += 1;
-  return run_rounds(ctx, rds, hb, probs, reinterpret_cast<hipStream_t>(hip_stream), sc);
+  const hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  if (int rc = run_rounds(ctx, rds, hb, probs, st, sc)) return rc;
+  return poison_after(ctx, free_before, ctx->call_written, st);
 }
 
 }  // namespace
@@ -1086,6 +1173,8 @@ int jev_score_candidates(jev_ctx* ctx, int32_t n, const int32_t* tokens, const i
   for (int32_t i = 0; i < n; ++i)
     if (tok_offsets[i + 1] - tok_offsets[i] > ctx->desc.max_positions)
       return fail(JEV_EINVAL, "candidate " + std::to_string(i) + " runs past max_positions");
+  begin_call(ctx, JEV_CALL_CANDIDATES);
+  const std::set<int32_t> free_before = poison_before(ctx);
   // the tree work (splits, evictions, the plan) on copies; the rounds and
   // their descriptors are built against the copies, which are committed only
   // once every check has passed
@@ -1142,7 +1231,9 @@ int jev_score_candidates(jev_ctx* ctx, int32_t n, const int32_t* tokens, const i
       }
     for (int64_t h : made) ctx->tree->release(h);
   }
-  return run_rounds(ctx, rds, hb, probs, reinterpret_cast<hipStream_t>(hip_stream), ws_scratch(ctx));
+  const hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  if (int rc = run_rounds(ctx, rds, hb, probs, st, ws_scratch(ctx))) return rc;
+  return poison_after(ctx, free_before, ctx->call_written, st);
 }
 
 // ----------------------------------------------------------------- scheduler
@@ -1203,7 +1294,10 @@ int jev_sched_destroy(jev_sched* s) {
   if (ctx) {
     if (!ctx->dry && ctx->have_last && hipEventSynchronize(ctx->last_done) != hipSuccess)
       rc = fail(JEV_EHIP, "sync failed");
+    const std::set<int32_t> free_before = poison_before(ctx);
     for (int64_t h : s->held) ctx->tree->release(h);
+    if (rc == JEV_OK && !ctx->dead)
+      rc = poison_after(ctx, free_before, {}, ctx->have_last ? ctx->last_stream : nullptr);
     if (s->dprobs) (void)hipFree(s->dprobs);
     ctx->scheds.erase(std::remove(ctx->scheds.begin(), ctx->scheds.end(), s), ctx->scheds.end());
   }
@@ -1279,6 +1373,9 @@ int jev_sched_step(jev_sched* s, void* hip_stream, int32_t* plan_out, int64_t pl
   if (!ctx) return fail(JEV_ESTATE, "the scheduler's context was destroyed");
   if (int rc = check_alive(ctx)) return rc;
   if (plan_n) *plan_n = 0;
+  begin_call(ctx, JEV_CALL_SCHED_STEP);
+  const std::set<int32_t> free_before = poison_before(ctx);
+  bool ran = false;
   {
     std::lock_guard<std::mutex> lk(s->mu);
     for (auto& r : s->queued) {
@@ -1392,6 +1489,7 @@ int jev_sched_step(jev_sched* s, void* hip_stream, int32_t* plan_out, int64_t pl
   if (!ctx->dry) {
     const hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
     if (int rc = run_rounds(ctx, rds, hb, s->dprobs, st, ws_scratch(ctx))) return rc;
+    ran = true;
     std::vector<float> hp(size_t(loff.back()));
     HIPCHK(hipMemcpyAsync(hp.data(), s->dprobs, hp.size() * sizeof(float), hipMemcpyDeviceToHost, st));
     HIPCHK(hipStreamSynchronize(st));
@@ -1438,7 +1536,8 @@ int jev_sched_step(jev_sched* s, void* hip_stream, int32_t* plan_out, int64_t pl
       ctx->tree->release(h);
   }
   s->held = std::move(keep);
-  return JEV_OK;
+  return poison_after(ctx, free_before, ran ? ctx->call_written : std::vector<int32_t>{},
+                      reinterpret_cast<hipStream_t>(hip_stream));
 }
 
 int jev_set_plan_mode(jev_ctx* ctx, int32_t mode) {
@@ -1470,12 +1569,15 @@ int jev_free_pages(jev_ctx* ctx, int32_t n, const jev_prefix* handles) {
   }
   for (auto& kv : count)
     if (ctx->tree->node(kv.first).refs < kv.second) return fail(JEV_EHANDLE, "handle released more times than held");
+  const std::set<int32_t> free_before = poison_before(ctx);
   ctx->clock += 1;
   for (int32_t i = 0; i < n; ++i) {
     ctx->tree->touch_path(handles[i], ctx->clock);
     ctx->tree->release(handles[i]);
   }
-  return JEV_OK;
+  // freed pages are poisoned after the work already queued that may read them
+  if (ctx->dead) return JEV_OK;
+  return poison_after(ctx, free_before, {}, ctx->have_last ? ctx->last_stream : nullptr);
 }
 
 int jev_plan(jev_ctx* ctx, int32_t n, const int32_t* tokens, const int64_t* tok_offsets, int32_t* out,
@@ -1527,7 +1629,48 @@ int jev_stats(jev_ctx* ctx, jev_stats_t* out) {
   ctx->stats.cached_prefixes = ctx->tree->cached_count();
   ctx->stats.cached_pages = ctx->tree->cached_pages();
   ctx->stats.evictions = ctx->tree->evictions();
+  ctx->stats.debug_flags = ctx->debug;
+  ctx->stats.last_prefill_ms = -1.0;
+  ctx->stats.last_branch_ms = -1.0;
+  if (ctx->n_round_ev > 1 && !ctx->dead) {
+    HIPCHK(hipEventSynchronize(ctx->round_ev[size_t(ctx->n_round_ev - 1)]));
+    double pre = 0.0, br = 0.0;
+    for (int32_t r = 0; r + 1 < ctx->n_round_ev; ++r) {
+      float ms = 0.f;
+      HIPCHK(hipEventElapsedTime(&ms, ctx->round_ev[size_t(r)], ctx->round_ev[size_t(r) + 1]));
+      (ctx->round_reads[size_t(r)] ? br : pre) += ms;
+    }
+    ctx->stats.last_prefill_ms = pre;
+    ctx->stats.last_branch_ms = br;
+  }
   *out = ctx->stats;
+  return JEV_OK;
+}
+
+int jev_set_debug(jev_ctx* ctx, uint32_t flags) {
+  if (!ctx) return fail(JEV_EINVAL, "ctx is NULL");
+  if (flags & ~uint32_t(JEV_DEBUG_POISON_FREED_PAGES | JEV_DEBUG_TIME_CALLS))
+    return fail(JEV_EINVAL, "unknown debug flag");
+  ctx->debug = flags;
+  if (!(flags & JEV_DEBUG_TIME_CALLS)) ctx->n_round_ev = 0;
+  return JEV_OK;
+}
+
+int jev_limits(jev_ctx* ctx, jev_limits_t* out) {
+  if (!ctx || !out) return fail(JEV_EINVAL, "NULL ctx/out");
+  jev_limits_t l{};
+  l.page_tokens = jev::kPage;
+  l.min_labels = JEV_MIN_LABELS;
+  l.max_labels = JEV_MAX_LABELS;
+  l.max_positions = ctx->desc.max_positions;
+  l.max_round_tokens = ctx->desc.max_round_tokens;
+  l.n_pages = ctx->pages.n_total();
+  l.split_k_rows = jev::kSplitRows;
+  l.max_tile_pages = jev::kMaxTilePages;
+  l.noalloc_scratch_bytes = int64_t(kNoAllocScratchBytes);
+  l.noalloc_partial_rows = ctx->dry ? 0 : noalloc_rows(ctx);
+  l.workspace_partial_rows = ctx->dry ? 0 : ctx->L.part_rows;
+  *out = l;
   return JEV_OK;
 }
 

@@ -18,6 +18,7 @@
 // log-normaliser cancels in the label softmax.
 #include <float.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "common.hpp"
@@ -223,8 +224,6 @@ __device__ __forceinline__ int v_off(int d, int key) {
 // softmax; only the rounding order changes.
 constexpr float RESCALE_SLACK = 8.0f;
 
-// Longest page list of one attention tile (the host checks max_positions).
-constexpr int kMaxTilePages = 4096;
 
 template <typename T, int DH, int GROUPS>
 __global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(const AttnTile* __restrict__ tiles,
@@ -827,6 +826,21 @@ __global__ __launch_bounds__(256) void readout_kernel(const T* __restrict__ U, c
   }
 }
 
+// ------------------------------------------------------------------ page poison
+// Debug fill of a run of `count` KV pages starting at page `first`, in every
+// layer: each 16-byte unit of their K and V blocks gets the bytes 0x7F.
+__global__ __launch_bounds__(256) void poison_pages_kernel(u32x4* __restrict__ pool, size_t layer_units,
+                                                           size_t page_units, int32_t first, int32_t count,
+                                                           int32_t n_layers) {
+  const size_t run = page_units * (size_t)count;
+  const size_t total = run * (size_t)n_layers;
+  const u32x4 v = {0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
+  for (size_t u = (size_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += (size_t)gridDim.x * blockDim.x) {
+    const size_t layer = u / run, within = u % run;
+    pool[layer * layer_units + (size_t)first * page_units + within] = v;
+  }
+}
+
 }  // namespace dev
 
 thread_local LaunchTiming g_launch_timing{nullptr, nullptr};
@@ -915,6 +929,19 @@ hipError_t launch_merge(const ModelDims& m, const MergeItem* items, int32_t n_it
   } else {
     return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_poison_pages(const ModelDims& m, void* pool, int32_t first, int32_t count, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  if (first < 0 || count > m.n_pages - first) return hipErrorInvalidValue;
+  const size_t elt = m.dtype == 1 ? 2 : 4;
+  const size_t page_bytes = (size_t)m.hkv * 2 * 16 * m.dh * elt;  // a multiple of 16 (dh >= 64)
+  const size_t page_units = page_bytes / 16;
+  const size_t total = page_units * (size_t)count * (size_t)m.n_layers;
+  const unsigned blocks = (unsigned)std::min<size_t>((total + 255) / 256, 65536);
+  JEV_LAUNCH(dev::poison_pages_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<dev::u32x4*>(pool),
+             page_units * (size_t)m.n_pages, page_units, first, count, m.n_layers);
   return hipGetLastError();
 }
 

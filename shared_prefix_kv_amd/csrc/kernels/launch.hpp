@@ -51,6 +51,10 @@ struct LayerW {
   const void* wo;
 };
 
+// Longest page list of one attention tile (its page ids are staged in LDS);
+// the host keeps max_positions within it.
+constexpr int kMaxTilePages = 4096;
+
 // Scratch of the projection GEMMs with at most 256 rows: one fp32 [256][N]
 // partial tile per K split (up to kMaxSplits), overwritten by every launch.
 constexpr int kMaxSplits = 8;
@@ -119,6 +123,9 @@ hipError_t launch_merge(const ModelDims& m, const MergeItem* items, int32_t n_it
 // x += o Wo^T (stored)
 hipError_t launch_oproj(const ModelDims& m, const LayerW& w, const void* o, int32_t T, void* x,
                         const GemmWs& ws, hipStream_t s);
+// Debug: fills KV pages [first, first + count) of every layer with the bytes
+// 0x7F (finite, near the dtype's maximum).
+hipError_t launch_poison_pages(const ModelDims& m, void* pool, int32_t first, int32_t count, hipStream_t s);
 hipError_t launch_readout(const ModelDims& m, const void* unembed, const void* final_norm, const void* x,
                           const ReadoutItem* items, int32_t n_items, const int32_t* labels, float* probs,
                           hipStream_t s);

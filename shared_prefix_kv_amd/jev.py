@@ -25,6 +25,8 @@ JEV_ANSWER_NOUL, JEV_ANSWER_CHOICE, JEV_ANSWER_SCORE = 0, 1, 2
 JEV_PLAN_DEPTH, JEV_PLAN_CANDIDATE_FIRST = 0, 1
 JEV_CACHE_RELEASE, JEV_CACHE_LRU = 0, 1
 JEV_SCHED_QUEUED, JEV_SCHED_ACTIVE, JEV_SCHED_FINISHED = 0, 1, 2
+JEV_DEBUG_POISON_FREED_PAGES, JEV_DEBUG_TIME_CALLS = 1, 2
+JEV_CALL_NONE, JEV_CALL_PREFILL, JEV_CALL_BRANCHES, JEV_CALL_CANDIDATES, JEV_CALL_SCHED_STEP = 0, 1, 2, 3, 4
 _NAMES = {0: "JEV_OK", 1: "JEV_EINVAL", 2: "JEV_ENOMEM", 3: "JEV_EHANDLE", 4: "JEV_EHIP", 5: "JEV_ESTATE",
           6: "JEV_EPENDING"}
 
@@ -32,7 +34,8 @@ EXPORTED = ["jev_workspace_bytes", "jev_kv_pool_bytes", "jev_create", "jev_destr
             "jev_score_branches", "jev_score_branches_noalloc", "jev_score_candidates", "jev_free_pages", "jev_plan", "jev_page_table",
             "jev_match", "jev_stats", "jev_debug_tap", "jev_profile", "jev_profile_read", "jev_answers",
             "jev_set_plan_mode", "jev_set_cache_policy", "jev_sched_create", "jev_sched_destroy",
-            "jev_sched_submit", "jev_sched_step", "jev_sched_status", "jev_sched_result", "jev_last_error"]
+            "jev_sched_submit", "jev_sched_step", "jev_sched_status", "jev_sched_result", "jev_last_error",
+            "jev_set_debug", "jev_limits"]
 KERNELS = ["embed", "rmsnorm", "qkv", "attn", "merge", "oproj", "readout"]
 
 
@@ -65,7 +68,21 @@ class Stats(ctypes.Structure):
     _fields_ = [("logical_tokens", ctypes.c_int64), ("computed_tokens", ctypes.c_int64),
                 ("cached_tokens", ctypes.c_int64), ("rounds", ctypes.c_int32), ("pages_in_use", ctypes.c_int32),
                 ("pages_total", ctypes.c_int32), ("resident_prefixes", ctypes.c_int32), ("calls", ctypes.c_int64),
-                ("cached_prefixes", ctypes.c_int32), ("cached_pages", ctypes.c_int32), ("evictions", ctypes.c_int64)]
+                ("cached_prefixes", ctypes.c_int32), ("cached_pages", ctypes.c_int32), ("evictions", ctypes.c_int64),
+                ("last_call_kind", ctypes.c_int32), ("debug_flags", ctypes.c_uint32),
+                ("last_prepare_ns", ctypes.c_int64), ("last_enqueue_ns", ctypes.c_int64),
+                ("last_prefill_ms", ctypes.c_double), ("last_branch_ms", ctypes.c_double)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+class Limits(ctypes.Structure):
+    _fields_ = [("page_tokens", ctypes.c_int32), ("min_labels", ctypes.c_int32), ("max_labels", ctypes.c_int32),
+                ("max_positions", ctypes.c_int32), ("max_round_tokens", ctypes.c_int32), ("n_pages", ctypes.c_int32),
+                ("split_k_rows", ctypes.c_int32), ("max_tile_pages", ctypes.c_int32),
+                ("noalloc_scratch_bytes", ctypes.c_int64), ("noalloc_partial_rows", ctypes.c_int64),
+                ("workspace_partial_rows", ctypes.c_int64)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -111,6 +128,8 @@ def lib() -> ctypes.CDLL:
         L.jev_sched_status.argtypes = [vp, i64, P(i32)]
         L.jev_sched_result.argtypes = [vp, i64, P(ctypes.c_float), i64]
         L.jev_last_error.restype = ctypes.c_char_p
+        L.jev_set_debug.argtypes = [vp, ctypes.c_uint32]
+        L.jev_limits.argtypes = [vp, P(Limits)]
         _lib = L
     return _lib
 
@@ -282,6 +301,15 @@ class Context:
     def set_cache_policy(self, policy: int) -> None:
         """JEV_CACHE_RELEASE or JEV_CACHE_LRU (jev_set_cache_policy)."""
         _check(lib().jev_set_cache_policy(self.ctx, policy))
+
+    def set_debug(self, flags: int) -> None:
+        """JEV_DEBUG_* bit flags (jev_set_debug); 0 turns them off."""
+        _check(lib().jev_set_debug(self.ctx, flags))
+
+    def limits(self) -> dict:
+        out = Limits()
+        _check(lib().jev_limits(self.ctx, ctypes.byref(out)))
+        return out.as_dict()
 
     def plan(self, seqs) -> List[int]:
         flat, off = _segments(seqs)

@@ -191,6 +191,76 @@ def test_w1_unshared_and_candidate_paths_match_oracle(w1):
     assert ctx.stats()["rounds"] == 2 and ctx.stats()["pages_in_use"] == 0
 
 
+def test_w1_poisoned_freed_pages_change_nothing(w1):
+    """With freed-page poisoning on, every page a call frees or borrows is
+    filled with 0x7F bytes after the call's kernels: a kernel that read a freed
+    page as live keys would turn the probabilities into NaN.  The prefix,
+    branch, candidate (two rounds) and scheduler paths all still match the
+    oracle, a re-prefill into the poisoned pages gives bitwise the same
+    result, and the freed prefix pages really hold the poison."""
+    from shared_prefix_kv_amd import jev
+    wl, inst, m, ref, ctx, _ = w1
+    ctx.set_debug(jev.JEV_DEBUG_POISON_FREED_PAGES)
+    try:
+        br = inst.passes[0]
+        runs = []
+        for _ in range(2):
+            (h,) = ctx.prefill_prefix([0], [inst.prefixes[0]])
+            pages = ctx.page_table(h)[0]
+            probs, loff = ctx.score_branches([h] * len(br), [b.tokens for b in br], [b.labels for b in br])
+            _sync()
+            got = split_probs(probs, loff)
+            close("w1 poisoned pool, shared prefix", got, ref, TOL_F32)
+            runs.append(probs.cpu().numpy().copy())
+            ctx.free_pages([h])
+            _sync()
+            page_bytes = m.hkv * 2 * 16 * m.dh * 4
+            pool = ctx.pool.view(torch.uint8)
+            for p in pages:
+                blk = pool[p * page_bytes:(p + 1) * page_bytes]
+                assert bool((blk == 0x7F).all()), f"freed page {p} not poisoned"
+        assert np.array_equal(runs[0], runs[1])
+        seqs = inst.full_sequences(0)
+        probs, loff = ctx.score_candidates([s for s, _ in seqs], [l for _, l in seqs])
+        _sync()
+        close("w1 poisoned pool, candidates", split_probs(probs, loff), ref, TOL_F32)
+        assert ctx.stats()["pages_in_use"] == 0
+    finally:
+        ctx.set_debug(0)
+
+
+def test_w1_call_timing_splits_prefill_and_branch_rounds(w1):
+    """jev_stats with call timing on: a prefill call is all shared-prefix time,
+    a branch call all branch time, a candidate call (prefix round, then the
+    read-out round) has both; the host preparation and enqueue times are
+    recorded for every call that runs device work."""
+    from shared_prefix_kv_amd import jev
+    wl, inst, m, ref, ctx, _ = w1
+    ctx.set_debug(jev.JEV_DEBUG_TIME_CALLS)
+    try:
+        br = inst.passes[0]
+        (h,) = ctx.prefill_prefix([0], [inst.prefixes[0]])
+        st = ctx.stats()
+        assert st["last_call_kind"] == jev.JEV_CALL_PREFILL
+        assert st["last_prefill_ms"] > 0 and st["last_branch_ms"] == 0
+        assert st["last_prepare_ns"] > 0 and st["last_enqueue_ns"] > 0
+        probs, loff = ctx.score_branches([h] * len(br), [b.tokens for b in br], [b.labels for b in br])
+        st = ctx.stats()
+        assert st["last_call_kind"] == jev.JEV_CALL_BRANCHES
+        assert st["last_branch_ms"] > 0 and st["last_prefill_ms"] == 0
+        close("w1 timed calls", split_probs(probs, loff), ref, TOL_F32)
+        ctx.free_pages([h])
+        seqs = inst.full_sequences(0)
+        ctx.score_candidates([s for s, _ in seqs], [l for _, l in seqs])
+        st = ctx.stats()
+        assert st["last_call_kind"] == jev.JEV_CALL_CANDIDATES and st["rounds"] == 2
+        assert st["last_prefill_ms"] > 0 and st["last_branch_ms"] > 0
+    finally:
+        ctx.set_debug(0)
+    st = ctx.stats()
+    assert st["last_prefill_ms"] == -1.0 and st["last_branch_ms"] == -1.0
+
+
 def test_w1_scheduler_requests_match_oracle(w1):
     """Three requests through the scheduler: two submitted together, one (new
     branches over the same prefix plus a second state) after the first step.

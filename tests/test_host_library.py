@@ -168,3 +168,43 @@ def test_unsupported_shapes_rejected():
     assert L.jev_workspace_bytes(ctypes.byref(bad)) == 0
     with pytest.raises(jev.JevError):
         jev.Context(bad, 10)
+
+
+def test_limits_of_a_planning_only_context():
+    wl = workload(2)
+    ctx = jev.Context(desc_for(wl, max_pos=40000, max_tok=4096), 777)
+    lim = ctx.limits()
+    assert lim["page_tokens"] == 16 and lim["min_labels"] == 2 and lim["max_labels"] == 64
+    assert lim["max_positions"] == 40000 and lim["max_round_tokens"] == 4096 and lim["n_pages"] == 777
+    assert lim["split_k_rows"] == 256 and lim["max_tile_pages"] == 4096
+    assert lim["noalloc_scratch_bytes"] == 96 << 20
+    assert lim["noalloc_partial_rows"] == 0 and lim["workspace_partial_rows"] == 0  # no device memory
+    # every sequence that max_positions allows fits one attention tile's page list
+    assert (lim["max_positions"] + lim["page_tokens"] - 1) // lim["page_tokens"] <= lim["max_tile_pages"]
+    with pytest.raises(jev.JevError) as e:
+        jev._check(jev.lib().jev_limits(None, None))
+    assert e.value.code == jev.JEV_EINVAL
+
+
+def test_debug_flags_and_call_statistics_on_a_planning_only_context():
+    wl = workload(1)
+    inst = make_instance(wl)
+    ctx = dry(wl, 256)
+    st = ctx.stats()
+    assert st["debug_flags"] == 0 and st["last_call_kind"] == jev.JEV_CALL_NONE
+    assert st["last_prefill_ms"] == -1.0 and st["last_branch_ms"] == -1.0
+    ctx.set_debug(jev.JEV_DEBUG_POISON_FREED_PAGES | jev.JEV_DEBUG_TIME_CALLS)
+    assert ctx.stats()["debug_flags"] == 3
+    with pytest.raises(jev.JevError) as e:
+        ctx.set_debug(4)
+    assert e.value.code == jev.JEV_EINVAL
+    assert ctx.stats()["debug_flags"] == 3  # a refused call changes nothing
+    # tree work runs on a planning-only context, with no device work: poisoning
+    # and timing have nothing to do, and no call is recorded as timed
+    (h,) = ctx.prefill_prefix([0], [inst.prefixes[0]])
+    ctx.free_pages([h])
+    st = ctx.stats()
+    assert st["last_call_kind"] == jev.JEV_CALL_NONE and st["last_prefill_ms"] == -1.0
+    assert st["pages_in_use"] == 0
+    ctx.set_debug(0)
+    assert ctx.stats()["debug_flags"] == 0
