@@ -107,6 +107,30 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
+def kernel_fractions(per_key: dict, dtype: str, n_steps: int) -> dict:
+    """Each kernel instance against its own binding roofline, each kind timed
+    with events on its own launches over untimed steps: the
+    prefill projections and every attention against MFMA peak (algorithmic
+    FLOPs), the projections of rounds of at most 256 rows (weight streaming)
+    and the norm / embedding kernels against HBM peak (algorithmic bytes).
+    Kernels whose algorithmic bytes are not recorded (merge, readout) get
+    their time only."""
+    peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_F32_TFLOPS
+    out = {}
+    for key, (n, ms, flops, nbytes) in sorted(per_key.items(), key=lambda x: -x[1][1]):
+        kind = key.split("[")[0]
+        rows = int(key.split("[")[1].split()[0])
+        e = {"launches_per_step": n // n_steps, "avg_us": round(1e3 * ms / n, 2)}
+        if flops > 0 and not (kind in ("qkv", "oproj") and rows <= 256):
+            ach = flops / (ms * 1e-3) / 1e12
+            e.update({"bound": "mfma", "achieved": round(ach, 1), "unit": "TFLOP/s", "frac": round(ach / peak, 4)})
+        elif nbytes > 0:
+            ach = nbytes / (ms * 1e-3) / 1e9
+            e.update({"bound": "hbm", "achieved": round(ach, 1), "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)})
+        out[key] = e
+    return out
+
+
 def launch_key(rec) -> str:
     """Launches of one kind over the same number of rows run the same kernel instance."""
     return f"{rec['kernel']}[{rec['rows']} rows]"
@@ -147,8 +171,8 @@ def measured_traffic(key: str):
 def library_gemms() -> dict:
     """Context for the GEMM rooflines: torch.matmul (the ROCm BLAS library) on
     the projection shapes of the headline workload, bf16 operands drawn like
-    the weights (N(0, 0.02)) and the activations (N(0, 1)), median over 50
-    calls.  Not part of the scoring path."""
+    the weights (N(0, 0.02)) and the activations (N(0, 1)); the median of 5
+    batches of 20 back-to-back calls.  Not part of the scoring path."""
     import numpy as np
     import torch
     g = torch.Generator(device="cuda:0").manual_seed(0)
@@ -161,14 +185,15 @@ def library_gemms() -> dict:
         for _ in range(5):
             torch.matmul(a, wt)
         ts = []
-        for _ in range(50):
+        for _ in range(5):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record()
-            torch.matmul(a, wt)
+            for _ in range(20):
+                torch.matmul(a, wt)
             e1.record()
             torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e3)
+            ts.append(e0.elapsed_time(e1) * 1e3 / 20)
         us = float(np.median(ts))
         res[name] = {"us": round(us, 2), "tflop_s": round(2.0 * M * N * K / us / 1e6, 1),
                      "note": "plain GEMM, no RoPE / page-write / residual epilogue"}
@@ -522,20 +547,33 @@ def main(argv=None) -> int:
             ev[2].record(stream)
         ctx.free_pages(hs)
 
-    # warmup, then one fully profiled step to find the dominant kernel
+    # warmup, then the per-kernel timing that also picks the dominant kernel
     for _ in range(max(1, args.warmup)):
         step()
     torch.cuda.synchronize()
-    ctx.profile(jev.KERNELS)
-    step()
-    recs = ctx.profile_read()
-    ctx.profile(())
+    # each kernel kind timed on its own (events on its launches only) over 3
+    # untimed steps: time per step by kind and by instance, and the dominant
+    # instance (events on every launch of a step would slow the step down)
+    n_prof = 3
     per_kind = {}
     per_launch = {}
-    for r in recs:
-        per_kind[r["kernel"]] = per_kind.get(r["kernel"], 0.0) + r["ms"]
-        key = launch_key(r)
-        per_launch[key] = per_launch.get(key, 0.0) + r["ms"]
+    per_key = {}
+    for kind in jev.KERNELS:
+        ctx.profile([kind])
+        for _ in range(n_prof):
+            step()
+        torch.cuda.synchronize()
+        for r in ctx.profile_read():
+            key = launch_key(r)
+            per_kind[r["kernel"]] = per_kind.get(r["kernel"], 0.0) + r["ms"] / n_prof
+            per_launch[key] = per_launch.get(key, 0.0) + r["ms"] / n_prof
+            a = per_key.setdefault(key, [0, 0.0, 0.0, 0.0])
+            a[0] += 1
+            a[1] += r["ms"]
+            a[2] += r["flops"]
+            a[3] += r["bytes"]
+        ctx.profile(())
+    per_kernel = kernel_fractions(per_key, m.dtype, n_prof)
     key = max(per_launch, key=per_launch.get) if args.roofline_kernel == "auto" else args.roofline_kernel
     kern = key.split("[")[0]
 
@@ -607,6 +645,7 @@ def main(argv=None) -> int:
             "branch_hbm_frac": round(alg["branch_bytes"] / (sc_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "branch_algorithmic_mb": round(alg["branch_bytes"] / 1e6, 2),
             "kernel_ms_per_step": {k: round(v, 4) for k, v in sorted(per_kind.items(), key=lambda x: -x[1])},
+            "per_kernel": per_kernel,
         },
         "stats_last_call": {k: st[k] for k in ("logical_tokens", "computed_tokens", "cached_tokens", "rounds")},
         "roofline": roof,
