@@ -261,6 +261,7 @@ int poison_after(jev_ctx* ctx, const std::set<int32_t>& before, const std::vecto
     if (!before.count(p)) pages.insert(p);
   for (int32_t p : written)
     if (now.count(p)) pages.insert(p);
+  if (pages.empty()) return JEV_OK;
   for (auto it = pages.begin(); it != pages.end();) {
     const int32_t first = *it;
     int32_t count = 0;
@@ -270,6 +271,10 @@ int poison_after(jev_ctx* ctx, const std::set<int32_t>& before, const std::vecto
     }
     HIPCHK(jev::launch_poison_pages(ctx->dims, ctx->pool, first, count, s));
   }
+  // the next call (possibly on another stream) is ordered after the fills
+  HIPCHK(hipEventRecord(ctx->last_done, s));
+  ctx->have_last = true;
+  ctx->last_stream = s;
   return JEV_OK;
 }
 
