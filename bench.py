@@ -32,14 +32,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
 def algorithmic(wl, inst):
-    """Algorithmic FLOPs of the prefix prefill and bytes of the branch phase."""
+    """Algorithmic FLOPs of the prefix prefill and bytes of the branch phase.
+
+    What the method needs: a prefill produces the KV cache at every position
+    and the logits at the last one only (jdon.com article, prefill-only
+    section).  So the last layer needs the K/V projections of every token, and
+    the query projection, attention and output projection only at the read-out
+    positions (none in the prefix prefill, the last token of each branch)."""
     m = wl.model
     E = 2 if m.dtype == "bf16" else 4
     d, hq, hkv, dh, L = m.d, m.hq, m.hkv, m.dh, m.n_layers
     nqkv = (hq + 2 * hkv) * dh
+    nkv = 2 * hkv * dh
     P = sum(len(p) for p in inst.prefixes)
-    proj = sum(2 * len(p) * d * nqkv + 2 * len(p) * hq * dh * d for p in inst.prefixes) * L
-    attn = sum(4 * dh * hq * len(p) * (len(p) + 1) / 2 for p in inst.prefixes) * L
+    proj = sum(2 * len(p) * d * nqkv + 2 * len(p) * hq * dh * d for p in inst.prefixes) * (L - 1)
+    proj += sum(2 * len(p) * d * nkv for p in inst.prefixes)
+    attn = sum(4 * dh * hq * len(p) * (len(p) + 1) / 2 for p in inst.prefixes) * (L - 1)
     br = inst.passes[0]
     tb = sum(len(b.tokens) for b in br)
     w_bytes = L * (nqkv * d + d * hq * dh) * E
@@ -48,9 +56,11 @@ def algorithmic(wl, inst):
     emb = tb * d * E
     labels = sum(len(b.labels) for b in br) * d * E
     plen = [len(inst.prefixes[b.request]) for b in br]
-    br_flops = L * sum(2 * len(b.tokens) * d * nqkv + 2 * len(b.tokens) * hq * dh * d
-                       + 4 * dh * hq * len(b.tokens) * (pl + (len(b.tokens) + 1) / 2)
-                       for b, pl in zip(br, plen))
+    br_flops = (L - 1) * sum(2 * len(b.tokens) * d * nqkv + 2 * len(b.tokens) * hq * dh * d
+                             + 4 * dh * hq * len(b.tokens) * (pl + (len(b.tokens) + 1) / 2)
+                             for b, pl in zip(br, plen))
+    br_flops += sum(2 * len(b.tokens) * d * nkv + 2 * d * hq * dh + 2 * hq * dh * d
+                    + 4 * dh * hq * (pl + len(b.tokens)) for b, pl in zip(br, plen))
     return {"prefill_flops": proj + attn, "branch_bytes": w_bytes + kv_prefix + kv_suffix + emb + labels,
             "branch_flops": br_flops}
 
@@ -58,18 +68,25 @@ def algorithmic(wl, inst):
 def tree_flops(wl, inst):
     """Algorithmic FLOPs of a candidate-tree call: projections of every token
     computed once (the trie's nodes) and causal attention of each node's tokens
-    over their whole path."""
+    over their whole path; in the last layer K/V projections of every token and
+    the rest only at the candidates' read-out positions (the leaves' last
+    tokens), as in algorithmic()."""
     m = wl.model
     d, hq, hkv, dh, L = m.d, m.hq, m.hkv, m.dh, m.n_layers
     nqkv = (hq + 2 * hkv) * dh
+    nkv = 2 * hkv * dh
     t = wl.tree
     nodes = [(t.root_len, 0)]
+    leaves = []
     for ci, cl in enumerate(t.child_lens):
         nodes.append((cl, t.root_len))
         nodes += [(t.leaf_len, t.root_len + cl)] * t.leaves_per_child[ci]
-    proj = sum(2 * n * d * nqkv + 2 * n * hq * dh * d for n, _ in nodes) * L
-    attn = sum(4 * dh * hq * n * (p + (n + 1) / 2) for n, p in nodes) * L
-    return proj + attn
+        leaves += [(t.leaf_len, t.root_len + cl)] * t.leaves_per_child[ci]
+    proj = sum(2 * n * d * nqkv + 2 * n * hq * dh * d for n, _ in nodes) * (L - 1)
+    attn = sum(4 * dh * hq * n * (p + (n + 1) / 2) for n, p in nodes) * (L - 1)
+    last = sum(2 * n * d * nkv for n, _ in nodes)
+    last += sum(2 * d * hq * dh + 2 * hq * dh * d + 4 * dh * hq * (p + n) for n, p in leaves)
+    return proj + attn + last
 
 
 def cpu_baseline(wl, inst, weights, n_branches: int):

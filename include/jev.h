@@ -291,8 +291,20 @@ int jev_stats(jev_ctx* ctx, jev_stats_t* out);
  *    Costs one fill launch per call; results are unchanged.
  *  - JEV_DEBUG_TIME_CALLS: the device time of each call's rounds is recorded
  *    with events (two fence-free event records per round) for jev_stats.
+ *  - JEV_DEBUG_FULL_LAST_LAYER: the last layer's attention and output
+ *    projection run for every row of a round, as in the other layers.  By
+ *    default (and unless a debug tap is registered) they run only for the rows
+ *    whose final state is read out, or not at all in a round without
+ *    read-outs: a prefill produces the KV cache at every position and the
+ *    logits at the last one only (jdon.com article, prefill-only section), and
+ *    nothing else reads a row's last-layer output.  A round's read-out rows
+ *    get the tiles, chunks and wave groups they have in the whole round, so
+ *    their probabilities are bitwise the same either way when the round has
+ *    at most 256 rows (larger rounds project the whole round without a K
+ *    split and the read-out rows with one: equal to the accumulation-order
+ *    floor).
  * Errors: JEV_EINVAL (unknown bit, NULL ctx). */
-enum { JEV_DEBUG_POISON_FREED_PAGES = 1, JEV_DEBUG_TIME_CALLS = 2 };
+enum { JEV_DEBUG_POISON_FREED_PAGES = 1, JEV_DEBUG_TIME_CALLS = 2, JEV_DEBUG_FULL_LAST_LAYER = 4 };
 int jev_set_debug(jev_ctx* ctx, uint32_t flags);
 
 /* Limits of a context (host-only; also on a planning-only context). */

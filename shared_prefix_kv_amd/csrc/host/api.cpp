@@ -153,7 +153,17 @@ struct RoundDesc {
   double attn_pairs = 0;  // visible (query row, key) pairs of one layer
   int64_t n_part_rows = 0;
   int32_t attn_groups = 1;  // wave groups per attention workgroup
+  // last layer: every row, none (only its K/V pages are needed), or the
+  // read-out rows alone (ll_R of them, compacted: round rows at ll_off_rows,
+  // positions at ll_off_pos, their own tiles and merges)
+  int32_t last_mode = 0;
+  int32_t ll_R = 0;
+  int64_t ll_off_rows = 0, ll_off_pos = 0, ll_off_tiles = 0, ll_off_merge = 0;
+  int32_t ll_n_tiles = 0, ll_n_merge = 0;
+  int64_t ll_part_slots = 0;
+  double ll_attn_pairs = 0;
 };
+enum { LAST_ALL = 0, LAST_NONE = 1, LAST_READ_ROWS = 2 };
 
 // Device scratch of a call's kernels: attention partial states (rows of dh
 // floats plus their log2-sum-exp) and the split-K partial tiles of the
@@ -534,9 +544,6 @@ int build_round(jev_ctx* ctx, std::vector<RNode>& nodes, std::vector<int32_t>& h
     n_chunks = std::max<int64_t>(1, std::min<int64_t>({n_chunks, kMaxChunks, min_anc_pages / 8}));
   }
 
-  std::vector<jev::AttnTile> tiles;
-  std::vector<jev::MergeItem> merges;
-  int64_t slot = 0;
   // When a round has too few attention tiles to occupy every CU, its time is
   // set by the longest causal tile; tiles longer than cpo pages are then split
   // in two: the pages before the tile's first query page (every key visible,
@@ -551,30 +558,54 @@ int build_round(jev_ctx* ctx, std::vector<RNode>& nodes, std::vector<int32_t>& h
     cpo = (max_own_pages + 1) / 2;
     cpo += cpo & 1;
   }
-  std::vector<int32_t> own_slot(T, -1), own_ti(T, -1), own_n(T, 0);
-  for (size_t i = 0; i < nodes.size(); ++i) {
-    const RNode& nd = nodes[i];
-    const bool has_anc = !nd.anc.empty();
-    for (int64_t i0 = 0; i0 < nd.n; i0 += TT) {
-      const int64_t nt = std::min<int64_t>(TT, nd.n - i0);
+
+  // One attention plan over a set of query tokens.  A query range is tokens
+  // [i0, i0 + nt) of node `node`, whose first token is query row tq of the
+  // launch (q, positions and output rows); `tile_i0` is the first token of the
+  // round tile that holds it, which fixes the split point, so that a range
+  // planned alone gets the same tiles, page steps and merge order as in the
+  // whole round.  grows[g] are the query rows of group g.
+  struct QRange {
+    size_t node;
+    int64_t i0, nt, tq, tile_i0;
+  };
+  struct AttnPlan {
+    std::vector<jev::AttnTile> tiles;
+    std::vector<jev::MergeItem> merges;
+    int64_t slots = 0;
+    double pairs = 0;
+  };
+  auto plan_attention = [&](const std::vector<QRange>& qr, int64_t n_rows,
+                            const std::vector<std::pair<int64_t, int64_t>>& grows, AttnPlan* ap) {
+    std::vector<jev::AttnTile>& tiles = ap->tiles;
+    std::vector<jev::MergeItem>& merges = ap->merges;
+    int64_t slot = 0;
+    std::vector<int32_t> own_slot(size_t(n_rows), -1), own_ti(size_t(n_rows), -1), own_n(size_t(n_rows), 0);
+    for (const QRange& r : qr) {
+      const RNode& nd = nodes[r.node];
+      const bool has_anc = !nd.anc.empty();
+      const int64_t nt = r.nt, i0 = r.i0;
       const int64_t np = (i0 + nt - 1) / jev::kPage + 1;
-      // split point: an even page count, at or before the first query's page
+      // split point of the round tile: an even page count, at or before its
+      // first query's page
+      const int64_t tile_nt = std::min<int64_t>(TT, nd.n - r.tile_i0);
+      const int64_t tile_np = (r.tile_i0 + tile_nt - 1) / jev::kPage + 1;
       int64_t sp = 0;
-      if (np > cpo) sp = std::min<int64_t>(np / 2, i0 / jev::kPage) & ~int64_t(1);
+      if (tile_np > cpo) sp = std::min<int64_t>(tile_np / 2, r.tile_i0 / jev::kPage) & ~int64_t(1);
       const bool partial = has_anc || sp > 0;
-      // causal pairs of the tile: token i0+j sees i0+j+1 own keys
-      rd->attn_pairs += double(G) * double(ctx->desc.n_kv_heads) * double(nt * i0 + nt * (nt + 1) / 2);
+      // causal pairs of the range: token i0+j sees i0+j+1 own keys
+      ap->pairs += double(G) * double(ctx->desc.n_kv_heads) * double(nt * i0 + nt * (nt + 1) / 2);
       if (partial)
         for (int64_t j = 0; j < nt; ++j) {
-          own_slot[node_t0[i] + i0 + j] = int32_t(slot);
-          own_ti[node_t0[i] + i0 + j] = int32_t(j);
-          own_n[node_t0[i] + i0 + j] = sp > 0 ? 2 : 1;
+          own_slot[size_t(r.tq + j)] = int32_t(slot);
+          own_ti[size_t(r.tq + j)] = int32_t(j);
+          own_n[size_t(r.tq + j)] = sp > 0 ? 2 : 1;
         }
       if (sp > 0) {
         jev::AttnTile tl{};
-        tl.t0 = int32_t(node_t0[i] + i0);
+        tl.t0 = int32_t(r.tq);
         tl.n_tok = int32_t(nt);
-        tl.page_off = int32_t(own_off[i]);
+        tl.page_off = int32_t(own_off[r.node]);
         tl.n_pages = int32_t(sp);
         tl.causal = 0;
         tl.kv_pos0 = int32_t(nd.start);
@@ -583,9 +614,9 @@ int build_round(jev_ctx* ctx, std::vector<RNode>& nodes, std::vector<int32_t>& h
         tiles.push_back(tl);
       }
       jev::AttnTile tl{};
-      tl.t0 = int32_t(node_t0[i] + i0);
+      tl.t0 = int32_t(r.tq);
       tl.n_tok = int32_t(nt);
-      tl.page_off = int32_t(own_off[i] + sp);
+      tl.page_off = int32_t(own_off[r.node] + sp);
       tl.n_pages = int32_t(np - sp);
       tl.causal = 1;
       tl.kv_pos0 = int32_t(nd.start + jev::kPage * sp);
@@ -593,58 +624,126 @@ int build_round(jev_ctx* ctx, std::vector<RNode>& nodes, std::vector<int32_t>& h
       tl.part_slot = partial ? int32_t(slot++) : 0;
       tiles.push_back(tl);
     }
-  }
-  std::vector<char> merged(T, 0);
-  for (auto& g : groups) {
-    if (g.anc_pages == 0) continue;
-    int64_t cp = (g.anc_pages + n_chunks - 1) / n_chunks;
-    cp += cp & 1;  // whole two-page steps per chunk
-    const int64_t nch = (g.anc_pages + cp - 1) / cp;
-    int64_t anc_keys = 0;
-    for (int64_t pi = 0; pi < g.anc_pages; ++pi) anc_keys += plist[2 * (g.anc_off + pi) + 1];
-    rd->attn_pairs += double(g.t1 - g.t0) * G * double(ctx->desc.n_kv_heads) * double(anc_keys);
-    for (int64_t t0 = g.t0; t0 < g.t1; t0 += TT) {
-      const int64_t nt = std::min<int64_t>(TT, g.t1 - t0);
-      const int64_t slot0 = slot;
-      for (int64_t c = 0; c < nch; ++c) {
-        jev::AttnTile tl{};
-        tl.t0 = int32_t(t0);
-        tl.n_tok = int32_t(nt);
-        tl.page_off = int32_t(g.anc_off + c * cp);
-        tl.n_pages = int32_t(std::min(cp, g.anc_pages - c * cp));
-        tl.causal = 0;
-        tl.out_mode = 1;
-        tl.part_slot = int32_t(slot++);
-        tiles.push_back(tl);
-      }
-      for (int64_t j = 0; j < nt; ++j) {
-        const int64_t t = t0 + j;
-        merges.push_back(jev::MergeItem{int32_t(t), own_slot[t], own_ti[t], own_n[t], int32_t(slot0), int32_t(j),
-                                        int32_t(nch), 0});
-        merged[t] = 1;
+    std::vector<char> merged(size_t(n_rows), 0);
+    for (size_t gi = 0; gi < groups.size(); ++gi) {
+      const Group& g = groups[gi];
+      const int64_t r0 = grows[gi].first, r1 = grows[gi].second;
+      if (g.anc_pages == 0 || r1 <= r0) continue;
+      int64_t cp = (g.anc_pages + n_chunks - 1) / n_chunks;
+      cp += cp & 1;  // whole two-page steps per chunk
+      const int64_t nch = (g.anc_pages + cp - 1) / cp;
+      int64_t anc_keys = 0;
+      for (int64_t pi = 0; pi < g.anc_pages; ++pi) anc_keys += plist[2 * (g.anc_off + pi) + 1];
+      ap->pairs += double(r1 - r0) * G * double(ctx->desc.n_kv_heads) * double(anc_keys);
+      for (int64_t t0 = r0; t0 < r1; t0 += TT) {
+        const int64_t nt = std::min<int64_t>(TT, r1 - t0);
+        const int64_t slot0 = slot;
+        for (int64_t c = 0; c < nch; ++c) {
+          jev::AttnTile tl{};
+          tl.t0 = int32_t(t0);
+          tl.n_tok = int32_t(nt);
+          tl.page_off = int32_t(g.anc_off + c * cp);
+          tl.n_pages = int32_t(std::min(cp, g.anc_pages - c * cp));
+          tl.causal = 0;
+          tl.out_mode = 1;
+          tl.part_slot = int32_t(slot++);
+          tiles.push_back(tl);
+        }
+        for (int64_t j = 0; j < nt; ++j) {
+          const size_t t = size_t(t0 + j);
+          merges.push_back(jev::MergeItem{int32_t(t), own_slot[t], own_ti[t], own_n[t], int32_t(slot0),
+                                          int32_t(j), int32_t(nch), 0});
+          merged[t] = 1;
+        }
       }
     }
+    // rows of split tiles without a prefix part
+    for (int64_t t = 0; t < n_rows; ++t)
+      if (!merged[size_t(t)] && own_n[size_t(t)] > 1)
+        merges.push_back(jev::MergeItem{int32_t(t), own_slot[size_t(t)], own_ti[size_t(t)], own_n[size_t(t)], 0,
+                                        0, 0, 0});
+    // heavy tiles first
+    std::stable_sort(tiles.begin(), tiles.end(),
+                     [](const jev::AttnTile& a, const jev::AttnTile& b) { return a.n_pages > b.n_pages; });
+    ap->slots = slot;
+  };
+
+  // the whole round
+  AttnPlan full;
+  {
+    std::vector<QRange> qr;
+    for (size_t i = 0; i < nodes.size(); ++i)
+      for (int64_t i0 = 0; i0 < nodes[i].n; i0 += TT)
+        qr.push_back(QRange{i, i0, std::min<int64_t>(TT, nodes[i].n - i0), node_t0[i] + i0, i0});
+    std::vector<std::pair<int64_t, int64_t>> grows;
+    for (auto& g : groups) grows.emplace_back(g.t0, g.t1);
+    plan_attention(qr, T, grows, &full);
   }
-  // tokens of split tiles without a prefix part
-  for (int64_t t = 0; t < T; ++t)
-    if (!merged[t] && own_n[t] > 1)
-      merges.push_back(jev::MergeItem{int32_t(t), own_slot[t], own_ti[t], own_n[t], 0, 0, 0, 0});
-  if (slot * ctx->desc.n_kv_heads * kRowsPerTile > ctx->L.part_rows)
+  if (full.slots * ctx->desc.n_kv_heads * kRowsPerTile > ctx->L.part_rows)
     return fail(JEV_ENOMEM, "round needs more partial-state rows than the workspace holds");
-  rd->part_slots = slot;
-  rd->n_part_rows = int64_t(merges.size());
-  // heavy tiles first
-  std::stable_sort(tiles.begin(), tiles.end(),
-                   [](const jev::AttnTile& a, const jev::AttnTile& b) { return a.n_pages > b.n_pages; });
-  rd->n_tiles = int32_t(tiles.size());
+  rd->part_slots = full.slots;
+  rd->n_part_rows = int64_t(full.merges.size());
+  rd->attn_pairs = full.pairs;
+  rd->n_tiles = int32_t(full.tiles.size());
   // a round whose longest tile has many steps splits every tile's steps over
   // two wave groups, halving the chain that sets the kernel's length
-  rd->attn_groups = (!tiles.empty() && tiles.front().n_pages >= kTwoGroupPages) ? 2 : 1;
-  rd->off_tiles = push(int64_t(tiles.size()) * 8);
-  std::memcpy(hb.data() + rd->off_tiles, tiles.data(), tiles.size() * sizeof(jev::AttnTile));
-  rd->n_merge = int32_t(merges.size());
-  rd->off_merge = push(int64_t(merges.size()) * int64_t(sizeof(jev::MergeItem) / sizeof(int32_t)));
-  std::memcpy(hb.data() + rd->off_merge, merges.data(), merges.size() * sizeof(jev::MergeItem));
+  rd->attn_groups = (!full.tiles.empty() && full.tiles.front().n_pages >= kTwoGroupPages) ? 2 : 1;
+  rd->off_tiles = push(int64_t(full.tiles.size()) * 8);
+  std::memcpy(hb.data() + rd->off_tiles, full.tiles.data(), full.tiles.size() * sizeof(jev::AttnTile));
+  rd->n_merge = int32_t(full.merges.size());
+  rd->off_merge = push(int64_t(full.merges.size()) * int64_t(sizeof(jev::MergeItem) / sizeof(int32_t)));
+  std::memcpy(hb.data() + rd->off_merge, full.merges.data(), full.merges.size() * sizeof(jev::MergeItem));
+
+  // The last layer.  Nothing reads a token's last-layer attention or output
+  // projection except the read-out of its own final state, and later rounds
+  // read only K/V pages: a round without read-outs skips them, and a round
+  // whose read-out rows are few computes them for those rows only, with the
+  // tiles they have in the whole round (same chunks, split points and wave
+  // groups), so their values are bitwise those of the whole round.  The
+  // debug taps and JEV_DEBUG_FULL_LAST_LAYER keep every row.
+  int64_t R = 0;
+  for (auto& nd : nodes) R += nd.reads.empty() ? 0 : 1;
+  rd->last_mode = LAST_ALL;
+  if (ctx->taps.empty() && !(ctx->debug & JEV_DEBUG_FULL_LAST_LAYER)) {
+    if (R == 0)
+      rd->last_mode = LAST_NONE;
+    else if (4 * R <= T)
+      rd->last_mode = LAST_READ_ROWS;
+  }
+  if (rd->last_mode == LAST_READ_ROWS) {
+    // compact query rows, in round order (so grouped like the round's)
+    std::vector<QRange> qr;
+    std::vector<std::pair<int64_t, int64_t>> grows(groups.size(), {0, 0});
+    std::vector<int32_t> rows, pos;
+    size_t gi = 0;
+    for (size_t i = 0; i < nodes.size(); ++i) {
+      while (gi + 1 < groups.size() && node_t0[i] >= groups[gi].t1) ++gi;
+      if (nodes[i].reads.empty()) continue;
+      const int64_t r = int64_t(rows.size()), i0 = nodes[i].n - 1;
+      if (grows[gi].second <= grows[gi].first)
+        grows[gi] = {r, r + 1};
+      else
+        grows[gi].second = r + 1;
+      qr.push_back(QRange{i, i0, 1, r, (i0 / TT) * TT});
+      rows.push_back(int32_t(node_t0[i] + i0));
+      pos.push_back(int32_t(nodes[i].start + i0));
+    }
+    AttnPlan ll;
+    plan_attention(qr, R, grows, &ll);
+    rd->ll_R = int32_t(R);
+    rd->ll_off_rows = push(R);
+    std::copy(rows.begin(), rows.end(), hb.begin() + rd->ll_off_rows);
+    rd->ll_off_pos = push(R);
+    std::copy(pos.begin(), pos.end(), hb.begin() + rd->ll_off_pos);
+    rd->ll_part_slots = ll.slots;
+    rd->ll_attn_pairs = ll.pairs;
+    rd->ll_n_tiles = int32_t(ll.tiles.size());
+    rd->ll_off_tiles = push(int64_t(ll.tiles.size()) * 8);
+    std::memcpy(hb.data() + rd->ll_off_tiles, ll.tiles.data(), ll.tiles.size() * sizeof(jev::AttnTile));
+    rd->ll_n_merge = int32_t(ll.merges.size());
+    rd->ll_off_merge = push(int64_t(ll.merges.size()) * int64_t(sizeof(jev::MergeItem) / sizeof(int32_t)));
+    std::memcpy(hb.data() + rd->ll_off_merge, ll.merges.data(), ll.merges.size() * sizeof(jev::MergeItem));
+  }
   // readouts
   std::vector<jev::ReadoutItem> reads;
   std::vector<int32_t> labs;
@@ -668,7 +767,7 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
   if (int64_t(hb.size()) > ctx->L.desc_ints)
     return fail(JEV_ENOMEM, "call descriptors exceed the workspace descriptor region");
   for (const RoundDesc& rd : rds)
-    if (rd.part_slots * ctx->desc.n_kv_heads * kRowsPerTile > sc.part_rows)
+    if (std::max(rd.part_slots, rd.ll_part_slots) * ctx->desc.n_kv_heads * kRowsPerTile > sc.part_rows)
       return fail(JEV_ENOMEM, "round needs more partial-state rows than the scratch holds");
   const int64_t prepare_ns = ns_since(ctx->call_t0);
   const auto enqueue_t0 = std::chrono::steady_clock::now();
@@ -762,6 +861,31 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
       HIPCHK(timed(JEV_K_QKV, l, rd.T, 2 * T * NQKV * D, (T * D + NQKV * D + T * NQKV) * E, [&] {
         return jev::launch_qkv(m, w, l, h, rd.T, dd + rd.off_pos, dd + rd.off_slot, rope, q, ctx->pool, gws, s);
       }));
+      // last layer without read-outs: its K/V pages are all that is needed
+      if (l + 1 == m.n_layers && rd.last_mode == LAST_NONE) break;
+      if (l + 1 == m.n_layers && rd.last_mode == LAST_READ_ROWS) {
+        // the read-out rows alone: their queries gathered behind their
+        // outputs (o rows [R, 2R) and [0, R)), the output projection's
+        // residual written back to their rows of x
+        const int32_t* rows = dd + rd.ll_off_rows;
+        const double R = rd.ll_R;
+        const size_t qrow = size_t(m.hq) * m.dh * elt;
+        void* qc = ctx->ws + ctx->L.o + size_t(rd.ll_R) * qrow;
+        HIPCHK(jev::launch_gather_rows(q, rows, rd.ll_R, int32_t(qrow), qc, s));
+        HIPCHK(timed(JEV_K_ATTN, l, rd.ll_R, 4.0 * m.dh * rd.ll_attn_pairs, 0, [&] {
+          return jev::launch_attention(m, l, reinterpret_cast<const jev::AttnTile*>(dd + rd.ll_off_tiles),
+                                       rd.ll_n_tiles, dd + rd.off_plist, dd + rd.ll_off_pos, qc, ctx->pool, o,
+                                       part_o, part_lse, rd.attn_groups, s);
+        }));
+        if (rd.ll_n_merge > 0)
+          HIPCHK(timed(JEV_K_MERGE, l, rd.ll_n_merge, 0, 0, [&] {
+            return jev::launch_merge(m, reinterpret_cast<const jev::MergeItem*>(dd + rd.ll_off_merge),
+                                     rd.ll_n_merge, part_o, part_lse, o, s);
+          }));
+        HIPCHK(timed(JEV_K_OPROJ, l, rd.ll_R, 2 * R * D * HD, (R * HD + D * HD + 2 * R * D) * E,
+                     [&] { return jev::launch_oproj(m, w, o, rd.ll_R, x, gws, s, rows); }));
+        break;
+      }
       HIPCHK(timed(JEV_K_ATTN, l, rd.T, 4.0 * m.dh * rd.attn_pairs, 0, [&] {
         return jev::launch_attention(m, l, reinterpret_cast<const jev::AttnTile*>(dd + rd.off_tiles), rd.n_tiles,
                                      dd + rd.off_plist, dd + rd.off_pos, q, ctx->pool, o, part_o, part_lse,
@@ -1654,7 +1778,7 @@ int jev_stats(jev_ctx* ctx, jev_stats_t* out) {
 
 int jev_set_debug(jev_ctx* ctx, uint32_t flags) {
   if (!ctx) return fail(JEV_EINVAL, "ctx is NULL");
-  if (flags & ~uint32_t(JEV_DEBUG_POISON_FREED_PAGES | JEV_DEBUG_TIME_CALLS))
+  if (flags & ~uint32_t(JEV_DEBUG_POISON_FREED_PAGES | JEV_DEBUG_TIME_CALLS | JEV_DEBUG_FULL_LAST_LAYER))
     return fail(JEV_EINVAL, "unknown debug flag");
   ctx->debug = flags;
   if (!(flags & JEV_DEBUG_TIME_CALLS)) ctx->n_round_ev = 0;

@@ -93,6 +93,7 @@ struct QkvOut {
 struct ResOut {
   void* x;
   int ld;
+  const int32_t* rows;  // row r of the product updates x row rows[r] (null: row r)
 };
 
 enum { EPI_QKV = 0, EPI_RES = 1 };
@@ -152,7 +153,8 @@ __device__ __forceinline__ void tile_epilogue(const float* tile, int ld, int row
     const int rstep = nthreads / cpr;
     const int c8 = tid % cpr;
     for (int r = tid / cpr; r < rows && tid < rstep * cpr; r += rstep) {
-      T* xp = reinterpret_cast<T*>(ro.x) + (size_t)(m0 + r) * ro.ld + (size_t)nt * BN + 8 * c8;
+      const int xr = ro.rows ? ro.rows[m0 + r] : m0 + r;
+      T* xp = reinterpret_cast<T*>(ro.x) + (size_t)xr * ro.ld + (size_t)nt * BN + 8 * c8;
       const float* tp = tile + (size_t)r * ld + 8 * c8;
       float v[8];
       load8<T>(xp, v);
@@ -999,11 +1001,11 @@ hipError_t launch_oproj_split(const ModelDims& m, const LayerW& w, const void* o
 }
 
 hipError_t launch_oproj(const ModelDims& m, const LayerW& w, const void* o, int32_t T_, void* x, const GemmWs& ws,
-                        hipStream_t s) {
+                        hipStream_t s, const int32_t* x_rows) {
   if (T_ <= 0) return hipSuccess;
   dev::ColMap cm{w.wo, nullptr, nullptr, 0, 0, m.dh, 0};
   dev::QkvOut qo{};
-  dev::ResOut ro{x, m.d};
+  dev::ResOut ro{x, m.d, x_rows};
   if (m.dtype == 1) return gemm_dispatch<bf16s, dev::EPI_RES>(m, ws, o, T_, m.hq * m.dh, m.d, cm, qo, ro, s);
   return gemm_dispatch<float, dev::EPI_RES>(m, ws, o, T_, m.hq * m.dh, m.d, cm, qo, ro, s);
 }

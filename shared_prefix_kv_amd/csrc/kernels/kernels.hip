@@ -841,6 +841,15 @@ __global__ __launch_bounds__(256) void poison_pages_kernel(u32x4* __restrict__ p
   }
 }
 
+// ------------------------------------------------------------------ row gather
+// dst row r = src row rows[r]; one workgroup per row, 16-byte units.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restrict__ src,
+                                                          const int32_t* __restrict__ rows, int32_t units,
+                                                          u32x4* __restrict__ dst) {
+  const size_t from = (size_t)rows[blockIdx.x] * units, to = (size_t)blockIdx.x * units;
+  for (int u = threadIdx.x; u < units; u += blockDim.x) dst[to + u] = src[from + u];
+}
+
 }  // namespace dev
 
 thread_local LaunchTiming g_launch_timing{nullptr, nullptr};
@@ -942,6 +951,15 @@ hipError_t launch_poison_pages(const ModelDims& m, void* pool, int32_t first, in
   const unsigned blocks = (unsigned)std::min<size_t>((total + 255) / 256, 65536);
   JEV_LAUNCH(dev::poison_pages_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<dev::u32x4*>(pool),
              page_units * (size_t)m.n_pages, page_units, first, count, m.n_layers);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* src, const int32_t* rows, int32_t n, int32_t row_bytes, void* dst,
+                              hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (row_bytes <= 0 || row_bytes % 16) return hipErrorInvalidValue;
+  JEV_LAUNCH(dev::gather_rows_kernel, dim3(n), dim3(256), 0, s, reinterpret_cast<const dev::u32x4*>(src), rows,
+             row_bytes / 16, reinterpret_cast<dev::u32x4*>(dst));
   return hipGetLastError();
 }
 

@@ -25,7 +25,7 @@ JEV_ANSWER_NOUL, JEV_ANSWER_CHOICE, JEV_ANSWER_SCORE = 0, 1, 2
 JEV_PLAN_DEPTH, JEV_PLAN_CANDIDATE_FIRST = 0, 1
 JEV_CACHE_RELEASE, JEV_CACHE_LRU = 0, 1
 JEV_SCHED_QUEUED, JEV_SCHED_ACTIVE, JEV_SCHED_FINISHED = 0, 1, 2
-JEV_DEBUG_POISON_FREED_PAGES, JEV_DEBUG_TIME_CALLS = 1, 2
+JEV_DEBUG_POISON_FREED_PAGES, JEV_DEBUG_TIME_CALLS, JEV_DEBUG_FULL_LAST_LAYER = 1, 2, 4
 JEV_CALL_NONE, JEV_CALL_PREFILL, JEV_CALL_BRANCHES, JEV_CALL_CANDIDATES, JEV_CALL_SCHED_STEP = 0, 1, 2, 3, 4
 _NAMES = {0: "JEV_OK", 1: "JEV_EINVAL", 2: "JEV_ENOMEM", 3: "JEV_EHANDLE", 4: "JEV_EHIP", 5: "JEV_ESTATE",
           6: "JEV_EPENDING"}

@@ -641,6 +641,41 @@ def test_w2_repeated_calls_are_bitwise_identical(w2):
         assert np.array_equal(r, runs[0])
 
 
+def test_w2_last_layer_for_read_out_rows_is_bitwise_the_full_layer(w2):
+    """The last layer runs its attention and output projection only where a
+    final state is read out: nowhere in the prefill round, at the five branch
+    ends in the branch round.  The read-out rows keep the tiles, prefix chunks
+    and wave groups they have in the whole round, so the probabilities are
+    bitwise those of the full last layer (JEV_DEBUG_FULL_LAST_LAYER); the
+    launch records show which path ran."""
+    from shared_prefix_kv_amd import jev
+    wl, inst, g, ctx, _ = w2
+    br = inst.passes[0]
+    L = wl.model.n_layers
+    runs = {}
+    for flags in (0, jev.JEV_DEBUG_FULL_LAST_LAYER):
+        ctx.set_debug(flags)
+        ctx.profile(("attn", "oproj"))
+        (h,) = ctx.prefill_prefix([0], [inst.prefixes[0]])
+        probs, loff = ctx.score_branches([h] * 5, [b.tokens for b in br], [b.labels for b in br])
+        _sync()
+        recs = ctx.profile_read()
+        ctx.profile(())
+        ctx.free_pages([h])
+        runs[flags] = (probs.float().cpu().numpy().copy(), recs)
+    ctx.set_debug(0)
+    pruned, full = runs[0], runs[jev.JEV_DEBUG_FULL_LAST_LAYER]
+    assert np.array_equal(pruned[0], full[0])
+    check_branches("w2 last layer at read-out rows vs oracle", split_probs(torch.from_numpy(pruned[0]), loff),
+                   g["passes"][0]["probs"], stored_bars(g))
+    for kern in ("attn", "oproj"):
+        got = [(r["layer"], r["rows"]) for r in pruned[1] if r["kernel"] == kern]
+        want = [(l, 2000) for l in range(L - 1)] + [(l, 240) for l in range(L - 1)] + [(L - 1, 5)]
+        assert got == want, (kern, got)
+        got_full = [(r["layer"], r["rows"]) for r in full[1] if r["kernel"] == kern]
+        assert got_full == [(l, 2000) for l in range(L)] + [(l, 240) for l in range(L)], (kern, got_full)
+
+
 def test_w2_round_size_moves_a_branch_within_its_bar(w2):
     """Round-composition variance, measured: the same five branches scored in
     a round of their own (240 rows: split-K projections, 7 prefix chunks) and

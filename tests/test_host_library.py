@@ -196,9 +196,12 @@ def test_debug_flags_and_call_statistics_on_a_planning_only_context():
     ctx.set_debug(jev.JEV_DEBUG_POISON_FREED_PAGES | jev.JEV_DEBUG_TIME_CALLS)
     assert ctx.stats()["debug_flags"] == 3
     with pytest.raises(jev.JevError) as e:
-        ctx.set_debug(4)
+        ctx.set_debug(8)
     assert e.value.code == jev.JEV_EINVAL
     assert ctx.stats()["debug_flags"] == 3  # a refused call changes nothing
+    ctx.set_debug(jev.JEV_DEBUG_FULL_LAST_LAYER)
+    assert ctx.stats()["debug_flags"] == 4
+    ctx.set_debug(jev.JEV_DEBUG_POISON_FREED_PAGES | jev.JEV_DEBUG_TIME_CALLS)
     # tree work runs on a planning-only context, with no device work: poisoning
     # and timing have nothing to do, and no call is recorded as timed
     (h,) = ctx.prefill_prefix([0], [inst.prefixes[0]])
