@@ -138,7 +138,7 @@ def kernel_fractions(per_key: dict, dtype: str, n_steps: int) -> dict:
         kind = key.split("[")[0]
         rows = int(key.split("[")[1].split()[0])
         e = {"launches_per_step": n // n_steps, "avg_us": round(1e3 * ms / n, 2)}
-        if flops > 0 and not (kind in ("qkv", "oproj") and rows <= 256):
+        if flops > 0 and not (kind in ("qkv", "qkv_kv", "oproj") and rows <= 256):
             ach = flops / (ms * 1e-3) / 1e12
             e.update({"bound": "mfma", "achieved": round(ach, 1), "unit": "TFLOP/s", "frac": round(ach / peak, 4)})
         elif nbytes > 0:
@@ -149,8 +149,17 @@ def kernel_fractions(per_key: dict, dtype: str, n_steps: int) -> dict:
 
 
 def launch_key(rec) -> str:
-    """Launches of one kind over the same number of rows run the same kernel instance."""
-    return f"{rec['kernel']}[{rec['rows']} rows]"
+    """Launches of one kind over the same number of rows run the same kernel
+    instance; the K/V-only projection of a last layer without read-outs is
+    keyed apart (its FLOPs per row are those of 2 * kv_heads * head_dim
+    columns, below the full projection's)."""
+    kind = rec["kernel"]
+    if kind == "qkv" and rec["rows"] > 0 and _QKV_ROW_FLOPS and rec["flops"] < 0.999 * _QKV_ROW_FLOPS * rec["rows"]:
+        kind = "qkv_kv"
+    return f"{kind}[{rec['rows']} rows]"
+
+
+_QKV_ROW_FLOPS = 0.0  # FLOPs per row of the full QKV projection (set by main)
 
 
 def kernel_sources_sha() -> str:
@@ -283,8 +292,9 @@ def summarize(d: str) -> int:
 # Kernel instances that make up one launch of each timed kind on the headline
 # workload (the split-K GEMMs of the branch round include their epilogue).
 TRAFFIC_LAUNCHES = {
-    "qkv[2000 rows]": ["gemm_pc_kernel<160, 0>"],
-    "oproj[2000 rows]": ["gemm_pc_kernel<128, 1>"],
+    "qkv[2000 rows]": ["gemm_pc_kernel<256, 160, 0>"],
+    "qkv_kv[2000 rows]": ["gemm_pc_kernel<128, 64, 0>"],
+    "oproj[2000 rows]": ["gemm_pc_kernel<256, 128, 1>"],
     "attn[2000 rows]": ["attn_kernel<bf16s, 128, 2>"],
     "attn[240 rows]": ["attn_kernel<bf16s, 128, 1>"],
     "merge[240 rows]": ["merge_kernel<bf16s, 128>"],
@@ -536,6 +546,8 @@ def main(argv=None) -> int:
         print("bench.py times the prefix + branches workloads", file=sys.stderr)
         return 2
     m = wl.model
+    global _QKV_ROW_FLOPS
+    _QKV_ROW_FLOPS = 2.0 * m.d * (m.hq + 2 * m.hkv) * m.dh
     inst = make_instance(wl)
     weights = make_weights(wl)
     wdev = jev.upload_weights(weights)

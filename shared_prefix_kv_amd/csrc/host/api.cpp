@@ -858,11 +858,14 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
         HIPCHK(timed(JEV_K_RMSNORM, l, rd.T, 0, (2 * T + 1) * D * E,
                      [&] { return jev::launch_rmsnorm(m, x, w.norm, rd.T, h, s); }));
       h_ready = false;
-      HIPCHK(timed(JEV_K_QKV, l, rd.T, 2 * T * NQKV * D, (T * D + NQKV * D + T * NQKV) * E, [&] {
-        return jev::launch_qkv(m, w, l, h, rd.T, dd + rd.off_pos, dd + rd.off_slot, rope, q, ctx->pool, gws, s);
-      }));
       // last layer without read-outs: its K/V pages are all that is needed
-      if (l + 1 == m.n_layers && rd.last_mode == LAST_NONE) break;
+      const bool kv_only = l + 1 == m.n_layers && rd.last_mode == LAST_NONE;
+      const double NP = kv_only ? double(2 * m.hkv) * m.dh : NQKV;
+      HIPCHK(timed(JEV_K_QKV, l, rd.T, 2 * T * NP * D, (T * D + NP * D + T * NP) * E, [&] {
+        return jev::launch_qkv(m, w, l, h, rd.T, dd + rd.off_pos, dd + rd.off_slot, rope, q, ctx->pool, gws, s,
+                               kv_only);
+      }));
+      if (kv_only) break;
       if (l + 1 == m.n_layers && rd.last_mode == LAST_READ_ROWS) {
         // the read-out rows alone: their queries gathered behind their
         // outputs (o rows [R, 2R) and [0, R)), the output projection's

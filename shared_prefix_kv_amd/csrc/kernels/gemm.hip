@@ -718,24 +718,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // starts, then waits for stage k + 1 and joins the stage barrier.  Same
 // tile, LDS layout, k order and epilogue (run by all eight waves): results
 // are bitwise those of gemm_dl_kernel.  Measured 4% faster on the QKV GEMM
-// at 2,000 rows (81 vs 84.4 us in the bench).
-template <int BN, int EPI>
+// at 2,000 rows (81 vs 84.4 us in the bench).  BM = 128 (MFMA waves of 32
+// rows) makes twice the tiles for narrow products; every output element still
+// accumulates its K in the same order, so the values do not depend on BM.
+template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_pc_kernel(
     const bf16s* __restrict__ A, int M, int K, int N, ColMap cm, QkvOut qo, ResOut ro) {
   using T = bf16s;
   using MF = Mfma<T>;
   using frag = typename MF::frag;
-  constexpr int BM = 256, NW = 4, NTH = 512;
+  constexpr int NW = 4, NTH = 512;
   constexpr int CH = 8, BK = 64, KS = BK / MF::KSTEP;
   constexpr int NSTG = 3;
-  constexpr int NRB = 2, TN = BN / 32;
+  constexpr int NRB = BM / 128, TN = BN / 32;
   constexpr int NL = (BM + BN) / 8;
   constexpr int LPW = NL / NW;             // loads per loader wave per stage
   constexpr int STAGE = (BM + BN) * 8;
   constexpr int LDS_MAIN = NSTG * STAGE;
   constexpr int LDS_EPI = 128 * (BN + 4) / 4;
   constexpr int LDS_UNITS = LDS_MAIN > LDS_EPI ? LDS_MAIN : LDS_EPI;
-  static_assert(KS == 4 && BN % 32 == 0 && NL % NW == 0, "tile");
+  static_assert(KS == 4 && BN % 32 == 0 && NL % NW == 0 && (BM == 128 || BM == 256), "tile");
   static_assert(LDS_UNITS * 16 <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(16))) u32x4 smem[LDS_UNITS];
 
@@ -743,7 +745,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 7;
   const int w4 = wave & 3;
   const int c = lane & 31, hh = lane >> 5;
-  const int rowA0 = 64 * w4;
+  const int rowA0 = (BM / 4) * w4;
   int mt, nt;
   xcd_tile(blockIdx.x, gridDim.x, (M + BM - 1) / BM, &mt, &nt);
   const int m0 = mt * BM, n0 = nt * BN;
@@ -832,7 +834,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int LD = BN + 4;
   vm_lds_barrier<0>();  // every load and read of the main loop done
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
+  for (int half = 0; half < BM / 128; ++half) {
     if (wave < NW && rowA0 / 128 == half) {
 #pragma unroll
       for (int i = 0; i < NRB; ++i)
@@ -920,6 +922,23 @@ hipError_t gemm_dispatch(const ModelDims& m, const GemmWs& ws, const void* A, in
     return hipGetLastError();
   }
   const int mt = (M + 255) / 256;
+  if constexpr (sizeof(T) == 2) {
+    // narrow products (the K/V projection alone): 256-row tiles would leave
+    // most CUs idle; 128-row tiles, and 64 columns if that is still too few
+    const int t128 = mt * (N / 128);
+    if (N % 128 == 0 && t128 < 192 && K % 64 == 0 && g_gemm_tuning.large == 0) {
+      const int mt2 = (M + 127) / 128;
+      dim3 grid2;
+      if (mt2 * (N / 128) >= 192 || N % 64) {
+        grid2 = dim3(mt2 * (N / 128));
+        JEV_LAUNCH((dev::gemm_pc_kernel<128, 128, EPI>), grid2, dim3(512), 0, s, a, M, K, N, cm, qo, ro);
+      } else {
+        grid2 = dim3(mt2 * (N / 64));
+        JEV_LAUNCH((dev::gemm_pc_kernel<128, 64, EPI>), grid2, dim3(512), 0, s, a, M, K, N, cm, qo, ro);
+      }
+      return hipGetLastError();
+    }
+  }
   // tile width: 160 when it divides N and fills the CUs better than 128
   int bn = 128;
   if (N % 160 == 0) {
@@ -936,9 +955,9 @@ hipError_t gemm_dispatch(const ModelDims& m, const GemmWs& ws, const void* A, in
     const int kind = g_gemm_tuning.large == 0 ? 4 : g_gemm_tuning.large;
     if (kind == 4 && K % 64 == 0) {
       if (bn == 160)
-        JEV_LAUNCH((dev::gemm_pc_kernel<160, EPI>), grid, dim3(512), 0, s, a, M, K, N, cm, qo, ro);
+        JEV_LAUNCH((dev::gemm_pc_kernel<256, 160, EPI>), grid, dim3(512), 0, s, a, M, K, N, cm, qo, ro);
       else
-        JEV_LAUNCH((dev::gemm_pc_kernel<128, EPI>), grid, dim3(512), 0, s, a, M, K, N, cm, qo, ro);
+        JEV_LAUNCH((dev::gemm_pc_kernel<256, 128, EPI>), grid, dim3(512), 0, s, a, M, K, N, cm, qo, ro);
       return hipGetLastError();
     }
     if (kind >= 2 && K % 64 == 0) {
@@ -967,10 +986,12 @@ hipError_t gemm_dispatch(const ModelDims& m, const GemmWs& ws, const void* A, in
 
 hipError_t launch_qkv(const ModelDims& m, const LayerW& w, int32_t layer, const void* h, int32_t T_,
                       const int32_t* pos, const int32_t* kvslot, const float* rope, void* qbuf, void* pool,
-                      const GemmWs& ws, hipStream_t s) {
+                      const GemmWs& ws, hipStream_t s, bool kv_only) {
   if (T_ <= 0) return hipSuccess;
-  const int N = (m.hq + 2 * m.hkv) * m.dh;
-  dev::ColMap cm{w.wq, w.wk, w.wv, m.hq, m.hkv, m.dh, (m.hq + m.hkv) * m.dh / 2};
+  // K/V only: the same column layout without the query heads (no q written)
+  const int hq = kv_only ? 0 : m.hq;
+  const int N = (hq + 2 * m.hkv) * m.dh;
+  dev::ColMap cm{w.wq, w.wk, w.wv, hq, m.hkv, m.dh, (hq + m.hkv) * m.dh / 2};
   const size_t elt = m.dtype == 1 ? 2 : 4;
   dev::QkvOut qo{pos, kvslot, reinterpret_cast<const float2*>(rope), qbuf,
                  reinterpret_cast<char*>(pool) + (size_t)layer * m.n_pages * m.hkv * 2 * 16 * m.dh * elt,

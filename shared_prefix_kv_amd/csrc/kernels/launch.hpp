@@ -95,9 +95,11 @@ hipError_t launch_rmsnorm(const ModelDims& m, const void* x, const void* g, int3
                           hipStream_t s);
 // q/k/v projections of h with RoPE at pos[t]; q -> qbuf [T][Hq][dh]; k, v -> the
 // layer's pages at kvslot[t] = page*16 + slot.  rope: float2 [pos][dh/2].
+// kv_only: k and v alone (q is not written), each element summed in the
+// order of the full projection.
 hipError_t launch_qkv(const ModelDims& m, const LayerW& w, int32_t layer, const void* h, int32_t T,
                       const int32_t* pos, const int32_t* kvslot, const float* rope, void* qbuf,
-                      void* pool, const GemmWs& ws, hipStream_t s);
+                      void* pool, const GemmWs& ws, hipStream_t s, bool kv_only = false);
 // x = E[tok], then h = RMSNorm(x) * g (the first layer's norm), with the same
 // arithmetic as launch_rmsnorm on the gathered rows.
 hipError_t launch_embed_norm(const ModelDims& m, const void* embed, const int32_t* tok, int32_t T, const void* g,

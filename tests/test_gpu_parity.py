@@ -655,7 +655,7 @@ def test_w2_last_layer_for_read_out_rows_is_bitwise_the_full_layer(w2):
     runs = {}
     for flags in (0, jev.JEV_DEBUG_FULL_LAST_LAYER):
         ctx.set_debug(flags)
-        ctx.profile(("attn", "oproj"))
+        ctx.profile(("qkv", "attn", "oproj"))
         (h,) = ctx.prefill_prefix([0], [inst.prefixes[0]])
         probs, loff = ctx.score_branches([h] * 5, [b.tokens for b in br], [b.labels for b in br])
         _sync()
@@ -674,6 +674,12 @@ def test_w2_last_layer_for_read_out_rows_is_bitwise_the_full_layer(w2):
         assert got == want, (kern, got)
         got_full = [(r["layer"], r["rows"]) for r in full[1] if r["kernel"] == kern]
         assert got_full == [(l, 2000) for l in range(L)] + [(l, 240) for l in range(L)], (kern, got_full)
+    # the prefill's last projection writes K/V alone (the branch round's last
+    # one still needs the read-out rows' queries)
+    md = wl.model
+    row_flops = [r["flops"] / r["rows"] for r in pruned[1] if r["kernel"] == "qkv"]
+    full_row, kv_row = 2.0 * md.d * (md.hq + 2 * md.hkv) * md.dh, 2.0 * md.d * 2 * md.hkv * md.dh
+    assert row_flops == [full_row] * (L - 1) + [kv_row] + [full_row] * L, row_flops
 
 
 def test_w2_round_size_moves_a_branch_within_its_bar(w2):
