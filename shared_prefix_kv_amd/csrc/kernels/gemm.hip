@@ -263,12 +263,18 @@ __device__ __forceinline__ void xcd_tile(int b, int n_blocks, int m_tiles, int* 
 // blockIdx.y selects a slice of K and the fp32 partial tile is stored to its
 // own [256][N] scratch slice; split_epilogue (next launch) sums the slices and
 // runs the epilogue.
-template <typename T, int BN, int EPI, bool SPLIT, int WM, int WN>
+//
+// BM_ = 64 (split K only): the same K slices, stages, k-steps and MFMA shape
+// on a 64-row tile, for rounds of at most 64 rows; every output element is
+// summed in the same order as on the 256-row tile, so the partial slices are
+// bitwise those of the 256-row kernel.
+template <typename T, int BN, int EPI, bool SPLIT, int WM, int WN, int BM_ = 256>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_kernel(const T* __restrict__ A, int M, int K, int N, ColMap cm,
                                                    QkvOut qo, ResOut ro, float* __restrict__ scratch) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
-  constexpr int BM = 256;
+  constexpr int BM = BM_;
+  static_assert(BM == 256 || SPLIT, "row tiles below 256 rows are split-K only");
   constexpr int CH = 16 / sizeof(T);   // elements per 16-byte chunk
   constexpr int BK = 8 * CH;           // 128 bytes of K per stage
   constexpr int KS = BK / MF::KSTEP;   // MFMA k-steps per stage
@@ -484,7 +490,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WM
 #undef G_GROUPS
 
   if constexpr (SPLIT) {
-    float* part = scratch + (size_t)blockIdx.y * BM * N;
+    float* part = scratch + (size_t)blockIdx.y * kSplitRows * N;
 #pragma unroll
     for (int i = 0; i < NRB; ++i)
 #pragma unroll
@@ -913,8 +919,12 @@ hipError_t gemm_dispatch(const ModelDims& m, const GemmWs& ws, const void* A, in
     const int tiles = N / BN;
     const int S = split_count(tiles, K, int(sizeof(T)));
     if ((size_t)S * 256 * N > ws.partial_elems) return hipErrorInvalidValue;
-    JEV_LAUNCH((dev::gemm_kernel<T, BN, EPI, true, 4, 2>), dim3(tiles, S), dim3(512), 0, s, a, M, K, N, cm,
-                       qo, ro, ws.partial);
+    if (M <= 64)
+      JEV_LAUNCH((dev::gemm_kernel<T, BN, EPI, true, 1, 4, 64>), dim3(tiles, S), dim3(256), 0, s, a, M, K, N, cm,
+                 qo, ro, ws.partial);
+    else
+      JEV_LAUNCH((dev::gemm_kernel<T, BN, EPI, true, 4, 2>), dim3(tiles, S), dim3(512), 0, s, a, M, K, N, cm,
+                 qo, ro, ws.partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     JEV_LAUNCH((dev::split_epilogue<T, EPI>), dim3(tiles, (M + 15) / 16), dim3(256), 0, s, ws.partial, S, M,
@@ -1012,9 +1022,15 @@ hipError_t launch_oproj_split(const ModelDims& m, const LayerW& w, const void* o
   const int S = split_count(tiles, K, m.dtype == 1 ? 2 : 4);
   if ((size_t)S * 256 * N > ws.partial_elems) return hipErrorInvalidValue;
   *splits = S;
-  if (m.dtype == 1)
+  if (m.dtype == 1 && T_ <= 64)
+    JEV_LAUNCH((dev::gemm_kernel<bf16s, BN, dev::EPI_RES, true, 1, 4, 64>), dim3(tiles, S), dim3(256), 0, s,
+               reinterpret_cast<const bf16s*>(o), T_, K, N, cm, dev::QkvOut{}, dev::ResOut{}, ws.partial);
+  else if (m.dtype == 1)
     JEV_LAUNCH((dev::gemm_kernel<bf16s, BN, dev::EPI_RES, true, 4, 2>), dim3(tiles, S), dim3(512), 0, s,
                reinterpret_cast<const bf16s*>(o), T_, K, N, cm, dev::QkvOut{}, dev::ResOut{}, ws.partial);
+  else if (T_ <= 64)
+    JEV_LAUNCH((dev::gemm_kernel<float, BN, dev::EPI_RES, true, 1, 4, 64>), dim3(tiles, S), dim3(256), 0, s,
+               reinterpret_cast<const float*>(o), T_, K, N, cm, dev::QkvOut{}, dev::ResOut{}, ws.partial);
   else
     JEV_LAUNCH((dev::gemm_kernel<float, BN, dev::EPI_RES, true, 4, 2>), dim3(tiles, S), dim3(512), 0, s,
                reinterpret_cast<const float*>(o), T_, K, N, cm, dev::QkvOut{}, dev::ResOut{}, ws.partial);
