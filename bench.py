@@ -289,17 +289,22 @@ def summarize(d: str) -> int:
     return 0
 
 
-# Kernel instances that make up one launch of each timed kind on the headline
-# workload (the split-K GEMMs of the branch round include their epilogue).
+# Kernel instances (name, rocprofv3 counter-run grid size: threads over all
+# grid dimensions) that make up one
+# launch of each timed kind on the headline workload (the split-K GEMMs of the
+# branch round include their epilogue).
 TRAFFIC_LAUNCHES = {
-    "qkv[2000 rows]": ["gemm_pc_kernel<256, 160, 0>"],
-    "qkv_kv[2000 rows]": ["gemm_pc_kernel<128, 64, 0>"],
-    "oproj[2000 rows]": ["gemm_pc_kernel<256, 128, 1>"],
-    "attn[2000 rows]": ["attn_kernel<bf16s, 128, 2>"],
-    "attn[240 rows]": ["attn_kernel<bf16s, 128, 1>"],
-    "merge[240 rows]": ["merge_kernel<bf16s, 128>"],
-    "qkv[240 rows]": ["gemm_kernel<bf16s, 128, 0, true, 4, 2>", "split_epilogue<bf16s, 0>"],
-    "oproj[240 rows]": ["gemm_kernel<bf16s, 128, 1, true, 4, 2>", "split_res_norm_kernel<bf16s>"],
+    "qkv[2000 rows]": [("gemm_pc_kernel<256, 160, 0>", 131072)],
+    "qkv_kv[2000 rows]": [("gemm_pc_kernel<128, 64, 0>", 131072)],
+    "oproj[2000 rows]": [("gemm_pc_kernel<256, 128, 1>", 131072)],
+    "attn[2000 rows]": [("attn_kernel<bf16s, 128, 2>", 256000)],
+    "attn[240 rows]": [("attn_kernel<bf16s, 128, 1>", 122880)],
+    "merge[240 rows]": [("merge_kernel<bf16s, 128>", 245760)],
+    "qkv[240 rows]": [("gemm_kernel<bf16s, 128, 0, true, 4, 2, 256>", 122880), ("split_epilogue<bf16s, 0>", 153600)],
+    "oproj[240 rows]": [("gemm_kernel<bf16s, 128, 1, true, 4, 2, 256>", 98304),
+                        ("split_res_norm_kernel<bf16s>", 61440)],
+    "attn[5 rows]": [("attn_kernel<bf16s, 128, 1>", 12288)],
+    "oproj[5 rows]": [("gemm_kernel<bf16s, 128, 1, true, 1, 4, 64>", 49152), ("split_epilogue<bf16s, 1>", 8192)],
 }
 
 
@@ -330,10 +335,10 @@ def write_traffic(fetch_dir: str, write_dir: str, copy_mib: int = 1024) -> int:
     nbytes = copy_mib << 20
     copy_grid = nbytes // 8192  # the runtime's copy kernel: 8 KiB per workgroup of the 1 GiB copy
 
-    def per_kernel(m, name):
-        vals = [v for (kn, g), v in m.items() if kn == name]
+    def per_kernel(m, name, grid):
+        vals = [v for (kn, g), v in m.items() if kn == name and g == grid]
         if len(vals) != 1:
-            raise SystemExit(f"{name}: {len(vals)} instances in the counter run")
+            raise SystemExit(f"{name} (grid {grid}): {len(vals)} instances in the counter run")
         return vals[0]
 
     copy_f = [v for (kn, g), v in fetch.items() if kn == "__amd_rocclr_copyBuffer" and g == copy_grid]
@@ -348,8 +353,8 @@ def write_traffic(fetch_dir: str, write_dir: str, copy_mib: int = 1024) -> int:
                     "write_kib": round(copy_w[0], 1)},
            "kernels": {}}
     for key, names in TRAFFIC_LAUNCHES.items():
-        out["kernels"][key] = {"fetch_kib": round(sum(per_kernel(fetch, n) for n in names), 1),
-                               "write_kib": round(sum(per_kernel(write, n) for n in names), 1),
+        out["kernels"][key] = {"fetch_kib": round(sum(per_kernel(fetch, n, g) for n, g in names), 1),
+                               "write_kib": round(sum(per_kernel(write, n, g) for n, g in names), 1),
                                "kernel_sources_sha256": sha}
     path = os.path.join(ROOT, "profiles", "traffic.json")
     with open(path, "w") as f:
