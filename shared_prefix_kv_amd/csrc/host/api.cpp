@@ -193,8 +193,9 @@ struct jev_ctx {
   WsLayout L{};
   char* ws = nullptr;
   char* static_scratch = nullptr;  // this device's copy of the file-scope scratch array
-  int32_t* desc_host = nullptr;  // pinned staging
-  hipEvent_t desc_copied = nullptr;
+  int32_t* desc_host = nullptr;      // pinned staging of a call's descriptors
+  int32_t* desc_host_dev = nullptr;  // its device-side address
+  hipEvent_t desc_copied = nullptr;  // the call's first kernel has copied them up
   hipEvent_t last_done = nullptr;
   bool have_last = false;
   hipStream_t last_stream = nullptr;
@@ -787,8 +788,16 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
   if (timed_call) HIPCHK(hipEventRecord(ctx->round_ev[0], s));
   std::memcpy(ctx->desc_host, hb.data(), hb.size() * sizeof(int32_t));
   int32_t* dd = reinterpret_cast<int32_t*>(ctx->ws + ctx->L.desc);
-  HIPCHK(hipMemcpyAsync(dd, ctx->desc_host, hb.size() * sizeof(int32_t), hipMemcpyHostToDevice, s));
-  HIPCHK(hipEventRecord(ctx->desc_copied, s));
+  // No separate copy (a host-to-device copy on the stream left the GPU idle
+  // for ~15 us per call): the first round's embedding kernel reads its tokens
+  // from the pinned staging buffer and copies the descriptors up, in 16-byte
+  // units (the buffers hold a multiple of 16 bytes), for the kernels after it.
+  const int64_t up_bytes = (int64_t(hb.size()) * int64_t(sizeof(int32_t)) + 15) / 16 * 16;
+  const bool upload = !rds.empty() && rds[0].T > 0;
+  if (!upload) {
+    HIPCHK(hipMemcpyAsync(dd, ctx->desc_host, hb.size() * sizeof(int32_t), hipMemcpyHostToDevice, s));
+    HIPCHK(hipEventRecord(ctx->desc_copied, s));
+  }
   const jev::ModelDims& m = ctx->dims;
   void* x = ctx->ws + ctx->L.x;
   void* h = ctx->ws + ctx->L.h;
@@ -844,12 +853,16 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
   for (const RoundDesc& rd : rds) {
     for (int64_t t = 0; t < rd.T; ++t) ctx->call_written.push_back(hb[size_t(rd.off_slot + t)] >> 4);
     ctx->round_reads.push_back(rd.n_read > 0);
-    const int32_t* tok = dd + rd.off_tok;
+    const bool first = upload && &rd == &rds[0];
+    const int32_t* tok = (first ? ctx->desc_host_dev : dd) + rd.off_tok;
     const double T = rd.T;
     // the embedding gather also writes layer 0's normalised input
     HIPCHK(timed(JEV_K_EMBED, -1, rd.T, 0, 3 * T * D * E + 4 * T, [&] {
-      return jev::launch_embed_norm(m, ctx->embed, tok, rd.T, ctx->layers[0].norm, x, h, s);
+      return jev::launch_embed_norm(m, ctx->embed, tok, rd.T, ctx->layers[0].norm, x, h, s,
+                                    first ? ctx->desc_host_dev : nullptr, first ? dd : nullptr,
+                                    first ? up_bytes : 0);
     }));
+    if (first) HIPCHK(hipEventRecord(ctx->desc_copied, s));
     bool h_ready = true;  // h of this layer already written (by the gather or the previous projection)
     for (int l = 0; l < m.n_layers; ++l) {
       const jev::LayerW& w = ctx->layers[l];
@@ -1020,6 +1033,7 @@ int jev_create(const jev_model_desc* desc, const jev_weights* weights, void* kv_
     if (int rc = device_scratch(&ctx->static_scratch)) return rc;
     HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&ctx->desc_host), size_t(ctx->L.desc_ints) * sizeof(int32_t),
                          hipHostMallocDefault));
+    HIPCHK(hipHostGetDevicePointer(reinterpret_cast<void**>(&ctx->desc_host_dev), ctx->desc_host, 0));
     HIPCHK(hipEventCreateWithFlags(&ctx->desc_copied, hipEventDisableTiming));
     HIPCHK(hipEventCreateWithFlags(&ctx->last_done, hipEventDisableTiming));
     // RoPE table: angle = pos * theta^(-2i/dh) in double, stored as float (cos, sin)

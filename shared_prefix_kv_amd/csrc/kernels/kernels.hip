@@ -98,13 +98,23 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x, c
 // Embedding gather fused with layer 0's norm: one block per token; x = E[tok]
 // and h = RMSNorm(x) * g with rmsnorm_kernel's element and reduction order
 // (bitwise those of the two kernels).
+//
+// With up_units > 0 the workgroups also copy up_units 16-byte units from
+// up_src (the call's descriptors in pinned host memory, which tok then points
+// into) to up_dst in device memory, a share each, for the kernels that follow.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_norm_kernel(const T* __restrict__ E, const int32_t* __restrict__ tok,
                                                          int d, const T* __restrict__ g, float eps, T* __restrict__ x,
-                                                         T* __restrict__ h) {
+                                                         T* __restrict__ h, const u32x4* __restrict__ up_src,
+                                                         u32x4* __restrict__ up_dst, int up_units) {
   constexpr int CH = 16 / sizeof(T);
   constexpr int MAXV = 4;
   __shared__ float scratch[4];
+  if (up_units > 0) {
+    const int per = (up_units + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int u0 = (int)blockIdx.x * per, u1 = min(u0 + per, up_units);
+    for (int u = u0 + (int)threadIdx.x; u < u1; u += blockDim.x) up_dst[u] = up_src[u];
+  }
   const T* er = E + (size_t)tok[blockIdx.x] * d;
   T* xr = x + (size_t)blockIdx.x * d;
   T* hr = h + (size_t)blockIdx.x * d;
@@ -876,11 +886,15 @@ hipError_t launch_rmsnorm(const ModelDims& m, const void* x, const void* g, int3
 }
 
 hipError_t launch_embed_norm(const ModelDims& m, const void* embed, const int32_t* tok, int32_t T_, const void* g,
-                             void* x, void* h, hipStream_t s) {
+                             void* x, void* h, hipStream_t s, const void* up_src, void* up_dst, int64_t up_bytes) {
   if (T_ <= 0) return hipSuccess;
+  if (up_bytes < 0 || up_bytes % 16 || up_bytes / 16 > INT32_MAX || (up_bytes > 0 && (!up_src || !up_dst)))
+    return hipErrorInvalidValue;
   JEV_DISPATCH_T(m, {
     JEV_LAUNCH(dev::embed_norm_kernel<T>, dim3(T_), dim3(256), 0, s, reinterpret_cast<const T*>(embed), tok, m.d,
-               reinterpret_cast<const T*>(g), m.eps, reinterpret_cast<T*>(x), reinterpret_cast<T*>(h));
+               reinterpret_cast<const T*>(g), m.eps, reinterpret_cast<T*>(x), reinterpret_cast<T*>(h),
+               reinterpret_cast<const dev::u32x4*>(up_src), reinterpret_cast<dev::u32x4*>(up_dst),
+               int(up_bytes / 16));
   })
   return hipGetLastError();
 }

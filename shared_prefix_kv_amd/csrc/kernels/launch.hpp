@@ -101,9 +101,12 @@ hipError_t launch_qkv(const ModelDims& m, const LayerW& w, int32_t layer, const 
                       const int32_t* pos, const int32_t* kvslot, const float* rope, void* qbuf,
                       void* pool, const GemmWs& ws, hipStream_t s, bool kv_only = false);
 // x = E[tok], then h = RMSNorm(x) * g (the first layer's norm), with the same
-// arithmetic as launch_rmsnorm on the gathered rows.
+// arithmetic as launch_rmsnorm on the gathered rows.  With up_bytes > 0 (a
+// multiple of 16) the kernel also copies up_bytes from up_src (device-visible
+// pinned host memory) to up_dst, for the kernels launched after it.
 hipError_t launch_embed_norm(const ModelDims& m, const void* embed, const int32_t* tok, int32_t T, const void* g,
-                             void* x, void* h, hipStream_t s);
+                             void* x, void* h, hipStream_t s, const void* up_src = nullptr, void* up_dst = nullptr,
+                             int64_t up_bytes = 0);
 // Residual projection of a round of at most kSplitRows rows without its
 // epilogue: the split-K partial tiles go to ws.partial (slice y at
 // y * 256 * d), *splits receives their count.  launch_split_res_norm adds them.
