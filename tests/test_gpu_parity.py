@@ -745,6 +745,17 @@ def test_w3_staged_rounds_match_oracle(w2):
     probs3, loff3 = ctx.score_candidates(inst.candidates, inst.cand_labels)
     _sync()
     assert np.array_equal(probs3.cpu().numpy(), probs2.cpu().numpy())
+    # depth rounds with the full last layer in every round: the root round
+    # (800 rows, no read-out) and the middle round (120 rows, no read-out)
+    # write their last-layer K/V alone, the leaf round (240 rows) computes its
+    # read-out rows alone; every K/V element and read-out row is summed in the
+    # same order either way, so the probabilities are bitwise equal
+    ctx.set_plan_mode(jev.JEV_PLAN_DEPTH)
+    ctx.set_debug(jev.JEV_DEBUG_FULL_LAST_LAYER)
+    probs4, loff4 = ctx.score_candidates(inst.candidates, inst.cand_labels)
+    _sync()
+    ctx.set_debug(0)
+    assert np.array_equal(probs4.cpu().numpy(), probs.cpu().numpy())
 
 
 def test_w3_requests_through_the_continuous_batching_scheduler(w2):
@@ -797,6 +808,19 @@ def test_w4_batch_of_requests_matches_oracle():
     assert ctx.stats()["pages_in_use"] == 0
     for p in got:
         assert abs(float(np.sum(p)) - 1.0) < 1e-4 and len(p) == 64
+    # the full last layer: the branch round (8,192 rows) projects all rows
+    # without a K split and its 128 read-out rows alone with one, so the two
+    # runs are held to each other like two faithful orders of the oracle
+    from shared_prefix_kv_amd import jev
+    ctx.set_debug(jev.JEV_DEBUG_FULL_LAST_LAYER)
+    hs = ctx.prefill_prefix([0] * len(inst.prefixes), inst.prefixes)
+    probs2, loff2 = ctx.score_branches([hs[b.request] for b in br], [b.tokens for b in br],
+                                       [b.labels for b in br])
+    _sync()
+    ctx.free_pages(hs)
+    ctx.set_debug(0)
+    check_branches("w4 full last layer vs read-out rows alone", split_probs(probs2, loff2), got,
+                   stored_bars(g))
 
 
 # ------------------------------------------------------------------ workload 2 cut to one block
