@@ -215,11 +215,18 @@ __device__ __forceinline__ bf16x8 frag_zero<bf16s>() {
 template <>
 __device__ __forceinline__ float frag_zero<float>() { return 0.f; }
 
-// LDS V^T tile [DH][32 keys] for bf16: within each 16-key half the key quads
-// are stored in the order (0-3, 8-11, 4-7, 12-15), so that the 8 keys one lane
-// feeds to an MFMA (quads hh and hh+2 of the half) are 16 contiguous bytes; the
-// four 16-byte units of a 64-byte row are XOR-swizzled by (d >> 2) & 3, which
-// puts the 16 rows of a 16-lane read in 16 different bank groups.
+// Key order of the bf16 score product.  The score MFMA's output register r
+// of lane half hh holds row 8 (r / 4) + 4 hh + r % 4 of its A operand; lane c
+// loads K row key_of_row(c) there, so that register r holds key
+// 16 (r / 8) + 8 hh + r % 8: the 8 probabilities a lane feeds to one P.V MFMA
+// (keys 16 tt + 8 hh .. + 7) are then 8 consecutive keys of one page, 16
+// contiguous bytes of its V^T row.
+__device__ __forceinline__ int key_of_row(int c) {
+  return 16 * (c >> 4) + 8 * ((c >> 2) & 1) + 4 * ((c >> 3) & 1) + (c & 3);
+}
+// LDS V^T tile [DH][32 keys] for bf16: four 16-byte units per 64-byte row
+// (keys 8u .. 8u+7 in unit u), XOR-swizzled by (d >> 2) & 3, which puts the
+// 16 rows of a 16-lane read in 16 different bank groups.
 __device__ __forceinline__ int vq_unit(int d, int unit) { return d * 4 + (unit ^ ((d >> 2) & 3)); }
 // f32 (8 quads of 4 keys per 32-key row): plain 16-byte units swizzled by d.
 __device__ __forceinline__ int v_off(int d, int key) {
@@ -314,7 +321,8 @@ __global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     const int e = ks * KSTEP + KL * hh;
-    koff[ks] = c * DH + (((e / CH) ^ (c & (KCH - 1))) * CH) + e % CH;
+    const int kr = KL == 8 ? key_of_row(c) : c;  // the K row this lane feeds
+    koff[ks] = kr * DH + (((e / CH) ^ (kr & (KCH - 1))) * CH) + e % CH;
   }
   const int st_krow = tid / KCH, st_kch = tid % KCH;
   const int st_koff = st_krow * DH + ((st_kch ^ (st_krow & (KCH - 1))) * CH);  // + 16*DH*i for page i
@@ -368,14 +376,9 @@ __global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       if constexpr (CH == 8) {
-        // page i holds keys 16i..16i+15 = half i of the row; this chunk is
-        // quads 2*st_half and 2*st_half+1 of that half (stored order 0, 2, 1, 3)
-        u32x2* vrow = reinterpret_cast<u32x2*>(&sV[buf][0]);
-        const int q0 = 2 * st_half, q1 = q0 + 1;
-        const int pos0 = (q0 & 1) * 2 + (q0 >> 1), pos1 = (q1 & 1) * 2 + (q1 >> 1);  // quad slot 0..3 in the half
-        const int u0 = 2 * i + (pos0 >> 1), u1 = 2 * i + (pos1 >> 1);
-        vrow[vq_unit(st_d, u0) * 2 + (pos0 & 1)] = u32x2{rv[i].x, rv[i].y};
-        vrow[vq_unit(st_d, u1) * 2 + (pos1 & 1)] = u32x2{rv[i].z, rv[i].w};
+        // page i holds keys 16i..16i+15; this chunk is keys 16i + 8 st_half ..
+        // + 7 of V^T row st_d: unit 2i + st_half
+        reinterpret_cast<u32x4*>(&sV[buf][0])[vq_unit(st_d, 2 * i + st_half)] = rv[i];
       } else {
         *reinterpret_cast<u32x4*>(&sV[buf][v_off(st_d, 16 * i + st_half * CH)]) = rv[i];
       }
@@ -439,7 +442,7 @@ __global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2,
     if (mask) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = 8 * (r >> 2) + 4 * hh + (r & 3);
+        const int key = KL == 8 ? 16 * (r >> 3) + 8 * hh + (r & 7) : 8 * (r >> 2) + 4 * hh + (r & 3);
         const int pi = key >> 4, slot = key & 15;
         const bool ok = slot < (pi ? v1 : v0) && (!tile.causal || tile.kv_pos0 + 16 * (lp0 + pi) + slot <= qpos);
         S[r] = ok ? S[r] : kNegInf;
@@ -494,8 +497,8 @@ __global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2,
       }
     }
   };
-  // O^T += V^T P^T from V buffer buf; MFMA tt covers keys
-  // {8j + 4*hh + i : 4j + i in [tt*KL, tt*KL+KL)}
+  // O^T += V^T P^T from V buffer buf; MFMA tt covers keys 16tt + 8hh + i,
+  // i < 8 (bf16), or key 8 (tt / 4) + 4 hh + tt % 4 (f32)
   auto pv = [&](const int buf, const frag* pb, const frag* pl) __attribute__((always_inline)) {
 #pragma unroll
     for (int tt = 0; tt < 16 / KL; ++tt) {
@@ -504,8 +507,7 @@ __global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2,
       for (int b = 0; b < NDB; ++b) {
         const int d = 32 * b + c;
         if constexpr (KL == 8) {
-          // keys 16tt + {4hh..4hh+3, 8+4hh..8+4hh+3}: quads hh, hh+2 of half tt,
-          // stored at quad slots 2hh, 2hh+1 = unit 2tt + hh
+          // keys 16tt + 8hh .. 16tt + 8hh + 7 (page tt): unit 2tt + hh
           va[b] = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(&sV[buf][0])[vq_unit(d, 2 * tt + hh)]);
         } else {
           const int key = 8 * (tt >> 2) + 4 * hh + (tt & 3);
