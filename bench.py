@@ -289,6 +289,56 @@ def summarize(d: str) -> int:
     return 0
 
 
+def sq_summary(dirs) -> int:
+    """Instruction mix and MFMA occupancy per launch of the timed kinds, from
+    rocprofv3 --pmc passes (each a directory) that together hold SQ_WAVES,
+    SQ_INSTS_{VALU,MFMA,VALU_TRANS_F32,SALU,LDS,VMEM}, SQ_VALU_MFMA_BUSY_CYCLES,
+    SQ_VALU_MFMA_COEXEC_CYCLES and GRBM_GUI_ACTIVE.  Per wave: instructions
+    issued (VALU without the MFMAs).  MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES
+    (cycles summed over the SIMDs) / (GRBM_GUI_ACTIVE / XCDs x SIMDs), the
+    share of the kernel's cycles in which an average SIMD's matrix unit
+    worked.  Co-issue: SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES."""
+    import csv
+    import glob
+
+    def short(name: str) -> str:
+        return name.split("(")[0].replace("void ", "").replace("jev::dev::", "")
+
+    vals, agent = {}, {}
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    k = (short(r["Kernel_Name"]), int(r.get("Grid_Size", 0) or 0))
+                    a = vals.setdefault(k, {}).setdefault(r["Counter_Name"], [0, 0.0])
+                    a[0] += 1
+                    a[1] += float(r["Counter_Value"])
+        for path in glob.glob(os.path.join(d, "**", "*agent_info.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if r.get("Name", "").startswith("gfx"):
+                        agent = r
+    simds, xcc = int(agent.get("Simd_Count", 1024)), int(agent.get("Num_Xcc", 8))
+    print("| launch | kernel | waves | VALU / wave | MFMA / wave | exp / wave | SALU / wave | LDS / wave | "
+          "VMEM / wave | MFMA busy | VALU co-issued with MFMA |")
+    print("|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|")
+    for key, parts in TRAFFIC_LAUNCHES.items():
+        name, grid = parts[0]
+        c = {n: v / k for n, (k, v) in vals.get((name, grid), {}).items()}
+        if "SQ_WAVES" not in c:
+            continue
+        w = c["SQ_WAVES"]
+        mf = c.get("SQ_INSTS_MFMA", 0.0)
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / xcc
+        occ = f"{busy / (cyc * simds):.1%}" if cyc else "—"
+        co = f"{c.get('SQ_VALU_MFMA_COEXEC_CYCLES', 0.0) / busy:.1%}" if busy else "—"
+        print(f"| `{key}` | `{name}` | {w:.0f} | {(c.get('SQ_INSTS_VALU', 0.0) - mf) / w:.0f} | {mf / w:.0f} | "
+              f"{c.get('SQ_INSTS_VALU_TRANS_F32', 0.0) / w:.0f} | {c.get('SQ_INSTS_SALU', 0.0) / w:.0f} | "
+              f"{c.get('SQ_INSTS_LDS', 0.0) / w:.0f} | {c.get('SQ_INSTS_VMEM', 0.0) / w:.0f} | {occ} | {co} |")
+    return 0
+
+
 # Kernel instances (name, rocprofv3 counter-run grid size: threads over all
 # grid dimensions) that make up one
 # launch of each timed kind on the headline workload (the split-K GEMMs of the
@@ -529,6 +579,8 @@ def main(argv=None) -> int:
                     help="print a summary of the rocprofv3 CSV output under DIR and exit")
     ap.add_argument("--library-gemms", action="store_true",
                     help="add torch.matmul times of the projection shapes ('library_gemm', context only)")
+    ap.add_argument("--sq-summary", nargs="+", metavar="DIR", default=None,
+                    help="instruction mix and MFMA occupancy from rocprofv3 --pmc SQ counter passes")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
                     help="write profiles/traffic.json from a FETCH_SIZE and a WRITE_SIZE rocprofv3 run and exit")
     args = ap.parse_args(argv)
@@ -536,6 +588,8 @@ def main(argv=None) -> int:
         return summarize(args.summarize)
     if args.write_traffic:
         return write_traffic(*args.write_traffic)
+    if args.sq_summary:
+        return sq_summary(args.sq_summary)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU sharding of this path is "
               f"a design note, not built", file=sys.stderr)
