@@ -880,18 +880,15 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
       }));
       if (kv_only) break;
       if (l + 1 == m.n_layers && rd.last_mode == LAST_READ_ROWS) {
-        // the read-out rows alone: their queries gathered behind their
-        // outputs (o rows [R, 2R) and [0, R)), the output projection's
-        // residual written back to their rows of x
+        // the read-out rows alone: attention of their queries (rows of q
+        // named by the compact row list) into o rows [0, R), the output
+        // projection's residual written back to their rows of x
         const int32_t* rows = dd + rd.ll_off_rows;
         const double R = rd.ll_R;
-        const size_t qrow = size_t(m.hq) * m.dh * elt;
-        void* qc = ctx->ws + ctx->L.o + size_t(rd.ll_R) * qrow;
-        HIPCHK(jev::launch_gather_rows(q, rows, rd.ll_R, int32_t(qrow), qc, s));
         HIPCHK(timed(JEV_K_ATTN, l, rd.ll_R, 4.0 * m.dh * rd.ll_attn_pairs, 0, [&] {
           return jev::launch_attention(m, l, reinterpret_cast<const jev::AttnTile*>(dd + rd.ll_off_tiles),
-                                       rd.ll_n_tiles, dd + rd.off_plist, dd + rd.ll_off_pos, qc, ctx->pool, o,
-                                       part_o, part_lse, rd.attn_groups, s);
+                                       rd.ll_n_tiles, dd + rd.off_plist, dd + rd.ll_off_pos, q, ctx->pool, o,
+                                       part_o, part_lse, rd.attn_groups, s, rows);
         }));
         if (rd.ll_n_merge > 0)
           HIPCHK(timed(JEV_K_MERGE, l, rd.ll_n_merge, 0, 0, [&] {

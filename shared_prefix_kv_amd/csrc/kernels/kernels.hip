@@ -248,7 +248,8 @@ __global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2,
                                                    const int32_t* __restrict__ tok_pos, const T* __restrict__ q,
                                                    const T* __restrict__ pool, T* __restrict__ o,
                                                    float* __restrict__ part_o, float* __restrict__ part_lse,
-                                                   int hq, int hkv, size_t layer_base, float scale_log2) {
+                                                   int hq, int hkv, size_t layer_base, float scale_log2,
+                                                   const int32_t* __restrict__ qrows) {
   using MF = Mfma<T>;
   using frag = typename MF::frag;
   constexpr int KL = MF::KL, KSTEP = MF::KSTEP;
@@ -298,7 +299,8 @@ __global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2,
 
   frag qf[NKS];
   {
-    const T* qrow = q + ((size_t)t * hq + qhead) * DH;
+    // query row t of the launch is row qrows[t] of q (qrows null: row t)
+    const T* qrow = q + ((size_t)(qrows ? qrows[t] : t) * hq + qhead) * DH;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = row_ok ? MF::load(qrow + ks * KSTEP + KL * hh) : frag_zero<T>();
   }
@@ -853,15 +855,6 @@ __global__ __launch_bounds__(256) void poison_pages_kernel(u32x4* __restrict__ p
   }
 }
 
-// ------------------------------------------------------------------ row gather
-// dst row r = src row rows[r]; one workgroup per row, 16-byte units.
-__global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restrict__ src,
-                                                          const int32_t* __restrict__ rows, int32_t units,
-                                                          u32x4* __restrict__ dst) {
-  const size_t from = (size_t)rows[blockIdx.x] * units, to = (size_t)blockIdx.x * units;
-  for (int u = threadIdx.x; u < units; u += blockDim.x) dst[to + u] = src[from + u];
-}
-
 }  // namespace dev
 
 thread_local LaunchTiming g_launch_timing{nullptr, nullptr};
@@ -914,7 +907,8 @@ hipError_t launch_split_res_norm(const ModelDims& m, const float* partial, int32
 
 hipError_t launch_attention(const ModelDims& m, int32_t layer, const AttnTile* tiles, int32_t n_tiles,
                             const int32_t* page_list, const int32_t* tok_pos, const void* qbuf, const void* pool,
-                            void* o, float* part_o, float* part_lse, int32_t groups, hipStream_t s) {
+                            void* o, float* part_o, float* part_lse, int32_t groups, hipStream_t s,
+                            const int32_t* qrows) {
   if (n_tiles <= 0) return hipSuccess;
   if (groups != 1 && groups != 2) return hipErrorInvalidValue;
   const size_t layer_base = (size_t)layer * m.n_pages * m.hkv * 2 * 16 * m.dh;
@@ -924,7 +918,7 @@ hipError_t launch_attention(const ModelDims& m, int32_t layer, const AttnTile* t
 #define JEV_ATTN(T_, DH_, G_)                                                                              \
   JEV_LAUNCH((dev::attn_kernel<T_, DH_, G_>), grid, block, 0, s, tiles, page_list, tok_pos,                 \
              reinterpret_cast<const T_*>(qbuf), reinterpret_cast<const T_*>(pool), reinterpret_cast<T_*>(o), \
-             part_o, part_lse, m.hq, m.hkv, layer_base, scale_log2)
+             part_o, part_lse, m.hq, m.hkv, layer_base, scale_log2, qrows)
   if (m.dtype == 1 && m.dh == 128) {
     if (groups == 2)
       JEV_ATTN(bf16s, 128, 2);
@@ -967,15 +961,6 @@ hipError_t launch_poison_pages(const ModelDims& m, void* pool, int32_t first, in
   const unsigned blocks = (unsigned)std::min<size_t>((total + 255) / 256, 65536);
   JEV_LAUNCH(dev::poison_pages_kernel, dim3(blocks), dim3(256), 0, s, reinterpret_cast<dev::u32x4*>(pool),
              page_units * (size_t)m.n_pages, page_units, first, count, m.n_layers);
-  return hipGetLastError();
-}
-
-hipError_t launch_gather_rows(const void* src, const int32_t* rows, int32_t n, int32_t row_bytes, void* dst,
-                              hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  if (row_bytes <= 0 || row_bytes % 16) return hipErrorInvalidValue;
-  JEV_LAUNCH(dev::gather_rows_kernel, dim3(n), dim3(256), 0, s, reinterpret_cast<const dev::u32x4*>(src), rows,
-             row_bytes / 16, reinterpret_cast<dev::u32x4*>(dst));
   return hipGetLastError();
 }
 

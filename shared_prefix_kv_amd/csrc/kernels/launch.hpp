@@ -118,19 +118,17 @@ hipError_t launch_oproj_split(const ModelDims& m, const LayerW& w, const void* o
 hipError_t launch_split_res_norm(const ModelDims& m, const float* partial, int32_t splits, int32_t T, void* x,
                                  const void* g, void* h, hipStream_t s);
 // attention tiles (grid n_tiles x Hkv); groups = wave groups per workgroup (1
-// or 2: two split every tile's steps in halves, for rounds with long tiles)
+// or 2: two split every tile's steps in halves, for rounds with long tiles);
+// with qrows, query row t of the tiles reads row qrows[t] of qbuf
 hipError_t launch_attention(const ModelDims& m, int32_t layer, const AttnTile* tiles, int32_t n_tiles,
                             const int32_t* page_list, const int32_t* tok_pos, const void* qbuf,
                             const void* pool, void* o, float* part_o, float* part_lse, int32_t groups,
-                            hipStream_t s);
+                            hipStream_t s, const int32_t* qrows = nullptr);
 hipError_t launch_merge(const ModelDims& m, const MergeItem* items, int32_t n_items, const float* part_o,
                         const float* part_lse, void* o, hipStream_t s);
 // x += o Wo^T (stored); with x_rows, row r of o updates x row x_rows[r]
 hipError_t launch_oproj(const ModelDims& m, const LayerW& w, const void* o, int32_t T, void* x,
                         const GemmWs& ws, hipStream_t s, const int32_t* x_rows = nullptr);
-// dst row r = src row rows[r] (rows of row_bytes bytes, a multiple of 16)
-hipError_t launch_gather_rows(const void* src, const int32_t* rows, int32_t n, int32_t row_bytes, void* dst,
-                              hipStream_t s);
 // Debug: fills KV pages [first, first + count) of every layer with the bytes
 // 0x7F (finite, near the dtype's maximum).
 hipError_t launch_poison_pages(const ModelDims& m, void* pool, int32_t first, int32_t count, hipStream_t s);
