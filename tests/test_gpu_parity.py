@@ -369,6 +369,17 @@ def test_w1_long_prefix_split_causal_tiles(w1):
     ref = om.score_from_scratch(m, [pre + s for s in sufs], labs)
     ctx.free_pages([h])
     close("w1 600-token prefix", split_probs(probs, loff), ref, TOL_F32)
+    # the same with the full last layer in both rounds: the read-out rows
+    # alone (3 of 234, the long branch's last token in a split own tile, its
+    # output projection on the 64-row split-K tile) are bitwise the full layer
+    from shared_prefix_kv_amd import jev
+    ctx.set_debug(jev.JEV_DEBUG_FULL_LAST_LAYER)
+    (h,) = ctx.prefill_prefix([0], [pre])
+    probs2, _ = ctx.score_branches([h] * 3, sufs, labs)
+    _sync()
+    ctx.free_pages([h])
+    ctx.set_debug(0)
+    assert np.array_equal(probs2.cpu().numpy(), probs.cpu().numpy())
 
 
 def test_w1_nested_prefixes_candidates_and_errors(w1):
