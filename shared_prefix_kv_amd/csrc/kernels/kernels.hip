@@ -52,6 +52,25 @@ __device__ __forceinline__ void load16<bf16s>(const bf16s* p, float* out) {
     out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
   }
 }
+// the elements of one 16-byte unit already loaded, as fp32
+template <typename T>
+__device__ __forceinline__ void unpack16(const u32x4& u, float* out);
+template <>
+__device__ __forceinline__ void unpack16<bf16s>(const u32x4& u, float* out) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void unpack16<float>(const u32x4& u, float* out) {
+  out[0] = __uint_as_float(u.x);
+  out[1] = __uint_as_float(u.y);
+  out[2] = __uint_as_float(u.z);
+  out[3] = __uint_as_float(u.w);
+}
 template <>
 __device__ __forceinline__ void load16<float>(const float* p, float* out) {
   float4 u = *reinterpret_cast<const float4*>(p);
@@ -95,51 +114,80 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x, c
   }
 }
 
-// Embedding gather fused with layer 0's norm: one block per token; x = E[tok]
-// and h = RMSNorm(x) * g with rmsnorm_kernel's element and reduction order
-// (bitwise those of the two kernels).
+// Embedding gather fused with layer 0's norm: ROWS tokens per block, each
+// row x = E[tok] and h = RMSNorm(x) * g with rmsnorm_kernel's element and
+// reduction order (bitwise those of the two kernels).  The block's token ids
+// are read by one load of its first wave: when they sit in pinned host memory
+// (the first round of a call) every read is a bus transaction, so ROWS = 4
+// takes a quarter of them; all rows' embedding loads are in flight together.
 //
 // With up_units > 0 the workgroups also copy up_units 16-byte units from
 // up_src (the call's descriptors in pinned host memory, which tok then points
-// into) to up_dst in device memory, a share each, for the kernels that follow.
-template <typename T>
+// into) to up_dst in device memory, for the kernels that follow: consecutive
+// threads copy consecutive units (grid-stride), so a wave reads 1 KiB of
+// contiguous host memory.
+template <typename T, int ROWS>
 __global__ __launch_bounds__(256) void embed_norm_kernel(const T* __restrict__ E, const int32_t* __restrict__ tok,
-                                                         int d, const T* __restrict__ g, float eps, T* __restrict__ x,
-                                                         T* __restrict__ h, const u32x4* __restrict__ up_src,
-                                                         u32x4* __restrict__ up_dst, int up_units) {
+                                                         int n_tok, int d, const T* __restrict__ g, float eps,
+                                                         T* __restrict__ x, T* __restrict__ h,
+                                                         const u32x4* __restrict__ up_src, u32x4* __restrict__ up_dst,
+                                                         int up_units) {
   constexpr int CH = 16 / sizeof(T);
   constexpr int MAXV = 4;
   __shared__ float scratch[4];
-  if (up_units > 0) {
-    const int per = (up_units + (int)gridDim.x - 1) / (int)gridDim.x;
-    const int u0 = (int)blockIdx.x * per, u1 = min(u0 + per, up_units);
-    for (int u = u0 + (int)threadIdx.x; u < u1; u += blockDim.x) up_dst[u] = up_src[u];
+  __shared__ int32_t stok[ROWS];
+  for (int u = (int)blockIdx.x * 256 + (int)threadIdx.x; u < up_units; u += (int)gridDim.x * 256)
+    up_dst[u] = up_src[u];
+  const int r0 = (int)blockIdx.x * ROWS;
+  const int nr = min(ROWS, n_tok - r0);
+  int tk[ROWS];
+  if constexpr (ROWS > 1) {
+    if (threadIdx.x < (unsigned)nr) stok[threadIdx.x] = tok[r0 + threadIdx.x];
+    __syncthreads();
+    // rows past the last token repeat it (loaded, never stored)
+#pragma unroll
+    for (int rr = 0; rr < ROWS; ++rr) tk[rr] = stok[min(rr, nr - 1)];
+  } else {
+    tk[0] = tok[r0];  // one uniform load, no barrier
   }
-  const T* er = E + (size_t)tok[blockIdx.x] * d;
-  T* xr = x + (size_t)blockIdx.x * d;
-  T* hr = h + (size_t)blockIdx.x * d;
-  float v[MAXV][CH], gg[MAXV][CH];
-  float ss = 0.f;
+  // the embedding rows first, then the norm weights, with no branch between
+  u32x4 raw[ROWS][MAXV];
+  float gg[MAXV][CH];
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) {
     const int i = (threadIdx.x + 256 * j) * CH;
     if (i < d) {
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(er + i);
-      *reinterpret_cast<u32x4*>(xr + i) = raw;
-      load16<T>(er + i, v[j]);
-      load16<T>(g + i, gg[j]);
 #pragma unroll
-      for (int e = 0; e < CH; ++e) ss += v[j][e] * v[j][e];
+      for (int rr = 0; rr < ROWS; ++rr) raw[rr][j] = *reinterpret_cast<const u32x4*>(E + (size_t)tk[rr] * d + i);
+      load16<T>(g + i, gg[j]);
     }
   }
-  ss = block_sum256(ss, scratch);
-  const float r = 1.0f / sqrtf(ss / float(d) + eps);
 #pragma unroll
-  for (int j = 0; j < MAXV; ++j) {
-    const int i = (threadIdx.x + 256 * j) * CH;
-    if (i < d) {
+  for (int rr = 0; rr < ROWS; ++rr) {
+    if (rr >= nr) break;
+    T* xr = x + (size_t)(r0 + rr) * d;
+    T* hr = h + (size_t)(r0 + rr) * d;
+    float v[MAXV][CH];
+    float ss = 0.f;
 #pragma unroll
-      for (int e = 0; e < CH; ++e) hr[i + e] = from_f32<T>(v[j][e] * r * gg[j][e]);
+    for (int j = 0; j < MAXV; ++j) {
+      const int i = (threadIdx.x + 256 * j) * CH;
+      if (i < d) {
+        *reinterpret_cast<u32x4*>(xr + i) = raw[rr][j];
+        unpack16<T>(raw[rr][j], v[j]);
+#pragma unroll
+        for (int e = 0; e < CH; ++e) ss += v[j][e] * v[j][e];
+      }
+    }
+    ss = block_sum256(ss, scratch);
+    const float r = 1.0f / sqrtf(ss / float(d) + eps);
+#pragma unroll
+    for (int j = 0; j < MAXV; ++j) {
+      const int i = (threadIdx.x + 256 * j) * CH;
+      if (i < d) {
+#pragma unroll
+        for (int e = 0; e < CH; ++e) hr[i + e] = from_f32<T>(v[j][e] * r * gg[j][e]);
+      }
     }
   }
 }
@@ -799,6 +847,19 @@ __global__ __launch_bounds__(256) void readout_kernel(const T* __restrict__ U, c
   const ReadoutItem it = items[blockIdx.x];
   const T* xr = x + (size_t)it.row * d;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // loads issued together (one memory latency, not one per step): the row,
+  // the norm weights and the first unembedding row of each wave (label k =
+  // wave), held in registers while the norm is computed
+  constexpr int MAXU = 16;  // 16-byte units per lane of a row: d <= 1024 * CH, the norm kernels' limit
+  u32x4 u0[MAXU];
+  if (wave < it.k) {
+    const T* ur = U + (size_t)labels[it.label_off + wave] * d;
+#pragma unroll
+    for (int j = 0; j < MAXU; ++j) {
+      const int i = (lane + 64 * j) * CH;
+      if (i < d) u0[j] = *reinterpret_cast<const u32x4*>(ur + i);
+    }
+  }
   float ss = 0.f;
   for (int i = tid * CH; i < d; i += 256 * CH) {
     float v[CH];
@@ -821,11 +882,18 @@ __global__ __launch_bounds__(256) void readout_kernel(const T* __restrict__ U, c
   for (int k = wave; k < it.k; k += 4) {
     const T* ur = U + (size_t)labels[it.label_off + k] * d;
     float z = 0.f;
-    for (int i = lane * CH; i < d; i += 64 * CH) {
-      float u[CH];
-      load16<T>(ur + i, u);
 #pragma unroll
-      for (int e = 0; e < CH; ++e) z += hn[i + e] * u[e];
+    for (int j = 0; j < MAXU; ++j) {
+      const int i = (lane + 64 * j) * CH;
+      if (i < d) {
+        float u[CH];
+        if (k == wave)
+          unpack16<T>(u0[j], u);
+        else
+          load16<T>(ur + i, u);
+#pragma unroll
+        for (int e = 0; e < CH; ++e) z += hn[i + e] * u[e];
+      }
     }
     z = wave_sum(z);
     if (lane == 0) logit[k] = z;
@@ -885,11 +953,18 @@ hipError_t launch_embed_norm(const ModelDims& m, const void* embed, const int32_
   if (T_ <= 0) return hipSuccess;
   if (up_bytes < 0 || up_bytes % 16 || up_bytes / 16 > INT32_MAX || (up_bytes > 0 && (!up_src || !up_dst)))
     return hipErrorInvalidValue;
+  // four rows per block where that still leaves a few blocks per CU
   JEV_DISPATCH_T(m, {
-    JEV_LAUNCH(dev::embed_norm_kernel<T>, dim3(T_), dim3(256), 0, s, reinterpret_cast<const T*>(embed), tok, m.d,
-               reinterpret_cast<const T*>(g), m.eps, reinterpret_cast<T*>(x), reinterpret_cast<T*>(h),
-               reinterpret_cast<const dev::u32x4*>(up_src), reinterpret_cast<dev::u32x4*>(up_dst),
-               int(up_bytes / 16));
+    if (T_ >= 1024)
+      JEV_LAUNCH((dev::embed_norm_kernel<T, 4>), dim3((T_ + 3) / 4), dim3(256), 0, s,
+                 reinterpret_cast<const T*>(embed), tok, T_, m.d, reinterpret_cast<const T*>(g), m.eps,
+                 reinterpret_cast<T*>(x), reinterpret_cast<T*>(h), reinterpret_cast<const dev::u32x4*>(up_src),
+                 reinterpret_cast<dev::u32x4*>(up_dst), int(up_bytes / 16));
+    else
+      JEV_LAUNCH((dev::embed_norm_kernel<T, 1>), dim3(T_), dim3(256), 0, s, reinterpret_cast<const T*>(embed), tok,
+                 T_, m.d, reinterpret_cast<const T*>(g), m.eps, reinterpret_cast<T*>(x), reinterpret_cast<T*>(h),
+                 reinterpret_cast<const dev::u32x4*>(up_src), reinterpret_cast<dev::u32x4*>(up_dst),
+                 int(up_bytes / 16));
   })
   return hipGetLastError();
 }
