@@ -132,6 +132,66 @@ __device__ __forceinline__ void store8<float>(float* dst, const float v[8]) {
   reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
+// What the epilogue of a tile reads besides the tile, for a thread's first
+// unit of each kind (for tiles of at most 16 rows every thread has at most one
+// unit of each kind): loaded before the tile exists, so that those loads and
+// the tile's own overlap.  The same index rules as tile_epilogue.
+struct EpiPre {
+  float xv[8];        // RES: the row's x elements
+  int pos;            // QKV pairs: the row's position
+  int sl;             // QKV pairs: the row's KV slot (key heads)
+  float4 cs01, cs23;  // QKV pairs: (cos, sin) of its four pairs
+  int slv[8];         // QKV V columns: the KV slots of the unit's 8 rows
+};
+
+// first part: loads that depend on nothing.  Every thread loads (rows and
+// units clamped into the tile, so every address is valid), which keeps the
+// code free of branches and lets the second part wait for these loads alone.
+template <typename T, int EPI>
+__device__ __forceinline__ void epilogue_preload(int rows, int m0, int M, int nt, int BN, const ColMap& cm,
+                                                 const QkvOut& qo, const ResOut& ro, int tid, int nthreads,
+                                                 EpiPre* pre) {
+  rows = min(rows, M - m0);
+  if constexpr (EPI == EPI_RES) {
+    const int cpr = BN / 8;
+    const int r = min(tid / cpr, rows - 1);
+    const int xr = ro.rows ? ro.rows[m0 + r] : m0 + r;
+    load8<T>(reinterpret_cast<const T*>(ro.x) + (size_t)xr * ro.ld + (size_t)nt * BN + 8 * (tid % cpr), pre->xv);
+  } else {
+    const int half = BN >> 1;
+    const int np_t = max(0, min(half, cm.n_pairs - half * nt));
+    if (np_t > 0) {
+      const int r = min(tid / (np_t >> 2), rows - 1);
+      pre->pos = qo.pos[m0 + r];
+      pre->sl = qo.kvslot[m0 + r];
+    }
+    const int nv = BN - 2 * np_t;
+    if (nv > 0) {
+      const int r = min((tid / nv) * 8, rows - 1);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) pre->slv[q] = qo.kvslot[m0 + min(r + q, rows - 1)];
+    }
+  }
+}
+
+// second part: the rotation table rows at the positions of the first part
+template <int EPI>
+__device__ __forceinline__ void epilogue_preload_rope(int nt, int BN, const ColMap& cm, const QkvOut& qo, int tid,
+                                                      EpiPre* pre) {
+  if constexpr (EPI == EPI_QKV) {
+    const int h2 = cm.dh >> 1;
+    const int half = BN >> 1;
+    const int np_t = max(0, min(half, cm.n_pairs - half * nt));
+    const int pairs_before = min(cm.n_pairs, half * nt);
+    if (np_t > 0) {
+      const int i0 = (pairs_before + 4 * (tid % (np_t >> 2))) % h2;
+      const float4* rp = reinterpret_cast<const float4*>(qo.rope + (size_t)pre->pos * h2 + i0);
+      pre->cs01 = rp[0];
+      pre->cs23 = rp[1];
+    }
+  }
+}
+
 // Epilogue over an fp32 tile: rows [0, rows) are output rows m0.., columns
 // [0, BN) are column tile nt; element (r, j) at tile[r * ld + j] (LDS or
 // global).  Work is cut into vector units so that every thread issues 16-byte
@@ -143,10 +203,10 @@ __device__ __forceinline__ void store8<float>(float* dst, const float v[8]) {
 //  * QKV, V columns: one column over 8 rows; when the rows' KV slots are 8
 //    consecutive, 8-aligned slots of one page (the usual case) they are one
 //    16-byte run of the transposed V block, else single stores.
-template <typename T, int EPI>
+template <typename T, int EPI, bool PRE = false>
 __device__ __forceinline__ void tile_epilogue(const float* tile, int ld, int rows, int m0, int M, int nt, int BN,
                                               const ColMap& cm, const QkvOut& qo, const ResOut& ro, int tid,
-                                              int nthreads) {
+                                              int nthreads, const EpiPre* pre = nullptr) {
   rows = min(rows, M - m0);
   if constexpr (EPI == EPI_RES) {
     const int cpr = BN / 8;
@@ -157,7 +217,12 @@ __device__ __forceinline__ void tile_epilogue(const float* tile, int ld, int row
       T* xp = reinterpret_cast<T*>(ro.x) + (size_t)xr * ro.ld + (size_t)nt * BN + 8 * c8;
       const float* tp = tile + (size_t)r * ld + 8 * c8;
       float v[8];
-      load8<T>(xp, v);
+      if (PRE && r == tid / cpr) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = pre->xv[q];
+      } else {
+        load8<T>(xp, v);
+      }
       const float4 t0 = reinterpret_cast<const float4*>(tp)[0], t1 = reinterpret_cast<const float4*>(tp)[1];
       v[0] += t0.x; v[1] += t0.y; v[2] += t0.z; v[3] += t0.w;
       v[4] += t1.x; v[5] += t1.y; v[6] += t1.z; v[7] += t1.w;
@@ -182,8 +247,16 @@ __device__ __forceinline__ void tile_epilogue(const float* tile, int ld, int row
         const float* tp = tile + (size_t)r * ld + 4 * g;
         const float4 a0 = *reinterpret_cast<const float4*>(tp);
         const float4 a1 = *reinterpret_cast<const float4*>(tp + np_t);
-        const float4* rp = reinterpret_cast<const float4*>(qo.rope + (size_t)qo.pos[m] * h2 + i0);
-        const float4 cs01 = rp[0], cs23 = rp[1];  // (cos, sin) of pairs i0 .. i0+3
+        const bool first = PRE && r == tid / g4;
+        float4 cs01, cs23;  // (cos, sin) of pairs i0 .. i0+3
+        if (first) {
+          cs01 = pre->cs01;
+          cs23 = pre->cs23;
+        } else {
+          const float4* rp = reinterpret_cast<const float4*>(qo.rope + (size_t)qo.pos[m] * h2 + i0);
+          cs01 = rp[0];
+          cs23 = rp[1];
+        }
         float v[8];
         v[0] = a0.x * cs01.x - a1.x * cs01.y; v[1] = a1.x * cs01.x + a0.x * cs01.y;
         v[2] = a0.y * cs01.z - a1.y * cs01.w; v[3] = a1.y * cs01.z + a0.y * cs01.w;
@@ -195,7 +268,7 @@ __device__ __forceinline__ void tile_epilogue(const float* tile, int ld, int row
         if (head < cm.hq) {
           dst = qbuf + ((size_t)m * qo.hq + head) * qo.dh + 2 * i0;
         } else {
-          const int sl = qo.kvslot[m];
+          const int sl = first ? pre->sl : qo.kvslot[m];
           dst = pool + ((size_t)(sl >> 4) * qo.hkv + (head - cm.hq)) * 2 * pe + (size_t)(sl & 15) * qo.dh + 2 * i0;
         }
         store8<T>(dst, v);
@@ -213,9 +286,10 @@ __device__ __forceinline__ void tile_epilogue(const float* tile, int ld, int row
         const int n = min(8, rows - r);
         int sl[8];
         float v[8];
+        const bool first = PRE && r == (tid / nv) * 8;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          sl[q] = qo.kvslot[m0 + r + min(q, n - 1)];
+          sl[q] = first ? pre->slv[q] : qo.kvslot[m0 + r + min(q, n - 1)];
           v[q] = tp[(size_t)min(q, n - 1) * ld];
         }
         bool run = n == 8 && (sl[0] & 7) == 0;
@@ -865,27 +939,43 @@ template <typename T, int EPI>
 __global__ __launch_bounds__(256) void split_epilogue(const float* __restrict__ scratch, int splits, int M, int N,
                                                       ColMap cm, QkvOut qo, ResOut ro) {
   constexpr int BN = 128, RB = 16, LD = BN + 4;
+  constexpr int PER = RB * (BN / 4) / 256;  // float4 units per thread
   __shared__ __attribute__((aligned(16))) float stile[RB * LD];
   const int nt = blockIdx.x, r0 = blockIdx.y * RB;
   const int rows = min(RB, M - r0);
   const float* tile = scratch + (size_t)r0 * N + nt * BN;
   const size_t slice = (size_t)256 * N;
-  for (int e = threadIdx.x; e < rows * (BN / 4); e += 256) {
-    const int r = e / (BN / 4), q4 = e % (BN / 4);
-    float4 w[kMaxSplits];
+  const int tid = threadIdx.x;
+  // the epilogue's own loads (positions, slots, residual rows), then every
+  // slice of both units, then the rotation rows: one memory latency for all
+  EpiPre pre;
+  epilogue_preload<T, EPI>(rows, r0, M, nt, BN, cm, qo, ro, tid, 256, &pre);
+  // unconditional loads (slice and row clamped: slices past the count reload
+  // the last one, rows past the tile its last row) keep the code branch-free
+  float4 w[PER][kMaxSplits];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int e = tid + 256 * k, r = min(e / (BN / 4), rows - 1), q4 = e % (BN / 4);
 #pragma unroll
     for (int y = 0; y < kMaxSplits; ++y)
-      if (y < splits) w[y] = *reinterpret_cast<const float4*>(tile + y * slice + (size_t)r * N + 4 * q4);
-    float4 v = w[0];
+      w[k][y] = *reinterpret_cast<const float4*>(tile + min(y, splits - 1) * slice + (size_t)r * N + 4 * q4);
+  }
+  epilogue_preload_rope<EPI>(nt, BN, cm, qo, tid, &pre);
 #pragma unroll
-    for (int y = 1; y < kMaxSplits; ++y)
-      if (y < splits) {
-        v.x += w[y].x; v.y += w[y].y; v.z += w[y].z; v.w += w[y].w;
-      }
-    *reinterpret_cast<float4*>(&stile[r * LD + 4 * q4]) = v;
+  for (int k = 0; k < PER; ++k) {
+    const int e = tid + 256 * k, r = e / (BN / 4), q4 = e % (BN / 4);
+    if (r < rows) {
+      float4 v = w[k][0];
+#pragma unroll
+      for (int y = 1; y < kMaxSplits; ++y)
+        if (y < splits) {
+          v.x += w[k][y].x; v.y += w[k][y].y; v.z += w[k][y].z; v.w += w[k][y].w;
+        }
+      *reinterpret_cast<float4*>(&stile[r * LD + 4 * q4]) = v;
+    }
   }
   __syncthreads();
-  tile_epilogue<T, EPI>(stile, LD, rows, r0, M, nt, BN, cm, qo, ro, threadIdx.x, 256);
+  tile_epilogue<T, EPI, true>(stile, LD, rows, r0, M, nt, BN, cm, qo, ro, tid, 256, &pre);
 }
 
 }  // namespace dev

@@ -197,12 +197,12 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(const T* __restrict__ E
 // order and rounded to T (as split_epilogue's residual epilogue does), then h
 // = RMSNorm(x) * g with the rows's elements, squares and block sum in
 // rmsnorm_kernel's order: both outputs are bitwise those of the two kernels.
-template <typename T>
+// MAXV = 16-byte chunks per thread that the row needs (d <= 256 * CH * MAXV).
+template <typename T, int MAXV>
 __global__ __launch_bounds__(256) void split_res_norm_kernel(const float* __restrict__ part, int splits, int d,
                                                              T* __restrict__ x, const T* __restrict__ g, float eps,
                                                              T* __restrict__ h) {
   constexpr int CH = 16 / sizeof(T);
-  constexpr int MAXV = 4;
   __shared__ float scratch[4];
   const size_t slice = (size_t)256 * d;
   T* xr = x + (size_t)blockIdx.x * d;
@@ -210,18 +210,47 @@ __global__ __launch_bounds__(256) void split_res_norm_kernel(const float* __rest
   T* hr = h + (size_t)blockIdx.x * d;
   float v[MAXV][CH], gg[MAXV][CH];
   float ss = 0.f;
+  // every slice of every chunk is loaded before the first sum (the slice
+  // count is at most kMaxSplits; slices past it are not read)
+  u32x4 raw_x[MAXV];
+  float4 sp[MAXV][kMaxSplits][CH / 4];
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) {
+    const int i = (threadIdx.x + 256 * j) * CH;
+    if (i < d) {
+      raw_x[j] = *reinterpret_cast<const u32x4*>(xr + i);
+      load16<T>(g + i, gg[j]);
+#pragma unroll
+      for (int y = 0; y < kMaxSplits; ++y)
+        if (y < splits)
+#pragma unroll
+          for (int q = 0; q < CH / 4; ++q) sp[j][y][q] = reinterpret_cast<const float4*>(pr + y * slice + i)[q];
+    }
+  }
 #pragma unroll
   for (int j = 0; j < MAXV; ++j) {
     const int i = (threadIdx.x + 256 * j) * CH;
     if (i < d) {
       float xs[CH], acc[CH];
-      load16<T>(xr + i, xs);
-      load16<T>(g + i, gg[j]);
+      unpack16<T>(raw_x[j], xs);
 #pragma unroll
-      for (int e = 0; e < CH; ++e) acc[e] = pr[i + e];
-      for (int y = 1; y < splits; ++y)
+      for (int q = 0; q < CH / 4; ++q) {
+        acc[4 * q] = sp[j][0][q].x;
+        acc[4 * q + 1] = sp[j][0][q].y;
+        acc[4 * q + 2] = sp[j][0][q].z;
+        acc[4 * q + 3] = sp[j][0][q].w;
+      }
+      // slice order, as the separate residual epilogue sums them
 #pragma unroll
-        for (int e = 0; e < CH; ++e) acc[e] += pr[y * slice + i + e];
+      for (int y = 1; y < kMaxSplits; ++y)
+        if (y < splits)
+#pragma unroll
+          for (int q = 0; q < CH / 4; ++q) {
+            acc[4 * q] += sp[j][y][q].x;
+            acc[4 * q + 1] += sp[j][y][q].y;
+            acc[4 * q + 2] += sp[j][y][q].z;
+            acc[4 * q + 3] += sp[j][y][q].w;
+          }
 #pragma unroll
       for (int e = 0; e < CH; ++e) {
         const T r = from_f32<T>(xs[e] + acc[e]);
@@ -973,9 +1002,20 @@ hipError_t launch_split_res_norm(const ModelDims& m, const float* partial, int32
                                  const void* g, void* h, hipStream_t s) {
   if (T_ <= 0) return hipSuccess;
   if (T_ > kSplitRows || splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
+  // the slice loads of all chunks of a row are held in registers together:
+  // as many chunks as the row has
   JEV_DISPATCH_T(m, {
-    JEV_LAUNCH(dev::split_res_norm_kernel<T>, dim3(T_), dim3(256), 0, s, partial, splits, m.d,
-               reinterpret_cast<T*>(x), reinterpret_cast<const T*>(g), m.eps, reinterpret_cast<T*>(h));
+    constexpr int ROW_CHUNK = 256 * 16 / (int)sizeof(T);
+    const int nv = (m.d + ROW_CHUNK - 1) / ROW_CHUNK;
+    if (nv <= 1)
+      JEV_LAUNCH((dev::split_res_norm_kernel<T, 1>), dim3(T_), dim3(256), 0, s, partial, splits, m.d,
+                 reinterpret_cast<T*>(x), reinterpret_cast<const T*>(g), m.eps, reinterpret_cast<T*>(h));
+    else if (nv == 2)
+      JEV_LAUNCH((dev::split_res_norm_kernel<T, 2>), dim3(T_), dim3(256), 0, s, partial, splits, m.d,
+                 reinterpret_cast<T*>(x), reinterpret_cast<const T*>(g), m.eps, reinterpret_cast<T*>(h));
+    else
+      JEV_LAUNCH((dev::split_res_norm_kernel<T, 4>), dim3(T_), dim3(256), 0, s, partial, splits, m.d,
+                 reinterpret_cast<T*>(x), reinterpret_cast<const T*>(g), m.eps, reinterpret_cast<T*>(h));
   })
   return hipGetLastError();
 }
