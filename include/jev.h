@@ -340,7 +340,11 @@ int jev_debug_tap(jev_ctx* ctx, int32_t what, int32_t layer, void* dst, int64_t 
  * query-key pair) and bytes for the memory-bound kernels (each input and
  * output element once).  jev_profile(ctx, 0) disables and clears the records.
  * jev_profile_read waits for the recorded events and copies up to cap records;
- * *n receives the number recorded. */
+ * *n receives the number recorded.  jev_profile_rows is jev_profile restricted
+ * to the launches of exactly `rows` token rows (rows = 0: every launch), so
+ * that a measurement puts events on the launches it times and on no other
+ * (an event pair costs the stream a short idle between kernels); errors:
+ * JEV_EINVAL for rows < 0, otherwise those of jev_profile. */
 enum {
   JEV_K_EMBED = 0,
   JEV_K_RMSNORM = 1,
@@ -360,6 +364,7 @@ typedef struct {
   float ms;       /* event-measured duration */
 } jev_launch_record;
 int jev_profile(jev_ctx* ctx, uint32_t kind_mask);
+int jev_profile_rows(jev_ctx* ctx, uint32_t kind_mask, int64_t rows);
 int jev_profile_read(jev_ctx* ctx, jev_launch_record* out, int64_t cap, int64_t* n);
 
 /* Answer layer (jdon.com openjev-sglang article, "three question types" and

@@ -213,6 +213,7 @@ struct jev_ctx {
     hipEvent_t e0, e1;
   };
   uint32_t prof_mask = 0;
+  int64_t prof_rows = 0;  // only launches of this many rows are timed (0: all)
   std::vector<Prof> prof;
   std::vector<hipEvent_t> prof_free;  // events kept for re-use
   std::vector<jev_sched*> scheds;     // schedulers on this context (detached when it is destroyed)
@@ -810,7 +811,8 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
   const size_t elt = size_t(elt_size(ctx->desc));
   // times one launch with events when its kind is being profiled
   auto timed = [&](int kind, int layer, int64_t rows, double flops, double bytes, auto&& launch) -> hipError_t {
-    if (sc.no_alloc || !(ctx->prof_mask & (1u << kind))) return launch();
+    if (sc.no_alloc || !(ctx->prof_mask & (1u << kind)) || (ctx->prof_rows > 0 && rows != ctx->prof_rows))
+      return launch();
     jev_ctx::Prof p;
     p.rec = jev_launch_record{kind, layer, rows, flops, bytes, 0.f};
     for (hipEvent_t* e : {&p.e0, &p.e1}) {
@@ -1831,8 +1833,11 @@ int jev_debug_tap(jev_ctx* ctx, int32_t what, int32_t layer, void* dst, int64_t 
   return JEV_OK;
 }
 
-int jev_profile(jev_ctx* ctx, uint32_t kind_mask) {
+int jev_profile(jev_ctx* ctx, uint32_t kind_mask) { return jev_profile_rows(ctx, kind_mask, 0); }
+
+int jev_profile_rows(jev_ctx* ctx, uint32_t kind_mask, int64_t rows) {
   if (!ctx) return fail(JEV_EINVAL, "NULL ctx");
+  if (rows < 0) return fail(JEV_EINVAL, "rows < 0");
   if (ctx->dry) return fail(JEV_ESTATE, "profiling needs a device context");
   if (kind_mask >> JEV_K_COUNT) return fail(JEV_EINVAL, "unknown kernel kind");
   if (kind_mask == 0) {
@@ -1844,6 +1849,7 @@ int jev_profile(jev_ctx* ctx, uint32_t kind_mask) {
     ctx->prof.clear();
   }
   ctx->prof_mask = kind_mask;
+  ctx->prof_rows = rows;
   return JEV_OK;
 }
 

@@ -32,7 +32,7 @@ _NAMES = {0: "JEV_OK", 1: "JEV_EINVAL", 2: "JEV_ENOMEM", 3: "JEV_EHANDLE", 4: "J
 
 EXPORTED = ["jev_workspace_bytes", "jev_kv_pool_bytes", "jev_create", "jev_destroy", "jev_prefill_prefix",
             "jev_score_branches", "jev_score_branches_noalloc", "jev_score_candidates", "jev_free_pages", "jev_plan", "jev_page_table",
-            "jev_match", "jev_stats", "jev_debug_tap", "jev_profile", "jev_profile_read", "jev_answers",
+            "jev_match", "jev_stats", "jev_debug_tap", "jev_profile", "jev_profile_rows", "jev_profile_read", "jev_answers",
             "jev_set_plan_mode", "jev_set_cache_policy", "jev_sched_create", "jev_sched_destroy",
             "jev_sched_submit", "jev_sched_step", "jev_sched_status", "jev_sched_result", "jev_last_error",
             "jev_set_debug", "jev_limits"]
@@ -116,6 +116,7 @@ def lib() -> ctypes.CDLL:
         L.jev_stats.argtypes = [vp, P(Stats)]
         L.jev_debug_tap.argtypes = [vp, i32, i32, vp, i64]
         L.jev_profile.argtypes = [vp, ctypes.c_uint32]
+        L.jev_profile_rows.argtypes = [vp, ctypes.c_uint32, i64]
         L.jev_profile_read.argtypes = [vp, P(LaunchRecord), i64, P(i64)]
         L.jev_set_plan_mode.argtypes = [vp, i32]
         L.jev_set_cache_policy.argtypes = [vp, i32]
@@ -350,12 +351,13 @@ class Context:
         else:
             _check(lib().jev_debug_tap(self.ctx, what, layer, ctypes.c_void_p(dst.data_ptr()), dst.shape[0]))
 
-    def profile(self, kinds: Sequence[str] = ()) -> None:
-        """Enables event timing of the named kernels; () disables and clears."""
+    def profile(self, kinds: Sequence[str] = (), rows: int = 0) -> None:
+        """Enables event timing of the named kernels (with rows > 0: of their
+        launches of exactly that many rows); () disables and clears."""
         mask = 0
         for k in kinds:
             mask |= 1 << KERNELS.index(k)
-        _check(lib().jev_profile(self.ctx, mask))
+        _check(lib().jev_profile_rows(self.ctx, mask, rows))
 
     def profile_read(self) -> List[dict]:
         n = ctypes.c_int64()

@@ -693,6 +693,35 @@ def test_w2_last_layer_for_read_out_rows_is_bitwise_the_full_layer(w2):
     assert row_flops == [full_row] * (L - 1) + [kv_row] + [full_row] * L, row_flops
 
 
+def test_profile_rows_times_only_launches_of_that_size(w2):
+    """jev_profile_rows puts events on the launches of one row count only (the
+    bench's live timing of its dominant kernel): the branch round's 240-row
+    projections are recorded, the prefill's 2000-row ones and the last layer's
+    5-row output projection are not, and the probabilities are unchanged."""
+    wl, inst, g, ctx, _ = w2
+    br = inst.passes[0]
+    L = wl.model.n_layers
+    out = []
+    for rows in (None, 240):
+        if rows:
+            ctx.profile(("qkv", "oproj"), rows=rows)
+        (h,) = ctx.prefill_prefix([0], [inst.prefixes[0]])
+        probs, loff = ctx.score_branches([h] * 5, [b.tokens for b in br], [b.labels for b in br])
+        _sync()
+        recs = ctx.profile_read() if rows else []
+        ctx.profile(())
+        ctx.free_pages([h])
+        out.append((probs.float().cpu().numpy().copy(), recs))
+    assert np.array_equal(out[0][0], out[1][0])
+    got = [(r["kernel"], r["layer"], r["rows"]) for r in out[1][1]]
+    want = []
+    for l in range(L):
+        want.append(("qkv", l, 240))
+        if l + 1 < L:
+            want.append(("oproj", l, 240))
+    assert got == want, got
+
+
 def test_w2_round_size_moves_a_branch_within_its_bar(w2):
     """Round-composition variance, measured: the same five branches scored in
     a round of their own (240 rows: split-K projections, 7 prefix chunks) and

@@ -186,6 +186,24 @@ def test_limits_of_a_planning_only_context():
     assert e.value.code == jev.JEV_EINVAL
 
 
+def test_profile_arguments_on_a_planning_only_context():
+    wl = workload(1)
+    ctx = dry(wl, 256)
+    L = jev.lib()
+    with pytest.raises(jev.JevError) as e:
+        jev._check(L.jev_profile_rows(None, 1 << 2, 0))
+    assert e.value.code == jev.JEV_EINVAL
+    with pytest.raises(jev.JevError) as e:
+        ctx.profile(["qkv"], rows=-1)
+    assert e.value.code == jev.JEV_EINVAL
+    with pytest.raises(jev.JevError) as e:
+        ctx.profile(["qkv"], rows=240)   # no device: nothing to time
+    assert e.value.code == jev.JEV_ESTATE
+    with pytest.raises(jev.JevError) as e:
+        ctx.profile(["qkv"])
+    assert e.value.code == jev.JEV_ESTATE
+
+
 def test_debug_flags_and_call_statistics_on_a_planning_only_context():
     wl = workload(1)
     inst = make_instance(wl)
