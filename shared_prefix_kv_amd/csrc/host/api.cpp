@@ -193,10 +193,16 @@ struct jev_ctx {
   WsLayout L{};
   char* ws = nullptr;
   char* static_scratch = nullptr;  // this device's copy of the file-scope scratch array
-  int32_t* desc_host = nullptr;      // pinned staging of a call's descriptors
+  // Pinned staging of a call's descriptors: two halves of L.desc_ints ints,
+  // used by calls in turn.  A call reads its half on the device (the first
+  // kernel copies it up) only before its end event, so the host rewrites a
+  // half once the end event of the call before last that used it has passed:
+  // no event between kernels.
+  int32_t* desc_host = nullptr;
   int32_t* desc_host_dev = nullptr;  // its device-side address
-  hipEvent_t desc_copied = nullptr;  // the call's first kernel has copied them up
-  hipEvent_t last_done = nullptr;
+  hipEvent_t done_ev[2] = {nullptr, nullptr};  // end of the latest call on each half
+  int32_t desc_half = 0;                       // half of the next call
+  hipEvent_t last_done = nullptr;              // end of the latest call (one of done_ev)
   bool have_last = false;
   hipStream_t last_stream = nullptr;
   jev::PagePool pages;
@@ -785,9 +791,14 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
     }
   ctx->n_round_ev = 0;
   if (ctx->have_last && s != ctx->last_stream) HIPCHK(hipStreamWaitEvent(s, ctx->last_done, 0));
-  if (ctx->have_last) HIPCHK(hipEventSynchronize(ctx->desc_copied));
+  // this call's staging half: free once the last call that used it has ended
+  // (an event never recorded has nothing to wait for)
+  const int32_t half = ctx->desc_half;
+  HIPCHK(hipEventSynchronize(ctx->done_ev[half]));
+  int32_t* const desc_host = ctx->desc_host + size_t(half) * size_t(ctx->L.desc_ints);
+  const int32_t* const desc_host_dev = ctx->desc_host_dev + size_t(half) * size_t(ctx->L.desc_ints);
   if (timed_call) HIPCHK(hipEventRecord(ctx->round_ev[0], s));
-  std::memcpy(ctx->desc_host, hb.data(), hb.size() * sizeof(int32_t));
+  std::memcpy(desc_host, hb.data(), hb.size() * sizeof(int32_t));
   int32_t* dd = reinterpret_cast<int32_t*>(ctx->ws + ctx->L.desc);
   // No separate copy (a host-to-device copy on the stream left the GPU idle
   // for ~15 us per call): the first round's embedding kernel reads its tokens
@@ -795,10 +806,7 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
   // units (the buffers hold a multiple of 16 bytes), for the kernels after it.
   const int64_t up_bytes = (int64_t(hb.size()) * int64_t(sizeof(int32_t)) + 15) / 16 * 16;
   const bool upload = !rds.empty() && rds[0].T > 0;
-  if (!upload) {
-    HIPCHK(hipMemcpyAsync(dd, ctx->desc_host, hb.size() * sizeof(int32_t), hipMemcpyHostToDevice, s));
-    HIPCHK(hipEventRecord(ctx->desc_copied, s));
-  }
+  if (!upload) HIPCHK(hipMemcpyAsync(dd, desc_host, hb.size() * sizeof(int32_t), hipMemcpyHostToDevice, s));
   const jev::ModelDims& m = ctx->dims;
   void* x = ctx->ws + ctx->L.x;
   void* h = ctx->ws + ctx->L.h;
@@ -856,15 +864,14 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
     for (int64_t t = 0; t < rd.T; ++t) ctx->call_written.push_back(hb[size_t(rd.off_slot + t)] >> 4);
     ctx->round_reads.push_back(rd.n_read > 0);
     const bool first = upload && &rd == &rds[0];
-    const int32_t* tok = (first ? ctx->desc_host_dev : dd) + rd.off_tok;
+    const int32_t* tok = (first ? desc_host_dev : dd) + rd.off_tok;
     const double T = rd.T;
     // the embedding gather also writes layer 0's normalised input
     HIPCHK(timed(JEV_K_EMBED, -1, rd.T, 0, 3 * T * D * E + 4 * T, [&] {
       return jev::launch_embed_norm(m, ctx->embed, tok, rd.T, ctx->layers[0].norm, x, h, s,
-                                    first ? ctx->desc_host_dev : nullptr, first ? dd : nullptr,
+                                    first ? desc_host_dev : nullptr, first ? dd : nullptr,
                                     first ? up_bytes : 0);
     }));
-    if (first) HIPCHK(hipEventRecord(ctx->desc_copied, s));
     bool h_ready = true;  // h of this layer already written (by the gather or the previous projection)
     for (int l = 0; l < m.n_layers; ++l) {
       const jev::LayerW& w = ctx->layers[l];
@@ -937,7 +944,9 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
     if (timed_call) HIPCHK(hipEventRecord(ctx->round_ev[&rd - rds.data() + 1], s));
   }
   if (timed_call) ctx->n_round_ev = int32_t(rds.size()) + 1;
-  HIPCHK(hipEventRecord(ctx->last_done, s));
+  HIPCHK(hipEventRecord(ctx->done_ev[half], s));
+  ctx->last_done = ctx->done_ev[half];
+  ctx->desc_half = half ^ 1;
   ctx->have_last = true;
   ctx->last_stream = s;
   ctx->stats.last_call_kind = ctx->call_kind;
@@ -1030,11 +1039,11 @@ int jev_create(const jev_model_desc* desc, const jev_weights* weights, void* kv_
     ctx->pool = reinterpret_cast<char*>(kv_pool);
     ctx->ws = reinterpret_cast<char*>(workspace);
     if (int rc = device_scratch(&ctx->static_scratch)) return rc;
-    HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&ctx->desc_host), size_t(ctx->L.desc_ints) * sizeof(int32_t),
+    HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&ctx->desc_host), 2 * size_t(ctx->L.desc_ints) * sizeof(int32_t),
                          hipHostMallocDefault));
     HIPCHK(hipHostGetDevicePointer(reinterpret_cast<void**>(&ctx->desc_host_dev), ctx->desc_host, 0));
-    HIPCHK(hipEventCreateWithFlags(&ctx->desc_copied, hipEventDisableTiming));
-    HIPCHK(hipEventCreateWithFlags(&ctx->last_done, hipEventDisableTiming));
+    for (hipEvent_t& e : ctx->done_ev) HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    ctx->last_done = ctx->done_ev[0];
     // RoPE table: angle = pos * theta^(-2i/dh) in double, stored as float (cos, sin)
     const int half = desc->head_dim / 2;
     std::vector<float> rope(size_t(desc->max_positions) * half * 2);
@@ -1066,8 +1075,8 @@ int jev_destroy(jev_ctx* ctx) {
   if (!ctx->dry) {
     if (ctx->have_last && hipEventSynchronize(ctx->last_done) != hipSuccess) rc = fail(JEV_EHIP, "sync failed");
     if (ctx->desc_host) (void)hipHostFree(ctx->desc_host);
-    if (ctx->desc_copied) (void)hipEventDestroy(ctx->desc_copied);
-    if (ctx->last_done) (void)hipEventDestroy(ctx->last_done);
+    for (hipEvent_t e : ctx->done_ev)
+      if (e) (void)hipEventDestroy(e);
     for (auto& p : ctx->prof) {
       (void)hipEventDestroy(p.e0);
       (void)hipEventDestroy(p.e1);

@@ -652,6 +652,36 @@ def test_w2_repeated_calls_are_bitwise_identical(w2):
         assert np.array_equal(r, runs[0])
 
 
+def test_w2_back_to_back_calls_on_two_streams(w2):
+    """Calls queued without a host synchronisation in between, alternating
+    between two streams (the prefill on one, the scoring on the other, the
+    pages freed and reused by the next prefill): the descriptor staging
+    halves are rewritten while earlier calls are still queued, and every call
+    is ordered after the one before.  Each result is bitwise that of a call
+    made after a full synchronisation."""
+    import ctypes
+    wl, inst, g, ctx, _ = w2
+    br = inst.passes[0]
+    n_lab = sum(len(b.labels) for b in br)
+    (h,) = ctx.prefill_prefix([0], [inst.prefixes[0]])
+    ref, loff = ctx.score_branches([h] * 5, [b.tokens for b in br], [b.labels for b in br])
+    _sync()
+    ref = ref.float().cpu().numpy().copy()
+    ctx.free_pages([h])
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty(n_lab, dtype=torch.float32, device="cuda:0") for _ in range(6)]
+    _sync()
+    for i in range(6):
+        sa, sb = streams[i % 2], streams[(i + 1) % 2]
+        (h,) = ctx.prefill_prefix([0], [inst.prefixes[0]], stream=ctypes.c_void_p(sa.cuda_stream))
+        ctx.score_branches([h] * 5, [b.tokens for b in br], [b.labels for b in br], probs=outs[i],
+                           stream=ctypes.c_void_p(sb.cuda_stream))
+        ctx.free_pages([h])
+    _sync()
+    for i, o in enumerate(outs):
+        assert np.array_equal(o.cpu().numpy(), ref), i
+
+
 def test_w2_last_layer_for_read_out_rows_is_bitwise_the_full_layer(w2):
     """The last layer runs its attention and output projection only where a
     final state is read out: nowhere in the prefill round, at the five branch
