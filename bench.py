@@ -352,7 +352,7 @@ TRAFFIC_LAUNCHES = {
     "merge[240 rows]": [("merge_kernel<bf16s, 128>", 245760)],
     "qkv[240 rows]": [("gemm_kernel<bf16s, 128, 0, true, 4, 2, 256>", 122880), ("split_epilogue<bf16s, 0>", 153600)],
     "oproj[240 rows]": [("gemm_kernel<bf16s, 128, 1, true, 4, 2, 256>", 98304),
-                        ("split_res_norm_kernel<bf16s>", 61440)],
+                        ("split_res_norm_kernel<bf16s, 2>", 61440)],
     "attn[5 rows]": [("attn_kernel<bf16s, 128, 1>", 12288)],
     "oproj[5 rows]": [("gemm_kernel<bf16s, 128, 1, true, 1, 4, 64>", 49152), ("split_epilogue<bf16s, 1>", 8192)],
 }
