@@ -983,6 +983,32 @@ def test_w8_tiny_batch_of_requests_float32():
     ctx.close()
 
 
+def test_w9_ragged_long_round_embedding_rows_float32():
+    """A 1,030-token prefill round on the float32 model: rounds of at least
+    1,024 rows gather four embedding rows per workgroup, and 1,030 leaves a
+    last workgroup with two.  The residual stream entering layer 0 is exactly
+    the embedding rows, and the branches scored on that prefix match the
+    oracle within 1e-5."""
+    wl = workload(9)
+    inst = make_instance(wl)
+    m = om.from_weights(host_weights(9))
+    P = list(inst.prefixes[0][:1030])
+    ctx, _ = device_context(9, n_pages=512, max_pos=4096, max_tok=4096)
+    tap = torch.zeros((len(P), m.d), dtype=torch.float32, device="cuda:0")
+    ctx.debug_tap(TAP_RESID, 0, tap)
+    (h,) = ctx.prefill_prefix([0], [P])
+    _sync()
+    ctx.debug_tap()
+    assert np.array_equal(tap.cpu().numpy(), np.asarray(m.embed, np.float32)[np.asarray(P)])
+    br = inst.passes[0]
+    probs, loff = ctx.score_branches([h] * len(br), [b.tokens for b in br], [b.labels for b in br])
+    _sync()
+    ref = om.score_from_scratch(m, [P + list(b.tokens) for b in br], [b.labels for b in br])
+    close("w9 1030-token prefix branches", split_probs(probs, loff), ref, TOL_F32)
+    ctx.free_pages([h])
+    ctx.close()
+
+
 def test_w9_tiny_long_prefix_two_wave_groups_and_split_tiles_float32():
     """A 2,100-token prefix on the float32 model: the prefill round's longest
     causal tile has 132 pages, so the attention runs two wave groups per
