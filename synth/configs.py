@@ -86,6 +86,7 @@ class Workload:
 
 
 TINY_F32 = ModelShape(n_layers=1, d=256, hq=4, hkv=4, dh=64, vocab=1024, dtype="f32")
+TINY_F32_GQA2 = ModelShape(n_layers=2, d=256, hq=2, hkv=1, dh=64, vocab=1024, dtype="f32")
 QWEN_LIKE_4L = ModelShape(n_layers=4, d=4096, hq=32, hkv=4, dh=128, vocab=151936, dtype="bf16")
 LONG_8L = ModelShape(n_layers=8, d=4096, hq=32, hkv=8, dh=128, vocab=151936, dtype="bf16")
 QWEN_LIKE_1L = ModelShape(n_layers=1, d=4096, hq=32, hkv=4, dh=128, vocab=151936, dtype="bf16")
@@ -120,7 +121,10 @@ WORKLOADS: List[Workload] = [
 #    (the other reading of "same model shapes as config 1");
 # 9  a 2,100-token prefix on the tiny float32 model: a round whose longest
 #    attention tile has more than 48 pages (two wave groups per workgroup) and
-#    whose long causal tiles are split in two.
+#    whose long causal tiles are split in two;
+# 10 a tiny float32 model with two query heads on one KV head (three rotated
+#    heads, so one 128-column projection tile holds both rotated and V
+#    columns), two blocks, a prefix long enough for full-K projections.
 PARITY_WORKLOADS: List[Workload] = [
     Workload(6, "prefix2000_x5x48_yesno_1block", QWEN_LIKE_1L,
              requests=(Request(prefix_len=2000, n_branches=5, suffix_len=48, k_labels=2,
@@ -133,6 +137,8 @@ PARITY_WORKLOADS: List[Workload] = [
                             for _ in range(16))),
     Workload(9, "prefix2100_x4x20_tiny_f32", TINY_F32,
              requests=(Request(prefix_len=2100, n_branches=4, suffix_len=20, k_labels=3),)),
+    Workload(10, "prefix300_x6x24_tiny_f32_gqa2", TINY_F32_GQA2,
+             requests=(Request(prefix_len=300, n_branches=6, suffix_len=24, k_labels=3),)),
 ]
 
 

@@ -983,6 +983,32 @@ def test_w8_tiny_batch_of_requests_float32():
     ctx.close()
 
 
+def test_w10_two_query_heads_per_kv_head_float32():
+    """Two float32 blocks with two query heads on one KV head: the projection
+    has three rotated heads, so its second 128-column tile holds a key head's
+    rotated columns and the value columns, in the full-K epilogue (300-row
+    prefill) and in the split-K one (144-row branch round); attention tiles
+    pack 64 tokens x 2 heads.  Shared-prefix branches and the same sequences
+    as candidates match the oracle within 1e-5."""
+    wl = workload(10)
+    inst = make_instance(wl)
+    m = om.from_weights(host_weights(10))
+    seqs = inst.full_sequences(0)
+    ref = om.score_from_scratch(m, [s for s, _ in seqs], [l for _, l in seqs])
+    ctx, _ = device_context(10, n_pages=256, max_pos=1024, max_tok=1024)
+    br = inst.passes[0]
+    (h,) = ctx.prefill_prefix([0], [inst.prefixes[0]])
+    probs, loff = ctx.score_branches([h] * len(br), [b.tokens for b in br], [b.labels for b in br])
+    _sync()
+    close("w10 GQA 2:1 shared prefix", split_probs(probs, loff), ref, TOL_F32)
+    ctx.free_pages([h])
+    probs, loff = ctx.score_candidates([s for s, _ in seqs], [l for _, l in seqs])
+    _sync()
+    close("w10 GQA 2:1 candidates", split_probs(probs, loff), ref, TOL_F32)
+    assert ctx.stats()["pages_in_use"] == 0
+    ctx.close()
+
+
 def test_w9_ragged_long_round_embedding_rows_float32():
     """A 1,030-token prefill round on the float32 model: rounds of at least
     1,024 rows gather four embedding rows per workgroup, and 1,030 leaves a
