@@ -704,6 +704,10 @@ __global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2,
           v0[b] = v0_pf[b];
           v1[b] = __builtin_bit_cast(bf16x8, reinterpret_cast<const u32x4*>(&sV[buf][0])[vq_unit(32 * b + c, 2 + hh)]);
         }
+        // every read issued before the first MFMA, and the MFMAs in the
+        // source order below (the scheduler would otherwise move the score
+        // chain last and the second V reads next to their MFMAs)
+        __builtin_amdgcn_sched_barrier(0);
         f32x16 S;
 #pragma unroll
         for (int r = 0; r < 16; ++r) S[r] = 0.f;
@@ -711,6 +715,10 @@ __global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2,
         for (int i = 0; i < 2 * NDB; ++i) {
           oacc[i % NDB] = MF::mma(v0[i % NDB], i < NDB ? pb[0] : pl[0], oacc[i % NDB]);
           if (i < NKS) S = MF::mma(kf[i], qf[i], S);
+          // an opaque use of the running score keeps each score MFMA next to
+          // its output-block MFMA (without it the chain is sunk to its end)
+          asm volatile("" : "+v"(S));
+          __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int i = 2 * NDB; i < NKS; ++i) S = MF::mma(kf[i], qf[i], S);
@@ -718,17 +726,6 @@ __global__ __launch_bounds__(256 * GROUPS) __attribute__((amdgpu_waves_per_eu(2,
         for (int i = 0; i < 2 * NDB; ++i)
           oacc[i % NDB] = MF::mma(v1[i % NDB], i < NDB ? pb[1] : pl[1], oacc[i % NDB]);
         S_out = S;
-        // issue order: the global loads, the K fragment reads not read ahead,
-        // then two MFMAs at a time (the second V reads among the first),
-        // then the last eight
-        __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, NKS - PF_K, 0);
-#pragma unroll
-        for (int i = 0; i < NKS; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          if (i >= 2 && i < 2 + NDB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NDB, 0);
       } else {
         S_out = qk(buf ^ 1);
         pv(buf, pb, pl);
