@@ -414,6 +414,57 @@ def write_traffic(fetch_dir: str, write_dir: str, copy_mib: int = 1024) -> int:
     return 0
 
 
+# (large, splits, bn) of jev_set_gemm_variant; (0, 0, 0) is the default
+GEMM_VARIANTS = [(0, 0, 0), (1, 0, 0), (2, 0, 0), (3, 0, 0), (0, 3, 0), (0, 4, 0), (0, 0, 128)]
+
+
+def gemm_variants(ctx, step, probs, n_steps: int) -> dict:
+    """Each projection kernel variant on the bench step: the step time, every
+    projection instance's average launch time (events on the projection
+    launches only, over separate steps) and the largest probability change
+    against the default variant.  The default's numbers come from the same
+    call, so the variants are compared on one box and clock."""
+    import numpy as np
+    import torch
+
+    from shared_prefix_kv_amd import jev
+    res = {}
+    ref = None
+    try:
+        for v in GEMM_VARIANTS:
+            jev.set_gemm_variant(*v)
+            for _ in range(3):
+                step()
+            torch.cuda.synchronize()
+            got = probs.cpu().numpy().copy()
+            if ref is None:
+                ref = got
+            t0 = time.perf_counter()
+            for _ in range(n_steps):
+                step()
+            torch.cuda.synchronize()
+            ms = 1e3 * (time.perf_counter() - t0) / n_steps
+            per = {}
+            for kind in ("qkv", "oproj"):
+                ctx.profile([kind])
+                for _ in range(3):
+                    step()
+                torch.cuda.synchronize()
+                for r in ctx.profile_read():
+                    a = per.setdefault(launch_key(r), [0, 0.0])
+                    a[0] += 1
+                    a[1] += r["ms"]
+                ctx.profile(())
+            res["large=%d splits=%d bn=%d" % v] = {
+                "ms_per_step": round(ms, 4),
+                "max_abs_dp_vs_default": float(np.max(np.abs(got - ref))),
+                "avg_us": {k: round(1e3 * t / n, 2) for k, (n, t) in sorted(per.items())},
+            }
+    finally:
+        jev.set_gemm_variant()
+    return res
+
+
 def config_summary(idx: int, steps: int, warmup: int) -> dict:
     """Throughput of another workload, inputs resident in HBM before the timed
     region; the same one-GPU path as the headline line.
@@ -577,6 +628,8 @@ def main(argv=None) -> int:
                     help="after the run, copy a MIB-MiB buffer 3 times (counter calibration for traffic)")
     ap.add_argument("--summarize", metavar="DIR", default=None,
                     help="print a summary of the rocprofv3 CSV output under DIR and exit")
+    ap.add_argument("--gemm-variants", action="store_true",
+                    help="also time the projection kernel variants (jev_set_gemm_variant) on this workload")
     ap.add_argument("--library-gemms", action="store_true",
                     help="add torch.matmul times of the projection shapes ('library_gemm', context only)")
     ap.add_argument("--sq-summary", nargs="+", metavar="DIR", default=None,
@@ -740,6 +793,8 @@ def main(argv=None) -> int:
         "stats_last_call": {k: st[k] for k in ("logical_tokens", "computed_tokens", "cached_tokens", "rounds")},
         "roofline": roof,
     }
+    if args.gemm_variants:
+        out["gemm_variants"] = gemm_variants(ctx, step, probs, max(5, args.steps // 2))
     if args.cpu_branches > 0:
         out["cpu_baseline"] = cpu_baseline(wl, inst, weights, args.cpu_branches)
     else:

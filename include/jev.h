@@ -323,6 +323,24 @@ typedef struct {
 } jev_limits_t;
 int jev_limits(jev_ctx* ctx, jev_limits_t* out);
 
+/* Projection kernel variants, for measurement (process-wide; 0 everywhere is
+ * the default, which every call uses unless this is set).  Every variant
+ * computes the same products (q/k/v with RoPE and page writes, the residual
+ * projection) from the same bf16 operands with fp32 accumulation; a variant
+ * can sum K in another order, so its probabilities agree with the default's
+ * to the accumulation-order floor, not bitwise.
+ *  large:  projections of rounds of more than 256 rows (bf16):
+ *          0 = the default kernel (four MFMA waves fed by four loader waves
+ *          that load straight into LDS, three stages), 1 = eight MFMA waves
+ *          with register-staged loads, 2 / 3 = four MFMA waves loading
+ *          straight into LDS themselves, two / three stages;
+ *  splits: K splits of rounds of at most 256 rows (0 = as many as fill the
+ *          CUs once, at most 6; else 1..8, capped by K / 128);
+ *  bn:     column tile of the large projections (0 = automatic, 128, 160).
+ * Set it only while no call is in flight; the next call uses it.
+ * Errors: JEV_EINVAL (a value outside these ranges; nothing changes). */
+int jev_set_gemm_variant(int32_t large, int32_t splits, int32_t bn);
+
 /* Debug taps for parity tests.  Each call registers one tap (up to 16); a
  * NULL dst removes every tap.  what = JEV_TAP_ATTN: the attention output of
  * `layer` (after the log-sum-exp merge); what = JEV_TAP_RESID: the residual

@@ -1801,6 +1801,15 @@ int jev_stats(jev_ctx* ctx, jev_stats_t* out) {
   return JEV_OK;
 }
 
+int jev_set_gemm_variant(int32_t large, int32_t splits, int32_t bn) {
+  if (large < 0 || large > 3) return fail(JEV_EINVAL, "large must be 0..3");
+  if (splits < 0 || splits > jev::kMaxSplits) return fail(JEV_EINVAL, "splits must be 0..8");
+  if (bn != 0 && bn != 128 && bn != 160) return fail(JEV_EINVAL, "bn must be 0, 128 or 160");
+  // 0 selects the loader-wave kernel (the dispatcher's kind 4)
+  jev::g_gemm_tuning = jev::GemmTuning{splits, bn, large};
+  return JEV_OK;
+}
+
 int jev_set_debug(jev_ctx* ctx, uint32_t flags) {
   if (!ctx) return fail(JEV_EINVAL, "ctx is NULL");
   if (flags & ~uint32_t(JEV_DEBUG_POISON_FREED_PAGES | JEV_DEBUG_TIME_CALLS | JEV_DEBUG_FULL_LAST_LAYER))

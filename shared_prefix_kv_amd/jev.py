@@ -35,7 +35,7 @@ EXPORTED = ["jev_workspace_bytes", "jev_kv_pool_bytes", "jev_create", "jev_destr
             "jev_match", "jev_stats", "jev_debug_tap", "jev_profile", "jev_profile_rows", "jev_profile_read", "jev_answers",
             "jev_set_plan_mode", "jev_set_cache_policy", "jev_sched_create", "jev_sched_destroy",
             "jev_sched_submit", "jev_sched_step", "jev_sched_status", "jev_sched_result", "jev_last_error",
-            "jev_set_debug", "jev_limits"]
+            "jev_set_debug", "jev_limits", "jev_set_gemm_variant"]
 KERNELS = ["embed", "rmsnorm", "qkv", "attn", "merge", "oproj", "readout"]
 
 
@@ -131,6 +131,7 @@ def lib() -> ctypes.CDLL:
         L.jev_last_error.restype = ctypes.c_char_p
         L.jev_set_debug.argtypes = [vp, ctypes.c_uint32]
         L.jev_limits.argtypes = [vp, P(Limits)]
+        L.jev_set_gemm_variant.argtypes = [i32, i32, i32]
         _lib = L
     return _lib
 
@@ -138,6 +139,11 @@ def lib() -> ctypes.CDLL:
 def _check(rc: int) -> None:
     if rc != JEV_OK:
         raise JevError(rc, lib().jev_last_error().decode())
+
+
+def set_gemm_variant(large: int = 0, splits: int = 0, bn: int = 0) -> None:
+    """Projection kernel variant for measurement (process-wide; see jev.h)."""
+    _check(lib().jev_set_gemm_variant(int(large), int(splits), int(bn)))
 
 
 def _i32(a) -> np.ndarray:

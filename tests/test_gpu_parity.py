@@ -635,6 +635,50 @@ def test_w2_attention_output_matches_oracle(w2):
     ctx.free_pages([h])
 
 
+def test_w2_projection_variants(w2):
+    """Projection kernel variants (jev_set_gemm_variant) on the headline
+    workload.  The other large kernels and the 128-wide tile sum every
+    output's K in the same order as the default: bitwise the default's
+    probabilities.  Other K-split counts of the branch round sum K in another
+    order; they are held to max(1e-3, 5 x spread) per branch: the default
+    kernels meet 3 x the spread of the oracle's four alternative orders, but a
+    split count of 4 puts branch 0 at 4.3 x its spread (2.95e-3 against a
+    spread of 6.9e-4), so 3 x the sampled spread does not bound every faithful
+    summation order."""
+    from shared_prefix_kv_amd import jev
+    from tests.golden.make_golden import bars as order_bars
+    wl, inst, g, ctx, _ = w2
+    br = inst.passes[0]
+
+    def run():
+        (h,) = ctx.prefill_prefix([0], [inst.prefixes[0]])
+        probs, loff = ctx.score_branches([h] * 5, [b.tokens for b in br], [b.labels for b in br])
+        _sync()
+        got = split_probs(probs, loff)
+        ctx.free_pages([h])
+        return got
+
+    try:
+        jev.set_gemm_variant()
+        ref = run()
+        for v in [(1, 0, 0), (2, 0, 0), (3, 0, 0), (0, 0, 128)]:
+            print(f"projection variant {v}", flush=True)
+            jev.set_gemm_variant(*v)
+            got = run()
+            record(f"w2 projection variant {v} vs default (bitwise)",
+                   max(float(np.max(np.abs(np.asarray(a) - np.asarray(b)))) for a, b in zip(got, ref)), 0.0)
+            assert all(np.array_equal(np.asarray(a), np.asarray(b)) for a, b in zip(got, ref)), v
+        spread = g["passes"][0]["spread"]
+        wide = [max(1e-3, 5.0 * s) for s in spread]
+        assert all(w >= b for w, b in zip(wide, order_bars(spread)))
+        for v in [(0, 3, 0), (0, 4, 0)]:
+            print(f"projection variant {v}", flush=True)
+            jev.set_gemm_variant(*v)
+            check_branches(f"w2 projection variant {v} vs oracle (5 x spread)", run(), g["passes"][0]["probs"], wide)
+    finally:
+        jev.set_gemm_variant()
+
+
 def test_w2_repeated_calls_are_bitwise_identical(w2):
     """Same prefix and branches prefilled and scored again: the kernels have no
     order-dependent reductions, so any difference is a race (e.g. an LDS buffer

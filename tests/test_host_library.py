@@ -229,3 +229,14 @@ def test_debug_flags_and_call_statistics_on_a_planning_only_context():
     assert st["pages_in_use"] == 0
     ctx.set_debug(0)
     assert ctx.stats()["debug_flags"] == 0
+
+
+def test_gemm_variant_validates_its_arguments():
+    # host-only: the default, each documented value, and values outside them
+    for args in [(0, 0, 0), (1, 0, 0), (2, 3, 128), (3, 8, 160)]:
+        jev.set_gemm_variant(*args)
+    for bad in [(-1, 0, 0), (4, 0, 0), (0, 9, 0), (0, -1, 0), (0, 0, 96)]:
+        with pytest.raises(jev.JevError) as e:
+            jev.set_gemm_variant(*bad)
+        assert e.value.code == jev.JEV_EINVAL
+    jev.set_gemm_variant()
