@@ -628,6 +628,8 @@ def main(argv=None) -> int:
                     help="after the run, copy a MIB-MiB buffer 3 times (counter calibration for traffic)")
     ap.add_argument("--summarize", metavar="DIR", default=None,
                     help="print a summary of the rocprofv3 CSV output under DIR and exit")
+    ap.add_argument("--round-invariant", action="store_true",
+                    help="run with round-invariant numerics (jev_set_round_invariant); noted in config")
     ap.add_argument("--gemm-variants", action="store_true",
                     help="also time the projection kernel variants (jev_set_gemm_variant) on this workload")
     ap.add_argument("--library-gemms", action="store_true",
@@ -671,6 +673,8 @@ def main(argv=None) -> int:
     desc = jev.make_desc(m.n_layers, m.d, m.hq, m.hkv, m.dh, m.vocab, m.dtype, m.rope_theta, m.eps,
                          max_pos, max_tok)
     ctx = jev.Context(desc, n_pages, wdev)
+    if args.round_invariant:
+        ctx.set_round_invariant(True)
     suffixes = [b.tokens for b in br]
     labels = [b.labels for b in br]
     n_lab = sum(len(l) for l in labels)
@@ -778,7 +782,8 @@ def main(argv=None) -> int:
         "config": {"workload": wl.name, "prefix_tokens": [len(p) for p in prefixes], "branches": n_br,
                    "suffix_tokens": len(br[0].tokens), "labels_per_branch": len(labels[0]),
                    "layers": m.n_layers, "d_model": m.d, "q_heads": m.hq, "kv_heads": m.hkv,
-                   "head_dim": m.dh, "vocab": m.vocab, "page_tokens": 16},
+                   "head_dim": m.dh, "vocab": m.vocab, "page_tokens": 16,
+                   "numerics": "round-invariant" if args.round_invariant else "default"},
         "effective_prefill_tok_s": round(logical * args.steps / elapsed, 1),
         "computed_tok_s": round(computed * args.steps / elapsed, 1),
         "phases": {

@@ -198,6 +198,22 @@ int jev_score_candidates(jev_ctx* ctx, int32_t n, const int32_t* tokens, const i
 enum { JEV_PLAN_DEPTH = 0, JEV_PLAN_CANDIDATE_FIRST = 1 };
 int jev_set_plan_mode(jev_ctx* ctx, int32_t mode);
 
+/* Round-invariant numerics on this context (0 off, the default; 1 on).  By
+ * default a token's values depend, within the accumulation-order floor, on
+ * the round it is computed in: rounds of at most 256 rows split the
+ * projections' K over workgroups and larger ones do not, and the number of
+ * prefix chunks, the split of long causal tiles and the attention's wave
+ * groups follow the round's occupancy.  With this on, every projection sums K
+ * in the large rounds' order (no K split; the residual projection and the
+ * next layer's norm as two kernels), prefix chunks are 32 pages (more when a
+ * prefix would need over 8), long causal tiles are not split, and every round
+ * splits each tile's steps over two wave groups: a token's K/V, attention
+ * output and probabilities are then bitwise the same whichever round
+ * computes it (both plan orders, any batch), at the cost of speed in rounds
+ * of at most 256 rows.  Takes effect at the next call.
+ * Errors: JEV_EINVAL (NULL ctx, on not 0 or 1). */
+int jev_set_round_invariant(jev_ctx* ctx, int32_t on);
+
 /* What happens to a prefix whose last caller reference is dropped
  * (openjev-multimodal performance page, repeated-state section: the KV at the
  * end of a state is kept for the next request that repeats it, and several

@@ -54,6 +54,8 @@ constexpr int kRowsPerTile = 128;
 // attention rounds whose longest tile has at least this many pages run two
 // wave groups per workgroup
 constexpr int32_t kTwoGroupPages = 48;
+// prefix chunk length of round-invariant numerics (jev_set_round_invariant)
+constexpr int64_t kInvariantChunkPages = 32;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -183,6 +185,7 @@ struct jev_ctx {
   bool dry = true;
   bool dead = false;
   jev::PlanMode plan_mode = jev::PlanMode::DEPTH;
+  bool round_invariant = false;  // jev_set_round_invariant
   uint64_t clock = 0;  // stamp of the last call (cache recency)
   jev::ModelDims dims{};
   std::vector<jev::LayerW> layers;
@@ -562,7 +565,7 @@ int build_round(jev_ctx* ctx, std::vector<RNode>& nodes, std::vector<int32_t>& h
     max_own_pages = std::max<int64_t>(max_own_pages, (nd.n + jev::kPage - 1) / jev::kPage);
   }
   int64_t cpo = INT64_MAX;
-  if (n_own_tiles * ctx->desc.n_kv_heads < kSplitTilesBelow && max_own_pages >= 32) {
+  if (!ctx->round_invariant && n_own_tiles * ctx->desc.n_kv_heads < kSplitTilesBelow && max_own_pages >= 32) {
     cpo = (max_own_pages + 1) / 2;
     cpo += cpo & 1;
   }
@@ -638,6 +641,11 @@ int build_round(jev_ctx* ctx, std::vector<RNode>& nodes, std::vector<int32_t>& h
       const int64_t r0 = grows[gi].first, r1 = grows[gi].second;
       if (g.anc_pages == 0 || r1 <= r0) continue;
       int64_t cp = (g.anc_pages + n_chunks - 1) / n_chunks;
+      if (ctx->round_invariant) {
+        // chunks set by the prefix alone: kInvariantChunkPages pages, more
+        // when that would exceed the merge's chunk count
+        cp = std::max<int64_t>(kInvariantChunkPages, (g.anc_pages + jev::kMaxAncParts - 1) / jev::kMaxAncParts);
+      }
       cp += cp & 1;  // whole two-page steps per chunk
       const int64_t nch = (g.anc_pages + cp - 1) / cp;
       int64_t anc_keys = 0;
@@ -696,6 +704,9 @@ int build_round(jev_ctx* ctx, std::vector<RNode>& nodes, std::vector<int32_t>& h
   // a round whose longest tile has many steps splits every tile's steps over
   // two wave groups, halving the chain that sets the kernel's length
   rd->attn_groups = (!full.tiles.empty() && full.tiles.front().n_pages >= kTwoGroupPages) ? 2 : 1;
+  // round-invariant numerics: every round splits each tile's steps over two
+  // groups (a split that depends on the tile alone)
+  if (ctx->round_invariant) rd->attn_groups = 2;
   rd->off_tiles = push(int64_t(full.tiles.size()) * 8);
   std::memcpy(hb.data() + rd->off_tiles, full.tiles.data(), full.tiles.size() * sizeof(jev::AttnTile));
   rd->n_merge = int32_t(full.merges.size());
@@ -815,7 +826,8 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
   float* rope = reinterpret_cast<float*>(ctx->ws + ctx->L.rope);
   float* part_o = sc.part_o;
   float* part_lse = sc.part_lse;
-  const jev::GemmWs gws = sc.gemm;
+  jev::GemmWs gws = sc.gemm;
+  gws.no_split = ctx->round_invariant;
   const size_t elt = size_t(elt_size(ctx->desc));
   // times one launch with events when its kind is being profiled
   auto timed = [&](int kind, int layer, int64_t rows, double flops, double bytes, auto&& launch) -> hipError_t {
@@ -919,7 +931,7 @@ int run_rounds(jev_ctx* ctx, const std::vector<RoundDesc>& rds, const std::vecto
                                    part_o, part_lse, o, s);
         }));
       if (int rc = tap(JEV_TAP_ATTN, l, o, rd.T, size_t(m.hq) * m.dh)) return rc;
-      if (rd.T <= jev::kSplitRows && l + 1 < m.n_layers) {
+      if (rd.T <= jev::kSplitRows && l + 1 < m.n_layers && !ctx->round_invariant) {
         // split-K projection whose residual epilogue also writes the next
         // layer's normalised input (one launch fewer per layer)
         HIPCHK(timed(JEV_K_OPROJ, l, rd.T, 2 * T * D * HD, (T * HD + D * HD + 2 * T * D) * E, [&] {
@@ -1798,6 +1810,13 @@ int jev_stats(jev_ctx* ctx, jev_stats_t* out) {
     ctx->stats.last_branch_ms = br;
   }
   *out = ctx->stats;
+  return JEV_OK;
+}
+
+int jev_set_round_invariant(jev_ctx* ctx, int32_t on) {
+  if (!ctx) return fail(JEV_EINVAL, "ctx is NULL");
+  if (on != 0 && on != 1) return fail(JEV_EINVAL, "on must be 0 or 1");
+  ctx->round_invariant = on != 0;
   return JEV_OK;
 }
 

@@ -1002,7 +1002,7 @@ template <typename T, int EPI>
 hipError_t gemm_dispatch(const ModelDims& m, const GemmWs& ws, const void* A, int M, int K, int N,
                          const dev::ColMap& cm, const dev::QkvOut& qo, const dev::ResOut& ro, hipStream_t s) {
   const T* a = reinterpret_cast<const T*>(A);
-  if (M <= kSplitRows) {
+  if (M <= kSplitRows && !ws.no_split) {
     // split K so that the column tiles times the splits fill the CUs once
     constexpr int BN = 128;
     if (N % BN) return hipErrorInvalidValue;

@@ -63,6 +63,9 @@ constexpr int kSplitRows = 256;
 struct GemmWs {
   float* partial;
   size_t partial_elems;
+  // rounds of at most kSplitRows rows too project without a K split, with the
+  // large rounds' K order (round-invariant numerics)
+  bool no_split = false;
 };
 
 // Timing of the next launcher call (profiling): its first kernel records

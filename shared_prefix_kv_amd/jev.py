@@ -35,7 +35,7 @@ EXPORTED = ["jev_workspace_bytes", "jev_kv_pool_bytes", "jev_create", "jev_destr
             "jev_match", "jev_stats", "jev_debug_tap", "jev_profile", "jev_profile_rows", "jev_profile_read", "jev_answers",
             "jev_set_plan_mode", "jev_set_cache_policy", "jev_sched_create", "jev_sched_destroy",
             "jev_sched_submit", "jev_sched_step", "jev_sched_status", "jev_sched_result", "jev_last_error",
-            "jev_set_debug", "jev_limits", "jev_set_gemm_variant"]
+            "jev_set_debug", "jev_limits", "jev_set_gemm_variant", "jev_set_round_invariant"]
 KERNELS = ["embed", "rmsnorm", "qkv", "attn", "merge", "oproj", "readout"]
 
 
@@ -132,6 +132,7 @@ def lib() -> ctypes.CDLL:
         L.jev_set_debug.argtypes = [vp, ctypes.c_uint32]
         L.jev_limits.argtypes = [vp, P(Limits)]
         L.jev_set_gemm_variant.argtypes = [i32, i32, i32]
+        L.jev_set_round_invariant.argtypes = [vp, i32]
         _lib = L
     return _lib
 
@@ -308,6 +309,10 @@ class Context:
     def set_cache_policy(self, policy: int) -> None:
         """JEV_CACHE_RELEASE or JEV_CACHE_LRU (jev_set_cache_policy)."""
         _check(lib().jev_set_cache_policy(self.ctx, policy))
+
+    def set_round_invariant(self, on: bool) -> None:
+        """Round-invariant numerics (jev_set_round_invariant)."""
+        _check(lib().jev_set_round_invariant(self.ctx, int(bool(on))))
 
     def set_debug(self, flags: int) -> None:
         """JEV_DEBUG_* bit flags (jev_set_debug); 0 turns them off."""

@@ -872,6 +872,79 @@ def test_w3_staged_rounds_match_oracle(w2):
     assert np.array_equal(probs4.cpu().numpy(), probs.cpu().numpy())
 
 
+def _bitwise(what, got, ref):
+    record(f"{what} (bitwise)",
+           max(float(np.max(np.abs(np.asarray(a) - np.asarray(b)))) for a, b in zip(got, ref)), 0.0)
+    assert all(np.array_equal(np.asarray(a), np.asarray(b)) for a, b in zip(got, ref)), what
+
+
+def test_w2_round_invariant_round_size_is_bitwise(w2):
+    """Round-invariant numerics (jev_set_round_invariant): the same five
+    branches in a round of their own (240 rows) and with a sixth that takes
+    the round past 256 rows give bitwise the same probabilities (the default
+    numerics move them by up to 2.1e-3, see the round-size test), and stay
+    within the per-branch bars of the oracle."""
+    wl, inst, g, ctx, _ = w2
+    br = inst.passes[0]
+    bars = stored_bars(g)
+    ctx.set_round_invariant(True)
+    try:
+        (h,) = ctx.prefill_prefix([0], [inst.prefixes[0]])
+        probs, loff = ctx.score_branches([h] * 5, [b.tokens for b in br], [b.labels for b in br])
+        _sync()
+        alone = split_probs(probs, loff)
+        extra = list(br[0].tokens[:32])
+        probs2, loff2 = ctx.score_branches([h] * 6, [b.tokens for b in br] + [extra],
+                                           [b.labels for b in br] + [br[0].labels])
+        _sync()
+        ctx.free_pages([h])
+        check_branches("w2 round-invariant, 240-row round vs oracle", alone, g["passes"][0]["probs"], bars)
+        _bitwise("w2 round-invariant, 272-row vs 240-row round", split_probs(probs2, loff2)[:5], alone)
+    finally:
+        ctx.set_round_invariant(False)
+
+
+def test_w3_round_invariant_plan_orders_are_bitwise(w2):
+    """Round-invariant numerics on workload 3: depth rounds and the page's
+    candidate-first rounds compute the same nodes in other round
+    compositions; with the mode on they give bitwise the same probabilities,
+    within the per-branch bars of the oracle."""
+    from shared_prefix_kv_amd import jev
+    g = golden(3)
+    wl = workload(3)
+    inst = make_instance(wl)
+    ctx, _ = device_context(3, n_pages=1024, max_pos=4096, max_tok=4096)
+    ctx.set_round_invariant(True)
+    probs, loff = ctx.score_candidates(inst.candidates, inst.cand_labels)
+    _sync()
+    dep = split_probs(probs, loff)
+    check_branches("w3 round-invariant depth rounds vs oracle", dep, g["passes"][0]["probs"], stored_bars(g))
+    ctx.set_plan_mode(jev.JEV_PLAN_CANDIDATE_FIRST)
+    probs2, loff2 = ctx.score_candidates(inst.candidates, inst.cand_labels)
+    _sync()
+    _bitwise("w3 round-invariant, candidate-first vs depth rounds", split_probs(probs2, loff2), dep)
+    assert ctx.stats()["pages_in_use"] == 0
+
+
+def test_w7_round_invariant_plan_orders_are_bitwise_float32():
+    """The same on the float32 tree: both plan orders bitwise equal, and
+    within 1e-5 of the oracle."""
+    from shared_prefix_kv_amd import jev
+    wl = workload(7)
+    inst = make_instance(wl)
+    ref = om.score_from_scratch(om.from_weights(host_weights(7)), inst.candidates, inst.cand_labels)
+    ctx, _ = device_context(7, n_pages=256, max_pos=2048, max_tok=2048)
+    ctx.set_round_invariant(True)
+    runs = []
+    for mode in (jev.JEV_PLAN_DEPTH, jev.JEV_PLAN_CANDIDATE_FIRST):
+        ctx.set_plan_mode(mode)
+        probs, loff = ctx.score_candidates(inst.candidates, inst.cand_labels)
+        _sync()
+        runs.append(split_probs(probs, loff))
+        close(f"w7 round-invariant, plan mode {mode}", runs[-1], ref, TOL_F32)
+    _bitwise("w7 round-invariant, candidate-first vs depth rounds", runs[1], runs[0])
+
+
 def test_w3_requests_through_the_continuous_batching_scheduler(w2):
     """Workload 3's candidates as two requests, the second submitted after the
     first step: every distribution matches the stored oracle values, and the

@@ -240,3 +240,21 @@ def test_gemm_variant_validates_its_arguments():
             jev.set_gemm_variant(*bad)
         assert e.value.code == jev.JEV_EINVAL
     jev.set_gemm_variant()
+
+
+def test_round_invariant_mode_validates_and_keeps_plans():
+    # host-only: the setter's errors, and the staged-round plan is the same
+    # with the mode on (it changes only how the rounds' kernels sum)
+    wl = workload(3)
+    inst = make_instance(wl)
+    ctx = dry(wl, 4096)
+    seqs = [s for s, _ in inst.full_sequences(0)]
+    before = ctx.plan(seqs)
+    ctx.set_round_invariant(True)
+    assert ctx.plan(seqs) == before
+    for bad in (2, -1):
+        with pytest.raises(jev.JevError) as e:
+            jev._check(jev.lib().jev_set_round_invariant(ctx.ctx, bad))
+        assert e.value.code == jev.JEV_EINVAL
+    ctx.set_round_invariant(False)
+    ctx.close()
