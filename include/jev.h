@@ -331,7 +331,8 @@ typedef struct {
   int32_t max_positions;        /* longest sequence (prefix + suffix), from the model description */
   int32_t max_round_tokens;     /* most tokens computed in one round */
   int32_t n_pages;              /* KV pages of the pool */
-  int32_t split_k_rows;         /* rounds of at most this many rows split the projections' K */
+  int32_t split_k_rows;         /* rounds of at most this many rows split the projections' K
+                                   (0: none does, with round-invariant numerics) */
   int32_t max_tile_pages;       /* longest key list of one attention tile */
   int64_t noalloc_scratch_bytes;     /* static scratch of jev_score_branches_noalloc (per device) */
   int64_t noalloc_partial_rows;      /* attention partial-state rows it holds for this model (0: dry context) */

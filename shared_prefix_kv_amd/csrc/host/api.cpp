@@ -1847,7 +1847,7 @@ int jev_limits(jev_ctx* ctx, jev_limits_t* out) {
   l.max_positions = ctx->desc.max_positions;
   l.max_round_tokens = ctx->desc.max_round_tokens;
   l.n_pages = ctx->pages.n_total();
-  l.split_k_rows = jev::kSplitRows;
+  l.split_k_rows = ctx->round_invariant ? 0 : jev::kSplitRows;
   l.max_tile_pages = jev::kMaxTilePages;
   l.noalloc_scratch_bytes = int64_t(kNoAllocScratchBytes);
   l.noalloc_partial_rows = ctx->dry ? 0 : noalloc_rows(ctx);

@@ -250,8 +250,10 @@ def test_round_invariant_mode_validates_and_keeps_plans():
     ctx = dry(wl, 4096)
     seqs = [s for s, _ in inst.full_sequences(0)]
     before = ctx.plan(seqs)
+    assert ctx.limits()["split_k_rows"] == 256
     ctx.set_round_invariant(True)
     assert ctx.plan(seqs) == before
+    assert ctx.limits()["split_k_rows"] == 0
     for bad in (2, -1):
         with pytest.raises(jev.JevError) as e:
             jev._check(jev.lib().jev_set_round_invariant(ctx.ctx, bad))
